@@ -1,0 +1,188 @@
+/*
+ * zha.h - C ABI of the ZHA hot-path library for AMD Instinct MI355X (gfx950).
+ *
+ * Zyphra Hierarchical Attention ("Subquadratic Attention with a Hierarchical
+ * Tree-Structured Indexer") replaces dense decode attention by three steps,
+ * each one entry point here:
+ *
+ *   zha_build         tree of recursively compressed key summaries over a KV
+ *                     cache (paper §III-A "Tree Construction", App. D-B2);
+ *   zha_route         top-down routing of every query head through its KV
+ *                     head's tree, keeping at each level the smallest top-p
+ *                     set of the frontier (paper §III-C; the summary page's
+ *                     "Routing": m_ell(q) and the final index set I(q));
+ *   zha_attn          exact softmax attention over the surviving tokens,
+ *                     o(q) = Attn(q, K_I(q), V_I(q)) (summary page "Routing").
+ *
+ * plus zha_dense_decode, full attention over every cached key, the baseline
+ * the sparse path is measured against (paper App. D-A, dense decode model).
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Pointers named as device buffers must be device memory (or memory mapped
+ *   for the device); the caller owns every buffer.  The library never
+ *   allocates, never synchronises, and keeps no state between calls.  Calls
+ *   are asynchronous on `stream` (a hipStream_t; NULL is the null stream).
+ * - Return value 0 is success.  A negative value is an error detected on the
+ *   host before anything is launched (ZHA_ERR_*); nothing has been written.
+ *   zha_strerror() names it.  ZHA_ERR_LAUNCH reports a failed kernel launch.
+ * - Layouts are dense, row-major, head dimension fastest:
+ *     K, V   [B, H_kv, T, d]      storage dtype
+ *     Q, O   [B, n_pos, H_q, d]   storage dtype
+ *   Query head h reads KV head h / (H_q / H_kv).  Each (b, kvh) pair owns one
+ *   tree; its G = H_q / H_kv query heads share it (paper §III-B).
+ * - All n_pos positions of a call attend to the same T cached keys.
+ *
+ * Geometry (zha_geom): n_l = floor(T / C^l) full nodes at level l = 1..L;
+ * level 1 nodes are chunks of C consecutive keys, a level-l node has the C
+ * level-(l-1) nodes below it as children.  Requirements: B, H_q, H_kv >= 1,
+ * H_q % H_kv == 0, d in {64, 128, 256}, 2 <= C <= 1024, 1 <= L <= 16,
+ * 1 <= R <= 16, n_L >= 1 (T >= C^L), T < 2^31 * C.
+ */
+#ifndef ZHA_H
+#define ZHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtype of K, V, Q, O and of the stored summary keys k_hat. */
+enum { ZHA_F32 = 0, ZHA_BF16 = 1 };
+
+enum {
+  ZHA_OK = 0,
+  ZHA_ERR_NULL = -1,   /* a required pointer is NULL */
+  ZHA_ERR_GEOM = -2,   /* geometry violates the requirements above */
+  ZHA_ERR_DTYPE = -3,  /* dtype is not ZHA_F32 / ZHA_BF16 */
+  ZHA_ERR_DIM = -4,    /* head dimension d not supported */
+  ZHA_ERR_P = -5,      /* p is not in (0, 1] (or is NaN) */
+  ZHA_ERR_ALIGN = -6,  /* a buffer is not 16-byte aligned */
+  ZHA_ERR_CAP = -7,    /* cap < 1 */
+  ZHA_ERR_LAUNCH = -8, /* a kernel launch failed */
+  ZHA_ERR_NPOS = -9    /* n_pos < 1 */
+};
+
+typedef struct {
+  int32_t B;     /* sequences */
+  int32_t H_q;   /* query heads */
+  int32_t H_kv;  /* key/value heads (one tree each) */
+  int32_t d;     /* head dimension */
+  int64_t T;     /* cached tokens per sequence */
+  int32_t C;     /* chunk size = children per node */
+  int32_t L;     /* tree depth */
+  int32_t R;     /* reference queries per tree */
+  int32_t dtype; /* ZHA_F32 or ZHA_BF16 */
+} zha_geom;
+
+/* Human-readable text for a return code. */
+const char* zha_strerror(int code);
+
+/* ---------------------------------------------------------------------------
+ * Tree blob
+ *
+ * For each (b, kvh), at byte offset (b * H_kv + kvh) * tree_stride, the tree
+ * holds for every level l = 1..L:
+ *   k_hat_l [n_l, R, d]  storage dtype, at khat_offset(l)
+ *   b_hat_l [n_l, R]     fp32,          at bhat_offset(l)
+ * Every array starts on a 256-byte boundary.  k_hat_{l,i,r} is the tangent
+ * summary of node i for reference r, rounded to nearest-even from the exact
+ * value; b_hat is the matching bias rounded to fp32 (paper §III-A: t_r(q) =
+ * q . k_hat_r / sqrt(d) + b_hat_r).
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the tree blob and of the zha_build scratch buffer. */
+int zha_tree_bytes(const zha_geom* g, size_t* tree_bytes, size_t* build_scratch_bytes);
+
+/* Byte offsets, inside one tree, of level `level` (1..L) and the per-tree stride. */
+int zha_tree_level_offset(const zha_geom* g, int32_t level, size_t* khat_offset,
+                          size_t* bhat_offset, size_t* tree_stride);
+
+/* Build every tree (paper §III-A recursive summaries; App. D-B2 baseline merge).
+ *   K       device [B, H_kv, T, d] storage dtype
+ *   qref    device [H_kv, R, d] fp32 reference queries (all zero gives the
+ *           plain mean of each span's keys, with b_hat = ln(span))
+ *   tree    device, zha_tree_bytes() bytes, written
+ *   scratch device, build_scratch_bytes, clobbered
+ * Leaves: F = LSE_j(q_r . k_j / sqrt(d)), k_hat = softmax-weighted key mean,
+ * b_hat = F - q_r . k_hat / sqrt(d).  Parents, per reference: F_P = LSE_c F_c,
+ * k_hat_P = sum_c exp(F_c - F_P) k_hat_c.  Accumulation is fp64, so the stored
+ * copies are the correctly rounded values of the exact summaries. */
+int zha_build(const zha_geom* g, const void* K, const float* qref, void* tree, void* scratch,
+              void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Routing (paper §III-C; summary page "Routing")
+ *
+ * For every query head, from the top level down: the frontier starts as all
+ * n_L top nodes; each candidate i is scored s_i = max_r (q . k_hat_{r,i} /
+ * sqrt(d) + b_hat_{r,i}); candidates are ordered by score, descending, ties
+ * to the lower node id; the kept set S_l is the shortest prefix whose share
+ * of sum_i exp(s_i) over the frontier reaches p (p == 1 keeps all); the next
+ * frontier is the children of S_l, ascending, followed by the level-(l-1)
+ * nodes whose parent is incomplete (paper App. E-E).
+ * ------------------------------------------------------------------------- */
+
+/* Scratch bytes zha_route needs (0 is a valid answer: pass any pointer). */
+int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes);
+
+/*   tree        device, built by zha_build for the same geometry
+ *   Q           device [B, n_pos, H_q, d] storage dtype
+ *   p           top-p threshold in (0, 1]
+ *   sel         device [B, n_pos, H_q, cap] int32, written: the level-1 chunk
+ *               ids of S_1 in ascending order; entries past min(cnt, cap) are
+ *               left untouched
+ *   cnt         device [B, n_pos, H_q] int32, written: |S_1|, the true count
+ *               even when it exceeds cap (then sel holds the cap lowest ids);
+ *               -1 if a frontier exceeded the router's capacity
+ *               (zha_route_frontier_capacity())
+ *   level_stats device [B, n_pos, H_q, L, 2] int32 or NULL: for level l at
+ *               index l-1, (frontier size K_l, kept count |S_l|)
+ *   gap         device [B, n_pos, H_q, L] fp32 or NULL: s_(m) - s_(m+1) at
+ *               each level's cut, +inf when the whole frontier is kept
+ *   scratch     device, zha_route_scratch_bytes() bytes */
+int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos, float p,
+              int32_t* sel, int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap,
+              void* scratch, void* stream);
+
+/* Largest frontier (candidates at one level of one query head) zha_route handles. */
+int32_t zha_route_frontier_capacity(void);
+
+/* ---------------------------------------------------------------------------
+ * Sparse attention (summary page "Routing": I(q) and o(q))
+ *
+ * For query head h at position t, the attended token set is
+ *   I = {0} U {c*C .. c*C + C - 1 : c in sel[.., :cnt]} U [n_1*C, T)
+ * (token 0 is the attention sink, counted once; the tail after the last full
+ * chunk is the current partial chunk) and
+ *   O = sum_{j in I} softmax_j(q . k_j / sqrt(d)) v_j
+ * computed with fp32 arithmetic and rounded nearest-even to the storage dtype.
+ * ------------------------------------------------------------------------- */
+
+int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes);
+
+/*   Q, K, V  device, layouts above
+ *   sel, cnt device, as written by zha_route (ascending, distinct ids < n_1)
+ *   O        device [B, n_pos, H_q, d], written; rows whose cnt is negative or
+ *            exceeds cap are written as NaN
+ *   scratch  device, zha_attn_scratch_bytes() bytes */
+int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, const void* V,
+             const int32_t* sel, const int32_t* cnt, int32_t cap, void* O, void* scratch,
+             void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Dense decode baseline: O = softmax(q K^T / sqrt(d)) V over all T keys.
+ * ------------------------------------------------------------------------- */
+
+int zha_dense_decode_scratch_bytes(const zha_geom* g, int32_t n_pos, size_t* bytes);
+
+int zha_dense_decode(const zha_geom* g, const void* Q, int32_t n_pos, const void* K,
+                     const void* V, void* O, void* scratch, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZHA_H */

@@ -135,15 +135,19 @@ def merge_summaries(F_child, k_child, qref):
     F_child: [n, C, R], k_child: [n, C, R, d].  Per reference r, independently:
       F_P = LSE_c F_c,  k_hat_P = sum_c exp(F_c - F_P) k_hat_c,
       b_hat_P = F_P - q_r . k_hat_P / sqrt(d).
+    The sum is evaluated the way App. D-B2 keeps its statistics, a maximum m and a weight sum
+    Z = sum_c exp(F_c - m): k_hat_P = sum_c exp(F_c - m) k_hat_c / Z and F_P = m + ln Z (the
+    same quantity; with equal child masses every weight is exactly 1).
     """
     F_child = np.asarray(F_child, np.float64)
     k_child = np.asarray(k_child, np.float64)
     qref = np.asarray(qref, np.float64)
     d = k_child.shape[-1]
     m = F_child.max(axis=1, keepdims=True)  # [n, 1, R]
-    F_P = m[:, 0, :] + np.log(np.exp(F_child - m).sum(axis=1))  # [n, R]
-    a = np.exp(F_child - F_P[:, None, :])  # [n, C, R]
-    k_P = np.einsum("ncr,ncrd->nrd", a, k_child)
+    e = np.exp(F_child - m)  # [n, C, R]
+    Z = e.sum(axis=1)  # [n, R]
+    F_P = m[:, 0, :] + np.log(Z)
+    k_P = np.einsum("ncr,ncrd->nrd", e, k_child) / Z[..., None]
     b_P = F_P - np.einsum("nrd,rd->nr", k_P, qref) / math.sqrt(d)
     return F_P, k_P, b_P
 

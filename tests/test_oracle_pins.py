@@ -412,3 +412,20 @@ def test_golden_reference_queries_are_per_kv_group():
                  R=gold["R"])
     K, _ = W.make_kv(g, want_v=False)
     assert W.make_qref(g, K).size * gold["sparse_layers"] == gold["trainable_params"]
+
+
+def test_zero_reference_tree_stores_correctly_rounded_exact_means():
+    # With q_ref = 0 every level's k_hat is the exact mean of its span (sums of bf16 values are
+    # exact in fp64 and C is a power of two), so the stored copy is that mean rounded once.
+    C, L, d = 4, 3, 8
+    g = rng(33)
+    keys = W.bf16_bits_to_f32(W.f32_to_bf16_bits(g.standard_normal((C ** L * 2, d)).astype(
+        np.float32))).astype(np.float64)
+    tree = O.build_tree(keys, np.zeros((1, d)), C, L, O.BF16)
+    for ell in range(1, L + 1):
+        span = C ** ell
+        exact = keys.reshape(-1, span, d).sum(axis=1) / span  # exact: few-bit sums, 2^k divisor
+        np.testing.assert_array_equal(tree.levels[ell - 1].k_hat[:, 0], exact)
+        np.testing.assert_array_equal(tree.levels[ell - 1].k_store[:, 0], O.round_to_bf16(exact))
+        np.testing.assert_array_equal(tree.levels[ell - 1].b_store[:, 0],
+                                      np.float64(np.float32(math.log(span))))
