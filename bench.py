@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""ZHA decode benchmark on one MI355X.
+
+A step is one decode step of the whole hot path over one batch: zha_route
+(top-down top-p routing of every query head through its tree) followed by
+zha_attn (exact attention over the routed tokens), on seeded synthetic inputs
+already resident in HBM.  The tree is built once before timing (its time is
+reported separately).  Default workload: deep-tree decode at 256K context,
+B = 8 sequences, 32 query heads over 4 KV heads, d = 128, C = 8, L = 6,
+p = 0.95, bf16.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from hierarchical_tree_indexed_04_amd import workload as W  # noqa: E402
+
+METRIC = "ZHA decode queries/sec per layer at 256K and 1M ctx; % of HBM peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample, over host cores.
+# ----------------------------------------------------------------------------
+_CB = None
+
+
+def _cb_head(item):
+    import oracle as O
+    g, trees, Kf, Vf = _CB
+    q, kvh = item
+    r = O.route(trees[kvh], q, g.p)
+    O.attend(q, Kf[kvh], Vf[kvh], O.token_set(r.S1, g.C, g.T))
+    return 1
+
+
+def cpu_baseline(g, K, V, seconds: float, procs: int):
+    """Oracle route + attention per query head of sequence 0; rate in queries/s."""
+    global _CB
+    import multiprocessing as mp
+
+    import oracle as O
+    trees, Kf, Vf = {}, {}, {}
+    for kvh in range(g.H_kv):
+        Kf[kvh] = W.to_float(K[0, kvh], g.dtype)
+        Vf[kvh] = W.to_float(V[0, kvh], g.dtype)
+        trees[kvh] = O.build_tree(Kf[kvh].astype(np.float64), np.zeros((1, g.d)), g.C, g.L, g.dtype)
+    items = []
+    for step in range(1024):
+        Q = W.make_queries(g, K, step)
+        for h in range(g.H_q):
+            items.append((W.to_float(Q[0, h], g.dtype), h // g.G))
+    _CB = (g, trees, Kf, Vf)
+    ctx = mp.get_context("fork")
+    done = 0
+    with ctx.Pool(procs) as pool:
+        t0 = time.perf_counter()
+        for _ in pool.imap_unordered(_cb_head, items, chunksize=2):
+            done += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        elapsed = time.perf_counter() - t0
+        pool.terminate()
+    _CB = None
+    heads_per_s = done / elapsed
+    return {"value": heads_per_s / g.H_q, "unit": "queries/s", "cores": procs, "kind": "oracle",
+            "sample": f"{done} query heads (sequence 0, decode steps in order, all {g.H_q} heads "
+                      f"per step) of the same workload, fp64 NumPy route + attention, "
+                      f"{elapsed:.1f} s wall over {procs} processes; tree build excluded"}
+
+
+# ----------------------------------------------------------------------------
+# Byte accounting (algorithmic bytes, per step)
+# ----------------------------------------------------------------------------
+
+def step_bytes(g, sel, cnt, stats):
+    """Bytes the routing and the sparse gather must touch in one step.
+
+    Attention: K and V rows of the attended tokens, counted once per KV head (union over the
+    G query heads of the group, the minimum any implementation moves) and summed per head;
+    plus each head's query read, output write and chunk-list read.  Routing: per query head,
+    the summary row (R d storage elements + R fp32 biases) of every candidate at every level,
+    the query, and the route outputs.
+    """
+    s = g.elem_bytes
+    row_kv = 2 * g.d * s
+    n1 = g.n_level(1)
+    tail = g.T - n1 * g.C
+    attn_union = attn_sum = 0
+    heads = g.B * g.H_q
+    for b in range(g.B):
+        for kvh in range(g.H_kv):
+            ids = []
+            for h in range(kvh * g.G, (kvh + 1) * g.G):
+                c = int(cnt[b, 0, h])
+                ch = sel[b, 0, h, :c]
+                ids.append(ch)
+                toks = c * g.C + tail + (0 if (c > 0 and ch[0] == 0) else 1)
+                attn_sum += toks * row_kv
+            u = np.unique(np.concatenate(ids)) if ids else np.zeros(0, np.int32)
+            toks_u = u.size * g.C + tail + (0 if (u.size and u[0] == 0) else 1)
+            attn_union += toks_u * row_kv
+    per_head_io = heads * (2 * g.d * s) + int(cnt.sum()) * 4
+    attn_union += per_head_io
+    attn_sum += per_head_io
+    route_row = g.R * g.d * s + 4 * g.R
+    K_levels = stats[..., 0].astype(np.int64)  # [B, 1, H_q, L]
+    route = int(K_levels.sum()) * route_row + heads * g.d * s + int(cnt.sum()) * 4 + heads * (
+        4 + 8 * g.L)
+    return {"attn_union": attn_union, "attn_per_head": attn_sum, "route": route,
+            "tokens_per_head": float((cnt.astype(np.int64) * g.C).mean())}
+
+
+# ----------------------------------------------------------------------------
+# GPU part
+# ----------------------------------------------------------------------------
+
+def to_dev(torch, a, dtype):
+    if dtype == W.BF16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def run_gpu(g, K, V, steps, warmup, dense_steps):
+    import torch
+
+    from hierarchical_tree_indexed_04_amd import zha as Z
+    Z.load()
+    torch.cuda.set_device(0)
+    gm = Z.geom(g)
+    n = warmup + steps
+    t0 = time.perf_counter()
+    Qs = np.stack([W.make_queries(g, K, i) for i in range(n)])[:, :, None]  # [n, B, 1, H_q, d]
+    log(f"[bench] queries for {n} steps: {time.perf_counter() - t0:.1f} s")
+    t0 = time.perf_counter()
+    Kd, Vd = to_dev(torch, K, g.dtype), to_dev(torch, V, g.dtype)
+    Qd = to_dev(torch, Qs, g.dtype)
+    qref = torch.zeros((g.H_kv, g.R, g.d), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] upload {Kd.numel() * 2 * Kd.element_size() / 1e9:.2f} GB: "
+        f"{time.perf_counter() - t0:.1f} s")
+
+    tb, sb = Z.tree_bytes(gm)
+    tree = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    bscratch = torch.empty(max(sb, 1), dtype=torch.uint8, device="cuda")
+    Z.build(gm, Kd, qref, tree, bscratch)  # first call: code load
+    torch.cuda.synchronize()
+    eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb0.record()
+    Z.build(gm, Kd, qref, tree, bscratch)
+    eb1.record()
+    torch.cuda.synchronize()
+    build_ms = eb0.elapsed_time(eb1)
+    log(f"[bench] tree build {build_ms:.2f} ms ({tb / 1e6:.1f} MB tree)")
+
+    cap = min(g.n_level(1), 8192)
+    sel = torch.empty((n, g.B, 1, g.H_q, cap), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((n, g.B, 1, g.H_q), dtype=torch.int32, device="cuda")
+    stats = torch.empty((n, g.B, 1, g.H_q, g.L, 2), dtype=torch.int32, device="cuda")
+    O = torch.empty((n, g.B, 1, g.H_q, g.d), dtype=Kd.dtype, device="cuda")
+    rscratch = torch.empty(max(Z.route_scratch_bytes(gm, 1, cap), 1), dtype=torch.uint8,
+                           device="cuda")
+    ascratch = torch.zeros(max(Z.attn_scratch_bytes(gm, 1, cap), 1), dtype=torch.uint8,
+                           device="cuda")
+
+    # Timed loop: direct C-ABI calls with pointers marshalled once, so host
+    # overhead stays far below the GPU time of a step.
+    import ctypes
+    lib = Z.load()
+    gref = ctypes.byref(gm)
+    vp = ctypes.c_void_p
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    tree_p, k_p, v_p = vp(tree.data_ptr()), vp(Kd.data_ptr()), vp(Vd.data_ptr())
+    rs_p, as_p = vp(rscratch.data_ptr()), vp(ascratch.data_ptr())
+    args_r = [(gref, tree_p, vp(Qd[i].data_ptr()), 1, ctypes.c_float(g.p), vp(sel[i].data_ptr()),
+               vp(cnt[i].data_ptr()), cap, vp(stats[i].data_ptr()), None, rs_p, stream)
+              for i in range(n)]
+    args_a = [(gref, vp(Qd[i].data_ptr()), 1, k_p, v_p, vp(sel[i].data_ptr()),
+               vp(cnt[i].data_ptr()), cap, vp(O[i].data_ptr()), as_p, stream) for i in range(n)]
+    zr, za = lib.zha_route, lib.zha_attn
+
+    def step(i):
+        if zr(*args_r[i]) != 0 or za(*args_a[i]) != 0:
+            raise RuntimeError("launch failed")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for j in range(steps):
+        i = warmup + j
+        if zr(*args_r[i]) != 0:
+            raise RuntimeError("zha_route failed")
+        ev[2 * j + 1].record()
+        if za(*args_a[i]) != 0:
+            raise RuntimeError("zha_attn failed")
+        ev[2 * j + 2].record()
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[2 * steps])
+    route_ms = np.array([ev[2 * j].elapsed_time(ev[2 * j + 1]) for j in range(steps)])
+    attn_ms = np.array([ev[2 * j + 1].elapsed_time(ev[2 * j + 2]) for j in range(steps)])
+    log(f"[bench] {steps} steps: {total_ms:.3f} ms total; route {route_ms.mean() * 1e3:.1f} us, "
+        f"attn {attn_ms.mean() * 1e3:.1f} us per step")
+
+    cnt_h = cnt.cpu().numpy()
+    if (cnt_h[warmup:] < 0).any() or (cnt_h[warmup:] > cap).any():
+        raise RuntimeError("a route overflowed the frontier capacity or the chunk-list cap")
+    sel_h = sel.cpu().numpy()
+    stats_h = stats.cpu().numpy()
+    acc = {"attn_union": 0, "attn_per_head": 0, "route": 0, "tokens_per_head": 0.0}
+    for j in range(steps):
+        i = warmup + j
+        b = step_bytes(g, sel_h[i], cnt_h[i], stats_h[i])
+        for k in acc:
+            acc[k] += b[k]
+    for k in acc:
+        acc[k] /= steps
+    if not np.isfinite(O.float().cpu().numpy()).all():
+        raise RuntimeError("non-finite attention output")
+
+    dense_ms = None
+    if dense_steps > 0:
+        dscratch = torch.zeros(max(Z.dense_scratch_bytes(gm, 1), 1), dtype=torch.uint8,
+                               device="cuda")
+        Od = torch.empty((g.B, 1, g.H_q, g.d), dtype=Kd.dtype, device="cuda")
+        Z.dense_decode(gm, Qd[0], 1, Kd, Vd, O=Od, scratch=dscratch)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for j in range(dense_steps):
+            Z.dense_decode(gm, Qd[warmup + j % steps], 1, Kd, Vd, O=Od, scratch=dscratch)
+        d1.record()
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / dense_steps
+        log(f"[bench] dense decode {dense_ms * 1e3:.1f} us per step")
+    return {"total_ms": total_ms, "route_ms": route_ms, "attn_ms": attn_ms, "bytes": acc,
+            "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: 256K)")
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-time budget of the oracle baseline (0 disables)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        log("bench.py measures one GPU: the hot path has no multi-GPU mode "
+            "(run with --gpus 1)")
+        sys.exit(2)
+    g = W.CONFIGS[args.config]
+    if g.block:
+        log("the chunked-query block workload is not a decode-step benchmark yet")
+        sys.exit(2)
+    t0 = time.perf_counter()
+    K, V = W.make_kv(g)
+    log(f"[bench] {g.name}: generated K, V ({2 * K.nbytes / 1e9:.2f} GB) in "
+        f"{time.perf_counter() - t0:.1f} s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        procs = max(1, min(16, os.cpu_count() or 1))
+        t0 = time.perf_counter()
+        cpu = cpu_baseline(g, K, V, args.cpu_seconds, procs)
+        log(f"[bench] oracle baseline {cpu['value']:.2f} queries/s ({time.perf_counter() - t0:.1f} s)")
+
+    r = run_gpu(g, K, V, args.steps, args.warmup, args.dense_steps)
+    ms_per_step = r["total_ms"] / args.steps
+    queries_per_step = g.B  # one query = one token position x all H_q heads
+    value = queries_per_step * args.steps / (r["total_ms"] / 1e3)
+    by = r["bytes"]
+    attn_us = float(r["attn_ms"].mean() * 1e3)
+    route_us = float(r["route_ms"].mean() * 1e3)
+    achieved = by["attn_union"] / (attn_us * 1e-6) / 1e9
+    step_union = by["attn_union"] + by["route"]
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": g.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{g.name}: B={g.B}, H_q={g.H_q}/H_kv={g.H_kv}, d={g.d}, T={g.T}, "
+                               f"C={g.C}, L={g.L}, R={g.R}, p={g.p}, one decode step per call",
+                   "global_batch": g.B, "seq_len": g.T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "zha_attn (attn_partial_kernel)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": cpu,
+        "route_us": route_us,
+        "attn_us": attn_us,
+        "step_bytes_union": step_union,
+        "step_bytes_per_head_sum": by["attn_per_head"] + by["route"],
+        "step_hbm_frac": step_union / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "tokens_per_head": by["tokens_per_head"],
+        "keys_attended_frac": by["tokens_per_head"] / g.T,
+        "build_ms": r["build_ms"],
+        "dense_ms_per_step": r["dense_ms"],
+        "speedup_vs_dense": (r["dense_ms"] / ms_per_step) if r["dense_ms"] else None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

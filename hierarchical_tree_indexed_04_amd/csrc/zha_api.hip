@@ -1,0 +1,252 @@
+// C ABI: argument validation, buffer layouts and launches.  Every check runs
+// on the host before any launch; nothing here allocates or synchronises.
+
+#include <math.h>
+#include <string.h>
+
+#include "zha_internal.hpp"
+
+using namespace zha;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_geom(const zha_geom* g) {
+  if (g == nullptr) return ZHA_ERR_NULL;
+  if (g->dtype != ZHA_F32 && g->dtype != ZHA_BF16) return ZHA_ERR_DTYPE;
+  if (g->d != 64 && g->d != 128 && g->d != 256) return ZHA_ERR_DIM;
+  if (g->B < 1 || g->H_q < 1 || g->H_kv < 1 || g->H_q % g->H_kv != 0) return ZHA_ERR_GEOM;
+  if (g->C < 2 || g->C > 1024 || g->L < 1 || g->L > kMaxLevels || g->R < 1 || g->R > 16)
+    return ZHA_ERR_GEOM;
+  if (g->T < 1 || g->T / g->C >= ((int64_t)1 << 31)) return ZHA_ERR_GEOM;
+  int64_t span = 1;
+  for (int l = 0; l < g->L; ++l) {
+    span *= g->C;
+    if (span > g->T) return ZHA_ERR_GEOM;  // n_L >= 1 needs T >= C^L
+  }
+  return ZHA_OK;
+}
+
+TreeLayout make_layout(const zha_geom* g) {
+  TreeLayout lay{};
+  lay.L = g->L;
+  lay.R = g->R;
+  lay.C = g->C;
+  const int64_t es = g->dtype == ZHA_BF16 ? 2 : 4;
+  int64_t span = 1, off = 0;
+  for (int l = 1; l <= g->L; ++l) {
+    span *= g->C;
+    lay.n[l] = g->T / span;
+  }
+  for (int l = 1; l <= g->L; ++l) {
+    lay.khat[l] = off;
+    off += align256(lay.n[l] * g->R * g->d * es);
+  }
+  for (int l = 1; l <= g->L; ++l) {
+    lay.bhat[l] = off;
+    off += align256(lay.n[l] * g->R * 4);
+  }
+  lay.stride = off;
+  return lay;
+}
+
+BuildArgs make_build_args(const zha_geom* g) {
+  BuildArgs a{};
+  a.lay = make_layout(g);
+  a.n_trees = g->B * g->H_kv;
+  a.H_kv = g->H_kv;
+  a.d = g->d;
+  a.T = g->T;
+  return a;
+}
+
+int attn_splits(int64_t n_heads) {
+  int64_t s = (2048 + n_heads - 1) / n_heads;
+  if (s < 1) s = 1;
+  if (s > 32) s = 32;
+  return (int)s;
+}
+
+int dense_splits(const zha_geom* g, int32_t n_pos) {
+  const int64_t groups = (int64_t)g->B * n_pos * g->H_kv * (g->H_q / g->H_kv / dense_head_tile(g->H_q / g->H_kv));
+  int64_t s = (4096 + groups - 1) / groups;
+  const int64_t smax = (g->T + 255) / 256;
+  if (s > smax) s = smax;
+  if (s > 65535) s = 65535;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zha_strerror(int code) {
+  switch (code) {
+    case ZHA_OK: return "success";
+    case ZHA_ERR_NULL: return "a required pointer is NULL";
+    case ZHA_ERR_GEOM: return "invalid geometry";
+    case ZHA_ERR_DTYPE: return "unsupported dtype";
+    case ZHA_ERR_DIM: return "unsupported head dimension";
+    case ZHA_ERR_P: return "p must be in (0, 1]";
+    case ZHA_ERR_ALIGN: return "buffer not 16-byte aligned";
+    case ZHA_ERR_CAP: return "cap must be >= 1";
+    case ZHA_ERR_LAUNCH: return "kernel launch failed";
+    case ZHA_ERR_NPOS: return "n_pos must be >= 1";
+    default: return "unknown error";
+  }
+}
+
+int zha_tree_bytes(const zha_geom* g, size_t* tree_bytes, size_t* build_scratch_bytes) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (tree_bytes == nullptr || build_scratch_bytes == nullptr) return ZHA_ERR_NULL;
+  const BuildArgs a = make_build_args(g);
+  *tree_bytes = (size_t)(a.lay.stride * a.n_trees);
+  *build_scratch_bytes = (size_t)build_scratch_layout(a).total;
+  return ZHA_OK;
+}
+
+int zha_tree_level_offset(const zha_geom* g, int32_t level, size_t* khat_offset,
+                          size_t* bhat_offset, size_t* tree_stride) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (khat_offset == nullptr || bhat_offset == nullptr || tree_stride == nullptr)
+    return ZHA_ERR_NULL;
+  if (level < 1 || level > g->L) return ZHA_ERR_GEOM;
+  const TreeLayout lay = make_layout(g);
+  *khat_offset = (size_t)lay.khat[level];
+  *bhat_offset = (size_t)lay.bhat[level];
+  *tree_stride = (size_t)lay.stride;
+  return ZHA_OK;
+}
+
+int zha_build(const zha_geom* g, const void* K, const float* qref, void* tree, void* scratch,
+              void* stream) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  const BuildArgs a = make_build_args(g);
+  const bool need_scratch = build_scratch_layout(a).total > 0;
+  if (K == nullptr || qref == nullptr || tree == nullptr || (need_scratch && scratch == nullptr))
+    return ZHA_ERR_NULL;
+  if (!aligned16(K) || !aligned16(qref) || !aligned16(tree) ||
+      (need_scratch && !aligned16(scratch)))
+    return ZHA_ERR_ALIGN;
+  return build_dispatch(a, g->dtype, g->d, K, qref, tree, scratch,
+                        reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t zha_route_frontier_capacity(void) { return kRouteFrontierMax; }
+
+int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (bytes == nullptr) return ZHA_ERR_NULL;
+  if (n_pos < 1) return ZHA_ERR_NPOS;
+  if (cap < 1) return ZHA_ERR_CAP;
+  *bytes = 0;
+  return ZHA_OK;
+}
+
+int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos, float p,
+              int32_t* sel, int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap,
+              void* scratch, void* stream) {
+  (void)scratch;
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (tree == nullptr || Q == nullptr || sel == nullptr || cnt == nullptr) return ZHA_ERR_NULL;
+  if (n_pos < 1) return ZHA_ERR_NPOS;
+  if (cap < 1) return ZHA_ERR_CAP;
+  if (!(p > 0.0f && p <= 1.0f)) return ZHA_ERR_P;
+  if (!aligned16(tree) || !aligned16(Q)) return ZHA_ERR_ALIGN;
+  RouteArgs a{};
+  a.lay = make_layout(g);
+  a.n_heads = (int64_t)g->B * n_pos * g->H_q;
+  a.n_pos = n_pos;
+  a.H_q = g->H_q;
+  a.H_kv = g->H_kv;
+  a.G = g->H_q / g->H_kv;
+  a.cap = cap;
+  a.p = p;
+  if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
+  return route_dispatch(a, g->dtype, g->d, tree, Q, sel, cnt, level_stats, gap,
+                        reinterpret_cast<hipStream_t>(stream));
+}
+
+int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (bytes == nullptr) return ZHA_ERR_NULL;
+  if (n_pos < 1) return ZHA_ERR_NPOS;
+  if (cap < 1) return ZHA_ERR_CAP;
+  const int64_t n_heads = (int64_t)g->B * n_pos * g->H_q;
+  *bytes = (size_t)splitkv_scratch_bytes(n_heads, attn_splits(n_heads), g->d);
+  return ZHA_OK;
+}
+
+int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, const void* V,
+             const int32_t* sel, const int32_t* cnt, int32_t cap, void* O, void* scratch,
+             void* stream) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (n_pos < 1) return ZHA_ERR_NPOS;
+  if (cap < 1) return ZHA_ERR_CAP;
+  AttnArgs a{};
+  a.T = g->T;
+  a.n_heads = (int64_t)g->B * n_pos * g->H_q;
+  a.n1 = g->T / g->C;
+  a.n_pos = n_pos;
+  a.H_q = g->H_q;
+  a.H_kv = g->H_kv;
+  a.G = g->H_q / g->H_kv;
+  a.C = g->C;
+  a.log2C = (g->C & (g->C - 1)) == 0 ? __builtin_ctz((unsigned)g->C) : -1;
+  a.cap = cap;
+  a.S = attn_splits(a.n_heads);
+  if (Q == nullptr || K == nullptr || V == nullptr || sel == nullptr || cnt == nullptr ||
+      O == nullptr || (a.S > 1 && scratch == nullptr))
+    return ZHA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+      (a.S > 1 && !aligned16(scratch)))
+    return ZHA_ERR_ALIGN;
+  if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
+  return attn_dispatch(a, g->dtype, g->d, Q, K, V, sel, cnt, O, scratch,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int zha_dense_decode_scratch_bytes(const zha_geom* g, int32_t n_pos, size_t* bytes) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (bytes == nullptr) return ZHA_ERR_NULL;
+  if (n_pos < 1) return ZHA_ERR_NPOS;
+  const int64_t n_heads = (int64_t)g->B * n_pos * g->H_q;
+  *bytes = (size_t)splitkv_scratch_bytes(n_heads, dense_splits(g, n_pos), g->d);
+  return ZHA_OK;
+}
+
+int zha_dense_decode(const zha_geom* g, const void* Q, int32_t n_pos, const void* K,
+                     const void* V, void* O, void* scratch, void* stream) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (n_pos < 1) return ZHA_ERR_NPOS;
+  DenseArgs a{};
+  a.T = g->T;
+  a.n_heads = (int64_t)g->B * n_pos * g->H_q;
+  a.n_pos = n_pos;
+  a.H_q = g->H_q;
+  a.H_kv = g->H_kv;
+  a.G = g->H_q / g->H_kv;
+  a.S = dense_splits(g, n_pos);
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr ||
+      (a.S > 1 && scratch == nullptr))
+    return ZHA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+      (a.S > 1 && !aligned16(scratch)))
+    return ZHA_ERR_ALIGN;
+  if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
+  return dense_dispatch(a, g->dtype, g->d, Q, K, V, O, scratch,
+                        reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,405 @@
+// Exact attention over the routed token set, and the dense decode baseline.
+//
+// Sparse path (summary page of the paper, "Routing": I(q) = {0} U selected
+// leaf chunks U C_cur, o(q) = Attn(q, K_I, V_I)): every query head's token
+// list is cut into S splits of consecutive selected chunks; a workgroup
+// streams its split's K and V rows (one 16-byte slice per lane, LPR lanes per
+// row, 8 rows in flight per lane), keeps an online softmax per row group and
+// combines the row groups in LDS in a fixed order.  Split-KV partials (a
+// d-vector plus max and sum, paper App. D-B) are merged by a second, small
+// launch in split order, so results are bit-reproducible.  (Merging inside the
+// first launch would need a device-scope release/acquire per workgroup, which
+// on a multi-XCD part means an L2 write-back and invalidate each time: far
+// slower than the extra launch.)
+//
+// Dense path (paper App. D-A decode model): the same structure over all T
+// keys; a workgroup serves the G query heads of one KV head so each K/V row
+// is read once per group.
+
+#include "zha_internal.hpp"
+
+namespace zha {
+namespace {
+
+constexpr int kThreads = 256;
+#ifndef ZHA_ATTN_ROWS
+#define ZHA_ATTN_ROWS 8
+#endif
+#ifndef ZHA_DENSE_ROWS
+#define ZHA_DENSE_ROWS 4
+#endif
+constexpr int kUA = ZHA_ATTN_ROWS;   // K/V rows in flight per lane (sparse)
+constexpr int kUD = ZHA_DENSE_ROWS;  // K/V rows in flight per lane (dense)
+constexpr int kIds = 1024;  // chunk ids staged in LDS per round (sparse)
+
+
+
+// Combines the online-softmax states of the RPB row groups of a workgroup and
+// writes either the final output row(s) or a split partial.
+template <typename T, int D, int RPB>
+__device__ __forceinline__ void combine_groups(float m, float l, const float* acc, int grp, int sub,
+                                               float* s_m, float* s_l, float* s_acc,
+                                               T* out_row, float* part_row) {
+  constexpr int VEC = Vec<T>::N;
+  if (sub == 0) {
+    s_m[grp] = m;
+    s_l[grp] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s_acc[grp * D + sub * VEC + e] = acc[e];
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < RPB; ++g) M = fmaxf(M, s_m[g]);
+  for (int t = threadIdx.x; t < D; t += kThreads) {
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int g = 0; g < RPB; ++g) {
+      const float w = (s_m[g] == -INFINITY) ? 0.f : __expf(s_m[g] - M);
+      num = fmaf(w, s_acc[g * D + t], num);
+      den = fmaf(w, s_l[g], den);
+    }
+    if (part_row != nullptr) {
+      part_row[t] = num;
+      if (t == 0) {
+        part_row[D] = M;
+        part_row[D + 1] = den;
+      }
+    } else {
+      store_elem(out_row, t, num / den);
+    }
+  }
+}
+
+// Online-softmax update of one row group with U scores and value slices.
+template <typename T, int U>
+__device__ __forceinline__ void online_update(float& m, float& l, float* acc, const float* s,
+                                              const uint4* vv) {
+  constexpr int VEC = Vec<T>::N;
+  float mloc = m;
+#pragma unroll
+  for (int u = 0; u < U; ++u) mloc = fmaxf(mloc, s[u]);
+  if (mloc == -INFINITY) return;
+  const float scale = __expf(m - mloc);  // m = -inf gives 0
+  l *= scale;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] *= scale;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float p = __expf(s[u] - mloc);  // -inf scores give 0
+    l += p;
+    float v[VEC];
+    Vec<T>::widen(vv[u], v);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = fmaf(p, v[e], acc[e]);
+  }
+  m = mloc;
+}
+
+// Merge of the S split partials of one head, in split order:
+// O = sum_s e^{M_s - M} acc_s / sum_s e^{M_s - M} l_s.
+template <typename T, int D>
+__device__ __forceinline__ void merge_partials(const float* part_head, int S, T* out_row) {
+  const volatile float* p = part_head;  // written by other workgroups: bypass L1
+  for (int t = threadIdx.x; t < D; t += kThreads) {
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, p[s * (D + 2) + D]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float ms = p[s * (D + 2) + D];
+      const float w = (ms == -INFINITY) ? 0.f : __expf(ms - M);
+      num = fmaf(w, p[s * (D + 2) + t], num);
+      den = fmaf(w, p[s * (D + 2) + D + 1], den);
+    }
+    store_elem(out_row, t, num / den);
+  }
+}
+
+// Split-KV merge as its own launch: one workgroup per query head (or per
+// dense head tile); the kernel boundary makes the partials visible without
+// device-wide fences.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict__ part,
+                                                         const int32_t* __restrict__ cnt,
+                                                         int32_t cap, T* __restrict__ O, int S) {
+  const int64_t head = blockIdx.x;
+  if (cnt != nullptr) {
+    const int c = cnt[head];
+    if (c < 0 || c > cap) return;  // NaN row already written by the partial kernel
+  }
+  merge_partials<T, D>(part + head * (int64_t)S * (D + 2), S, O + head * D);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
+    float* __restrict__ part, AttnArgs a) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int LPR = D / VEC;
+  constexpr int RPB = kThreads / LPR;
+  __shared__ float s_m[RPB], s_l[RPB];
+  __shared__ float s_acc[RPB * D];
+  __shared__ int32_t s_ids[kIds];
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR, grp = tid / LPR;
+  const int64_t head = blockIdx.x;
+  const int split = blockIdx.y;
+  const int c = cnt[head];
+  if (c < 0 || c > a.cap) {  // overflowed or failed route: the row is NaN
+    if (split == 0)
+      for (int t = tid; t < D; t += kThreads) store_elem(O + head * D, t, __int_as_float(0x7fc00000));
+    return;
+  }
+  const int h = (int)(head % a.H_q);
+  const int64_t b = head / ((int64_t)a.n_pos * a.H_q);
+  const int64_t tr = b * a.H_kv + h / a.G;
+  const T* Kt = K + tr * a.T * D;
+  const T* Vt = V + tr * a.T * D;
+  const int32_t* ids = sel + head * a.cap;
+
+  // This split's chunks, plus (last split) the sink when chunk 0 is not selected and C_cur.
+  const int c0 = (int)(((int64_t)split * c) / a.S);
+  const int c1 = (int)(((int64_t)(split + 1) * c) / a.S);
+  const int64_t nchunk_tok = (int64_t)(c1 - c0) * a.C;
+  int n_extra = 0;
+  bool sink = false;
+  const int64_t tail0 = a.n1 * a.C;
+  if (split == a.S - 1) {
+    sink = (c == 0) || (ids[0] != 0);
+    n_extra = (sink ? 1 : 0) + (int)(a.T - tail0);
+  }
+  const int64_t ntok = nchunk_tok + n_extra;
+
+  float q[VEC];
+  {
+    const uint4 v = ld16c(Q + head * D + sub * VEC);
+    Vec<T>::widen(v, q);
+    const float inv = 1.0f / sqrtf((float)D);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) q[e] *= inv;
+  }
+  float m = -INFINITY, l = 0.f, acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+
+  // Chunk ids are staged in LDS, kIds at a time, so the address of every K/V
+  // row comes from LDS and all loads of an iteration issue back to back (a
+  // global id load between them would wait, in order, for every earlier row).
+  const int nc = c1 - c0;
+  for (int r0 = 0;; r0 += kIds) {
+    const int rn = min(kIds, nc - r0);
+    const bool final_round = r0 + kIds >= nc;
+    if (rn > 0) {
+      __syncthreads();
+      for (int i = tid; i < rn; i += kThreads) s_ids[i] = ids[c0 + r0 + i];
+      __syncthreads();
+    }
+    const int64_t xb = (int64_t)r0 * a.C;
+    const int64_t xe = final_round ? ntok : (int64_t)(r0 + rn) * a.C;
+    for (int64_t base = xb; base < xe; base += (int64_t)RPB * kUA) {
+      uint4 kv[kUA], vv[kUA];
+      float s[kUA];
+#pragma unroll
+      for (int u = 0; u < kUA; ++u) {
+        const int64_t x = base + u * RPB + grp;
+        int64_t tok = -1;
+        if (x < nchunk_tok) {
+          const int64_t ci = a.log2C >= 0 ? (x >> a.log2C) : x / a.C;
+          tok = (int64_t)s_ids[ci - r0] * a.C + (x - ci * a.C);
+        } else if (x < xe) {
+          const int64_t e = x - nchunk_tok;
+          tok = sink ? (e == 0 ? 0 : tail0 + e - 1) : tail0 + e;
+        }
+        if (tok >= 0) {
+          kv[u] = ld16(Kt + tok * D + sub * VEC);
+          vv[u] = ld16(Vt + tok * D + sub * VEC);
+          s[u] = 0.f;
+        } else {
+          kv[u] = make_uint4(0u, 0u, 0u, 0u);
+          vv[u] = make_uint4(0u, 0u, 0u, 0u);
+          s[u] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUA; ++u) {
+        float k[VEC];
+        Vec<T>::widen(kv[u], k);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dot = fmaf(q[e], k[e], dot);
+        dot = group_sum<LPR>(dot);
+        s[u] = (s[u] == -INFINITY) ? -INFINITY : dot;
+      }
+      online_update<T, kUA>(m, l, acc, s, vv);
+    }
+    if (final_round) break;
+  }
+  float* phead = part + head * a.S * (int64_t)(D + 2);
+  float* prow = (a.S > 1) ? phead + split * (int64_t)(D + 2) : nullptr;
+  combine_groups<T, D, RPB>(m, l, acc, grp, sub, s_m, s_l, s_acc, O + head * D, prow);
+}
+
+// Dense decode: one workgroup per (b, t, kvh, head tile of GT) and split; GT
+// query heads share every K/V row.
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(kThreads) void dense_partial_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    T* __restrict__ O, float* __restrict__ part, DenseArgs a) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int LPR = D / VEC;
+  constexpr int RPB = kThreads / LPR;
+  __shared__ float s_m[RPB], s_l[RPB];
+  __shared__ float s_acc[RPB * D];
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR, grp = tid / LPR;
+  const int tiles = a.G / GT;
+  const int64_t blk = blockIdx.x;
+  const int tile = (int)(blk % tiles);
+  const int64_t bk = blk / tiles;  // (b * n_pos + t) * H_kv + kvh
+  const int kvh = (int)(bk % a.H_kv);
+  const int64_t bt = bk / a.H_kv;
+  const int64_t b = bt / a.n_pos;
+  const int split = blockIdx.y;
+  const int64_t head0 = bt * a.H_q + (int64_t)kvh * a.G + tile * GT;
+  const T* Kt = K + (b * a.H_kv + kvh) * a.T * D;
+  const T* Vt = V + (b * a.H_kv + kvh) * a.T * D;
+  const int64_t t0 = (a.T * split) / a.S, t1 = (a.T * (split + 1)) / a.S;
+
+  float q[GT][VEC];
+  const float inv = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    const uint4 v = ld16c(Q + (head0 + g) * D + sub * VEC);
+    Vec<T>::widen(v, q[g]);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) q[g][e] *= inv;
+  }
+  float m[GT], l[GT], acc[GT][VEC];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[g][e] = 0.f;
+  }
+  for (int64_t base = t0; base < t1; base += (int64_t)RPB * kUD) {
+    uint4 kv[kUD], vv[kUD];
+    bool ok[kUD];
+#pragma unroll
+    for (int u = 0; u < kUD; ++u) {
+      const int64_t tok = base + u * RPB + grp;
+      ok[u] = tok < t1;
+      if (ok[u]) {
+        kv[u] = ld16(Kt + tok * D + sub * VEC);
+        vv[u] = ld16(Vt + tok * D + sub * VEC);
+      } else {
+        kv[u] = make_uint4(0u, 0u, 0u, 0u);
+        vv[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float s[kUD];
+#pragma unroll
+      for (int u = 0; u < kUD; ++u) {
+        float k[VEC];
+        Vec<T>::widen(kv[u], k);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dot = fmaf(q[g][e], k[e], dot);
+        dot = group_sum<LPR>(dot);
+        s[u] = ok[u] ? dot : -INFINITY;
+      }
+      online_update<T, kUD>(m[g], l[g], acc[g], s, vv);
+    }
+  }
+  for (int g = 0; g < GT; ++g) {
+    float* prow = (a.S > 1) ? part + ((head0 + g) * a.S + split) * (int64_t)(D + 2) : nullptr;
+    combine_groups<T, D, RPB>(m[g], l[g], acc[g], grp, sub, s_m, s_l, s_acc, O + (head0 + g) * D,
+                              prow);
+    __syncthreads();
+  }
+}
+
+template <typename T, int D>
+int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
+                const int32_t* sel, const int32_t* cnt, void* O, void* scratch, hipStream_t s) {
+  dim3 grid((unsigned)a.n_heads, (unsigned)a.S);
+  float* part = reinterpret_cast<float*>(scratch);
+  attn_partial_kernel<T, D><<<grid, kThreads, 0, s>>>(
+      reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
+      reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), part, a);
+  if (a.S > 1) {
+    if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
+    merge_kernel<T, D><<<(unsigned)a.n_heads, kThreads, 0, s>>>(part, cnt, a.cap,
+                                                                reinterpret_cast<T*>(O), a.S);
+  }
+  return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
+}
+
+template <typename T, int D, int GT>
+int launch_dense_gt(const DenseArgs& a, const void* Q, const void* K, const void* V, void* O,
+                    void* scratch, hipStream_t s) {
+  const int64_t groups = (a.n_heads / a.H_q) * a.H_kv * (a.G / GT);
+  dim3 grid((unsigned)groups, (unsigned)a.S);
+  float* part = reinterpret_cast<float*>(scratch);
+  dense_partial_kernel<T, D, GT><<<grid, kThreads, 0, s>>>(
+      reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
+      reinterpret_cast<const T*>(V), reinterpret_cast<T*>(O), part, a);
+  if (a.S > 1) {
+    if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
+    merge_kernel<T, D><<<(unsigned)a.n_heads, kThreads, 0, s>>>(part, nullptr, 0,
+                                                                reinterpret_cast<T*>(O), a.S);
+  }
+  return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
+}
+
+template <typename T, int D>
+int launch_dense(const DenseArgs& a, const void* Q, const void* K, const void* V, void* O,
+                 void* scratch, hipStream_t s) {
+  const int gt = dense_head_tile(a.G);
+  if (gt == 8) return launch_dense_gt<T, D, 8>(a, Q, K, V, O, scratch, s);
+  if (gt == 4) return launch_dense_gt<T, D, 4>(a, Q, K, V, O, scratch, s);
+  if (gt == 2) return launch_dense_gt<T, D, 2>(a, Q, K, V, O, scratch, s);
+  return launch_dense_gt<T, D, 1>(a, Q, K, V, O, scratch, s);
+}
+
+}  // namespace
+
+int attn_dispatch(const AttnArgs& a, int dtype, int d, const void* Q, const void* K,
+                  const void* V, const int32_t* sel, const int32_t* cnt, void* O, void* scratch,
+                  hipStream_t s) {
+#define ZHA_ATTN_CASE(TT, DD) \
+  if (d == DD) return launch_attn<TT, DD>(a, Q, K, V, sel, cnt, O, scratch, s);
+  if (dtype == ZHA_BF16) {
+    ZHA_ATTN_CASE(bf16_t, 64)
+    ZHA_ATTN_CASE(bf16_t, 128)
+    ZHA_ATTN_CASE(bf16_t, 256)
+  } else {
+    ZHA_ATTN_CASE(float, 64)
+    ZHA_ATTN_CASE(float, 128)
+    ZHA_ATTN_CASE(float, 256)
+  }
+#undef ZHA_ATTN_CASE
+  return ZHA_ERR_DIM;
+}
+
+int dense_dispatch(const DenseArgs& a, int dtype, int d, const void* Q, const void* K,
+                   const void* V, void* O, void* scratch, hipStream_t s) {
+#define ZHA_DENSE_CASE(TT, DD) \
+  if (d == DD) return launch_dense<TT, DD>(a, Q, K, V, O, scratch, s);
+  if (dtype == ZHA_BF16) {
+    ZHA_DENSE_CASE(bf16_t, 64)
+    ZHA_DENSE_CASE(bf16_t, 128)
+    ZHA_DENSE_CASE(bf16_t, 256)
+  } else {
+    ZHA_DENSE_CASE(float, 64)
+    ZHA_DENSE_CASE(float, 128)
+    ZHA_DENSE_CASE(float, 256)
+  }
+#undef ZHA_DENSE_CASE
+  return ZHA_ERR_DIM;
+}
+
+}  // namespace zha

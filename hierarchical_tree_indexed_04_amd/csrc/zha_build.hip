@@ -1,0 +1,210 @@
+// Tree construction: leaf summaries and parent merges.
+//
+// Follows "Subquadratic Attention with a Hierarchical Tree-Structured
+// Indexer" §III-A (chunk log-mass F_C, tangent summaries k_hat_r, b_hat_r) and
+// App. D-B2 (leaf: reference/key scores and weighted key sums, two key reads;
+// parent: per reference, rescale and sum the children's weighted sums, keeping
+// a maximum, a weight sum and a d-vector).
+//
+// Accumulation is fp64.  With a zero reference every weight is exactly 1 and
+// every sum of stored keys is exact, so each stored k_hat is the correctly
+// rounded mean of its span; with other references the fp64 result is within
+// a few ulps of the exact summary before the single rounding to storage.
+//
+// One wave per node; lane l owns dims [l*DPL, l*DPL + DPL).  References are
+// processed one at a time (the chunk's keys are re-read from cache).
+
+#include "zha_internal.hpp"
+
+namespace zha {
+
+template <typename T, int D>
+__device__ __forceinline__ void load_row_f64(const T* row, int lane, double* out) {
+  constexpr int DPL = D / kWave;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) out[e] = (double)load_elem(row, lane * DPL + e);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
+                                                   const float* __restrict__ qref,
+                                                   char* __restrict__ tree,
+                                                   double* __restrict__ sF,
+                                                   double* __restrict__ sK, BuildArgs a) {
+  constexpr int DPL = D / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t node = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t n1 = a.lay.n[1];
+  if (node >= (int64_t)a.n_trees * n1) return;
+  const int64_t tr = node / n1;
+  const int64_t i = node - tr * n1;
+  const int kvh = (int)(tr % a.H_kv);
+  const int C = a.lay.C;
+  const int R = a.lay.R;
+  const double inv_sqrt_d = 1.0 / sqrt((double)D);
+  const T* keys = K + ((tr * a.T) + i * (int64_t)C) * D;
+  T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
+  float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
+
+  for (int r = 0; r < R; ++r) {
+    double q[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) q[e] = (double)qref[((int64_t)kvh * R + r) * D + lane * DPL + e];
+    // First key read: the maximum score of the chunk.
+    double m = -INFINITY;
+    for (int j = 0; j < C; ++j) {
+      double k[DPL];
+      load_row_f64<T, D>(keys + (int64_t)j * D, lane, k);
+      double part = 0.0;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) part = fma(q[e], k[e], part);
+      m = fmax(m, group_sum64<kWave>(part) * inv_sqrt_d);
+    }
+    // Second key read: weights exp(s - m), their sum and the weighted key sum.
+    double Z = 0.0;
+    double acc[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
+    for (int j = 0; j < C; ++j) {
+      double k[DPL];
+      load_row_f64<T, D>(keys + (int64_t)j * D, lane, k);
+      double part = 0.0;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) part = fma(q[e], k[e], part);
+      const double w = exp(group_sum64<kWave>(part) * inv_sqrt_d - m);
+      Z += w;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fma(w, k[e], acc[e]);
+    }
+    const double F = m + log(Z);
+    double part = 0.0;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      acc[e] = acc[e] / Z;
+      part = fma(q[e], acc[e], part);
+    }
+    const double b = F - group_sum64<kWave>(part) * inv_sqrt_d;
+    const int64_t row = i * R + r;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) store_elem64(khat, row * D + lane * DPL + e, acc[e]);
+    if (lane == 0) bhat[row] = (float)b;
+    if (sF != nullptr) {
+      const int64_t srow = tr * n1 * R + row;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sK[srow * D + lane * DPL + e] = acc[e];
+      if (lane == 0) sF[srow] = F;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qref,
+                                                    char* __restrict__ tree,
+                                                    const double* __restrict__ cF,
+                                                    const double* __restrict__ cK,
+                                                    double* __restrict__ pF,
+                                                    double* __restrict__ pK, BuildArgs a,
+                                                    int level) {
+  constexpr int DPL = D / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t np = a.lay.n[level];
+  const int64_t nc = a.lay.n[level - 1];
+  const int64_t node = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (node >= (int64_t)a.n_trees * np) return;
+  const int64_t tr = node / np;
+  const int64_t i = node - tr * np;
+  const int kvh = (int)(tr % a.H_kv);
+  const int C = a.lay.C;
+  const int R = a.lay.R;
+  const double inv_sqrt_d = 1.0 / sqrt((double)D);
+  T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[level]);
+  float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[level]);
+  const int64_t child0 = tr * nc + i * C;  // first child's row (per reference block)
+
+  for (int r = 0; r < R; ++r) {
+    // Maximum child log-mass.
+    double m = -INFINITY;
+    for (int c = lane; c < C; c += kWave) m = fmax(m, cF[(child0 + c) * R + r]);
+    m = group_max64<kWave>(m);
+    // Weight sum and rescaled sum of the children's summaries, children in order.
+    double Z = 0.0;
+    double acc[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
+    for (int c0 = 0; c0 < C; c0 += kWave) {
+      const double e_mine = (c0 + lane < C) ? exp(cF[(child0 + c0 + lane) * R + r] - m) : 0.0;
+      const int cn = min(kWave, C - c0);
+      for (int c = 0; c < cn; ++c) {
+        const double w = __shfl(e_mine, c, kWave);
+        Z += w;
+        const double* krow = cK + ((child0 + c0 + c) * R + r) * D + lane * DPL;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fma(w, krow[e], acc[e]);
+      }
+    }
+    const double F = m + log(Z);
+    double part = 0.0;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      acc[e] = acc[e] / Z;
+      part = fma((double)qref[((int64_t)kvh * R + r) * D + lane * DPL + e], acc[e], part);
+    }
+    const double b = F - group_sum64<kWave>(part) * inv_sqrt_d;
+    const int64_t row = i * R + r;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) store_elem64(khat, row * D + lane * DPL + e, acc[e]);
+    if (lane == 0) bhat[row] = (float)b;
+    if (pF != nullptr) {
+      const int64_t prow = (tr * np + i) * R + r;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) pK[prow * D + lane * DPL + e] = acc[e];
+      if (lane == 0) pF[prow] = F;
+    }
+  }
+}
+
+template <typename T, int D>
+static int launch_build(const BuildArgs& a, const void* K, const float* qref, void* tree,
+                        void* scratch, hipStream_t s) {
+  const BuildScratch sc = build_scratch_layout(a);
+  char* base = reinterpret_cast<char*>(scratch);
+  auto F = [&](int l) { return reinterpret_cast<double*>(base + sc.F[l]); };
+  auto Kp = [&](int l) { return reinterpret_cast<double*>(base + sc.K[l]); };
+  const int L = a.lay.L;
+  {
+    const int64_t nodes = (int64_t)a.n_trees * a.lay.n[1];
+    const unsigned blocks = (unsigned)((nodes + 3) / 4);
+    leaf_kernel<T, D><<<blocks, 256, 0, s>>>(reinterpret_cast<const T*>(K), qref,
+                                             reinterpret_cast<char*>(tree),
+                                             L > 1 ? F(1) : nullptr, L > 1 ? Kp(1) : nullptr, a);
+    if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
+  }
+  for (int l = 2; l <= L; ++l) {
+    const int64_t nodes = (int64_t)a.n_trees * a.lay.n[l];
+    const unsigned blocks = (unsigned)((nodes + 3) / 4);
+    merge_kernel<T, D><<<blocks, 256, 0, s>>>(qref, reinterpret_cast<char*>(tree), F(l - 1),
+                                              Kp(l - 1), l < L ? F(l) : nullptr,
+                                              l < L ? Kp(l) : nullptr, a, l);
+    if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
+  }
+  return ZHA_OK;
+}
+
+int build_dispatch(const BuildArgs& a, int dtype, int d, const void* K, const float* qref,
+                   void* tree, void* scratch, hipStream_t s) {
+#define ZHA_BUILD_CASE(TT, DD)                                                      \
+  if (d == DD) return launch_build<TT, DD>(a, K, qref, tree, scratch, s);
+  if (dtype == ZHA_BF16) {
+    ZHA_BUILD_CASE(bf16_t, 64)
+    ZHA_BUILD_CASE(bf16_t, 128)
+    ZHA_BUILD_CASE(bf16_t, 256)
+  } else {
+    ZHA_BUILD_CASE(float, 64)
+    ZHA_BUILD_CASE(float, 128)
+    ZHA_BUILD_CASE(float, 256)
+  }
+#undef ZHA_BUILD_CASE
+  return ZHA_ERR_DIM;
+}
+
+}  // namespace zha

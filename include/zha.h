@@ -161,13 +161,18 @@ int32_t zha_route_frontier_capacity(void);
  * computed with fp32 arithmetic and rounded nearest-even to the storage dtype.
  * ------------------------------------------------------------------------- */
 
+/* Scratch of zha_attn (and of zha_dense_decode below): split-KV partials
+ * (fp32, d + 2 values per query head and split).  Calls that overlap in time
+ * on the same buffer race.  0 bytes means no scratch is needed. */
 int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes);
 
 /*   Q, K, V  device, layouts above
  *   sel, cnt device, as written by zha_route (ascending, distinct ids < n_1)
  *   O        device [B, n_pos, H_q, d], written; rows whose cnt is negative or
  *            exceeds cap are written as NaN
- *   scratch  device, zha_attn_scratch_bytes() bytes */
+ *   scratch  device, zha_attn_scratch_bytes() bytes
+ * Split partials are merged in split order, so results do not depend on
+ * scheduling. */
 int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, const void* V,
              const int32_t* sel, const int32_t* cnt, int32_t cap, void* O, void* scratch,
              void* stream);
@@ -176,6 +181,7 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, con
  * Dense decode baseline: O = softmax(q K^T / sqrt(d)) V over all T keys.
  * ------------------------------------------------------------------------- */
 
+/* Same scratch contract as zha_attn. */
 int zha_dense_decode_scratch_bytes(const zha_geom* g, int32_t n_pos, size_t* bytes);
 
 int zha_dense_decode(const zha_geom* g, const void* Q, int32_t n_pos, const void* K,

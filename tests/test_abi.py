@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every declared symbol and validates arguments (no GPU).
+
+Only host-side paths are exercised: size queries and argument checks that
+return before any launch.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from hierarchical_tree_indexed_04_amd import zha as Z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zha.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zha_\w+)\s*\(", text)))
+
+
+def g(**kw):
+    base = dict(B=1, H_q=8, H_kv=2, d=128, T=4096, C=16, L=3, R=1, dtype=Z.ZHA_BF16)
+    base.update(kw)
+    return Z.Geom(**base)
+
+
+def test_library_exports_every_declared_function():
+    lib = Z.load()
+    names = declared_functions()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(Z.SIGNATURES)
+
+
+def test_strerror_names_every_code():
+    lib = Z.load()
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9]:
+        assert lib.zha_strerror(code) not in (None, b"", b"unknown error")
+    assert lib.zha_strerror(-1000) == b"unknown error"
+
+
+def expected_layout(gm, es):
+    n = [None] + [gm.T // gm.C ** l for l in range(1, gm.L + 1)]
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    off, khat, bhat = 0, {}, {}
+    for l in range(1, gm.L + 1):
+        khat[l] = off
+        off += a256(n[l] * gm.R * gm.d * es)
+    for l in range(1, gm.L + 1):
+        bhat[l] = off
+        off += a256(n[l] * gm.R * 4)
+    return khat, bhat, off
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(dtype=Z.ZHA_F32, R=3, T=5000), dict(C=8, L=6, T=8 ** 6 + 77)])
+def test_tree_layout_matches_documented_rules(kw):
+    gm = g(**kw)
+    es = 2 if gm.dtype == Z.ZHA_BF16 else 4
+    khat, bhat, stride = expected_layout(gm, es)
+    tb, sb = Z.tree_bytes(gm)
+    assert tb == stride * gm.B * gm.H_kv
+    for l in range(1, gm.L + 1):
+        assert Z.level_offset(gm, l) == (khat[l], bhat[l], stride)
+    # build scratch: fp64 F and k_hat for levels 1..L-1
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = sum(a256(gm.B * gm.H_kv * (gm.T // gm.C ** l) * gm.R * 8)
+               + a256(gm.B * gm.H_kv * (gm.T // gm.C ** l) * gm.R * gm.d * 8)
+               for l in range(1, gm.L))
+    assert sb == want
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), -4), (dict(dtype=7), -3), (dict(H_q=6, H_kv=4), -2), (dict(C=1), -2),
+    (dict(L=0), -2), (dict(R=17), -2), (dict(T=4095), -2), (dict(B=0), -2), (dict(L=17), -2),
+])
+def test_invalid_geometry_is_rejected(kw, code):
+    gm = g(**kw)
+    tb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert Z.load().zha_tree_bytes(ctypes.byref(gm), ctypes.byref(tb), ctypes.byref(sb)) == code
+
+
+def test_null_and_argument_errors_before_any_launch():
+    lib = Z.load()
+    gm = g()
+    buf = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation
+    n = ctypes.c_size_t()
+    assert lib.zha_tree_bytes(None, ctypes.byref(n), ctypes.byref(n)) == -1
+    assert lib.zha_build(ctypes.byref(gm), None, buf, buf, buf, None) == -1
+    assert lib.zha_build(ctypes.byref(gm), ctypes.c_void_p(17), buf, buf, buf, None) == -6
+    # p outside (0, 1]
+    for p in (0.0, -0.5, 1.5, math.nan):
+        assert lib.zha_route(ctypes.byref(gm), buf, buf, 1, p, buf, buf, 4, None, None, None,
+                             None) == -5
+    assert lib.zha_route(ctypes.byref(gm), buf, buf, 1, 0.9, buf, buf, 0, None, None, None,
+                         None) == -7
+    assert lib.zha_route(ctypes.byref(gm), buf, buf, 0, 0.9, buf, buf, 4, None, None, None,
+                         None) == -9
+    assert lib.zha_route(ctypes.byref(gm), None, buf, 1, 0.9, buf, buf, 4, None, None, None,
+                         None) == -1
+    assert lib.zha_attn(ctypes.byref(gm), buf, 1, buf, buf, None, buf, 4, buf, buf, None) == -1
+    assert lib.zha_attn(ctypes.byref(gm), buf, 1, buf, buf, buf, buf, 0, buf, buf, None) == -7
+    assert lib.zha_dense_decode(ctypes.byref(gm), buf, 0, buf, buf, buf, buf, None) == -9
+    assert lib.zha_dense_decode(ctypes.byref(gm), ctypes.c_void_p(24), 1, buf, buf, buf, buf,
+                                None) == -6
+    assert lib.zha_tree_level_offset(ctypes.byref(gm), 0, ctypes.byref(n), ctypes.byref(n),
+                                     ctypes.byref(n)) == -2
+
+
+def test_scratch_sizes_are_consistent():
+    gm = g(B=8, H_q=32, H_kv=4, T=262144, C=8, L=6)
+    assert Z.route_scratch_bytes(gm, 1, 32768) == 0
+    a = Z.attn_scratch_bytes(gm, 1, 32768)
+    assert a > 0 and a % (4 * (gm.d + 2)) == 0
+    assert Z.dense_scratch_bytes(gm, 1) % (4 * (gm.d + 2)) == 0
+    assert Z.frontier_capacity() >= 1024

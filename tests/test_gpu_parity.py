@@ -1,0 +1,237 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Tree: stored k_hat and b_hat must equal the oracle's correctly rounded values.
+Routes: S_1 and every level's (frontier size, kept count) must be identical,
+except for query heads where the oracle flags a fragile cut at or above the
+first divergent level (score gap < 1e-3 or prefix mass within 1e-4 of p);
+those are counted and printed.  Outputs: max-abs error <= 2e-2 (bf16) or
+1e-4 (fp32) on every head whose S_1 matched.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from hierarchical_tree_indexed_04_amd import workload as W
+from zha_testutil import (TOL, Parity, compare_head, from_device, oracle_trees, to_device,
+                          tree_mismatch)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def Z():
+    from hierarchical_tree_indexed_04_amd import zha
+    zha.load()
+    return zha
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_parity(Z, g, steps, pairs=None, p=None, R=None, qref=None, check_tree=True):
+    import torch
+    p = g.p if p is None else p
+    if R is not None and R != g.R:
+        g = W.replace(g, R=R)
+    pairs = pairs if pairs is not None else [(b, h) for b in range(g.B) for h in range(g.H_kv)]
+    K, V = W.make_kv(g, slices=pairs)
+    qref = W.make_qref(g, K) if qref is None else qref
+    Qn = W.make_query_block(g, K, steps)
+    gm = Z.geom(g)
+    n_pos = len(steps)
+    cap = g.n_level(1)
+    Kd, Vd, Qd = to_device(K, g.dtype), to_device(V, g.dtype), to_device(Qn, g.dtype)
+    qd = torch.from_numpy(qref).cuda()
+    tree = Z.build(gm, Kd, qd)
+    sel, cnt, stats, gap = Z.route(gm, tree, Qd, n_pos, p, cap)
+    Od = Z.attn(gm, Qd, n_pos, Kd, Vd, sel, cnt, cap)
+    torch.cuda.synchronize()
+    sel, cnt, stats = sel.cpu().numpy(), cnt.cpu().numpy(), stats.cpu().numpy()
+    Og = from_device(Od, g.dtype)
+    trees = oracle_trees(g, K, qref, pairs)
+    if check_tree:
+        bad_k, bad_b, total = tree_mismatch(Z, g, tree.cpu().numpy(), trees)
+        say(f"  tree: {bad_k} k_hat and {bad_b} b_hat mismatches over {total} stored values")
+        assert bad_k == 0 and bad_b == 0
+    par = Parity()
+    for (b, kvh) in pairs:
+        Kf = W.to_float(K[b, kvh], g.dtype)
+        Vf = W.to_float(V[b, kvh], g.dtype)
+        for t in range(n_pos):
+            for h in range(kvh * g.G, (kvh + 1) * g.G):
+                q = W.to_float(Qn[b, t, h], g.dtype)
+                r, o = O.zha_head(trees[(b, kvh)], q, Kf, Vf, p)
+                compare_head(par, r, sel[b, t, h], int(cnt[b, t, h]), stats[b, t, h],
+                             Og[b, t, h], o, TOL[g.dtype], (b, t, h))
+    say("  " + par.summary())
+    assert not par.mismatched, par.mismatched[:5]
+    assert not par.out_bad, par.out_bad[:5]
+    assert par.exact >= 0.8 * par.heads
+    return par
+
+
+def test_config1_tiny_fp32_all_queries(Z):
+    say("config 1: tiny fp32, 64 queries")
+    run_parity(Z, W.CONFIGS[1], range(64))
+
+
+def test_config2_gqa_128k(Z):
+    say("config 2: GQA 128K bf16, 8 steps x 32 heads")
+    run_parity(Z, W.CONFIGS[2], range(8))
+
+
+def test_config3_deep_256k_subset(Z):
+    say("config 3: deep 256K bf16, sequences 0 and 5, 4 steps")
+    g = W.CONFIGS[3]
+    run_parity(Z, g, range(4), pairs=[(b, h) for b in (0, 5) for h in range(g.H_kv)])
+
+
+def test_reference_queries_r4(Z):
+    say("R=4 random reference queries, C=8 L=3")
+    g = W.custom("r4", 110, dtype=W.BF16, B=2, H_q=8, H_kv=2, T=8 ** 3 * 3 + 8 * 5 + 3, C=8, L=3,
+                 p=0.9, R=4)
+    run_parity(Z, g, range(6))
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_other_head_dims(Z, d):
+    say(f"head dim {d}")
+    g = W.custom(f"d{d}", 111 + d, dtype=W.BF16, B=1, H_q=4, H_kv=1, d=d, T=16 ** 3 + 16 * 7 + 5,
+                 C=16, L=3, p=0.9)
+    run_parity(Z, g, range(8))
+
+
+def test_ragged_orphans_fp32_depth4(Z):
+    say("ragged T with orphan nodes at every level, fp32")
+    g = W.custom("ragged", 112, dtype=W.F32, B=2, H_q=2, H_kv=1, T=4 ** 4 * 3 + 4 ** 3 * 2 + 4 * 3 + 2,
+                 C=4, L=4, p=0.8)
+    run_parity(Z, g, range(10))
+
+
+def test_single_level_and_wide_chunks(Z):
+    say("L=1, C=256")
+    g = W.custom("wide", 113, dtype=W.BF16, B=1, H_q=8, H_kv=1, T=256 * 40 + 17, C=256, L=1,
+                 p=0.95)
+    run_parity(Z, g, range(4))
+
+
+def test_keep_all_p_one_is_every_chunk(Z):
+    say("p = 1 keeps every chunk (config 2 geometry)")
+    g = W.CONFIGS[2]
+    par = run_parity(Z, g, range(1), pairs=[(0, 1)], p=1.0, check_tree=False)
+    assert par.exact == par.heads
+
+
+def test_frontier_near_capacity_low_p_variants(Z):
+    say("near-uniform scores, large frontiers: p in {0.5, 0.99}")
+    g = W.custom("wide-front", 114, dtype=W.BF16, B=1, H_q=8, H_kv=1, T=32 ** 3, C=32, L=3, p=0.5)
+    run_parity(Z, g, range(4))
+    run_parity(Z, W.replace(g, p=0.99, cfg_id=115), range(4))
+
+
+def test_attention_on_random_chunk_sets(Z):
+    import torch
+    say("attention alone on random chunk sets, with sink, C_cur, overflow and invalid counts")
+    g = W.custom("attn-sets", 116, dtype=W.BF16, B=2, H_q=8, H_kv=2, T=16 * 300 + 9, C=16, L=2)
+    K, V = W.make_kv(g)
+    n_pos = 3
+    Qn = W.make_query_block(g, K, range(n_pos))
+    n_heads = g.B * n_pos * g.H_q
+    cap = 40
+    sel, cnt = W.random_chunk_sets(g, n_heads, 60, seed=1, cap=cap)
+    sel[0, :3], cnt[0] = [0, 3, 7], 3  # chunk 0 holds the sink: it must not be counted twice
+    cnt[1] = 0  # only the sink and the partial chunk
+    cnt[5] = -1  # a failed route
+    gm = Z.geom(g)
+    Kd, Vd, Qd = to_device(K, g.dtype), to_device(V, g.dtype), to_device(Qn, g.dtype)
+    seld = torch.from_numpy(sel.reshape(g.B, n_pos, g.H_q, cap)).cuda()
+    cntd = torch.from_numpy(cnt.reshape(g.B, n_pos, g.H_q)).cuda()
+    Od = Z.attn(gm, Qd, n_pos, Kd, Vd, seld, cntd, cap)
+    Og = from_device(Od, g.dtype).reshape(n_heads, g.d)
+    worst = 0.0
+    for i in range(n_heads):
+        b, t, h = i // (n_pos * g.H_q), (i // g.H_q) % n_pos, i % g.H_q
+        if cnt[i] < 0 or cnt[i] > cap:
+            assert np.isnan(Og[i]).all(), i
+            continue
+        idx = O.token_set(sel[i, :cnt[i]], g.C, g.T)
+        o = O.attend(W.to_float(Qn[b, t, h], g.dtype), W.to_float(K[b, h // g.G], g.dtype),
+                     W.to_float(V[b, h // g.G], g.dtype), idx)
+        worst = max(worst, float(np.abs(Og[i] - o).max()))
+    say(f"  max abs err {worst:.3g}; overflow rows NaN: {int((cnt > cap).sum())}")
+    assert worst <= TOL[g.dtype]
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_dense_decode_matches_oracle(Z, cfg):
+    say(f"dense decode, config {cfg}")
+    g = W.CONFIGS[cfg]
+    K, V = W.make_kv(g)
+    n_pos = 2
+    Qn = W.make_query_block(g, K, range(n_pos))
+    gm = Z.geom(g)
+    Od = Z.dense_decode(gm, to_device(Qn, g.dtype), n_pos, to_device(K, g.dtype),
+                        to_device(V, g.dtype))
+    Og = from_device(Od, g.dtype)
+    worst = 0.0
+    for b in range(g.B):
+        for t in range(n_pos):
+            for h in range(g.H_q):
+                o = O.dense(W.to_float(Qn[b, t, h], g.dtype), W.to_float(K[b, h // g.G], g.dtype),
+                            W.to_float(V[b, h // g.G], g.dtype))
+                worst = max(worst, float(np.abs(Og[b, t, h] - o).max()))
+    say(f"  max abs err {worst:.3g}")
+    assert worst <= TOL[g.dtype]
+
+
+def test_route_and_attn_are_deterministic(Z):
+    import torch
+    say("determinism: two runs are bit-identical (config 2, 4 steps)")
+    g = W.CONFIGS[2]
+    K, V = W.make_kv(g, slices=[(0, 0), (0, 1), (0, 2), (0, 3)])
+    Qn = W.make_query_block(g, K, range(4))
+    gm = Z.geom(g)
+    Kd, Vd, Qd = to_device(K, g.dtype), to_device(V, g.dtype), to_device(Qn, g.dtype)
+    qd = torch.zeros((g.H_kv, 1, g.d), dtype=torch.float32, device="cuda")
+    outs = []
+    tb, _ = Z.tree_bytes(gm)
+    for _ in range(2):
+        # zero-filled so that the alignment padding between levels compares equal too
+        tree = Z.build(gm, Kd, qd, tree=torch.zeros(tb, dtype=torch.uint8, device="cuda"))
+        sel, cnt, stats, gap = Z.route(gm, tree, Qd, 4, g.p, g.n_level(1))
+        Od = Z.attn(gm, Qd, 4, Kd, Vd, sel, cnt, g.n_level(1))
+        torch.cuda.synchronize()
+        outs.append((tree.cpu(), sel.cpu(), cnt.cpu(), stats.cpu(), gap.cpu(), Od.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+def test_single_position_calls_match_block_call(Z):
+    import torch
+    say("n_pos = 1 calls equal one n_pos = 4 call (config 3 geometry, one sequence)")
+    g = W.CONFIGS[3]
+    g1 = W.replace(g, B=1, cfg_id=120)
+    K, V = W.make_kv(g1)
+    Qn = W.make_query_block(g1, K, range(4))
+    gm = Z.geom(g1)
+    Kd, Vd, Qd = to_device(K, g1.dtype), to_device(V, g1.dtype), to_device(Qn, g1.dtype)
+    tree = Z.build(gm, Kd, torch.zeros((g1.H_kv, 1, g1.d), device="cuda"))
+    cap = g1.n_level(1)
+    sel, cnt, _, _ = Z.route(gm, tree, Qd, 4, g1.p, cap)
+    O4 = Z.attn(gm, Qd, 4, Kd, Vd, sel, cnt, cap)
+    for t in range(4):
+        q1 = Qd[:, t:t + 1].contiguous()
+        s1, c1, _, _ = Z.route(gm, tree, q1, 1, g1.p, cap)
+        o1 = Z.attn(gm, q1, 1, Kd, Vd, s1, c1, cap)
+        assert torch.equal(c1[:, 0], cnt[:, t])
+        for h in range(g1.H_q):
+            n = int(c1[0, 0, h])
+            assert torch.equal(s1[0, 0, h, :n], sel[0, t, h, :n])
+        # split counts differ between the two calls, so the fp32 sums may differ in the last bits
+        assert (o1[:, 0].float() - O4[:, t].float()).abs().max().item() <= 1e-2

@@ -1,0 +1,124 @@
+"""Helpers shared by the tests: device transfer, tree unpacking, oracle runs, parity accounting."""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle as O
+from hierarchical_tree_indexed_04_amd import workload as W
+
+TOL = {W.BF16: 2e-2, W.F32: 1e-4}
+
+
+def to_device(a: np.ndarray, dtype: str):
+    import torch
+    if dtype == W.BF16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.cuda()
+
+
+def from_device(t, dtype: str) -> np.ndarray:
+    """Device tensor of the storage dtype -> float32 numpy values."""
+    import torch
+    if dtype == W.BF16:
+        return W.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.float().cpu().numpy()
+
+
+def unpack_tree(Z, g: W.Geometry, tree_np: np.ndarray, b: int, kvh: int):
+    """Level arrays (k_hat [n, R, d] float, b_hat [n, R] float32) of one tree from the blob."""
+    gm = Z.geom(g)
+    out = []
+    for ell in range(1, g.L + 1):
+        ko, bo, stride = Z.level_offset(gm, ell)
+        base = (b * g.H_kv + kvh) * stride
+        n = g.n_level(ell)
+        nk = n * g.R * g.d
+        if g.dtype == W.BF16:
+            k = W.bf16_bits_to_f32(tree_np[base + ko: base + ko + 2 * nk].view(np.uint16))
+        else:
+            k = tree_np[base + ko: base + ko + 4 * nk].view(np.float32)
+        bh = tree_np[base + bo: base + bo + 4 * n * g.R].view(np.float32)
+        out.append((k.reshape(n, g.R, g.d), bh.reshape(n, g.R)))
+    return out
+
+
+@dataclass
+class Parity:
+    heads: int = 0
+    exact: int = 0  # S_1 and every level's (K, m) equal
+    fragile_diverged: int = 0  # differ, oracle flagged a fragile level at/above the divergence
+    mismatched: list = field(default_factory=list)  # non-fragile divergences (must stay empty)
+    fragile_levels: int = 0  # fragile levels seen by the oracle (reported)
+    max_err: float = 0.0  # over heads whose S_1 matched
+    out_checked: int = 0
+    out_bad: list = field(default_factory=list)
+
+    def summary(self) -> str:
+        return (f"heads={self.heads} exact={self.exact} fragile_diverged={self.fragile_diverged} "
+                f"mismatched={len(self.mismatched)} fragile_levels={self.fragile_levels} "
+                f"outputs_checked={self.out_checked} max_abs_err={self.max_err:.3g} "
+                f"out_bad={len(self.out_bad)}")
+
+
+def compare_head(par: Parity, r: O.Route, sel_row: np.ndarray, cnt: int, stats: np.ndarray,
+                 o_gpu: np.ndarray | None, o_ref: np.ndarray | None, tol: float, tag):
+    """Accumulates the parity verdict of one query head (route, then output)."""
+    par.heads += 1
+    L = len(r.S)
+    par.fragile_levels += sum(r.fragile)
+    gpu_S1 = sel_row[:cnt] if cnt >= 0 else None
+    first_div = None
+    for ell in range(L, 0, -1):
+        if stats[ell - 1, 0] != r.K[ell - 1] or stats[ell - 1, 1] != len(r.S[ell - 1]):
+            first_div = ell
+            break
+    same_S1 = gpu_S1 is not None and np.array_equal(gpu_S1, r.S1)
+    if first_div is None and same_S1:
+        par.exact += 1
+    else:
+        lim = first_div if first_div is not None else 1
+        if any(r.fragile[ell - 1] for ell in range(lim, L + 1)):
+            par.fragile_diverged += 1
+        else:
+            par.mismatched.append((tag, first_div, cnt, len(r.S1)))
+        return
+    if o_gpu is not None:
+        err = float(np.max(np.abs(o_gpu.astype(np.float64) - o_ref)))
+        par.out_checked += 1
+        par.max_err = max(par.max_err, err)
+        if not err <= tol:
+            par.out_bad.append((tag, err))
+
+
+def oracle_trees(g: W.Geometry, K: np.ndarray, qref: np.ndarray, pairs):
+    trees = {}
+    for b, kvh in pairs:
+        keys = W.to_float(K[b, kvh], g.dtype).astype(np.float64)
+        trees[(b, kvh)] = O.build_tree(keys, qref[kvh], g.C, g.L, g.dtype)
+    return trees
+
+
+def tree_mismatch(Z, g, tree_np, trees):
+    """Counts of stored k_hat / b_hat entries where the device tree differs from the oracle's."""
+    bad_k = bad_b = total = 0
+    for (b, kvh), t in trees.items():
+        levels = unpack_tree(Z, g, tree_np, b, kvh)
+        for ell, (k, bh) in enumerate(levels, start=1):
+            lv = t.levels[ell - 1]
+            bad_k += int(np.count_nonzero(k.astype(np.float64) != lv.k_store))
+            bad_b += int(np.count_nonzero(bh.astype(np.float64) != lv.b_store))
+            total += k.size
+    return bad_k, bad_b, total
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+
+def log2i(x):
+    return int(round(math.log2(x)))
