@@ -255,6 +255,18 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
             "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap}
 
 
+def copy_calibration():
+    """One plain copy of 1 GiB: reads and writes 2^30 bytes each, for scaling HBM counters."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,7 +276,12 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle baseline (0 disables)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU: the hot path has no multi-GPU mode "
             "(run with --gpus 1)")

@@ -61,10 +61,13 @@ BuildArgs make_build_args(const zha_geom* g) {
   return a;
 }
 
+#ifndef ZHA_ATTN_TARGET_BLOCKS
+#define ZHA_ATTN_TARGET_BLOCKS 2048
+#endif
 int attn_splits(int64_t n_heads) {
-  int64_t s = (2048 + n_heads - 1) / n_heads;
+  int64_t s = (ZHA_ATTN_TARGET_BLOCKS + n_heads - 1) / n_heads;
   if (s < 1) s = 1;
-  if (s > 32) s = 32;
+  if (s > 64) s = 64;
   return (int)s;
 }
 

@@ -17,6 +17,7 @@
 // is read once per group.
 
 #include "zha_internal.hpp"
+#include "zha_wave.hpp"
 
 namespace zha {
 namespace {
@@ -100,7 +101,7 @@ __device__ __forceinline__ void online_update(float& m, float& l, float* acc, co
 // O = sum_s e^{M_s - M} acc_s / sum_s e^{M_s - M} l_s.
 template <typename T, int D>
 __device__ __forceinline__ void merge_partials(const float* part_head, int S, T* out_row) {
-  const volatile float* p = part_head;  // written by other workgroups: bypass L1
+  const float* __restrict__ p = part_head;
   for (int t = threadIdx.x; t < D; t += kThreads) {
     float M = -INFINITY;
     for (int s = 0; s < S; ++s) M = fmaxf(M, p[s * (D + 2) + D]);
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) dot = fmaf(q[e], k[e], dot);
-        dot = group_sum<LPR>(dot);
+        dot = group_allreduce<LPR>(dot, OpAdd());
         s[u] = (s[u] == -INFINITY) ? -INFINITY : dot;
       }
       online_update<T, kUA>(m, l, acc, s, vv);
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) dot = fmaf(q[g][e], k[e], dot);
-        dot = group_sum<LPR>(dot);
+        dot = group_allreduce<LPR>(dot, OpAdd());
         s[u] = ok[u] ? dot : -INFINITY;
       }
       online_update<T, kUD>(m[g], l[g], acc[g], s, vv);

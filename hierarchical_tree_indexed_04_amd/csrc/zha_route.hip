@@ -19,135 +19,161 @@
 // masses make every partial sum exact, hence independent of summation order:
 // the result is deterministic and the prefix test W_m >= p Z is evaluated on
 // the exact sums of the quantised weights.
-//   1. A 256-bucket histogram over (s_max - s) (monotone in the key) finds the
-//      bucket where the running mass crosses p Z.
-//   2. If that bucket holds more than 64 candidates, 8-bit radix passes over
-//      the keys inside it narrow it further (ties in score fall to the id
-//      bits).
-//   3. One wave ranks the <= 64 boundary candidates: a candidate is kept iff
-//      the mass of all keys below it is < p Z.  The largest kept key, kappa,
-//      defines the cut: kept = {key <= kappa}.
+//   * Frontiers of at most 64 candidates: wave 0 holds one candidate per lane
+//     and keeps a candidate iff the mass of all smaller keys is < p Z.
+//   * Larger frontiers: a 256-bucket histogram over (s_max - s) (monotone in
+//     the key) finds the bucket where the running mass crosses p Z; 8-bit
+//     radix passes over the keys narrow a crowded bucket (ties in score fall
+//     to the id bits) until at most 64 candidates remain, which wave 0 then
+//     ranks as above.
+// kappa, the largest kept key, defines the cut: kept = {key <= kappa}.
 // Compaction keeps ascending id order with per-wave ballots, and the next
 // frontier is written as children of the kept nodes.
+//
+// Reductions and scans use DPP lane moves (zha_wave.hpp).
 
 #include "zha_internal.hpp"
+#include "zha_wave.hpp"
 
 namespace zha {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kU = 8;  // summary rows in flight per lane while scoring
-constexpr float kFix = 1099511627776.0f;  // 2^40
+#ifndef ZHA_ROUTE_ROWS
+#define ZHA_ROUTE_ROWS 16
+#endif
+#ifndef ZHA_ROUTE_XCD
+#define ZHA_ROUTE_XCD 1
+#endif
+constexpr int kU = ZHA_ROUTE_ROWS;  // summary rows in flight per lane while scoring
 
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-  const int lo = __shfl((int)(uint32_t)v, src, kWave);
-  const int hi = __shfl((int)(uint32_t)(v >> 32), src, kWave);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const int lo = __shfl_xor((int)(uint32_t)v, m, kWave);
-  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m, kWave);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
-  const int lo = __shfl_up((int)(uint32_t)v, d, kWave);
-  const int hi = __shfl_up((int)(uint32_t)(v >> 32), d, kWave);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int j) {
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, j);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), j);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t t = shfl_xor_u64(v, o);
-    v = t > v ? t : v;
-  }
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t t = shfl_xor_u64(v, o);
-    v = t < v ? t : v;
-  }
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += shfl_xor_u64(v, o);
-  return v;
-}
+#ifndef ZHA_ROUTE_PROFILE
+#define ZHA_ROUTE_PROFILE 0
+#endif
 
 __device__ __forceinline__ uint64_t make_key(float s, int32_t id) {
   return ((uint64_t)(~ord_f32(s)) << 32) | (uint32_t)id;
 }
-__device__ __forceinline__ float key_score(uint64_t k) {
-  return unord_f32(~(uint32_t)(k >> 32));
-}
+__device__ __forceinline__ float key_score(uint64_t k) { return unord_f32(~(uint32_t)(k >> 32)); }
+
+// floor(exp(s - smax) * 2^40), exactly: w * 2^8 = hi + frac with frac in [0, 1).
 __device__ __forceinline__ uint64_t fixed_mass(float s, float smax) {
-  return (uint64_t)(expf(s - smax) * kFix);
+  const float t = __expf(s - smax) * 256.0f;
+  const uint32_t hi = (uint32_t)t;
+  const uint32_t lo = (uint32_t)((t - (float)hi) * 4294967296.0f);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 template <int FMAX>
 struct RouteSmem {
-  int32_t fr[2][FMAX];         // frontier node ids, ascending (ping-pong)
-  float sc[FMAX];              // scores of the current frontier
-  int32_t comp[FMAX / 2];      // kept ids of a level > 1 (m * C <= FMAX, C >= 2)
-  uint32_t hcnt[256];          // histogram: candidates per bucket
-  unsigned long long hmass[256];  // histogram: fixed-point mass per bucket
-  unsigned long long bkey[64];    // boundary candidates
-  unsigned long long bw[64];
-  uint32_t wcnt[FMAX / kThreads][kWaves];  // kept per (round, wave), then offsets
-  unsigned long long redu[kWaves];
+  int32_t fr[2][FMAX];               // frontier node ids, ascending (ping-pong)
+  float sc[FMAX];                    // scores of the current frontier
+  uint32_t hcnt[256];                // histogram: candidates per bucket
+  unsigned long long hmass[256];     // histogram: fixed-point mass per bucket
+  unsigned long long bkey[kWave];    // boundary candidates
+  unsigned long long bw[kWave];
+  int32_t small_ids[kWave];          // kept ids of a frontier of <= 64 candidates
+  uint32_t wcnt[FMAX / kThreads * kWaves];  // kept per (round, wave)
   float redf[2][kWaves];
-  unsigned long long kappa, base, lo, hi;
+  unsigned long long redu[2][kWaves];
+  unsigned long long kappa, next, base;
   double target;
   int32_t bstar, bcount, bl_n, m;
 };
 
-// Block-wide reductions (all threads participate; result broadcast).
-template <int FMAX>
-__device__ __forceinline__ void block_minmax_f(RouteSmem<FMAX>& sm, float& mx, float& mn) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  mx = group_max<kWave>(mx);
-  mn = -group_max<kWave>(-mn);
-  if (lane == 0) {
-    sm.redf[0][wave] = mx;
-    sm.redf[1][wave] = mn;
+// Scores of the frontier: s_i = max_r (q . k_hat_{r,i} + b_hat_{r,i}), q pre-scaled by 1/sqrt(d).
+// LPR lanes read one 16-byte slice each of a summary row; kU rows per lane are in flight.
+template <typename T, int D, int FMAX>
+__device__ __forceinline__ void score_frontier(RouteSmem<FMAX>& sm, const int32_t* fr, int K,
+                                               int R, const char* __restrict__ khat,
+                                               const float* __restrict__ bhat, const float* q) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int LPR = D / VEC;
+  constexpr int RPB = kThreads / LPR;
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR, grp = tid / LPR;
+  uint32_t* sco = reinterpret_cast<uint32_t*>(sm.sc);
+  if (R > 1) {
+    for (int i = tid; i < K; i += kThreads) sco[i] = 0u;
+    __syncthreads();
   }
-  __syncthreads();
-  mx = fmaxf(fmaxf(sm.redf[0][0], sm.redf[0][1]), fmaxf(sm.redf[0][2], sm.redf[0][3]));
-  mn = fminf(fminf(sm.redf[1][0], sm.redf[1][1]), fminf(sm.redf[1][2], sm.redf[1][3]));
-  __syncthreads();
-}
-
-template <int FMAX, bool kMin>
-__device__ __forceinline__ uint64_t block_ext_u64(RouteSmem<FMAX>& sm, uint64_t v) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  v = kMin ? wave_min_u64(v) : wave_max_u64(v);
-  if (lane == 0) sm.redu[wave] = v;
-  __syncthreads();
-  uint64_t r = sm.redu[0];
+  const int NR = K * R;
+  for (int base = 0; base < NR; base += RPB * kU) {
+    // Slots beyond the last live row are skipped with uniform branches: a
+    // wave64 VALU op costs the SIMD 4 cycles, so dead slots are not free.
+    const int nu = min(kU, (NR - base + RPB - 1) / RPB);
+    uint4 v[kU];
+    float bias[kU];
+    // Loads are straight-line (dead slots are masked lanes, no traffic) so
+    // each slot's wait counts exactly the loads still in flight after it.
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) {
-    const uint64_t t = sm.redu[w];
-    r = kMin ? (t < r ? t : r) : (t > r ? t : r);
+    for (int u = 0; u < kU; ++u) {
+      const int x = base + u * RPB + grp;
+      if (x < NR) {
+        const int node = fr[R == 1 ? x : x / R];
+        const int r = R == 1 ? 0 : x % R;
+        const int64_t row = (int64_t)node * R + r;
+        v[u] = ld16c(khat + row * (int64_t)(D * sizeof(T)) + sub * 16);
+        bias[u] = bhat[row];
+      } else {
+        v[u] = make_uint4(0u, 0u, 0u, 0u);
+        bias[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (u < nu) {
+        const int x = base + u * RPB + grp;
+        float k[VEC];
+        Vec<T>::widen(v[u], k);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dot = fmaf(q[e], k[e], dot);
+        dot = group_allreduce<LPR>(dot, OpAdd());
+        if (sub == 0 && x < NR) {
+          const float s = dot + bias[u];
+          if (R == 1)
+            sm.sc[x] = s;
+          else
+            atomicMax(&sco[x / R], ord_f32(s));
+        }
+      }
+    }
+  }
+  if (R > 1) {
+    __syncthreads();
+    for (int i = tid; i < K; i += kThreads) sm.sc[i] = unord_f32(sco[i]);
   }
   __syncthreads();
-  return r;
 }
 
-// Wave 0: scan the 256-bucket histogram from `base0`, find the first bucket
+// Wave 0: exact resolution of n <= 64 boundary candidates (one per lane).  A
+// candidate is kept iff base + (mass of the candidates with smaller keys) < target.
+// Writes kappa (largest kept key) to LDS; returns the kept flag of this lane.
+template <int FMAX>
+__device__ __forceinline__ bool resolve_boundary(RouteSmem<FMAX>& sm, uint64_t key, uint64_t w,
+                                                 int n, uint64_t base, double target) {
+  const int lane = threadIdx.x;
+  uint64_t below = 0;
+  for (int j = 0; j < n; ++j) {
+    const uint64_t kj = readlane_u64(key, j);
+    const uint64_t wj = readlane_u64(w, j);
+    below += (kj < key) ? wj : 0ull;
+  }
+  const bool kept = lane < n && (double)(base + below) < target;
+  const uint64_t kappa = wave_allreduce_u64(kept ? key : 0ull, OpMax());
+  if (lane == 0) sm.kappa = kappa;
+  return kept;
+}
+
+// Wave 0: scan the 256-bucket histogram from base0 and find the first bucket
 // whose inclusive running mass reaches the target.  With `first`, the total
 // mass Z is the histogram's sum and the target p Z is set.
 template <int FMAX>
 __device__ __forceinline__ void scan_find(RouteSmem<FMAX>& sm, uint64_t base0, bool first,
                                           float p) {
-  const int lane = threadIdx.x;  // wave 0 only
+  const int lane = threadIdx.x;
   uint64_t c[4];
   uint64_t run = 0;
 #pragma unroll
@@ -155,17 +181,11 @@ __device__ __forceinline__ void scan_find(RouteSmem<FMAX>& sm, uint64_t base0, b
     run += sm.hmass[4 * lane + k];
     c[k] = run;
   }
-  uint64_t incl = run;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint64_t t = shfl_up_u64(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const uint64_t incl = wave_incl_scan_u64(run);
   const uint64_t excl = incl - run;
   double target;
   if (first) {
-    const uint64_t Z = readlane_u64(incl, kWave - 1);
-    target = (double)p * (double)Z;
+    target = (double)p * (double)readlane_u64(incl, kWave - 1);
   } else {
     target = sm.target;
   }
@@ -184,126 +204,46 @@ __device__ __forceinline__ void scan_find(RouteSmem<FMAX>& sm, uint64_t base0, b
   }
 }
 
-// Wave 0: exact resolution of n <= 64 boundary candidates (one per lane).  A
-// candidate is kept iff base + (mass of the candidates with smaller keys) < target.
-template <int FMAX>
-__device__ __forceinline__ void resolve_boundary(RouteSmem<FMAX>& sm, uint64_t key, uint64_t w,
-                                                 int n, uint64_t base, double target) {
-  const int lane = threadIdx.x;
-  const bool valid = lane < n;
-  uint64_t below = 0;
-  for (int j = 0; j < n; ++j) {
-    const uint64_t kj = readlane_u64(key, j);
-    const uint64_t wj = readlane_u64(w, j);
-    below += (kj < key) ? wj : 0ull;
-  }
-  const bool kept = valid && (double)(base + below) < target;
-  const uint64_t kappa = wave_max_u64(kept ? key : 0ull);
-  if (lane == 0) sm.kappa = kappa;
-}
-
-// Wave 0: resolve the candidates collected in bkey/bw (after a barrier).
-template <int FMAX>
-__device__ __forceinline__ void resolve_collected(RouteSmem<FMAX>& sm) {
-  const int lane = threadIdx.x;
-  const int n = min(sm.bl_n, kWave);
-  const uint64_t key = lane < n ? sm.bkey[lane] : ~0ull;
-  const uint64_t w = lane < n ? sm.bw[lane] : 0ull;
-  resolve_boundary(sm, key, w, n, sm.base, sm.target);
-}
-
-// Scores of the frontier: s_i = max_r (q . k_hat_{r,i} + b_hat_{r,i}), q pre-scaled by 1/sqrt(d).
-template <typename T, int D, int FMAX>
-__device__ __forceinline__ void score_frontier(RouteSmem<FMAX>& sm, const int32_t* fr, int K,
-                                               int R, const char* __restrict__ khat,
-                                               const float* __restrict__ bhat, const float* q) {
-  constexpr int VEC = Vec<T>::N;
-  constexpr int LPR = D / VEC;
-  constexpr int RPB = kThreads / LPR;
-  const int tid = threadIdx.x;
-  const int sub = tid % LPR, grp = tid / LPR;
-  uint32_t* sco = reinterpret_cast<uint32_t*>(sm.sc);
-  if (R > 1) {
-    for (int i = tid; i < K; i += kThreads) sco[i] = 0u;
-    __syncthreads();
-  }
-  const int NR = K * R;
-  for (int base = 0; base < NR; base += RPB * kU) {
-    uint4 v[kU];
-    float bias[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int x = base + u * RPB + grp;
-      if (x < NR) {
-        const int node = fr[R == 1 ? x : x / R];
-        const int r = R == 1 ? 0 : x % R;
-        const int64_t row = (int64_t)node * R + r;
-        v[u] = ld16c(khat + row * (int64_t)(D * sizeof(T)) + sub * 16);
-        bias[u] = bhat[row];
-      } else {
-        v[u] = make_uint4(0u, 0u, 0u, 0u);
-        bias[u] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int x = base + u * RPB + grp;
-      float k[VEC];
-      Vec<T>::widen(v[u], k);
-      float dot = 0.f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) dot = fmaf(q[e], k[e], dot);
-      dot = group_sum<LPR>(dot);
-      if (sub == 0 && x < NR) {
-        const float s = dot + bias[u];
-        if (R == 1)
-          sm.sc[x] = s;
-        else
-          atomicMax(&sco[x / R], ord_f32(s));
-      }
-    }
-  }
-  if (R > 1) {
-    __syncthreads();
-    for (int i = tid; i < K; i += kThreads) sm.sc[i] = unord_f32(sco[i]);
-  }
+template <int FMAX, typename Op>
+__device__ __forceinline__ uint64_t block_allreduce_u64(RouteSmem<FMAX>& sm, uint64_t v, Op op,
+                                                        int slot) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  v = wave_allreduce_u64(v, op);
+  if (lane == 0) sm.redu[slot][wave] = v;
   __syncthreads();
+  uint64_t r = sm.redu[slot][0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = op(r, (uint64_t)sm.redu[slot][w]);
+  __syncthreads();
+  return r;
 }
 
-// Finds kappa, the largest kept key, for a frontier of K > 1 candidates (p < 1).
+// Cut of a frontier of K > 64 candidates (p < 1).  The histogram and bl_n are
+// zeroed before the scoring barrier.  Returns kappa.
 template <int FMAX>
-__device__ __forceinline__ uint64_t top_p_cut(RouteSmem<FMAX>& sm, const int32_t* fr, int K,
-                                              float p) {
-  const int tid = threadIdx.x, wave = tid >> 6;
+__device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const int32_t* fr,
+                                                    int K, float p) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   float smax = -INFINITY, smin = INFINITY;
   for (int i = tid; i < K; i += kThreads) {
     const float s = sm.sc[i];
     smax = fmaxf(smax, s);
     smin = fminf(smin, s);
   }
-  block_minmax_f(sm, smax, smin);
-
-  if (K <= kWave) {
-    if (wave == 0) {
-      const int lane = tid;
-      const bool valid = lane < K;
-      const float s = valid ? sm.sc[lane] : 0.f;
-      const uint64_t key = valid ? make_key(s, fr[lane]) : ~0ull;
-      const uint64_t w = valid ? fixed_mass(s, smax) : 0ull;
-      const uint64_t Z = wave_sum_u64(w);
-      resolve_boundary(sm, key, w, K, 0ull, (double)p * (double)Z);
-    }
-    __syncthreads();
-    return sm.kappa;
+  smax = wave_allreduce_f32(smax, OpMax());
+  smin = wave_allreduce_f32(smin, OpMin());
+  if (lane == 0) {
+    sm.redf[0][wave] = smax;
+    sm.redf[1][wave] = smin;
   }
+  __syncthreads();
+  smax = fmaxf(fmaxf(sm.redf[0][0], sm.redf[0][1]), fmaxf(sm.redf[0][2], sm.redf[0][3]));
+  smin = fminf(fminf(sm.redf[1][0], sm.redf[1][1]), fminf(sm.redf[1][2], sm.redf[1][3]));
 
   // 1. Value-space histogram over (s_max - s).
   const float range = fminf(smax - smin, 32.f);
   const float bscale = range > 0.f ? 256.f / range : 0.f;
   auto bucket = [&](float s) { return min((int)((smax - s) * bscale), 255); };
-  sm.hcnt[tid] = 0u;
-  sm.hmass[tid] = 0ull;
-  __syncthreads();
   for (int i = tid; i < K; i += kThreads) {
     const float s = sm.sc[i];
     const int bk = bucket(s);
@@ -315,8 +255,6 @@ __device__ __forceinline__ uint64_t top_p_cut(RouteSmem<FMAX>& sm, const int32_t
   __syncthreads();
   const int bstar = sm.bstar;
   if (sm.bcount <= kWave) {
-    if (tid == 0) sm.bl_n = 0;
-    __syncthreads();
     for (int i = tid; i < K; i += kThreads) {
       const float s = sm.sc[i];
       if (bucket(s) == bstar) {
@@ -328,12 +266,18 @@ __device__ __forceinline__ uint64_t top_p_cut(RouteSmem<FMAX>& sm, const int32_t
       }
     }
     __syncthreads();
-    if (wave == 0) resolve_collected(sm);
+    if (wave == 0) {
+      const int n = min(sm.bl_n, kWave);
+      resolve_boundary(sm, lane < n ? sm.bkey[lane] : ~0ull, lane < n ? sm.bw[lane] : 0ull, n,
+                       sm.base, sm.target);
+    }
     __syncthreads();
     return sm.kappa;
   }
 
-  // 2. Radix refinement over the keys of the crowded bucket.
+  // 2. Radix refinement over the keys of the crowded bucket.  Keys are
+  // distinct (ids are), so every pass fixes at least 8 more bits; the pass
+  // bound is defensive.
   uint64_t lo = ~0ull, hi = 0ull;
   for (int i = tid; i < K; i += kThreads) {
     const float s = sm.sc[i];
@@ -343,16 +287,15 @@ __device__ __forceinline__ uint64_t top_p_cut(RouteSmem<FMAX>& sm, const int32_t
       hi = k > hi ? k : hi;
     }
   }
-  lo = block_ext_u64<FMAX, true>(sm, lo);
-  hi = block_ext_u64<FMAX, false>(sm, hi);
-  // Keys are distinct (ids are), so every pass fixes at least 8 more bits and
-  // at most 8 passes reach a single key; the bound below is defensive.
+  lo = block_allreduce_u64(sm, lo, OpMin(), 0);
+  hi = block_allreduce_u64(sm, hi, OpMax(), 1);
   for (int pass = 0;; ++pass) {
     const bool last_pass = pass >= 8 || lo == hi;
     const int hb = (lo == hi) ? 0 : 63 - __clzll((long long)(lo ^ hi));
     const int shift = hb > 7 ? hb - 7 : 0;
     sm.hcnt[tid] = 0u;
     sm.hmass[tid] = 0ull;
+    if (tid == 0) sm.bl_n = 0;
     __syncthreads();
     for (int i = tid; i < K; i += kThreads) {
       const float s = sm.sc[i];
@@ -372,8 +315,6 @@ __device__ __forceinline__ uint64_t top_p_cut(RouteSmem<FMAX>& sm, const int32_t
     const uint64_t nlo = first > lo ? first : lo;
     const uint64_t nhi = last < hi ? last : hi;
     if (sm.bcount <= kWave || last_pass) {
-      if (tid == 0) sm.bl_n = 0;
-      __syncthreads();
       for (int i = tid; i < K; i += kThreads) {
         const float s = sm.sc[i];
         const uint64_t k = make_key(s, fr[i]);
@@ -386,7 +327,11 @@ __device__ __forceinline__ uint64_t top_p_cut(RouteSmem<FMAX>& sm, const int32_t
         }
       }
       __syncthreads();
-      if (wave == 0) resolve_collected(sm);
+      if (wave == 0) {
+        const int n = min(sm.bl_n, kWave);
+        resolve_boundary(sm, lane < n ? sm.bkey[lane] : ~0ull, lane < n ? sm.bw[lane] : 0ull,
+                         n, sm.base, sm.target);
+      }
       __syncthreads();
       return sm.kappa;
     }
@@ -399,8 +344,8 @@ __device__ __forceinline__ uint64_t top_p_cut(RouteSmem<FMAX>& sm, const int32_t
         hi = k > hi ? k : hi;
       }
     }
-    lo = block_ext_u64<FMAX, true>(sm, lo);
-    hi = block_ext_u64<FMAX, false>(sm, hi);
+    lo = block_allreduce_u64(sm, lo, OpMin(), 0);
+    hi = block_allreduce_u64(sm, hi, OpMax(), 1);
   }
 }
 
@@ -413,14 +358,20 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
                                                          float* __restrict__ gapo) {
   constexpr int VEC = Vec<T>::N;
   constexpr int LPR = D / VEC;
+  constexpr int kRounds = FMAX / kThreads;
   __shared__ RouteSmem<FMAX> sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int64_t head = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
+  // range of heads so the heads sharing a tree share that XCD's L2.
+  const int64_t head = ZHA_ROUTE_XCD ? xcd_major_index(blockIdx.x, a.n_heads) : blockIdx.x;
   const int h = (int)(head % a.H_q);
   const int64_t b = head / ((int64_t)a.n_pos * a.H_q);
   const int kvh = h / a.G;
   const char* tb = tree + (b * a.H_kv + kvh) * a.lay.stride;
   const int R = a.lay.R, C = a.lay.C, L = a.lay.L;
+  const int log2C = (C & (C - 1)) == 0 ? __ffs(C) - 1 : -1;
+  const bool want_gap = gapo != nullptr;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   float q[VEC];
   {
@@ -441,52 +392,101 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
   for (int l = L; l >= 1 && !overflow; --l) {
     const int32_t* fr = sm.fr[cur];
     int32_t* nx = sm.fr[cur ^ 1];
-    uint64_t kappa = ~0ull;
-    if (K > 1) {
+#if ZHA_ROUTE_PROFILE
+    const uint64_t t0 = wall_clock64();
+    uint64_t t1 = t0, t2 = t0;
+#endif
+    const bool large = K > kWave;
+    if (large) {  // zeroed here, made visible by the scoring barrier
+      sm.hcnt[tid] = 0u;
+      sm.hmass[tid] = 0ull;
+      if (tid == 0) sm.bl_n = 0;
+    }
+    if (K > 1)
       score_frontier<T, D, FMAX>(sm, fr, K, R, tb + a.lay.khat[l],
                                  reinterpret_cast<const float*>(tb + a.lay.bhat[l]), q);
-      kappa = top_p_cut<FMAX>(sm, fr, K, a.p);
-    }
-    const bool all = kappa == ~0ull;
-
-    // Compaction: kept flags per round of 256 positions, ballots give ascending ranks.
-    const int rounds = (K + kThreads - 1) / kThreads;
+#if ZHA_ROUTE_PROFILE
+    t1 = wall_clock64();
+#endif
+    int m = 0;
     uint64_t next_key = ~0ull;
-    for (int e = 0; e < rounds; ++e) {
-      const int i = e * kThreads + tid;
-      bool kept = false;
-      if (i < K) {
-        const uint64_t k = all ? 0ull : make_key(sm.sc[i], fr[i]);
-        kept = all || k <= kappa;
-        if (!kept) next_key = k < next_key ? k : next_key;
-      }
-      const uint64_t bal = __ballot(kept);
-      if (lane == 0) sm.wcnt[e][wave] = (uint32_t)__popcll((unsigned long long)bal);
-    }
-    if (!all) next_key = block_ext_u64<FMAX, true>(sm, next_key);
-    else __syncthreads();
-    if (tid == 0) {
-      uint32_t run = 0;
-      for (int e = 0; e < rounds; ++e)
-        for (int w = 0; w < kWaves; ++w) {
-          const uint32_t c = sm.wcnt[e][w];
-          sm.wcnt[e][w] = run;
-          run += c;
+    uint64_t kappa = ~0ull;
+    if (!large) {
+      // Wave 0 cuts and compacts; the other waves wait at the barrier.
+      if (wave == 0) {
+        const bool valid = lane < K;
+        bool kept = valid;
+        if (K > 1) {
+          const float s = valid ? sm.sc[lane] : -INFINITY;
+          const float smax = wave_allreduce_f32(s, OpMax());
+          const uint64_t key = valid ? make_key(s, fr[lane]) : ~0ull;
+          const uint64_t w = valid ? fixed_mass(s, smax) : 0ull;
+          const uint64_t Z = wave_allreduce_u64(w, OpAdd());
+          kept = resolve_boundary(sm, key, w, K, 0ull, (double)a.p * (double)Z);
+          if (want_gap) {
+            const uint64_t nk = wave_allreduce_u64((valid && !kept) ? key : ~0ull, OpMin());
+            if (lane == 0) sm.next = nk;
+          }
+        } else if (lane == 0) {
+          sm.kappa = ~0ull;
+          sm.next = ~0ull;
         }
-      sm.m = (int32_t)run;
+        const uint64_t bal = __ballot(kept);
+        if (kept) sm.small_ids[__popcll((unsigned long long)(bal & lt))] = fr[lane];
+        if (lane == 0) sm.m = __popcll((unsigned long long)bal);
+      }
+      __syncthreads();
+      m = sm.m;
+      kappa = sm.kappa;
+      next_key = sm.next;
+    } else {
+      kappa = top_p_cut_large<FMAX>(sm, fr, K, a.p);
     }
-    __syncthreads();
-    const int m = sm.m;
+#if ZHA_ROUTE_PROFILE
+    t2 = wall_clock64();
+#endif
+    uint32_t mybits = 0;
+    if (large) {
+      // Kept flags per round of 256 positions; ballots give ascending ranks.
+      const int rounds = (K + kThreads - 1) / kThreads;
+#pragma unroll
+      for (int e = 0; e < kRounds; ++e) {
+        if (e < rounds) {
+          const int i = e * kThreads + tid;
+          bool kept = false;
+          if (i < K) {
+            const uint64_t k = make_key(sm.sc[i], fr[i]);
+            kept = k <= kappa;
+            if (!kept && k < next_key) next_key = k;
+          }
+          const uint64_t bal = __ballot(kept);
+          if (lane == 0) sm.wcnt[e * kWaves + wave] = (uint32_t)__popcll((unsigned long long)bal);
+          mybits |= (kept ? 1u : 0u) << e;
+        }
+      }
+      if (want_gap) {
+        next_key = wave_allreduce_u64(next_key, OpMin());
+        if (lane == 0) sm.redu[0][wave] = next_key;
+      }
+      __syncthreads();
+      for (int x = 0; x < rounds * kWaves; ++x) m += (int)sm.wcnt[x];
+      if (want_gap) {
+        next_key = sm.redu[0][0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+          next_key = sm.redu[0][w] < next_key ? (uint64_t)sm.redu[0][w] : next_key;
+      }
+    }
     if (tid == 0) {
       const int64_t o = head * L + (l - 1);
       if (stats != nullptr) {
         stats[2 * o] = K;
         stats[2 * o + 1] = m;
       }
-      if (gapo != nullptr)
-        gapo[o] = (all || next_key == ~0ull) ? INFINITY : key_score(kappa) - key_score(next_key);
+      if (want_gap)
+        gapo[o] = (next_key == ~0ull || kappa == ~0ull) ? INFINITY
+                                                        : key_score(kappa) - key_score(next_key);
     }
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if (l > 1) {
       const int n_orph = (int)(a.lay.n[l - 1] - (int64_t)C * a.lay.n[l]);
       const int64_t knext = (int64_t)m * C + n_orph;
@@ -494,14 +494,30 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
         overflow = true;
         break;
       }
-      for (int e = 0; e < rounds; ++e) {
-        const int i = e * kThreads + tid;
-        const bool kept = i < K && (all || make_key(sm.sc[i], fr[i]) <= kappa);
-        const uint64_t bal = __ballot(kept);
-        if (kept) sm.comp[sm.wcnt[e][wave] + __popcll((unsigned long long)(bal & lt))] = fr[i];
+      if (!large) {
+        for (int x = tid; x < m * C; x += kThreads) {
+          const int j = log2C >= 0 ? (x >> log2C) : x / C;
+          nx[x] = sm.small_ids[j] * C + (x - j * C);
+        }
+      } else {
+        uint32_t run = 0;
+        const int rounds = (K + kThreads - 1) / kThreads;
+#pragma unroll
+        for (int e = 0; e < kRounds; ++e) {
+          if (e < rounds) {
+            const bool kept = (mybits >> e) & 1u;
+            const uint64_t bal = __ballot(kept);
+            uint32_t off = run;
+            for (int w = 0; w < wave; ++w) off += sm.wcnt[e * kWaves + w];
+            for (int w = 0; w < kWaves; ++w) run += sm.wcnt[e * kWaves + w];
+            if (kept) {
+              const int j = (int)off + __popcll((unsigned long long)(bal & lt));
+              const int id = fr[e * kThreads + tid];
+              for (int c = 0; c < C; ++c) nx[j * C + c] = id * C + c;
+            }
+          }
+        }
       }
-      __syncthreads();
-      for (int x = tid; x < m * C; x += kThreads) nx[x] = sm.comp[x / C] * C + x % C;
       const int first_orphan = (int)((int64_t)C * a.lay.n[l]);
       for (int x = tid; x < n_orph; x += kThreads) nx[m * C + x] = first_orphan + x;
       __syncthreads();
@@ -509,17 +525,39 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
       cur ^= 1;
     } else {
       int32_t* out = sel + head * a.cap;
-      for (int e = 0; e < rounds; ++e) {
-        const int i = e * kThreads + tid;
-        const bool kept = i < K && (all || make_key(sm.sc[i], fr[i]) <= kappa);
-        const uint64_t bal = __ballot(kept);
-        if (kept) {
-          const int j = (int)sm.wcnt[e][wave] + __popcll((unsigned long long)(bal & lt));
-          if (j < a.cap) out[j] = fr[i];
+      if (!large) {
+        for (int j = tid; j < m && j < a.cap; j += kThreads) out[j] = sm.small_ids[j];
+      } else {
+        uint32_t run = 0;
+        const int rounds = (K + kThreads - 1) / kThreads;
+#pragma unroll
+        for (int e = 0; e < kRounds; ++e) {
+          if (e < rounds) {
+            const bool kept = (mybits >> e) & 1u;
+            const uint64_t bal = __ballot(kept);
+            uint32_t off = run;
+            for (int w = 0; w < wave; ++w) off += sm.wcnt[e * kWaves + w];
+            for (int w = 0; w < kWaves; ++w) run += sm.wcnt[e * kWaves + w];
+            if (kept) {
+              const int j = (int)off + __popcll((unsigned long long)(bal & lt));
+              if (j < a.cap) out[j] = fr[e * kThreads + tid];
+            }
+          }
         }
       }
       m1 = m;
     }
+#if ZHA_ROUTE_PROFILE
+    // Profiling build: (score, cut) ticks in level_stats, compaction ticks in gap.
+    __syncthreads();
+    if (tid == 0) {
+      const uint64_t t3 = wall_clock64();
+      const int64_t o = head * L + (l - 1);
+      stats[2 * o] = (int32_t)(t1 - t0);
+      stats[2 * o + 1] = (int32_t)(t2 - t1);
+      gapo[o] = (float)(t3 - t2);
+    }
+#endif
   }
   if (tid == 0) cnt[head] = overflow ? -1 : m1;
 }

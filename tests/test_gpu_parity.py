@@ -203,7 +203,12 @@ def test_route_and_attn_are_deterministic(Z):
     for _ in range(2):
         # zero-filled so that the alignment padding between levels compares equal too
         tree = Z.build(gm, Kd, qd, tree=torch.zeros(tb, dtype=torch.uint8, device="cuda"))
-        sel, cnt, stats, gap = Z.route(gm, tree, Qd, 4, g.p, g.n_level(1))
+        cap = g.n_level(1)
+        out = (torch.full((g.B, 4, g.H_q, cap), -1, dtype=torch.int32, device="cuda"),
+               torch.empty((g.B, 4, g.H_q), dtype=torch.int32, device="cuda"),
+               torch.empty((g.B, 4, g.H_q, g.L, 2), dtype=torch.int32, device="cuda"),
+               torch.empty((g.B, 4, g.H_q, g.L), dtype=torch.float32, device="cuda"))
+        sel, cnt, stats, gap = Z.route(gm, tree, Qd, 4, g.p, cap, out=out)
         Od = Z.attn(gm, Qd, 4, Kd, Vd, sel, cnt, g.n_level(1))
         torch.cuda.synchronize()
         outs.append((tree.cpu(), sel.cpu(), cnt.cpu(), stats.cpu(), gap.cpu(), Od.cpu()))
