@@ -61,15 +61,6 @@ BuildArgs make_build_args(const zha_geom* g) {
   return a;
 }
 
-#ifndef ZHA_ATTN_TARGET_BLOCKS
-#define ZHA_ATTN_TARGET_BLOCKS 2048
-#endif
-int attn_splits(int64_t n_heads) {
-  int64_t s = (ZHA_ATTN_TARGET_BLOCKS + n_heads - 1) / n_heads;
-  if (s < 1) s = 1;
-  if (s > 64) s = 64;
-  return (int)s;
-}
 
 int dense_splits(const zha_geom* g, int32_t n_pos) {
   const int64_t groups = (int64_t)g->B * n_pos * g->H_kv * (g->H_q / g->H_kv / dense_head_tile(g->H_q / g->H_kv));
@@ -184,7 +175,7 @@ int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t
   if (n_pos < 1) return ZHA_ERR_NPOS;
   if (cap < 1) return ZHA_ERR_CAP;
   const int64_t n_heads = (int64_t)g->B * n_pos * g->H_q;
-  *bytes = (size_t)splitkv_scratch_bytes(n_heads, attn_splits(n_heads), g->d);
+  *bytes = (size_t)attn_scratch_layout_bytes(n_heads, g->d);
   return ZHA_OK;
 }
 
@@ -206,12 +197,13 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, con
   a.C = g->C;
   a.log2C = (g->C & (g->C - 1)) == 0 ? __builtin_ctz((unsigned)g->C) : -1;
   a.cap = cap;
-  a.S = attn_splits(a.n_heads);
+  a.S = ZHA_ATTN_BLOCKS;
+  const bool need_scratch = attn_scratch_layout_bytes(a.n_heads, g->d) > 0;
   if (Q == nullptr || K == nullptr || V == nullptr || sel == nullptr || cnt == nullptr ||
-      O == nullptr || (a.S > 1 && scratch == nullptr))
+      O == nullptr || (need_scratch && scratch == nullptr))
     return ZHA_ERR_NULL;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
-      (a.S > 1 && !aligned16(scratch)))
+      (need_scratch && !aligned16(scratch)))
     return ZHA_ERR_ALIGN;
   if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
   return attn_dispatch(a, g->dtype, g->d, Q, K, V, sel, cnt, O, scratch,

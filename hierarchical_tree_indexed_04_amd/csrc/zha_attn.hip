@@ -1,16 +1,23 @@
 // Exact attention over the routed token set, and the dense decode baseline.
 //
 // Sparse path (summary page of the paper, "Routing": I(q) = {0} U selected
-// leaf chunks U C_cur, o(q) = Attn(q, K_I, V_I)): every query head's token
-// list is cut into S splits of consecutive selected chunks; a workgroup
-// streams its split's K and V rows (one 16-byte slice per lane, LPR lanes per
-// row, 8 rows in flight per lane), keeps an online softmax per row group and
-// combines the row groups in LDS in a fixed order.  Split-KV partials (a
-// d-vector plus max and sum, paper App. D-B) are merged by a second, small
-// launch in split order, so results are bit-reproducible.  (Merging inside the
-// first launch would need a device-scope release/acquire per workgroup, which
-// on a multi-XCD part means an L2 write-back and invalidate each time: far
-// slower than the extra launch.)
+// leaf chunks U C_cur, o(q) = Attn(q, K_I, V_I)).  Balanced split-KV: the
+// attended tokens of all query heads of the call, laid end to end, are cut
+// into equal ranges, one per workgroup (every workgroup computes the same
+// prefix of per-head token counts in LDS).  A workgroup streams the K and V
+// rows of its range (one 16-byte slice per lane, LPR lanes per row, 8 rows in
+// flight per lane, q . k with packed bf16 dot products), keeps an online
+// softmax per row group and combines the row groups in LDS in a fixed order.
+// A head whose tokens fall in one range is written directly; otherwise each
+// range writes a partial (a d-vector plus max and sum, paper App. D-B) to slot
+// (workgroup + head), which is unique, and a second launch merges the
+// partials of each head in range order, so results are bit-reproducible.
+// (Merging inside the first launch would need a device-scope release/acquire
+// per workgroup, which on a multi-XCD part means an L2 write-back and
+// invalidate each time: far slower than the extra launch.)
+//
+// With more query heads than a workgroup can prefix-sum in LDS, each head is
+// one workgroup (no split).
 //
 // Dense path (paper App. D-A decode model): the same structure over all T
 // keys; a workgroup serves the G query heads of one KV head so each K/V row
@@ -32,6 +39,39 @@ constexpr int kThreads = 256;
 constexpr int kUA = ZHA_ATTN_ROWS;   // K/V rows in flight per lane (sparse)
 constexpr int kUD = ZHA_DENSE_ROWS;  // K/V rows in flight per lane (dense)
 constexpr int kIds = 1024;  // chunk ids staged in LDS per round (sparse)
+constexpr int kWaves = kThreads / kWave;
+constexpr int kBalMinTokens = 64;  // smallest token range of a workgroup
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// q . k over one 16-byte slice of a row.  bf16: packed bf16 dot products
+// (exact products, fp32 sums); fp32: fused multiply-adds.
+template <typename T>
+__device__ __forceinline__ float slice_dot(const uint4& k, const uint4& q) {
+  if constexpr (sizeof(T) == 2) {
+    float d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.x), as_bf16x2(q.x), 0.0f, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.y), as_bf16x2(q.y), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.z), as_bf16x2(q.z), d, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.w), as_bf16x2(q.w), d, false);
+  } else {
+    float d = __uint_as_float(k.x) * __uint_as_float(q.x);
+    d = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), d);
+    d = fmaf(__uint_as_float(k.z), __uint_as_float(q.z), d);
+    return fmaf(__uint_as_float(k.w), __uint_as_float(q.w), d);
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a 32-bit value.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp_u32<kDppRowShr1>(0u, v);
+  v += dpp_u32<kDppRowShr2>(0u, v);
+  v += dpp_u32<kDppRowShr4>(0u, v);
+  v += dpp_u32<kDppRowShr8>(0u, v);
+  v += dpp_u32<kDppRowBcast15, 0xA>(0u, v);
+  v += dpp_u32<kDppRowBcast31, 0xC>(0u, v);
+  return v;
+}
 
 
 
@@ -172,14 +212,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   }
   const int64_t ntok = nchunk_tok + n_extra;
 
-  float q[VEC];
-  {
-    const uint4 v = ld16c(Q + head * D + sub * VEC);
-    Vec<T>::widen(v, q);
-    const float inv = 1.0f / sqrtf((float)D);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) q[e] *= inv;
-  }
+  const uint4 qv = ld16c(Q + head * D + sub * VEC);
+  const float inv = 1.0f / sqrtf((float)D);
   float m = -INFINITY, l = 0.f, acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
@@ -224,12 +258,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
       }
 #pragma unroll
       for (int u = 0; u < kUA; ++u) {
-        float k[VEC];
-        Vec<T>::widen(kv[u], k);
-        float dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) dot = fmaf(q[e], k[e], dot);
-        dot = group_allreduce<LPR>(dot, OpAdd());
+        const float dot = group_allreduce<LPR>(slice_dot<T>(kv[u], qv), OpAdd()) * inv;
         s[u] = (s[u] == -INFINITY) ? -INFINITY : dot;
       }
       online_update<T, kUA>(m, l, acc, s, vv);
@@ -239,6 +268,183 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   float* phead = part + head * a.S * (int64_t)(D + 2);
   float* prow = (a.S > 1) ? phead + split * (int64_t)(D + 2) : nullptr;
   combine_groups<T, D, RPB>(m, l, acc, grp, sub, s_m, s_l, s_acc, O + head * D, prow);
+}
+
+// |I(q)| of one query head: its chunks' tokens, the tail after the last full
+// chunk and the sink when chunk 0 is not selected; 0 for a failed route.
+__device__ __forceinline__ int head_tokens(int c, int first_id, const AttnArgs& a) {
+  if (c < 0 || c > a.cap) return 0;
+  const int sink = (c == 0 || first_id != 0) ? 1 : 0;
+  return c * a.C + (int)(a.T - a.n1 * a.C) + sink;
+}
+
+// Balanced split-KV over all heads of the call: workgroup w owns tokens
+// [w W, (w + 1) W) of the concatenated per-head token lists.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_balanced_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
+    float* __restrict__ part, int32_t* __restrict__ plan, AttnArgs a) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int LPR = D / VEC;
+  constexpr int RPB = kThreads / LPR;
+  constexpr int kE = kBalMaxHeads / kThreads;
+  __shared__ int32_t s_pre[kBalMaxHeads + 1];
+  __shared__ int32_t s_ids[kIds];
+  __shared__ float s_m[RPB], s_l[RPB];
+  __shared__ float s_acc[RPB * D];
+  __shared__ uint32_t s_wtot[kWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int sub = tid % LPR, grp = tid / LPR;
+  const int nh = (int)a.n_heads;
+  const int E = (nh + kThreads - 1) / kThreads;
+
+  // 1. Prefix of per-head token counts (thread tid owns heads [tid E, tid E + E)).
+  int cv[kE], fv[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    const int h = tid * E + e;
+    cv[e] = -1;
+    fv[e] = 0;
+    if (e < E && h < nh) {
+      cv[e] = cnt[h];
+      fv[e] = sel[(int64_t)h * a.cap];  // read even when unused: the buffer has it
+    }
+  }
+  uint32_t tv[kE];
+  uint32_t run = 0;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    tv[e] = (e < E && tid * E + e < nh) ? (uint32_t)head_tokens(cv[e], fv[e], a) : 0u;
+    run += tv[e];
+  }
+  const uint32_t incl = wave_incl_scan_u32(run);
+  if (lane == kWave - 1) s_wtot[wave] = incl;
+  __syncthreads();
+  uint32_t excl = incl - run;
+  uint32_t total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) excl += s_wtot[w];
+    total += s_wtot[w];
+  }
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    const int h = tid * E + e;
+    if (e < E && h < nh) {
+      s_pre[h] = (int32_t)excl;
+      excl += tv[e];
+    }
+  }
+  if (tid == 0) s_pre[nh] = (int32_t)total;
+  __syncthreads();
+  int64_t Wtok = ((int64_t)total + gridDim.x - 1) / gridDim.x;
+  if (Wtok < kBalMinTokens) Wtok = kBalMinTokens;
+  if (blockIdx.x == 0) {
+    for (int h = tid; h <= nh; h += kThreads) plan[h] = s_pre[h];
+    if (tid == 0) plan[nh + 1] = (int32_t)Wtok;
+  }
+  const int64_t lo = (int64_t)blockIdx.x * Wtok;
+  const int64_t hi = min(lo + Wtok, (int64_t)total);
+  if (lo >= hi) return;
+
+  // 2. First head of the range: the last h with s_pre[h] <= lo.
+  int h0 = 0, h1 = nh;  // invariant: s_pre[h0] <= lo < s_pre[h1] (s_pre[nh] = total > lo)
+  while (h1 - h0 > 1) {
+    const int mid = (h0 + h1) >> 1;
+    if (s_pre[mid] <= lo) h0 = mid; else h1 = mid;
+  }
+  const float inv = 1.0f / sqrtf((float)D);
+  const int64_t tail0 = a.n1 * a.C;
+
+  // 3. One segment per head overlapping the range.
+  for (int h = h0; h < nh && s_pre[h] < hi; ++h) {
+    const int64_t P0 = s_pre[h], P1 = s_pre[h + 1];
+    if (P1 <= lo) continue;
+    const int64_t x0 = max(lo, P0) - P0, x1 = min(hi, P1) - P0;
+    const int c = cnt[h];
+    const int32_t* ids = sel + (int64_t)h * a.cap;
+    const bool sink = (c == 0) || (ids[0] != 0);
+    const int hq = (int)(h % a.H_q);
+    const int64_t b = h / ((int64_t)a.n_pos * a.H_q);
+    const int64_t tr = b * a.H_kv + hq / a.G;
+    const T* Kt = K + tr * a.T * D;
+    const T* Vt = V + tr * a.T * D;
+    const uint4 qv = ld16c(Q + (int64_t)h * D + sub * VEC);
+    const int64_t ct = (int64_t)c * a.C;  // chunk tokens come first, then the extras
+    float m = -INFINITY, l = 0.f, acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+
+    for (int64_t xr = x0; xr < x1;) {
+      // Stage the chunk ids this round needs (positions [xr, xe) of the list).
+      const int64_t fc = xr < ct ? (a.log2C >= 0 ? (xr >> a.log2C) : xr / a.C) : 0;
+      const int64_t xe = xr < ct ? min(x1, (fc + kIds) * a.C) : x1;
+      if (xr < ct) {
+        const int64_t lc = (min(xe, ct) - 1) / a.C;  // last chunk touched
+        __syncthreads();
+        for (int64_t i = tid; i <= lc - fc; i += kThreads) s_ids[i] = ids[fc + i];
+        __syncthreads();
+      }
+      for (int64_t base = xr; base < xe; base += (int64_t)RPB * kUA) {
+        uint4 kv[kUA], vv[kUA];
+        float sc[kUA];
+#pragma unroll
+        for (int u = 0; u < kUA; ++u) {
+          const int64_t x = base + u * RPB + grp;
+          int64_t tok = -1;
+          if (x < xe) {
+            if (x < ct) {
+              const int64_t ci = a.log2C >= 0 ? (x >> a.log2C) : x / a.C;
+              tok = (int64_t)s_ids[ci - fc] * a.C + (x - ci * a.C);
+            } else {
+              const int64_t e = x - ct;
+              tok = sink ? (e == 0 ? 0 : tail0 + e - 1) : tail0 + e;
+            }
+          }
+          if (tok >= 0) {
+            kv[u] = ld16(Kt + tok * D + sub * VEC);
+            vv[u] = ld16(Vt + tok * D + sub * VEC);
+            sc[u] = 0.f;
+          } else {
+            kv[u] = make_uint4(0u, 0u, 0u, 0u);
+            vv[u] = make_uint4(0u, 0u, 0u, 0u);
+            sc[u] = -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kUA; ++u) {
+          const float dot = group_allreduce<LPR>(slice_dot<T>(kv[u], qv), OpAdd()) * inv;
+          sc[u] = (sc[u] == -INFINITY) ? -INFINITY : dot;
+        }
+        online_update<T, kUA>(m, l, acc, sc, vv);
+      }
+      xr = xe;
+    }
+    const bool whole = x0 == 0 && x1 == P1 - P0;
+    float* prow = whole ? nullptr : part + ((int64_t)blockIdx.x + h) * (D + 2);
+    combine_groups<T, D, RPB>(m, l, acc, grp, sub, s_m, s_l, s_acc, O + (int64_t)h * D, prow);
+    __syncthreads();
+  }
+}
+
+// Merge for the balanced split: head h's ranges are workgroups
+// [P_h / W, (P_{h+1} - 1) / W]; their partials sit at slots (workgroup + h).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void merge_balanced_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ plan,
+    const int32_t* __restrict__ cnt, int32_t cap, int32_t nh, T* __restrict__ O) {
+  const int h = blockIdx.x;
+  const int c = cnt[h];
+  if (c < 0 || c > cap) {  // failed or overflowed route: NaN row
+    for (int t = threadIdx.x; t < D; t += kThreads)
+      store_elem(O + (int64_t)h * D, t, __int_as_float(0x7fc00000));
+    return;
+  }
+  const int64_t W = plan[nh + 1];
+  const int64_t fb = plan[h] / W, lb = (plan[h + 1] - 1) / W;
+  if (fb == lb) return;  // written whole by its workgroup
+  merge_partials<T, D>(part + (fb + h) * (D + 2), (int)(lb - fb + 1), O + (int64_t)h * D);
 }
 
 // Dense decode: one workgroup per (b, t, kvh, head tile of GT) and split; GT
@@ -267,15 +473,10 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
   const T* Vt = V + (b * a.H_kv + kvh) * a.T * D;
   const int64_t t0 = (a.T * split) / a.S, t1 = (a.T * (split + 1)) / a.S;
 
-  float q[GT][VEC];
+  uint4 qv[GT];
   const float inv = 1.0f / sqrtf((float)D);
 #pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    const uint4 v = ld16c(Q + (head0 + g) * D + sub * VEC);
-    Vec<T>::widen(v, q[g]);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) q[g][e] *= inv;
-  }
+  for (int g = 0; g < GT; ++g) qv[g] = ld16c(Q + (head0 + g) * D + sub * VEC);
   float m[GT], l[GT], acc[GT][VEC];
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
@@ -304,12 +505,7 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
       float s[kUD];
 #pragma unroll
       for (int u = 0; u < kUD; ++u) {
-        float k[VEC];
-        Vec<T>::widen(kv[u], k);
-        float dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) dot = fmaf(q[g][e], k[e], dot);
-        dot = group_allreduce<LPR>(dot, OpAdd());
+        const float dot = group_allreduce<LPR>(slice_dot<T>(kv[u], qv[g]), OpAdd()) * inv;
         s[u] = ok[u] ? dot : -INFINITY;
       }
       online_update<T, kUD>(m[g], l[g], acc[g], s, vv);
@@ -326,16 +522,25 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
 template <typename T, int D>
 int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
                 const int32_t* sel, const int32_t* cnt, void* O, void* scratch, hipStream_t s) {
-  dim3 grid((unsigned)a.n_heads, (unsigned)a.S);
-  float* part = reinterpret_cast<float*>(scratch);
+  if (a.n_heads <= kBalMaxHeads) {
+    int32_t* plan = reinterpret_cast<int32_t*>(scratch);
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) +
+                                           align256((a.n_heads + 2) * 4));
+    attn_balanced_kernel<T, D><<<(unsigned)a.S, kThreads, 0, s>>>(
+        reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
+        reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), part, plan, a);
+    if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
+    merge_balanced_kernel<T, D><<<(unsigned)a.n_heads, kThreads, 0, s>>>(
+        part, plan, cnt, a.cap, (int32_t)a.n_heads, reinterpret_cast<T*>(O));
+    return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
+  }
+  // Many heads: one workgroup per head, written directly.
+  AttnArgs a1 = a;
+  a1.S = 1;
+  dim3 grid((unsigned)a.n_heads, 1u);
   attn_partial_kernel<T, D><<<grid, kThreads, 0, s>>>(
       reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
-      reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), part, a);
-  if (a.S > 1) {
-    if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
-    merge_kernel<T, D><<<(unsigned)a.n_heads, kThreads, 0, s>>>(part, cnt, a.cap,
-                                                                reinterpret_cast<T*>(O), a.S);
-  }
+      reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), nullptr, a1);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
 }
 

@@ -7,6 +7,18 @@
 namespace zha {
 
 constexpr int kRouteFrontierMax = 4096;  // candidates per level held in LDS by the router
+constexpr int kBalMaxHeads = 2048;       // balanced split-KV: per-head prefix held in LDS
+
+#ifndef ZHA_ATTN_BLOCKS
+#define ZHA_ATTN_BLOCKS 512
+#endif
+
+// zha_attn scratch: with n_heads <= kBalMaxHeads, a plan (n_heads + 2 int32)
+// and (workgroups + n_heads) partials of d + 2 floats; otherwise none.
+inline int64_t attn_scratch_layout_bytes(int64_t n_heads, int d) {
+  if (n_heads > kBalMaxHeads) return 0;
+  return ((n_heads + 2) * 4 + 255) / 256 * 256 + (ZHA_ATTN_BLOCKS + n_heads) * (int64_t)(d + 2) * 4;
+}
 
 struct BuildArgs {
   TreeLayout lay;
@@ -45,7 +57,7 @@ struct AttnArgs {
   int32_t C;
   int32_t log2C;  // log2(C) when C is a power of two, else -1
   int32_t cap;
-  int32_t S;      // splits per query head (1: write O directly)
+  int32_t S;      // workgroups of the balanced split (or splits per head)
 };
 
 struct DenseArgs {

@@ -115,6 +115,6 @@ def test_scratch_sizes_are_consistent():
     gm = g(B=8, H_q=32, H_kv=4, T=262144, C=8, L=6)
     assert Z.route_scratch_bytes(gm, 1, 32768) == 0
     a = Z.attn_scratch_bytes(gm, 1, 32768)
-    assert a > 0 and a % (4 * (gm.d + 2)) == 0
+    assert a >= (256 + 32) * 4 * (gm.d + 2)  # plan + at least one partial per workgroup and head
     assert Z.dense_scratch_bytes(gm, 1) % (4 * (gm.d + 2)) == 0
     assert Z.frontier_capacity() >= 1024

@@ -240,3 +240,56 @@ def test_single_position_calls_match_block_call(Z):
             assert torch.equal(s1[0, 0, h, :n], sel[0, t, h, :n])
         # split counts differ between the two calls, so the fp32 sums may differ in the last bits
         assert (o1[:, 0].float() - O4[:, t].float()).abs().max().item() <= 1e-2
+
+
+def run_full_size_sampled(Z, g, n_pos, steps, samples, seed):
+    """Full-size workload in the bench's launch configuration; oracle on sampled query heads."""
+    import torch
+    K, V = W.make_kv(g)
+    gm = Z.geom(g)
+    cap = g.n_level(1)
+    Kd, Vd = to_device(K, g.dtype), to_device(V, g.dtype)
+    tree = Z.build(gm, Kd, torch.zeros((g.H_kv, 1, g.d), device="cuda"))
+    rng = np.random.default_rng(seed)
+    trees = {}
+    par = Parity()
+    for s in range(steps):
+        Qn = W.make_query_block(g, K, range(s * n_pos, (s + 1) * n_pos))
+        Qd = to_device(Qn, g.dtype)
+        sel, cnt, stats, _ = Z.route(gm, tree, Qd, n_pos, g.p, cap)
+        Od = Z.attn(gm, Qd, n_pos, Kd, Vd, sel, cnt, cap)
+        torch.cuda.synchronize()
+        cnt_h, stats_h = cnt.cpu().numpy(), stats.cpu().numpy()
+        assert (cnt_h >= 0).all(), "router frontier overflow"
+        Og = from_device(Od, g.dtype)
+        for _ in range(samples):
+            b, t, h = (int(rng.integers(g.B)), int(rng.integers(n_pos)), int(rng.integers(g.H_q)))
+            kvh = h // g.G
+            if (b, kvh) not in trees:
+                say(f"  oracle tree for sequence {b}, KV head {kvh}")
+                trees[(b, kvh)] = O.build_tree(W.to_float(K[b, kvh], g.dtype).astype(np.float64),
+                                               np.zeros((1, g.d)), g.C, g.L, g.dtype)
+            q = W.to_float(Qn[b, t, h], g.dtype)
+            r, o = O.zha_head(trees[(b, kvh)], q, W.to_float(K[b, kvh], g.dtype),
+                              W.to_float(V[b, kvh], g.dtype), g.p)
+            compare_head(par, r, sel[b, t, h].cpu().numpy(), int(cnt_h[b, t, h]),
+                         stats_h[b, t, h], Og[b, t, h], o, TOL[g.dtype], (s, b, t, h))
+    say("  " + par.summary())
+    assert not par.mismatched, par.mismatched[:5]
+    assert not par.out_bad, par.out_bad[:5]
+    assert par.exact >= 0.8 * par.heads
+
+
+def test_config3_full_size_bench_launch_sampled(Z):
+    say("config 3 at full size (B=8, one position per call), 48 sampled query heads")
+    run_full_size_sampled(Z, W.CONFIGS[3], n_pos=1, steps=3, samples=16, seed=3)
+
+
+def test_config4_block_1m_sampled(Z):
+    say("config 4: 2048-position block at 1M, 48 sampled query heads")
+    run_full_size_sampled(Z, W.CONFIGS[4], n_pos=2048, steps=1, samples=48, seed=4)
+
+
+def test_config5_extreme_16m_sampled(Z):
+    say("config 5: 16.7M tokens, 8 decode steps, 16 sampled query heads")
+    run_full_size_sampled(Z, W.CONFIGS[5], n_pos=1, steps=4, samples=4, seed=5)
