@@ -29,6 +29,30 @@ from hierarchical_tree_indexed_04_amd import workload as W  # noqa: E402
 
 METRIC = "ZHA decode queries/sec per layer at 256K and 1M ctx; % of HBM peak"
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "hierarchical_tree_indexed_04_amd", "csrc")
+# Sources that determine the attention kernels; measured traffic is reported
+# only while their hash matches the one recorded with the counters.
+ATTN_SOURCES = ["zha_attn.hip", "zha_internal.hpp", "zha_common.hpp", "zha_wave.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_zha_attn_deep-decode-256k.json")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per zha_attn call from the committed counter runs, or None if stale."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != attn_source_hash():
+        return None
+    return rec.get("bytes_per_call")
 
 
 def log(*a):
@@ -255,6 +279,76 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
             "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap}
 
 
+def run_block_1m(reps: int = 3):
+    """Secondary figure: the 1M-token cache with a block of 2048 new positions routed and attended
+    in one call each (16 query heads over 2 KV heads, C=32, L=4, p=0.95); the tree is built from
+    scratch on the cache.  Queries/s counts the 2048 positions."""
+    import torch
+
+    from hierarchical_tree_indexed_04_amd import zha as Z
+    g = W.CONFIGS[4]
+    t0 = time.perf_counter()
+    K, V = W.make_kv(g)
+    Qn = W.make_query_block(g, K, range(g.n_steps))
+    log(f"[bench] {g.name}: inputs {time.perf_counter() - t0:.1f} s")
+    gm = Z.geom(g)
+    Kd, Vd, Qd = to_dev(torch, K, g.dtype), to_dev(torch, V, g.dtype), to_dev(torch, Qn, g.dtype)
+    n_pos = g.n_steps
+    cap = 2048
+    tb, sb = Z.tree_bytes(gm)
+    tree = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    bsc = torch.empty(max(sb, 1), dtype=torch.uint8, device="cuda")
+    qref = torch.zeros((g.H_kv, g.R, g.d), dtype=torch.float32, device="cuda")
+    sel = torch.empty((g.B, n_pos, g.H_q, cap), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((g.B, n_pos, g.H_q), dtype=torch.int32, device="cuda")
+    stats = torch.empty((g.B, n_pos, g.H_q, g.L, 2), dtype=torch.int32, device="cuda")
+    O = torch.empty((g.B, n_pos, g.H_q, g.d), dtype=Kd.dtype, device="cuda")
+    asc = torch.empty(max(Z.attn_scratch_bytes(gm, n_pos, cap), 1), dtype=torch.uint8, device="cuda")
+
+    def once():
+        Z.build(gm, Kd, qref, tree, bsc)
+        e1.record()
+        Z.route(gm, tree, Qd, n_pos, g.p, cap, out=(sel, cnt, stats, None))
+        e2.record()
+        Z.attn(gm, Qd, n_pos, Kd, Vd, sel, cnt, cap, O=O, scratch=asc)
+
+    e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    once()
+    torch.cuda.synchronize()
+    tb_ms, tr_ms, ta_ms = [], [], []
+    for _ in range(reps):
+        e0.record()
+        once()
+        e3.record()
+        torch.cuda.synchronize()
+        tb_ms.append(e0.elapsed_time(e1))
+        tr_ms.append(e1.elapsed_time(e2))
+        ta_ms.append(e2.elapsed_time(e3))
+    c = cnt.cpu().numpy()
+    if (c < 0).any() or (c > cap).any():
+        raise RuntimeError("1M block: a route overflowed")
+    s_h = sel.cpu().numpy()
+    n1 = g.n_level(1)
+    union = 0
+    for kvh in range(g.H_kv):
+        mark = np.zeros(n1, bool)
+        for h in range(kvh * g.G, (kvh + 1) * g.G):
+            for t in range(n_pos):
+                mark[s_h[0, t, h, :c[0, t, h]]] = True
+        union += int(mark.sum()) * g.C * 2 * g.d * g.elem_bytes
+    per_head = int(c.sum()) * g.C * 2 * g.d * g.elem_bytes
+    route_rows = int(stats.cpu().numpy()[..., 0].sum()) * (g.d * g.elem_bytes + 4)
+    b_ms, r_ms, a_ms = (float(np.median(x)) for x in (tb_ms, tr_ms, ta_ms))
+    log(f"[bench] 1M block: build {b_ms:.3f} ms, route {r_ms:.3f} ms, attn {a_ms:.3f} ms")
+    return {"workload": f"{g.name}: B={g.B}, H_q={g.H_q}/H_kv={g.H_kv}, d={g.d}, T={g.T}, C={g.C}, "
+                        f"L={g.L}, p={g.p}, {n_pos} positions per call",
+            "queries_per_s": n_pos / ((r_ms + a_ms) * 1e-3),
+            "queries_per_s_with_build": n_pos / ((b_ms + r_ms + a_ms) * 1e-3),
+            "build_ms": b_ms, "route_ms": r_ms, "attn_ms": a_ms,
+            "bytes_union": union + route_rows, "bytes_per_head_sum": per_head + route_rows,
+            "hbm_frac_union": (union + route_rows) / ((r_ms + a_ms) * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+
+
 def copy_calibration():
     """One plain copy of 1 GiB: reads and writes 2^30 bytes each, for scaling HBM counters."""
     import torch
@@ -276,6 +370,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle baseline (0 disables)")
+    ap.add_argument("--with-1m", type=int, default=1,
+                    help="also time the 1M-context block workload (2048 positions routed at once)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -327,9 +423,10 @@ def main():
         "config": {"workload": f"{g.name}: B={g.B}, H_q={g.H_q}/H_kv={g.H_kv}, d={g.d}, T={g.T}, "
                                f"C={g.C}, L={g.L}, R={g.R}, p={g.p}, one decode step per call",
                    "global_batch": g.B, "seq_len": g.T, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "zha_attn (attn_partial_kernel)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "zha_attn call (attn_balanced_kernel + merge_balanced_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "route_us": route_us,
         "attn_us": attn_us,
@@ -341,6 +438,7 @@ def main():
         "build_ms": r["build_ms"],
         "dense_ms_per_step": r["dense_ms"],
         "speedup_vs_dense": (r["dense_ms"] / ms_per_step) if r["dense_ms"] else None,
+        "at_1m": run_block_1m() if args.with_1m else None,
     }
     print(json.dumps(out), flush=True)
 
