@@ -19,7 +19,7 @@ int check_geom(const zha_geom* g) {
   if (g->B < 1 || g->H_q < 1 || g->H_kv < 1 || g->H_q % g->H_kv != 0) return ZHA_ERR_GEOM;
   if (g->C < 2 || g->C > 1024 || g->L < 1 || g->L > kMaxLevels || g->R < 1 || g->R > 16)
     return ZHA_ERR_GEOM;
-  if (g->T < 1 || g->T / g->C >= ((int64_t)1 << 31)) return ZHA_ERR_GEOM;
+  if (g->T < 1 || g->T >= ((int64_t)1 << 31)) return ZHA_ERR_GEOM;
   int64_t span = 1;
   for (int l = 0; l < g->L; ++l) {
     span *= g->C;

@@ -355,56 +355,60 @@ __global__ __launch_bounds__(kThreads) void attn_balanced_kernel(
     if (s_pre[mid] <= lo) h0 = mid; else h1 = mid;
   }
   const float inv = 1.0f / sqrtf((float)D);
-  const int64_t tail0 = a.n1 * a.C;
 
-  // 3. One segment per head overlapping the range.
+  // 3. One segment per head overlapping the range.  Token positions and ids
+  // fit in 31 bits (T < 2^31), so the index math is 32-bit; only the final
+  // row address is 64-bit.
   for (int h = h0; h < nh && s_pre[h] < hi; ++h) {
-    const int64_t P0 = s_pre[h], P1 = s_pre[h + 1];
+    const int P0 = s_pre[h], P1 = s_pre[h + 1];
     if (P1 <= lo) continue;
-    const int64_t x0 = max(lo, P0) - P0, x1 = min(hi, P1) - P0;
+    const int x0 = (int)max(lo, (int64_t)P0) - P0, x1 = (int)min(hi, (int64_t)P1) - P0;
     const int c = cnt[h];
     const int32_t* ids = sel + (int64_t)h * a.cap;
     const bool sink = (c == 0) || (ids[0] != 0);
     const int hq = (int)(h % a.H_q);
     const int64_t b = h / ((int64_t)a.n_pos * a.H_q);
     const int64_t tr = b * a.H_kv + hq / a.G;
-    const T* Kt = K + tr * a.T * D;
-    const T* Vt = V + tr * a.T * D;
+    const char* Kt = reinterpret_cast<const char*>(K + tr * a.T * D) + sub * 16;
+    const char* Vt = reinterpret_cast<const char*>(V + tr * a.T * D) + sub * 16;
     const uint4 qv = ld16c(Q + (int64_t)h * D + sub * VEC);
-    const int64_t ct = (int64_t)c * a.C;  // chunk tokens come first, then the extras
+    const int Cc = a.C, log2C = a.log2C;
+    const int ct = c * Cc;  // chunk tokens come first, then the extras
+    const int tail0 = (int)(a.n1 * a.C);
     float m = -INFINITY, l = 0.f, acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 
-    for (int64_t xr = x0; xr < x1;) {
+    for (int xr = x0; xr < x1;) {
       // Stage the chunk ids this round needs (positions [xr, xe) of the list).
-      const int64_t fc = xr < ct ? (a.log2C >= 0 ? (xr >> a.log2C) : xr / a.C) : 0;
-      const int64_t xe = xr < ct ? min(x1, (fc + kIds) * a.C) : x1;
+      const int fc = xr < ct ? (log2C >= 0 ? (xr >> log2C) : xr / Cc) : 0;
+      const int xe = xr < ct ? (int)min((int64_t)x1, (int64_t)(fc + kIds) * Cc) : x1;
       if (xr < ct) {
-        const int64_t lc = (min(xe, ct) - 1) / a.C;  // last chunk touched
+        const int lc = (min(xe, ct) - 1) / Cc;  // last chunk touched
         __syncthreads();
-        for (int64_t i = tid; i <= lc - fc; i += kThreads) s_ids[i] = ids[fc + i];
+        for (int i = tid; i <= lc - fc; i += kThreads) s_ids[i] = ids[fc + i];
         __syncthreads();
       }
-      for (int64_t base = xr; base < xe; base += (int64_t)RPB * kUA) {
+      for (int base = xr; base < xe; base += RPB * kUA) {
         uint4 kv[kUA], vv[kUA];
         float sc[kUA];
 #pragma unroll
         for (int u = 0; u < kUA; ++u) {
-          const int64_t x = base + u * RPB + grp;
-          int64_t tok = -1;
+          const int x = base + u * RPB + grp;
+          int tok = -1;
           if (x < xe) {
             if (x < ct) {
-              const int64_t ci = a.log2C >= 0 ? (x >> a.log2C) : x / a.C;
-              tok = (int64_t)s_ids[ci - fc] * a.C + (x - ci * a.C);
+              const int ci = log2C >= 0 ? (x >> log2C) : x / Cc;
+              tok = s_ids[ci - fc] * Cc + (x - ci * Cc);
             } else {
-              const int64_t e = x - ct;
+              const int e = x - ct;
               tok = sink ? (e == 0 ? 0 : tail0 + e - 1) : tail0 + e;
             }
           }
           if (tok >= 0) {
-            kv[u] = ld16(Kt + tok * D + sub * VEC);
-            vv[u] = ld16(Vt + tok * D + sub * VEC);
+            const size_t off = (size_t)(uint32_t)tok * (D * sizeof(T));
+            kv[u] = ld16(Kt + off);
+            vv[u] = ld16(Vt + off);
             sc[u] = 0.f;
           } else {
             kv[u] = make_uint4(0u, 0u, 0u, 0u);

@@ -38,8 +38,12 @@
 namespace zha {
 namespace {
 
-constexpr int kThreads = 256;
+#ifndef ZHA_ROUTE_THREADS
+#define ZHA_ROUTE_THREADS 512
+#endif
+constexpr int kThreads = ZHA_ROUTE_THREADS;  // 256 or 512
 constexpr int kWaves = kThreads / kWave;
+static_assert(kThreads >= 256, "histograms are cleared one bucket per thread");
 #ifndef ZHA_ROUTE_ROWS
 #define ZHA_ROUTE_ROWS 16
 #endif
@@ -237,8 +241,13 @@ __device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const i
     sm.redf[1][wave] = smin;
   }
   __syncthreads();
-  smax = fmaxf(fmaxf(sm.redf[0][0], sm.redf[0][1]), fmaxf(sm.redf[0][2], sm.redf[0][3]));
-  smin = fminf(fminf(sm.redf[1][0], sm.redf[1][1]), fminf(sm.redf[1][2], sm.redf[1][3]));
+  smax = sm.redf[0][0];
+  smin = sm.redf[1][0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    smax = fmaxf(smax, sm.redf[0][w]);
+    smin = fminf(smin, sm.redf[1][w]);
+  }
 
   // 1. Value-space histogram over (s_max - s).
   const float range = fminf(smax - smin, 32.f);
@@ -293,8 +302,10 @@ __device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const i
     const bool last_pass = pass >= 8 || lo == hi;
     const int hb = (lo == hi) ? 0 : 63 - __clzll((long long)(lo ^ hi));
     const int shift = hb > 7 ? hb - 7 : 0;
-    sm.hcnt[tid] = 0u;
-    sm.hmass[tid] = 0ull;
+    if (tid < 256) {
+      sm.hcnt[tid] = 0u;
+      sm.hmass[tid] = 0ull;
+    }
     if (tid == 0) sm.bl_n = 0;
     __syncthreads();
     for (int i = tid; i < K; i += kThreads) {
@@ -398,8 +409,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
 #endif
     const bool large = K > kWave;
     if (large) {  // zeroed here, made visible by the scoring barrier
-      sm.hcnt[tid] = 0u;
-      sm.hmass[tid] = 0ull;
+      if (tid < 256) {
+        sm.hcnt[tid] = 0u;
+        sm.hmass[tid] = 0ull;
+      }
       if (tid == 0) sm.bl_n = 0;
     }
     if (K > 1)

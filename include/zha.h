@@ -37,7 +37,7 @@
  * level 1 nodes are chunks of C consecutive keys, a level-l node has the C
  * level-(l-1) nodes below it as children.  Requirements: B, H_q, H_kv >= 1,
  * H_q % H_kv == 0, d in {64, 128, 256}, 2 <= C <= 1024, 1 <= L <= 16,
- * 1 <= R <= 16, n_L >= 1 (T >= C^L), T < 2^31 * C.
+ * 1 <= R <= 16, n_L >= 1 (T >= C^L), T < 2^31.
  */
 #ifndef ZHA_H
 #define ZHA_H
