@@ -36,6 +36,9 @@ constexpr int kThreads = 256;
 #ifndef ZHA_DENSE_ROWS
 #define ZHA_DENSE_ROWS 4
 #endif
+#ifndef ZHA_ATTN_WAVES
+#define ZHA_ATTN_WAVES 2
+#endif
 constexpr int kUA = ZHA_ATTN_ROWS;   // K/V rows in flight per lane (sparse)
 constexpr int kUD = ZHA_DENSE_ROWS;  // K/V rows in flight per lane (dense)
 constexpr int kIds = 1024;  // chunk ids staged in LDS per round (sparse)
@@ -120,14 +123,17 @@ __device__ __forceinline__ void online_update(float& m, float& l, float* acc, co
   float mloc = m;
 #pragma unroll
   for (int u = 0; u < U; ++u) mloc = fmaxf(mloc, s[u]);
-  if (mloc == -INFINITY) return;
-  const float scale = __expf(m - mloc);  // m = -inf gives 0
+  // Branch-free (a branch here lets the compiler sink the V loads into it,
+  // after the waits for K): with no finite score yet, the reference point is
+  // 0 and every weight below is exp(-inf) = 0, leaving the state unchanged.
+  const float mref = (mloc == -INFINITY) ? 0.f : mloc;
+  const float scale = __expf(m - mref);  // m = -inf gives 0
   l *= scale;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] *= scale;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const float p = __expf(s[u] - mloc);  // -inf scores give 0
+    const float p = __expf(s[u] - mref);  // -inf scores give 0
     l += p;
     float v[VEC];
     Vec<T>::widen(vv[u], v);
@@ -138,19 +144,45 @@ __device__ __forceinline__ void online_update(float& m, float& l, float* acc, co
 }
 
 // Merge of the S split partials of one head, in split order:
-// O = sum_s e^{M_s - M} acc_s / sum_s e^{M_s - M} l_s.
+// O = sum_s e^{M_s - M} acc_s / sum_s e^{M_s - M} l_s.  Partials are read kSB
+// at a time with independent loads (one memory round trip per batch); with
+// more than kSB partials the running sums are rescaled to each batch's max.
 template <typename T, int D>
 __device__ __forceinline__ void merge_partials(const float* part_head, int S, T* out_row) {
+  constexpr int kSB = 4;
   const float* __restrict__ p = part_head;
   for (int t = threadIdx.x; t < D; t += kThreads) {
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, p[s * (D + 2) + D]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ms = p[s * (D + 2) + D];
-      const float w = (ms == -INFINITY) ? 0.f : __expf(ms - M);
-      num = fmaf(w, p[s * (D + 2) + t], num);
-      den = fmaf(w, p[s * (D + 2) + D + 1], den);
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int s0 = 0; s0 < S; s0 += kSB) {
+      float ms[kSB], ls[kSB], as[kSB];
+#pragma unroll
+      for (int j = 0; j < kSB; ++j) {
+        const int s = s0 + j;
+        if (s < S) {
+          const float* r = p + (int64_t)s * (D + 2);
+          ms[j] = r[D];
+          ls[j] = r[D + 1];
+          as[j] = r[t];
+        } else {
+          ms[j] = -INFINITY;
+          ls[j] = 0.f;
+          as[j] = 0.f;
+        }
+      }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < kSB; ++j) Mn = fmaxf(Mn, ms[j]);
+      if (Mn == -INFINITY) continue;
+      const float r = (M == -INFINITY) ? 0.f : __expf(M - Mn);
+      num *= r;
+      den *= r;
+#pragma unroll
+      for (int j = 0; j < kSB; ++j) {
+        const float w = (ms[j] == -INFINITY) ? 0.f : __expf(ms[j] - Mn);
+        num = fmaf(w, as[j], num);
+        den = fmaf(w, ls[j], den);
+      }
+      M = Mn;
     }
     store_elem(out_row, t, num / den);
   }
@@ -171,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
   merge_partials<T, D>(part + head * (int64_t)S * (D + 2), S, O + head * D);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool POW2, bool BUF>
 __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
@@ -199,18 +231,24 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   const T* Vt = V + tr * a.T * D;
   const int32_t* ids = sel + head * a.cap;
 
-  // This split's chunks, plus (last split) the sink when chunk 0 is not selected and C_cur.
+  // This split's chunks, plus (last split) the sink when chunk 0 is not selected
+  // and C_cur.  Token positions and ids fit in 31 bits (T < 2^31).
+  const int Cc = a.C, log2C = a.log2C;
   const int c0 = (int)(((int64_t)split * c) / a.S);
   const int c1 = (int)(((int64_t)(split + 1) * c) / a.S);
-  const int64_t nchunk_tok = (int64_t)(c1 - c0) * a.C;
+  const int ct = (c1 - c0) * Cc;  // chunk tokens come first, then the extras
   int n_extra = 0;
   bool sink = false;
-  const int64_t tail0 = a.n1 * a.C;
+  const int tail0 = (int)(a.n1 * a.C);
   if (split == a.S - 1) {
     sink = (c == 0) || (ids[0] != 0);
-    n_extra = (sink ? 1 : 0) + (int)(a.T - tail0);
+    n_extra = (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C);
   }
-  const int64_t ntok = nchunk_tok + n_extra;
+  const int ntok = ct + n_extra;
+  const char* Kb = reinterpret_cast<const char*>(Kt) + sub * 16;
+  const char* Vb = reinterpret_cast<const char*>(Vt) + sub * 16;
+  const buf_t rK = make_buf(Kt, BUF ? a.T * D * (int64_t)sizeof(T) : 0);
+  const buf_t rV = make_buf(Vt, BUF ? a.T * D * (int64_t)sizeof(T) : 0);
 
   const uint4 qv = ld16c(Q + head * D + sub * VEC);
   const float inv = 1.0f / sqrtf((float)D);
@@ -230,36 +268,49 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
       for (int i = tid; i < rn; i += kThreads) s_ids[i] = ids[c0 + r0 + i];
       __syncthreads();
     }
-    const int64_t xb = (int64_t)r0 * a.C;
-    const int64_t xe = final_round ? ntok : (int64_t)(r0 + rn) * a.C;
-    for (int64_t base = xb; base < xe; base += (int64_t)RPB * kUA) {
-      uint4 kv[kUA], vv[kUA];
-      float s[kUA];
+    const int xb = r0 * Cc;
+    const int xe = final_round ? ntok : (r0 + rn) * Cc;
+    for (int base = xb; base < xe; base += RPB * kUA) {
+      int tok[kUA];
 #pragma unroll
       for (int u = 0; u < kUA; ++u) {
-        const int64_t x = base + u * RPB + grp;
-        int64_t tok = -1;
-        if (x < nchunk_tok) {
-          const int64_t ci = a.log2C >= 0 ? (x >> a.log2C) : x / a.C;
-          tok = (int64_t)s_ids[ci - r0] * a.C + (x - ci * a.C);
-        } else if (x < xe) {
-          const int64_t e = x - nchunk_tok;
-          tok = sink ? (e == 0 ? 0 : tail0 + e - 1) : tail0 + e;
-        }
-        if (tok >= 0) {
-          kv[u] = ld16(Kt + tok * D + sub * VEC);
-          vv[u] = ld16(Vt + tok * D + sub * VEC);
-          s[u] = 0.f;
-        } else {
-          kv[u] = make_uint4(0u, 0u, 0u, 0u);
-          vv[u] = make_uint4(0u, 0u, 0u, 0u);
-          s[u] = -INFINITY;
-        }
+        const int x = base + u * RPB + grp;
+        const int ci = POW2 ? (x >> log2C) : x / Cc;
+        tok[u] = s_ids[min(max(ci - r0, 0), kIds - 1)];
       }
 #pragma unroll
       for (int u = 0; u < kUA; ++u) {
+        const int x = base + u * RPB + grp;
+        const int ci = POW2 ? (x >> log2C) : x / Cc;
+        const int e = x - ct;
+        const int tt = sink ? (e == 0 ? 0 : tail0 + e - 1) : tail0 + e;
+        tok[u] = x < ct ? tok[u] * Cc + (x - ci * Cc) : tt;
+      }
+      uint4 kv[kUA], vv[kUA];
+#pragma unroll
+      for (int u = 0; u < kUA; ++u) {
+        const bool live = base + u * RPB + grp < xe;
+        if (BUF) {
+          const uint32_t off = live ? (uint32_t)tok[u] * (uint32_t)(D * sizeof(T)) +
+                                          (uint32_t)(sub * 16)
+                                    : kBufNone;
+          kv[u] = bld16(rK, off);
+          vv[u] = bld16(rV, off);
+        } else if (live) {
+          const size_t off = (size_t)(uint32_t)tok[u] * (D * sizeof(T));
+          kv[u] = ld16(Kb + off);
+          vv[u] = ld16(Vb + off);
+        } else {
+          kv[u] = make_uint4(0u, 0u, 0u, 0u);
+          vv[u] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float s[kUA];
+#pragma unroll
+      for (int u = 0; u < kUA; ++u) {
         const float dot = group_allreduce<LPR>(slice_dot<T>(kv[u], qv), OpAdd()) * inv;
-        s[u] = (s[u] == -INFINITY) ? -INFINITY : dot;
+        s[u] = (base + u * RPB + grp < xe) ? dot : -INFINITY;
       }
       online_update<T, kUA>(m, l, acc, s, vv);
     }
@@ -279,9 +330,14 @@ __device__ __forceinline__ int head_tokens(int c, int first_id, const AttnArgs& 
 }
 
 // Balanced split-KV over all heads of the call: workgroup w owns tokens
-// [w W, (w + 1) W) of the concatenated per-head token lists.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void attn_balanced_kernel(
+// [w W, (w + 1) W) of the concatenated per-head token lists.  POW2: C is a
+// power of two (chunk index by shift).
+// The launch keeps ZHA_ATTN_WAVES waves per SIMD resident (ZHA_ATTN_BLOCKS
+// workgroups of 4 waves); telling the compiler so lets it keep every row load
+// of an iteration in flight instead of trimming registers for occupancy that
+// the launch cannot use.
+template <typename T, int D, bool POW2, bool BUF>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_ATTN_WAVES, ZHA_ATTN_WAVES))) void attn_balanced_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
     float* __restrict__ part, int32_t* __restrict__ plan, AttnArgs a) {
@@ -371,6 +427,8 @@ __global__ __launch_bounds__(kThreads) void attn_balanced_kernel(
     const int64_t tr = b * a.H_kv + hq / a.G;
     const char* Kt = reinterpret_cast<const char*>(K + tr * a.T * D) + sub * 16;
     const char* Vt = reinterpret_cast<const char*>(V + tr * a.T * D) + sub * 16;
+    const buf_t rK = make_buf(K + tr * a.T * D, BUF ? a.T * D * (int64_t)sizeof(T) : 0);
+    const buf_t rV = make_buf(V + tr * a.T * D, BUF ? a.T * D * (int64_t)sizeof(T) : 0);
     const uint4 qv = ld16c(Q + (int64_t)h * D + sub * VEC);
     const int Cc = a.C, log2C = a.log2C;
     const int ct = c * Cc;  // chunk tokens come first, then the extras
@@ -390,36 +448,52 @@ __global__ __launch_bounds__(kThreads) void attn_balanced_kernel(
         __syncthreads();
       }
       for (int base = xr; base < xe; base += RPB * kUA) {
-        uint4 kv[kUA], vv[kUA];
-        float sc[kUA];
+        // Token of every slot first: the chunk-id reads from LDS are
+        // unconditional (clamped in bounds, one wait for all of them), so
+        // the 2 kUA row loads below issue back to back.
+        int tok[kUA];
 #pragma unroll
         for (int u = 0; u < kUA; ++u) {
           const int x = base + u * RPB + grp;
-          int tok = -1;
-          if (x < xe) {
-            if (x < ct) {
-              const int ci = log2C >= 0 ? (x >> log2C) : x / Cc;
-              tok = s_ids[ci - fc] * Cc + (x - ci * Cc);
-            } else {
-              const int e = x - ct;
-              tok = sink ? (e == 0 ? 0 : tail0 + e - 1) : tail0 + e;
-            }
-          }
-          if (tok >= 0) {
-            const size_t off = (size_t)(uint32_t)tok * (D * sizeof(T));
-            kv[u] = ld16(Kt + off);
-            vv[u] = ld16(Vt + off);
-            sc[u] = 0.f;
-          } else {
-            kv[u] = make_uint4(0u, 0u, 0u, 0u);
-            vv[u] = make_uint4(0u, 0u, 0u, 0u);
-            sc[u] = -INFINITY;
-          }
+          const int ci = POW2 ? (x >> log2C) : x / Cc;
+          tok[u] = s_ids[min(max(ci - fc, 0), kIds - 1)];
         }
 #pragma unroll
         for (int u = 0; u < kUA; ++u) {
+          const int x = base + u * RPB + grp;
+          const int ci = POW2 ? (x >> log2C) : x / Cc;
+          const int e = x - ct;
+          const int tt = sink ? (e == 0 ? 0 : tail0 + e - 1) : tail0 + e;
+          tok[u] = x < ct ? tok[u] * Cc + (x - ci * Cc) : tt;
+        }
+        uint4 kv[kUA], vv[kUA];
+#pragma unroll
+        for (int u = 0; u < kUA; ++u) {
+          const bool live = base + u * RPB + grp < xe;
+          if (BUF) {
+            // Straight-line: a slot without a row reads nothing and gets zeros.
+            const uint32_t off = live ? (uint32_t)tok[u] * (uint32_t)(D * sizeof(T)) +
+                                            (uint32_t)(sub * 16)
+                                      : kBufNone;
+            kv[u] = bld16(rK, off);
+            vv[u] = bld16(rV, off);
+          } else if (live) {
+            const size_t off = (size_t)(uint32_t)tok[u] * (D * sizeof(T));
+            kv[u] = ld16(Kt + off);
+            vv[u] = ld16(Vt + off);
+          } else {
+            kv[u] = make_uint4(0u, 0u, 0u, 0u);
+            vv[u] = make_uint4(0u, 0u, 0u, 0u);
+          }
+        }
+        // Keep all 2 kUA loads ahead of the arithmetic (the scheduler would
+        // otherwise delay some V loads to reuse K's registers).
+        __builtin_amdgcn_sched_barrier(0);
+        float sc[kUA];
+#pragma unroll
+        for (int u = 0; u < kUA; ++u) {
           const float dot = group_allreduce<LPR>(slice_dot<T>(kv[u], qv), OpAdd()) * inv;
-          sc[u] = (sc[u] == -INFINITY) ? -INFINITY : dot;
+          sc[u] = (base + u * RPB + grp < xe) ? dot : -INFINITY;
         }
         online_update<T, kUA>(m, l, acc, sc, vv);
       }
@@ -439,14 +513,15 @@ __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ plan,
     const int32_t* __restrict__ cnt, int32_t cap, int32_t nh, T* __restrict__ O) {
   const int h = blockIdx.x;
+  // Independent loads, issued together.
   const int c = cnt[h];
+  const int64_t P0 = plan[h], P1 = plan[h + 1], W = plan[nh + 1];
   if (c < 0 || c > cap) {  // failed or overflowed route: NaN row
     for (int t = threadIdx.x; t < D; t += kThreads)
       store_elem(O + (int64_t)h * D, t, __int_as_float(0x7fc00000));
     return;
   }
-  const int64_t W = plan[nh + 1];
-  const int64_t fb = plan[h] / W, lb = (plan[h + 1] - 1) / W;
+  const int64_t fb = P0 / W, lb = (P1 - 1) / W;
   if (fb == lb) return;  // written whole by its workgroup
   merge_partials<T, D>(part + (fb + h) * (D + 2), (int)(lb - fb + 1), O + (int64_t)h * D);
 }
@@ -530,9 +605,17 @@ int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
     int32_t* plan = reinterpret_cast<int32_t*>(scratch);
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) +
                                            align256((a.n_heads + 2) * 4));
-    attn_balanced_kernel<T, D><<<(unsigned)a.S, kThreads, 0, s>>>(
-        reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
-        reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), part, plan, a);
+    const bool buf = a.T * D * (int64_t)sizeof(T) < ((int64_t)1 << 31);
+#define ZHA_BAL(P2, BF)                                                                    \
+  attn_balanced_kernel<T, D, P2, BF><<<(unsigned)a.S, kThreads, 0, s>>>(                  \
+      reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),                       \
+      reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), part, plan, a)
+    if (a.log2C >= 0) {
+      if (buf) ZHA_BAL(true, true); else ZHA_BAL(true, false);
+    } else {
+      if (buf) ZHA_BAL(false, true); else ZHA_BAL(false, false);
+    }
+#undef ZHA_BAL
     if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
     merge_balanced_kernel<T, D><<<(unsigned)a.n_heads, kThreads, 0, s>>>(
         part, plan, cnt, a.cap, (int32_t)a.n_heads, reinterpret_cast<T*>(O));
@@ -542,9 +625,17 @@ int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
   AttnArgs a1 = a;
   a1.S = 1;
   dim3 grid((unsigned)a.n_heads, 1u);
-  attn_partial_kernel<T, D><<<grid, kThreads, 0, s>>>(
-      reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
-      reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), nullptr, a1);
+  const bool buf = a.T * D * (int64_t)sizeof(T) < ((int64_t)1 << 31);
+#define ZHA_PART(P2, BF)                                                                    \
+  attn_partial_kernel<T, D, P2, BF><<<grid, kThreads, 0, s>>>(                              \
+      reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),                        \
+      reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), nullptr, a1)
+  if (a.log2C >= 0) {
+    if (buf) ZHA_PART(true, true); else ZHA_PART(true, false);
+  } else {
+    if (buf) ZHA_PART(false, true); else ZHA_PART(false, false);
+  }
+#undef ZHA_PART
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
 }
 

@@ -139,6 +139,31 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 // 16-byte load through the caches (data likely reused).
 __device__ __forceinline__ uint4 ld16c(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Raw buffer loads.  A buffer resource covers [base, base + bytes) with
+// bytes < 2^31; a load whose offset lies past the end returns zeros and reads
+// no memory, so a load whose lane has no row is issued unconditionally with
+// offset kBufNone (every wait can then count exactly the loads after it).
+typedef __amdgpu_buffer_rsrc_t buf_t;
+constexpr uint32_t kBufNone = 0x80000000u;
+__device__ __forceinline__ buf_t make_buf(const void* base, int64_t bytes) {
+  // Fourth descriptor word for gfx9 raw buffers: 32-bit data format.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// Streaming (non-temporal) 16-byte buffer load.
+__device__ __forceinline__ uint4 bld16(buf_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, ZHA_NT_LOADS ? 2 : 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Cached 16-byte and 4-byte buffer loads.
+__device__ __forceinline__ uint4 bld16c(buf_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float bld4c(buf_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // ---------------------------------------------------------------------------
 // Reductions inside aligned lane groups of size W (power of two, <= 64).
 // ---------------------------------------------------------------------------

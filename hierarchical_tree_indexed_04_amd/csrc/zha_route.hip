@@ -8,7 +8,7 @@
 // E-E) form the next frontier.  The order is score descending, ties to the
 // lower node id.
 //
-// One workgroup (4 waves) per query head walks all levels in one launch.  The
+// One workgroup (8 waves) per query head walks all levels in one launch.  The
 // frontier, its scores and the cut's histograms stay in LDS; only the summary
 // rows of the candidates are read from memory (cached loads: the upper levels
 // are shared by every query head of the group).
@@ -19,14 +19,14 @@
 // masses make every partial sum exact, hence independent of summation order:
 // the result is deterministic and the prefix test W_m >= p Z is evaluated on
 // the exact sums of the quantised weights.
-//   * Frontiers of at most 64 candidates: wave 0 holds one candidate per lane
-//     and keeps a candidate iff the mass of all smaller keys is < p Z.
+//   * Frontiers of at most 64 candidates: every wave holds one candidate per
+//     lane; candidate i is kept iff the mass of all smaller keys is < p Z, the
+//     sum over smaller keys being split across the waves.
 //   * Larger frontiers: a 256-bucket histogram over (s_max - s) (monotone in
 //     the key) finds the bucket where the running mass crosses p Z; 8-bit
 //     radix passes over the keys narrow a crowded bucket (ties in score fall
 //     to the id bits) until at most 64 candidates remain, which wave 0 then
-//     ranks as above.
-// kappa, the largest kept key, defines the cut: kept = {key <= kappa}.
+//     ranks.  kappa, the largest kept key, defines the cut: kept = {key <= kappa}.
 // Compaction keeps ascending id order with per-wave ballots, and the next
 // frontier is written as children of the kept nodes.
 //
@@ -77,32 +77,40 @@ struct RouteSmem {
   unsigned long long hmass[256];     // histogram: fixed-point mass per bucket
   unsigned long long bkey[kWave];    // boundary candidates
   unsigned long long bw[kWave];
-  int32_t small_ids[kWave];          // kept ids of a frontier of <= 64 candidates
+  unsigned long long part[kWaves][kWave];   // small cut: partial masses below each lane
   uint32_t wcnt[FMAX / kThreads * kWaves];  // kept per (round, wave)
   float redf[2][kWaves];
   unsigned long long redu[2][kWaves];
   unsigned long long kappa, next, base;
   double target;
-  int32_t bstar, bcount, bl_n, m;
+  int32_t bstar, bcount, bl_n;
 };
 
-// Scores of the frontier: s_i = max_r (q . k_hat_{r,i} + b_hat_{r,i}), q pre-scaled by 1/sqrt(d).
-// LPR lanes read one 16-byte slice each of a summary row; kU rows per lane are in flight.
-template <typename T, int D, int FMAX>
-__device__ __forceinline__ void score_frontier(RouteSmem<FMAX>& sm, const int32_t* fr, int K,
-                                               int R, const char* __restrict__ khat,
-                                               const float* __restrict__ bhat, const float* q) {
+// Where a batch item lives: its level's k_hat / b_hat and its node id.
+struct Loc {
+  const char* k;
+  const float* b;
+  int node;
+};
+
+// Scores items [0, NI) of a batch into out[] (LDS): s = max_r (q . k_hat_r +
+// b_hat_r) over the R tangents of the item's node, q pre-scaled by 1/sqrt(d).
+// LPR lanes read one 16-byte slice each of a summary row; kU rows per lane are
+// in flight.  Ends with a barrier.
+template <typename T, int D, bool R1, typename Locate>
+__device__ __forceinline__ void score_items(float* out, int NI, int R, Locate locate,
+                                            const float* q) {
   constexpr int VEC = Vec<T>::N;
   constexpr int LPR = D / VEC;
   constexpr int RPB = kThreads / LPR;
   const int tid = threadIdx.x;
   const int sub = tid % LPR, grp = tid / LPR;
-  uint32_t* sco = reinterpret_cast<uint32_t*>(sm.sc);
-  if (R > 1) {
-    for (int i = tid; i < K; i += kThreads) sco[i] = 0u;
+  uint32_t* outu = reinterpret_cast<uint32_t*>(out);
+  if (!R1) {
+    for (int i = tid; i < NI; i += kThreads) outu[i] = 0u;
     __syncthreads();
   }
-  const int NR = K * R;
+  const int NR = R1 ? NI : NI * R;
   for (int base = 0; base < NR; base += RPB * kU) {
     // Slots beyond the last live row are skipped with uniform branches: a
     // wave64 VALU op costs the SIMD 4 cycles, so dead slots are not free.
@@ -115,11 +123,12 @@ __device__ __forceinline__ void score_frontier(RouteSmem<FMAX>& sm, const int32_
     for (int u = 0; u < kU; ++u) {
       const int x = base + u * RPB + grp;
       if (x < NR) {
-        const int node = fr[R == 1 ? x : x / R];
-        const int r = R == 1 ? 0 : x % R;
-        const int64_t row = (int64_t)node * R + r;
-        v[u] = ld16c(khat + row * (int64_t)(D * sizeof(T)) + sub * 16);
-        bias[u] = bhat[row];
+        const int item = R1 ? x : x / R;
+        const int r = R1 ? 0 : x - item * R;
+        const Loc lc = locate(item);
+        const int64_t row = R1 ? (int64_t)lc.node : (int64_t)lc.node * R + r;
+        v[u] = ld16c(lc.k + row * (int64_t)(D * sizeof(T)) + sub * 16);
+        bias[u] = lc.b[row];
       } else {
         v[u] = make_uint4(0u, 0u, 0u, 0u);
         bias[u] = 0.f;
@@ -137,27 +146,63 @@ __device__ __forceinline__ void score_frontier(RouteSmem<FMAX>& sm, const int32_
         dot = group_allreduce<LPR>(dot, OpAdd());
         if (sub == 0 && x < NR) {
           const float s = dot + bias[u];
-          if (R == 1)
-            sm.sc[x] = s;
+          if (R1)
+            out[x] = s;
           else
-            atomicMax(&sco[x / R], ord_f32(s));
+            atomicMax(&outu[x / R], ord_f32(s));
         }
       }
     }
   }
-  if (R > 1) {
+  if (!R1) {
     __syncthreads();
-    for (int i = tid; i < K; i += kThreads) sm.sc[i] = unord_f32(sco[i]);
+    for (int i = tid; i < NI; i += kThreads) out[i] = unord_f32(outu[i]);
   }
   __syncthreads();
 }
 
+// Cut of a frontier of 1 < K <= 64 candidates, evaluated by every wave with
+// candidate i in lane i: i is kept iff the mass of the candidates with smaller
+// keys is < p Z.  Wave w sums that mass over candidates [w J, (w + 1) J) and
+// the partial sums meet in LDS.  Returns the lane's kept flag (the same in
+// every wave); contains one barrier.
+template <int FMAX>
+__device__ __forceinline__ bool small_cut(RouteSmem<FMAX>& sm, const float* sc,
+                                          const int32_t* fr, int K, float p, uint64_t& key) {
+  constexpr int J = kWave / kWaves;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const bool valid = lane < K;
+  const float s = valid ? sc[lane] : -INFINITY;
+  const float smax = wave_allreduce_f32(s, OpMax());
+  key = valid ? make_key(s, fr[lane]) : ~0ull;
+  const uint64_t w = valid ? fixed_mass(s, smax) : 0ull;
+  uint64_t part = 0;
+  const int j0 = wave * J;
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {
+    const int j = j0 + jj;
+    if (j < K) {
+      const uint64_t kj = readlane_u64(key, j);
+      const uint64_t wj = readlane_u64(w, j);
+      part += (kj < key) ? wj : 0ull;
+    }
+  }
+  sm.part[wave][lane] = part;
+  const uint64_t Z = wave_allreduce_u64(w, OpAdd());
+  __syncthreads();
+  uint64_t below = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) below += sm.part[v][lane];
+  return valid && (double)below < (double)p * (double)Z;
+}
+
 // Wave 0: exact resolution of n <= 64 boundary candidates (one per lane).  A
 // candidate is kept iff base + (mass of the candidates with smaller keys) < target.
-// Writes kappa (largest kept key) to LDS; returns the kept flag of this lane.
+// Writes kappa (largest kept key) to LDS.
 template <int FMAX>
-__device__ __forceinline__ bool resolve_boundary(RouteSmem<FMAX>& sm, uint64_t key, uint64_t w,
-                                                 int n, uint64_t base, double target) {
+__device__ __forceinline__ void resolve_boundary(RouteSmem<FMAX>& sm, uint64_t key,
+                                                 uint64_t w, int n, uint64_t base,
+                                                 double target) {
   const int lane = threadIdx.x;
   uint64_t below = 0;
   for (int j = 0; j < n; ++j) {
@@ -168,7 +213,6 @@ __device__ __forceinline__ bool resolve_boundary(RouteSmem<FMAX>& sm, uint64_t k
   const bool kept = lane < n && (double)(base + below) < target;
   const uint64_t kappa = wave_allreduce_u64(kept ? key : 0ull, OpMax());
   if (lane == 0) sm.kappa = kappa;
-  return kept;
 }
 
 // Wave 0: scan the 256-bucket histogram from base0 and find the first bucket
@@ -209,8 +253,8 @@ __device__ __forceinline__ void scan_find(RouteSmem<FMAX>& sm, uint64_t base0, b
 }
 
 template <int FMAX, typename Op>
-__device__ __forceinline__ uint64_t block_allreduce_u64(RouteSmem<FMAX>& sm, uint64_t v, Op op,
-                                                        int slot) {
+__device__ __forceinline__ uint64_t block_allreduce_u64(RouteSmem<FMAX>& sm, uint64_t v,
+                                                        Op op, int slot) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   v = wave_allreduce_u64(v, op);
   if (lane == 0) sm.redu[slot][wave] = v;
@@ -223,14 +267,14 @@ __device__ __forceinline__ uint64_t block_allreduce_u64(RouteSmem<FMAX>& sm, uin
 }
 
 // Cut of a frontier of K > 64 candidates (p < 1).  The histogram and bl_n are
-// zeroed before the scoring barrier.  Returns kappa.
+// zero on entry.  Returns kappa.
 template <int FMAX>
-__device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const int32_t* fr,
-                                                    int K, float p) {
+__device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const float* sc,
+                                                    const int32_t* fr, int K, float p) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   float smax = -INFINITY, smin = INFINITY;
   for (int i = tid; i < K; i += kThreads) {
-    const float s = sm.sc[i];
+    const float s = sc[i];
     smax = fmaxf(smax, s);
     smin = fminf(smin, s);
   }
@@ -254,7 +298,7 @@ __device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const i
   const float bscale = range > 0.f ? 256.f / range : 0.f;
   auto bucket = [&](float s) { return min((int)((smax - s) * bscale), 255); };
   for (int i = tid; i < K; i += kThreads) {
-    const float s = sm.sc[i];
+    const float s = sc[i];
     const int bk = bucket(s);
     atomicAdd(&sm.hcnt[bk], 1u);
     atomicAdd(&sm.hmass[bk], (unsigned long long)fixed_mass(s, smax));
@@ -265,7 +309,7 @@ __device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const i
   const int bstar = sm.bstar;
   if (sm.bcount <= kWave) {
     for (int i = tid; i < K; i += kThreads) {
-      const float s = sm.sc[i];
+      const float s = sc[i];
       if (bucket(s) == bstar) {
         const int slot = atomicAdd(&sm.bl_n, 1);
         if (slot < kWave) {
@@ -289,7 +333,7 @@ __device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const i
   // bound is defensive.
   uint64_t lo = ~0ull, hi = 0ull;
   for (int i = tid; i < K; i += kThreads) {
-    const float s = sm.sc[i];
+    const float s = sc[i];
     if (bucket(s) == bstar) {
       const uint64_t k = make_key(s, fr[i]);
       lo = k < lo ? k : lo;
@@ -309,7 +353,7 @@ __device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const i
     if (tid == 0) sm.bl_n = 0;
     __syncthreads();
     for (int i = tid; i < K; i += kThreads) {
-      const float s = sm.sc[i];
+      const float s = sc[i];
       const uint64_t k = make_key(s, fr[i]);
       if (k >= lo && k <= hi) {
         const int dg = (int)((k >> shift) & 255u);
@@ -327,7 +371,7 @@ __device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const i
     const uint64_t nhi = last < hi ? last : hi;
     if (sm.bcount <= kWave || last_pass) {
       for (int i = tid; i < K; i += kThreads) {
-        const float s = sm.sc[i];
+        const float s = sc[i];
         const uint64_t k = make_key(s, fr[i]);
         if (k >= nlo && k <= nhi) {
           const int slot = atomicAdd(&sm.bl_n, 1);
@@ -349,7 +393,7 @@ __device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const i
     lo = ~0ull;
     hi = 0ull;
     for (int i = tid; i < K; i += kThreads) {
-      const uint64_t k = make_key(sm.sc[i], fr[i]);
+      const uint64_t k = make_key(sc[i], fr[i]);
       if (k >= nlo && k <= nhi) {
         lo = k < lo ? k : lo;
         hi = k > hi ? k : hi;
@@ -360,7 +404,7 @@ __device__ __forceinline__ uint64_t top_p_cut_large(RouteSmem<FMAX>& sm, const i
   }
 }
 
-template <typename T, int D, int FMAX>
+template <typename T, int D, int FMAX, bool R1>
 __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict__ tree,
                                                          const T* __restrict__ Q, RouteArgs a,
                                                          int32_t* __restrict__ sel,
@@ -379,10 +423,12 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
   const int64_t b = head / ((int64_t)a.n_pos * a.H_q);
   const int kvh = h / a.G;
   const char* tb = tree + (b * a.H_kv + kvh) * a.lay.stride;
-  const int R = a.lay.R, C = a.lay.C, L = a.lay.L;
-  const int log2C = (C & (C - 1)) == 0 ? __ffs(C) - 1 : -1;
+  const int R = R1 ? 1 : a.lay.R;
+  const int C = a.lay.C, L = a.lay.L;
   const bool want_gap = gapo != nullptr;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  auto khat = [&](int l) { return tb + a.lay.khat[l]; };
+  auto bhat = [&](int l) { return reinterpret_cast<const float*>(tb + a.lay.bhat[l]); };
 
   float q[VEC];
   {
@@ -397,7 +443,13 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
   bool overflow = a.lay.n[L] > FMAX;
   if (!overflow)
     for (int i = tid; i < K; i += kThreads) sm.fr[0][i] = i;
+  if (tid < 256) {
+    sm.hcnt[tid] = 0u;
+    sm.hmass[tid] = 0ull;
+  }
+  if (tid == 0) sm.bl_n = 0;
   __syncthreads();
+
   int cur = 0;
   int m1 = 0;
   for (int l = L; l >= 1 && !overflow; --l) {
@@ -407,60 +459,45 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
     const uint64_t t0 = wall_clock64();
     uint64_t t1 = t0, t2 = t0;
 #endif
-    const bool large = K > kWave;
-    if (large) {  // zeroed here, made visible by the scoring barrier
-      if (tid < 256) {
-        sm.hcnt[tid] = 0u;
-        sm.hmass[tid] = 0ull;
-      }
-      if (tid == 0) sm.bl_n = 0;
+    const int n_orph = l > 1 ? (int)(a.lay.n[l - 1] - (int64_t)C * a.lay.n[l]) : 0;
+    const int first_orphan = l > 1 ? (int)((int64_t)C * a.lay.n[l]) : 0;
+    // 1. Scores of the frontier.
+    const float* sc = sm.sc;
+    if (K > 1) {
+      const char* k0 = khat(l);
+      const float* b0 = bhat(l);
+      score_items<T, D, R1>(sm.sc, K, R, [&](int x) { return Loc{k0, b0, fr[x]}; }, q);
     }
-    if (K > 1)
-      score_frontier<T, D, FMAX>(sm, fr, K, R, tb + a.lay.khat[l],
-                                 reinterpret_cast<const float*>(tb + a.lay.bhat[l]), q);
 #if ZHA_ROUTE_PROFILE
     t1 = wall_clock64();
 #endif
+    // 2. The cut.
+    const bool large = K > kWave;
     int m = 0;
     uint64_t next_key = ~0ull;
     uint64_t kappa = ~0ull;
+    bool kept_small = false;  // small frontier: this lane's candidate is kept
     if (!large) {
-      // Wave 0 cuts and compacts; the other waves wait at the barrier.
-      if (wave == 0) {
-        const bool valid = lane < K;
-        bool kept = valid;
-        if (K > 1) {
-          const float s = valid ? sm.sc[lane] : -INFINITY;
-          const float smax = wave_allreduce_f32(s, OpMax());
-          const uint64_t key = valid ? make_key(s, fr[lane]) : ~0ull;
-          const uint64_t w = valid ? fixed_mass(s, smax) : 0ull;
-          const uint64_t Z = wave_allreduce_u64(w, OpAdd());
-          kept = resolve_boundary(sm, key, w, K, 0ull, (double)a.p * (double)Z);
-          if (want_gap) {
-            const uint64_t nk = wave_allreduce_u64((valid && !kept) ? key : ~0ull, OpMin());
-            if (lane == 0) sm.next = nk;
-          }
-        } else if (lane == 0) {
-          sm.kappa = ~0ull;
-          sm.next = ~0ull;
+      if (K > 1) {
+        uint64_t key;
+        kept_small = small_cut(sm, sc, fr, K, a.p, key);
+        if (want_gap) {
+          kappa = wave_allreduce_u64(kept_small ? key : 0ull, OpMax());
+          next_key = wave_allreduce_u64((lane < K && !kept_small) ? key : ~0ull, OpMin());
         }
-        const uint64_t bal = __ballot(kept);
-        if (kept) sm.small_ids[__popcll((unsigned long long)(bal & lt))] = fr[lane];
-        if (lane == 0) sm.m = __popcll((unsigned long long)bal);
+      } else {
+        kept_small = lane < K;
       }
-      __syncthreads();
-      m = sm.m;
-      kappa = sm.kappa;
-      next_key = sm.next;
+      m = __popcll((unsigned long long)__ballot(kept_small));
     } else {
-      kappa = top_p_cut_large<FMAX>(sm, fr, K, a.p);
+      kappa = top_p_cut_large(sm, sc, fr, K, a.p);
     }
 #if ZHA_ROUTE_PROFILE
     t2 = wall_clock64();
 #endif
     uint32_t mybits = 0;
     if (large) {
-      // Kept flags per round of 256 positions; ballots give ascending ranks.
+      // Kept flags per round of kThreads positions; ballots give ascending ranks.
       const int rounds = (K + kThreads - 1) / kThreads;
 #pragma unroll
       for (int e = 0; e < kRounds; ++e) {
@@ -468,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
           const int i = e * kThreads + tid;
           bool kept = false;
           if (i < K) {
-            const uint64_t k = make_key(sm.sc[i], fr[i]);
+            const uint64_t k = make_key(sc[i], fr[i]);
             kept = k <= kappa;
             if (!kept && k < next_key) next_key = k;
           }
@@ -489,6 +526,13 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
         for (int w = 1; w < kWaves; ++w)
           next_key = sm.redu[0][w] < next_key ? (uint64_t)sm.redu[0][w] : next_key;
       }
+      // The histogram is free again: clear it for the next large cut (the
+      // barrier that ends this level orders the clearing before that cut).
+      if (tid < 256) {
+        sm.hcnt[tid] = 0u;
+        sm.hmass[tid] = 0ull;
+      }
+      if (tid == 0) sm.bl_n = 0;
     }
     if (tid == 0) {
       const int64_t o = head * L + (l - 1);
@@ -500,17 +544,20 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
         gapo[o] = (next_key == ~0ull || kappa == ~0ull) ? INFINITY
                                                         : key_score(kappa) - key_score(next_key);
     }
+    // 3. Next frontier: children of the kept nodes in ascending order, then the
+    // orphans.
     if (l > 1) {
-      const int n_orph = (int)(a.lay.n[l - 1] - (int64_t)C * a.lay.n[l]);
       const int64_t knext = (int64_t)m * C + n_orph;
       if (knext > FMAX) {
         overflow = true;
         break;
       }
       if (!large) {
-        for (int x = tid; x < m * C; x += kThreads) {
-          const int j = log2C >= 0 ? (x >> log2C) : x / C;
-          nx[x] = sm.small_ids[j] * C + (x - j * C);
+        // Every wave knows the kept set; wave w writes children c = w, w + kWaves, ...
+        const int j = __popcll((unsigned long long)(__ballot(kept_small) & lt));
+        if (kept_small) {
+          const int id = fr[lane];
+          for (int c = wave; c < C; c += kWaves) nx[j * C + c] = id * C + c;
         }
       } else {
         uint32_t run = 0;
@@ -531,7 +578,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
           }
         }
       }
-      const int first_orphan = (int)((int64_t)C * a.lay.n[l]);
       for (int x = tid; x < n_orph; x += kThreads) nx[m * C + x] = first_orphan + x;
       __syncthreads();
       K = (int)knext;
@@ -539,7 +585,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
     } else {
       int32_t* out = sel + head * a.cap;
       if (!large) {
-        for (int j = tid; j < m && j < a.cap; j += kThreads) out[j] = sm.small_ids[j];
+        const int j = __popcll((unsigned long long)(__ballot(kept_small) & lt));
+        if (wave == 0 && kept_small && j < a.cap) out[j] = fr[lane];
       } else {
         uint32_t run = 0;
         const int rounds = (K + kThreads - 1) / kThreads;
@@ -602,12 +649,16 @@ template <typename T, int D>
 int launch_route(const RouteArgs& a, const void* tree, const void* Q, int32_t* sel, int32_t* cnt,
                  int32_t* stats, float* gap, hipStream_t s) {
   const unsigned blocks = (unsigned)a.n_heads;
+  const char* tr = reinterpret_cast<const char*>(tree);
+  const T* q = reinterpret_cast<const T*>(Q);
   if (!(a.p < 1.0f)) {
     route_keep_all_kernel<<<blocks, kThreads, 0, s>>>(a, sel, cnt, stats, gap);
+  } else if (a.lay.R == 1) {
+    route_kernel<T, D, kRouteFrontierMax, true>
+        <<<blocks, kThreads, 0, s>>>(tr, q, a, sel, cnt, stats, gap);
   } else {
-    route_kernel<T, D, kRouteFrontierMax><<<blocks, kThreads, 0, s>>>(
-        reinterpret_cast<const char*>(tree), reinterpret_cast<const T*>(Q), a, sel, cnt, stats,
-        gap);
+    route_kernel<T, D, kRouteFrontierMax, false>
+        <<<blocks, kThreads, 0, s>>>(tr, q, a, sel, cnt, stats, gap);
   }
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
 }
