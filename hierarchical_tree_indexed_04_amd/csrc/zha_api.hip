@@ -20,6 +20,7 @@ int check_geom(const zha_geom* g) {
   if (g->C < 2 || g->C > 1024 || g->L < 1 || g->L > kMaxLevels || g->R < 1 || g->R > 16)
     return ZHA_ERR_GEOM;
   if (g->T < 1 || g->T >= ((int64_t)1 << 31)) return ZHA_ERR_GEOM;
+  if (g->kv_layout != ZHA_KV_SPLIT && g->kv_layout != ZHA_KV_CHUNKED) return ZHA_ERR_LAYOUT;
   int64_t span = 1;
   for (int l = 0; l < g->L; ++l) {
     span *= g->C;
@@ -57,8 +58,20 @@ BuildArgs make_build_args(const zha_geom* g) {
   a.n_trees = g->B * g->H_kv;
   a.H_kv = g->H_kv;
   a.d = g->d;
+  a.chunked = g->kv_layout == ZHA_KV_CHUNKED;
   a.T = g->T;
   return a;
+}
+
+int log2_or_neg(int C) { return (C & (C - 1)) == 0 ? __builtin_ctz((unsigned)C) : -1; }
+
+// K and V pointers per layout: split needs both, chunked takes the KV buffer
+// as K and no V.
+int check_kv(const zha_geom* g, const void* K, const void* V) {
+  if (K == nullptr) return ZHA_ERR_NULL;
+  if (g->kv_layout == ZHA_KV_CHUNKED) return V == nullptr ? ZHA_OK : ZHA_ERR_LAYOUT;
+  if (V == nullptr) return ZHA_ERR_NULL;
+  return aligned16(V) ? ZHA_OK : ZHA_ERR_ALIGN;
 }
 
 
@@ -88,6 +101,7 @@ const char* zha_strerror(int code) {
     case ZHA_ERR_CAP: return "cap must be >= 1";
     case ZHA_ERR_LAUNCH: return "kernel launch failed";
     case ZHA_ERR_NPOS: return "n_pos must be >= 1";
+    case ZHA_ERR_LAYOUT: return "unknown kv_layout, or V given with the chunked layout";
     default: return "unknown error";
   }
 }
@@ -195,15 +209,17 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, con
   a.H_kv = g->H_kv;
   a.G = g->H_q / g->H_kv;
   a.C = g->C;
-  a.log2C = (g->C & (g->C - 1)) == 0 ? __builtin_ctz((unsigned)g->C) : -1;
+  a.log2C = log2_or_neg(g->C);
   a.cap = cap;
   a.S = ZHA_ATTN_BLOCKS;
+  a.chunked = g->kv_layout == ZHA_KV_CHUNKED;
   const bool need_scratch = attn_scratch_layout_bytes(a.n_heads, g->d) > 0;
-  if (Q == nullptr || K == nullptr || V == nullptr || sel == nullptr || cnt == nullptr ||
-      O == nullptr || (need_scratch && scratch == nullptr))
+  const int kv = check_kv(g, K, V);
+  if (kv) return kv;
+  if (Q == nullptr || sel == nullptr || cnt == nullptr || O == nullptr ||
+      (need_scratch && scratch == nullptr))
     return ZHA_ERR_NULL;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
-      (need_scratch && !aligned16(scratch)))
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(O) || (need_scratch && !aligned16(scratch)))
     return ZHA_ERR_ALIGN;
   if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
   return attn_dispatch(a, g->dtype, g->d, Q, K, V, sel, cnt, O, scratch,
@@ -233,11 +249,13 @@ int zha_dense_decode(const zha_geom* g, const void* Q, int32_t n_pos, const void
   a.H_kv = g->H_kv;
   a.G = g->H_q / g->H_kv;
   a.S = dense_splits(g, n_pos);
-  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr ||
-      (a.S > 1 && scratch == nullptr))
-    return ZHA_ERR_NULL;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
-      (a.S > 1 && !aligned16(scratch)))
+  a.C = g->C;
+  a.log2C = log2_or_neg(g->C);
+  a.chunked = g->kv_layout == ZHA_KV_CHUNKED;
+  const int kv = check_kv(g, K, V);
+  if (kv) return kv;
+  if (Q == nullptr || O == nullptr || (a.S > 1 && scratch == nullptr)) return ZHA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(O) || (a.S > 1 && !aligned16(scratch)))
     return ZHA_ERR_ALIGN;
   if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
   return dense_dispatch(a, g->dtype, g->d, Q, K, V, O, scratch,

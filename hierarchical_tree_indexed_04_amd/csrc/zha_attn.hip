@@ -78,6 +78,52 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
 
 
 
+// The K/V rows of one (b, kvh) pair in either cache layout.  Rows are
+// addressed by key row: token j of chunk c is key row c * CS + j, with CS = C
+// (split: K and V are [T, d] arrays, the value row has the same index in V)
+// or 2 C (chunked: pages of C key rows then C value rows, the value row is C
+// rows further in the same buffer).  Each lane reads its 16-byte slice `sub`.
+// BUF: buffer loads (block < 2^31 bytes), a slot without a row reads nothing.
+template <typename T, int D, bool BUF>
+struct KvBlock {
+  static constexpr uint32_t kRow = D * sizeof(T);
+  const char* k;
+  const char* v;
+  buf_t rk, rv;
+  int cs;
+  __device__ __forceinline__ KvBlock(const T* K, const T* V, int64_t tr, int64_t T_, int C,
+                                     int chunked, int sub) {
+    const int64_t n = kv_block_elems(T_, C, D, chunked);
+    const T* kb = K + tr * n;
+    const T* vb = chunked ? kb + (int64_t)C * D : V + tr * n;
+    k = reinterpret_cast<const char*>(kb) + sub * 16;
+    v = reinterpret_cast<const char*>(vb) + sub * 16;
+    const int64_t bytes = BUF ? n * (int64_t)sizeof(T) : 0;
+    rk = make_buf(kb, bytes);
+    rv = chunked ? rk : make_buf(vb, bytes);
+    cs = chunked ? 2 * C : C;
+    vdelta = chunked ? (uint32_t)C * kRow : 0u;
+    sub16 = (uint32_t)sub * 16u;
+  }
+  uint32_t vdelta, sub16;
+  __device__ __forceinline__ int key_row(int chunk, int j) const { return chunk * cs + j; }
+  __device__ __forceinline__ void load(int row, bool live, uint4& kv, uint4& vv) const {
+    if (BUF) {
+      // Straight-line: a slot without a row reads nothing and gets zeros.
+      const uint32_t off = live ? (uint32_t)row * kRow + sub16 : kBufNone;
+      kv = bld16(rk, off);
+      vv = bld16(rv, live ? off + vdelta : kBufNone);
+    } else if (live) {
+      const size_t off = (size_t)(uint32_t)row * kRow;
+      kv = ld16(k + off);
+      vv = ld16(v + off);
+    } else {
+      kv = make_uint4(0u, 0u, 0u, 0u);
+      vv = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+};
+
 // Combines the online-softmax states of the RPB row groups of a workgroup and
 // writes either the final output row(s) or a split partial.
 template <typename T, int D, int RPB>
@@ -227,9 +273,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   const int h = (int)(head % a.H_q);
   const int64_t b = head / ((int64_t)a.n_pos * a.H_q);
   const int64_t tr = b * a.H_kv + h / a.G;
-  const T* Kt = K + tr * a.T * D;
-  const T* Vt = V + tr * a.T * D;
   const int32_t* ids = sel + head * a.cap;
+  const KvBlock<T, D, BUF> kvb(K, V, tr, a.T, a.C, a.chunked, sub);
 
   // This split's chunks, plus (last split) the sink when chunk 0 is not selected
   // and C_cur.  Token positions and ids fit in 31 bits (T < 2^31).
@@ -239,16 +284,12 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   const int ct = (c1 - c0) * Cc;  // chunk tokens come first, then the extras
   int n_extra = 0;
   bool sink = false;
-  const int tail0 = (int)(a.n1 * a.C);
+  const int n1 = (int)a.n1;
   if (split == a.S - 1) {
     sink = (c == 0) || (ids[0] != 0);
     n_extra = (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C);
   }
   const int ntok = ct + n_extra;
-  const char* Kb = reinterpret_cast<const char*>(Kt) + sub * 16;
-  const char* Vb = reinterpret_cast<const char*>(Vt) + sub * 16;
-  const buf_t rK = make_buf(Kt, BUF ? a.T * D * (int64_t)sizeof(T) : 0);
-  const buf_t rV = make_buf(Vt, BUF ? a.T * D * (int64_t)sizeof(T) : 0);
 
   const uint4 qv = ld16c(Q + head * D + sub * VEC);
   const float inv = 1.0f / sqrtf((float)D);
@@ -271,40 +312,26 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     const int xb = r0 * Cc;
     const int xe = final_round ? ntok : (r0 + rn) * Cc;
     for (int base = xb; base < xe; base += RPB * kUA) {
-      int tok[kUA];
+      int row[kUA];
 #pragma unroll
       for (int u = 0; u < kUA; ++u) {
         const int x = base + u * RPB + grp;
         const int ci = POW2 ? (x >> log2C) : x / Cc;
-        tok[u] = s_ids[min(max(ci - r0, 0), kIds - 1)];
+        row[u] = s_ids[min(max(ci - r0, 0), kIds - 1)];
       }
 #pragma unroll
       for (int u = 0; u < kUA; ++u) {
         const int x = base + u * RPB + grp;
         const int ci = POW2 ? (x >> log2C) : x / Cc;
         const int e = x - ct;
-        const int tt = sink ? (e == 0 ? 0 : tail0 + e - 1) : tail0 + e;
-        tok[u] = x < ct ? tok[u] * Cc + (x - ci * Cc) : tt;
+        const bool is_sink = sink && e == 0;
+        const int chunk = x < ct ? row[u] : (is_sink ? 0 : n1);
+        const int j = x < ct ? x - ci * Cc : (is_sink ? 0 : e - (sink ? 1 : 0));
+        row[u] = kvb.key_row(chunk, j);
       }
       uint4 kv[kUA], vv[kUA];
 #pragma unroll
-      for (int u = 0; u < kUA; ++u) {
-        const bool live = base + u * RPB + grp < xe;
-        if (BUF) {
-          const uint32_t off = live ? (uint32_t)tok[u] * (uint32_t)(D * sizeof(T)) +
-                                          (uint32_t)(sub * 16)
-                                    : kBufNone;
-          kv[u] = bld16(rK, off);
-          vv[u] = bld16(rV, off);
-        } else if (live) {
-          const size_t off = (size_t)(uint32_t)tok[u] * (D * sizeof(T));
-          kv[u] = ld16(Kb + off);
-          vv[u] = ld16(Vb + off);
-        } else {
-          kv[u] = make_uint4(0u, 0u, 0u, 0u);
-          vv[u] = make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
+      for (int u = 0; u < kUA; ++u) kvb.load(row[u], base + u * RPB + grp < xe, kv[u], vv[u]);
       __builtin_amdgcn_sched_barrier(0);
       float s[kUA];
 #pragma unroll
@@ -425,14 +452,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
     const int hq = (int)(h % a.H_q);
     const int64_t b = h / ((int64_t)a.n_pos * a.H_q);
     const int64_t tr = b * a.H_kv + hq / a.G;
-    const char* Kt = reinterpret_cast<const char*>(K + tr * a.T * D) + sub * 16;
-    const char* Vt = reinterpret_cast<const char*>(V + tr * a.T * D) + sub * 16;
-    const buf_t rK = make_buf(K + tr * a.T * D, BUF ? a.T * D * (int64_t)sizeof(T) : 0);
-    const buf_t rV = make_buf(V + tr * a.T * D, BUF ? a.T * D * (int64_t)sizeof(T) : 0);
+    const KvBlock<T, D, BUF> kvb(K, V, tr, a.T, a.C, a.chunked, sub);
     const uint4 qv = ld16c(Q + (int64_t)h * D + sub * VEC);
     const int Cc = a.C, log2C = a.log2C;
     const int ct = c * Cc;  // chunk tokens come first, then the extras
-    const int tail0 = (int)(a.n1 * a.C);
+    const int n1 = (int)a.n1;
     float m = -INFINITY, l = 0.f, acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
@@ -448,44 +472,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
         __syncthreads();
       }
       for (int base = xr; base < xe; base += RPB * kUA) {
-        // Token of every slot first: the chunk-id reads from LDS are
+        // Key row of every slot first: the chunk-id reads from LDS are
         // unconditional (clamped in bounds, one wait for all of them), so
         // the 2 kUA row loads below issue back to back.
-        int tok[kUA];
+        int row[kUA];
 #pragma unroll
         for (int u = 0; u < kUA; ++u) {
           const int x = base + u * RPB + grp;
           const int ci = POW2 ? (x >> log2C) : x / Cc;
-          tok[u] = s_ids[min(max(ci - fc, 0), kIds - 1)];
+          row[u] = s_ids[min(max(ci - fc, 0), kIds - 1)];
         }
 #pragma unroll
         for (int u = 0; u < kUA; ++u) {
+          // Position x is token j of chunk `row` (a selected chunk), or an
+          // extra: the sink (chunk 0, token 0) or token e - sink of the
+          // partial chunk n1.
           const int x = base + u * RPB + grp;
           const int ci = POW2 ? (x >> log2C) : x / Cc;
           const int e = x - ct;
-          const int tt = sink ? (e == 0 ? 0 : tail0 + e - 1) : tail0 + e;
-          tok[u] = x < ct ? tok[u] * Cc + (x - ci * Cc) : tt;
+          const bool is_sink = sink && e == 0;
+          const int chunk = x < ct ? row[u] : (is_sink ? 0 : n1);
+          const int j = x < ct ? x - ci * Cc : (is_sink ? 0 : e - (sink ? 1 : 0));
+          row[u] = kvb.key_row(chunk, j);
         }
         uint4 kv[kUA], vv[kUA];
 #pragma unroll
-        for (int u = 0; u < kUA; ++u) {
-          const bool live = base + u * RPB + grp < xe;
-          if (BUF) {
-            // Straight-line: a slot without a row reads nothing and gets zeros.
-            const uint32_t off = live ? (uint32_t)tok[u] * (uint32_t)(D * sizeof(T)) +
-                                            (uint32_t)(sub * 16)
-                                      : kBufNone;
-            kv[u] = bld16(rK, off);
-            vv[u] = bld16(rV, off);
-          } else if (live) {
-            const size_t off = (size_t)(uint32_t)tok[u] * (D * sizeof(T));
-            kv[u] = ld16(Kt + off);
-            vv[u] = ld16(Vt + off);
-          } else {
-            kv[u] = make_uint4(0u, 0u, 0u, 0u);
-            vv[u] = make_uint4(0u, 0u, 0u, 0u);
-          }
-        }
+        for (int u = 0; u < kUA; ++u) kvb.load(row[u], base + u * RPB + grp < xe, kv[u], vv[u]);
         // Keep all 2 kUA loads ahead of the arithmetic (the scheduler would
         // otherwise delay some V loads to reuse K's registers).
         __builtin_amdgcn_sched_barrier(0);
@@ -548,8 +560,11 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
   const int64_t b = bt / a.n_pos;
   const int split = blockIdx.y;
   const int64_t head0 = bt * a.H_q + (int64_t)kvh * a.G + tile * GT;
-  const T* Kt = K + (b * a.H_kv + kvh) * a.T * D;
-  const T* Vt = V + (b * a.H_kv + kvh) * a.T * D;
+  // Key row of token t: t (split) or t + (t / C) C (chunked pages of C key
+  // rows then C value rows, the value row C rows further).
+  const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
+  const T* Kt = K + (b * a.H_kv + kvh) * nblk;
+  const T* Vt = a.chunked ? Kt + (int64_t)a.C * D : V + (b * a.H_kv + kvh) * nblk;
   const int64_t t0 = (a.T * split) / a.S, t1 = (a.T * (split + 1)) / a.S;
 
   uint4 qv[GT];
@@ -572,8 +587,10 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
       const int64_t tok = base + u * RPB + grp;
       ok[u] = tok < t1;
       if (ok[u]) {
-        kv[u] = ld16(Kt + tok * D + sub * VEC);
-        vv[u] = ld16(Vt + tok * D + sub * VEC);
+        const int64_t ci = a.log2C >= 0 ? (tok >> a.log2C) : tok / a.C;
+        const int64_t row = a.chunked ? tok + ci * a.C : tok;
+        kv[u] = ld16(Kt + row * D + sub * VEC);
+        vv[u] = ld16(Vt + row * D + sub * VEC);
       } else {
         kv[u] = make_uint4(0u, 0u, 0u, 0u);
         vv[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -605,7 +622,8 @@ int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
     int32_t* plan = reinterpret_cast<int32_t*>(scratch);
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) +
                                            align256((a.n_heads + 2) * 4));
-    const bool buf = a.T * D * (int64_t)sizeof(T) < ((int64_t)1 << 31);
+    const bool buf =
+        kv_block_elems(a.T, a.C, D, a.chunked) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
 #define ZHA_BAL(P2, BF)                                                                    \
   attn_balanced_kernel<T, D, P2, BF><<<(unsigned)a.S, kThreads, 0, s>>>(                  \
       reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),                       \
@@ -625,7 +643,8 @@ int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
   AttnArgs a1 = a;
   a1.S = 1;
   dim3 grid((unsigned)a.n_heads, 1u);
-  const bool buf = a.T * D * (int64_t)sizeof(T) < ((int64_t)1 << 31);
+  const bool buf =
+      kv_block_elems(a.T, a.C, D, a.chunked) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
 #define ZHA_PART(P2, BF)                                                                    \
   attn_partial_kernel<T, D, P2, BF><<<grid, kThreads, 0, s>>>(                              \
       reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),                        \

@@ -42,7 +42,10 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
   const int C = a.lay.C;
   const int R = a.lay.R;
   const double inv_sqrt_d = 1.0 / sqrt((double)D);
-  const T* keys = K + ((tr * a.T) + i * (int64_t)C) * D;
+  // Chunk i's C keys are consecutive rows in both layouts; only the chunk's
+  // first row differs (chunked: each page holds C key rows, then C value rows).
+  const T* keys = K + tr * kv_block_elems(a.T, C, D, a.chunked) +
+                  i * (int64_t)C * (a.chunked ? 2 : 1) * D;
   T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
   float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
 

@@ -25,6 +25,7 @@ struct BuildArgs {
   int32_t n_trees;  // B * H_kv
   int32_t H_kv;
   int32_t d;
+  int32_t chunked;  // ZHA_KV_CHUNKED layout
   int64_t T;
 };
 
@@ -58,6 +59,7 @@ struct AttnArgs {
   int32_t log2C;  // log2(C) when C is a power of two, else -1
   int32_t cap;
   int32_t S;      // workgroups of the balanced split (or splits per head)
+  int32_t chunked;  // ZHA_KV_CHUNKED layout
 };
 
 struct DenseArgs {
@@ -68,7 +70,16 @@ struct DenseArgs {
   int32_t H_kv;
   int32_t G;
   int32_t S;
+  int32_t C;
+  int32_t log2C;    // log2(C) when C is a power of two, else -1
+  int32_t chunked;  // ZHA_KV_CHUNKED layout
 };
+
+// Elements of one (b, kvh) block of the KV cache: [T, d] per tensor (split)
+// or [ceil(T / C), 2, C, d] holding both (chunked).
+__host__ __device__ inline int64_t kv_block_elems(int64_t T, int C, int d, bool chunked) {
+  return chunked ? (T + C - 1) / C * 2 * C * (int64_t)d : T * (int64_t)d;
+}
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 

@@ -51,6 +51,7 @@ static_assert(kThreads >= 256, "histograms are cleared one bucket per thread");
 #define ZHA_ROUTE_XCD 1
 #endif
 constexpr int kU = ZHA_ROUTE_ROWS;  // summary rows in flight per lane while scoring
+constexpr int kMaxChildren = 1024;  // C <= 1024
 
 #ifndef ZHA_ROUTE_PROFILE
 #define ZHA_ROUTE_PROFILE 0
@@ -78,10 +79,11 @@ struct RouteSmem {
   unsigned long long bkey[kWave];    // boundary candidates
   unsigned long long bw[kWave];
   unsigned long long part[kWaves][kWave];   // small cut: partial masses below each lane
+  float pre[kMaxChildren];                  // scores of the top candidate's children
   uint32_t wcnt[FMAX / kThreads * kWaves];  // kept per (round, wave)
   float redf[2][kWaves];
   unsigned long long redu[2][kWaves];
-  unsigned long long kappa, next, base;
+  unsigned long long kappa, next, base, kmask;
   double target;
   int32_t bstar, bcount, bl_n;
 };
@@ -161,39 +163,90 @@ __device__ __forceinline__ void score_items(float* out, int NI, int R, Locate lo
   __syncthreads();
 }
 
-// Cut of a frontier of 1 < K <= 64 candidates, evaluated by every wave with
-// candidate i in lane i: i is kept iff the mass of the candidates with smaller
-// keys is < p Z.  Wave w sums that mass over candidates [w J, (w + 1) J) and
-// the partial sums meet in LDS.  Returns the lane's kept flag (the same in
-// every wave); contains one barrier.
+// Waves 1 .. kWaves-1, while wave 0 cuts a frontier of K <= 64 candidates:
+// the top candidate (largest score, lowest id) is kept by every cut (nothing
+// precedes it, so its preceding mass 0 is < p Z), so its C children are
+// certainly in the next frontier.  Score them now (one tangent per node) into
+// pre[]; when the cut keeps only that node and the next level has no
+// orphans, the next frontier is exactly these children and its scoring costs
+// no memory round trip.
+template <typename T, int D, int FMAX>
+__device__ __forceinline__ void score_top_children(RouteSmem<FMAX>& sm, const float* sc,
+                                                   const int32_t* fr, int K, int C,
+                                                   const char* khat, const float* bhat,
+                                                   const float* q) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int LPR = D / VEC;
+  constexpr int RPW = kWave / LPR;  // rows per wave and pass
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;
+  const bool valid = lane < K;
+  const uint64_t key = valid ? make_key(sc[lane], fr[lane]) : ~0ull;
+  const int top = (int)(uint32_t)wave_allreduce_u64(key, OpMin());
+  for (int c = (wave - 1) * RPW + lane / LPR; c - lane / LPR < C; c += (kWaves - 1) * RPW) {
+    const int cc = min(c, C - 1);  // lanes past C recompute the last child, never stored
+    const int64_t row = (int64_t)top * C + cc;
+    float k[VEC];
+    Vec<T>::widen(ld16c(khat + row * (int64_t)(D * sizeof(T)) + sub * 16), k);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dot = fmaf(q[e], k[e], dot);
+    dot = group_allreduce<LPR>(dot, OpAdd());
+    if (sub == 0 && c < C) sm.pre[c] = dot + bhat[row];
+  }
+}
+
+// Cut of a frontier of 1 < K <= 64 candidates.  Lane i holds candidate i,
+// which is kept iff the mass of the candidates with smaller keys is < p Z.
+// The sum over smaller keys is split across nw = ceil(K / J) waves (wave w
+// takes candidates [w J, (w + 1) J)); with nw = 1 wave 0 works alone and no
+// partial goes through LDS.  Wave 0 decides and publishes the kept mask (and,
+// for the gap, kappa and the smallest dropped key); the other waves only wait.
+// Returns the kept mask (bit i = candidate i), the same in every wave.
 template <int FMAX>
-__device__ __forceinline__ bool small_cut(RouteSmem<FMAX>& sm, const float* sc,
-                                          const int32_t* fr, int K, float p, uint64_t& key) {
+__device__ __forceinline__ uint64_t small_cut(RouteSmem<FMAX>& sm, const float* sc,
+                                              const int32_t* fr, int K, float p, bool want_gap) {
   constexpr int J = kWave / kWaves;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const bool valid = lane < K;
-  const float s = valid ? sc[lane] : -INFINITY;
-  const float smax = wave_allreduce_f32(s, OpMax());
-  key = valid ? make_key(s, fr[lane]) : ~0ull;
-  const uint64_t w = valid ? fixed_mass(s, smax) : 0ull;
-  uint64_t part = 0;
-  const int j0 = wave * J;
+  const int nw = (K + J - 1) / J;
+  uint64_t key = ~0ull, w = 0, part = 0;
+  if (wave < nw) {
+    const bool valid = lane < K;
+    const float s = valid ? sc[lane] : -INFINITY;
+    const float smax = wave_max_f32_bcast(s);
+    key = valid ? make_key(s, fr[lane]) : ~0ull;
+    w = valid ? fixed_mass(s, smax) : 0ull;
+    const int j0 = wave * J;
 #pragma unroll
-  for (int jj = 0; jj < J; ++jj) {
-    const int j = j0 + jj;
-    if (j < K) {
-      const uint64_t kj = readlane_u64(key, j);
-      const uint64_t wj = readlane_u64(w, j);
-      part += (kj < key) ? wj : 0ull;
+    for (int jj = 0; jj < J; ++jj) {
+      const int j = j0 + jj;
+      if (j < K) {
+        const uint64_t kj = readlane_u64(key, j);
+        const uint64_t wj = readlane_u64(w, j);
+        part += (kj < key) ? wj : 0ull;
+      }
+    }
+    if (nw > 1) sm.part[wave][lane] = part;
+  }
+  if (nw > 1) __syncthreads();
+  if (wave == 0) {
+    const uint64_t Z = wave_sum_u64_bcast(w);
+    uint64_t below = part;
+    for (int v = 1; v < nw; ++v) below += sm.part[v][lane];
+    const bool kept = lane < K && (double)below < (double)p * (double)Z;
+    const uint64_t mask = __ballot(kept);
+    if (lane == 0) sm.kmask = mask;
+    if (want_gap) {
+      const uint64_t kappa = wave_allreduce_u64(kept ? key : 0ull, OpMax());
+      const uint64_t next = wave_allreduce_u64((lane < K && !kept) ? key : ~0ull, OpMin());
+      if (lane == 0) {
+        sm.kappa = kappa;
+        sm.next = next;
+      }
     }
   }
-  sm.part[wave][lane] = part;
-  const uint64_t Z = wave_allreduce_u64(w, OpAdd());
   __syncthreads();
-  uint64_t below = 0;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) below += sm.part[v][lane];
-  return valid && (double)below < (double)p * (double)Z;
+  return sm.kmask;
 }
 
 // Wave 0: exact resolution of n <= 64 boundary candidates (one per lane).  A
@@ -452,6 +505,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
 
   int cur = 0;
   int m1 = 0;
+  bool ready = false;  // sm.sc already holds the frontier's scores
   for (int l = L; l >= 1 && !overflow; --l) {
     const int32_t* fr = sm.fr[cur];
     int32_t* nx = sm.fr[cur ^ 1];
@@ -463,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
     const int first_orphan = l > 1 ? (int)((int64_t)C * a.lay.n[l]) : 0;
     // 1. Scores of the frontier.
     const float* sc = sm.sc;
-    if (K > 1) {
+    if (K > 1 && !ready) {
       const char* k0 = khat(l);
       const float* b0 = bhat(l);
       score_items<T, D, R1>(sm.sc, K, R, [&](int x) { return Loc{k0, b0, fr[x]}; }, q);
@@ -476,19 +530,23 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
     int m = 0;
     uint64_t next_key = ~0ull;
     uint64_t kappa = ~0ull;
-    bool kept_small = false;  // small frontier: this lane's candidate is kept
+    uint64_t kmask = 0;  // small frontier: bit i = candidate i kept
+    // Small frontiers that one wave cuts alone leave the other waves free to
+    // score the top candidate's children meanwhile.
+    const bool pre = R1 && l > 1 && K > 1 && K <= kWave / kWaves;
     if (!large) {
       if (K > 1) {
-        uint64_t key;
-        kept_small = small_cut(sm, sc, fr, K, a.p, key);
+        if (pre && wave != 0)
+          score_top_children<T, D, FMAX>(sm, sc, fr, K, C, khat(l - 1), bhat(l - 1), q);
+        kmask = small_cut(sm, sc, fr, K, a.p, want_gap);
         if (want_gap) {
-          kappa = wave_allreduce_u64(kept_small ? key : 0ull, OpMax());
-          next_key = wave_allreduce_u64((lane < K && !kept_small) ? key : ~0ull, OpMin());
+          kappa = sm.kappa;
+          next_key = sm.next;
         }
       } else {
-        kept_small = lane < K;
+        kmask = K == 1 ? 1ull : 0ull;
       }
-      m = __popcll((unsigned long long)__ballot(kept_small));
+      m = __popcll((unsigned long long)kmask);
     } else {
       kappa = top_p_cut_large(sm, sc, fr, K, a.p);
     }
@@ -554,7 +612,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
       }
       if (!large) {
         // Every wave knows the kept set; wave w writes children c = w, w + kWaves, ...
-        const int j = __popcll((unsigned long long)(__ballot(kept_small) & lt));
+        const bool kept_small = (kmask >> lane) & 1ull;
+        const int j = __popcll((unsigned long long)(kmask & lt));
         if (kept_small) {
           const int id = fr[lane];
           for (int c = wave; c < C; c += kWaves) nx[j * C + c] = id * C + c;
@@ -579,14 +638,18 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const char* __restrict_
         }
       }
       for (int x = tid; x < n_orph; x += kThreads) nx[m * C + x] = first_orphan + x;
+      // Exactly the top candidate's children: their scores are already known.
+      ready = pre && m == 1 && n_orph == 0;
+      if (ready)
+        for (int c = tid; c < C; c += kThreads) sm.sc[c] = sm.pre[c];
       __syncthreads();
       K = (int)knext;
       cur ^= 1;
     } else {
       int32_t* out = sel + head * a.cap;
       if (!large) {
-        const int j = __popcll((unsigned long long)(__ballot(kept_small) & lt));
-        if (wave == 0 && kept_small && j < a.cap) out[j] = fr[lane];
+        const int j = __popcll((unsigned long long)(kmask & lt));
+        if (wave == 0 && ((kmask >> lane) & 1ull) && j < a.cap) out[j] = fr[lane];
       } else {
         uint32_t run = 0;
         const int rounds = (K + kThreads - 1) / kThreads;

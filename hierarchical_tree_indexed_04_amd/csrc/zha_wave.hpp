@@ -106,6 +106,28 @@ __device__ __forceinline__ uint64_t wave_allreduce_u64(uint64_t v, Op op) {
             op(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
+// Whole-wave max of a float (uniform result), on order-preserving integer
+// images so each step is one integer op: all-reduce inside each 16-lane row,
+// then row_bcast15 / row_bcast31 carry the row results into lane 63.
+__device__ __forceinline__ float wave_max_f32_bcast(float v) {
+  uint32_t u = ord_f32(v);
+  u = max(u, dpp_u32<kDppRowRor8>(u, u));
+  u = max(u, dpp_u32<kDppRowRor4>(u, u));
+  u = max(u, dpp_u32<kDppQpXor2>(u, u));
+  u = max(u, dpp_u32<kDppQpXor1>(u, u));
+  u = max(u, dpp_u32<kDppRowBcast15, 0xA>(u, u));
+  u = max(u, dpp_u32<kDppRowBcast31, 0xC>(u, u));
+  return unord_f32((uint32_t)__builtin_amdgcn_readlane((int)u, kWave - 1));
+}
+
+// Whole-wave sum of a 64-bit value (uniform result), same pattern.
+__device__ __forceinline__ uint64_t wave_sum_u64_bcast(uint64_t v) {
+  v = row_allreduce_u64(v, OpAdd());
+  v += dpp_u64<kDppRowBcast15, 0xA>(0ull, v);
+  v += dpp_u64<kDppRowBcast31, 0xC>(0ull, v);
+  return readlane_u64(v, kWave - 1);
+}
+
 // Inclusive prefix sum over the 64 lanes of a 64-bit value.
 __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
   v += dpp_u64<kDppRowShr1>(0ull, v);

@@ -14,11 +14,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzha.so")
 
 ZHA_F32 = 0
 ZHA_BF16 = 1
+ZHA_KV_SPLIT = 0
+ZHA_KV_CHUNKED = 1
 
 ERRORS = {
     -1: "ZHA_ERR_NULL", -2: "ZHA_ERR_GEOM", -3: "ZHA_ERR_DTYPE", -4: "ZHA_ERR_DIM",
     -5: "ZHA_ERR_P", -6: "ZHA_ERR_ALIGN", -7: "ZHA_ERR_CAP", -8: "ZHA_ERR_LAUNCH",
-    -9: "ZHA_ERR_NPOS",
+    -9: "ZHA_ERR_NPOS", -10: "ZHA_ERR_LAYOUT",
 }
 
 # Every function the header declares, with its ctypes signature.
@@ -28,7 +30,8 @@ _c_size_p = ctypes.POINTER(ctypes.c_size_t)
 class Geom(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("T", ctypes.c_int64), ("C", ctypes.c_int32),
-                ("L", ctypes.c_int32), ("R", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("L", ctypes.c_int32), ("R", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("kv_layout", ctypes.c_int32)]
 
 
 _GP = ctypes.POINTER(Geom)
@@ -81,12 +84,19 @@ def _check(rc: int, where: str):
         raise ZhaError(rc, where)
 
 
-def geom(g) -> Geom:
+def geom(g, kv_layout: int = ZHA_KV_SPLIT) -> Geom:
     """zha_geom from any object with B, H_q, H_kv, d, T, C, L, R and dtype ('f32'/'bf16')."""
     dt = g.dtype
     if isinstance(dt, str):
         dt = ZHA_BF16 if dt == "bf16" else ZHA_F32
-    return Geom(g.B, g.H_q, g.H_kv, g.d, g.T, g.C, g.L, g.R, dt)
+    return Geom(g.B, g.H_q, g.H_kv, g.d, g.T, g.C, g.L, g.R, dt, kv_layout)
+
+
+def kv_shape(g: Geom):
+    """Shape of K (and V) in the split layout, or of the KV buffer in the chunked one."""
+    if g.kv_layout == ZHA_KV_CHUNKED:
+        return (g.B, g.H_kv, -(-g.T // g.C), 2, g.C, g.d)
+    return (g.B, g.H_kv, g.T, g.d)
 
 
 def tree_bytes(g: Geom):
@@ -165,6 +175,22 @@ def _bytes(n, device):
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
+def to_chunked(K, V, C: int):
+    """Device copy of split K, V [B, H_kv, T, d] into the chunked KV buffer
+    [B, H_kv, ceil(T / C), 2, C, d] (rows of the last page past T are zero)."""
+    torch = _torch()
+    B, H, T, d = K.shape
+    n1, r = T // C, T % C
+    KV = torch.zeros((B, H, -(-T // C), 2, C, d), dtype=K.dtype, device=K.device)
+    if n1:
+        KV[:, :, :n1, 0] = K[:, :, :n1 * C].reshape(B, H, n1, C, d)
+        KV[:, :, :n1, 1] = V[:, :, :n1 * C].reshape(B, H, n1, C, d)
+    if r:
+        KV[:, :, n1, 0, :r] = K[:, :, n1 * C:]
+        KV[:, :, n1, 1, :r] = V[:, :, n1 * C:]
+    return KV
+
+
 @dataclass
 class Workspace:
     """Device buffers reused across calls (allocated once by the caller)."""
@@ -178,7 +204,7 @@ class Workspace:
 def build(g: Geom, K, qref, tree=None, scratch=None, stream=None):
     """zha_build; returns the tree blob (uint8 tensor)."""
     torch = _torch()
-    _need(K, (g.B, g.H_kv, g.T, g.d), _store_dtype(g), "K")
+    _need(K, kv_shape(g), _store_dtype(g), "K")
     _need(qref, (g.H_kv, g.R, g.d), torch.float32, "qref")
     tb, sb = tree_bytes(g)
     if tree is None:
@@ -213,13 +239,22 @@ def route(g: Geom, tree, Q, n_pos: int, p: float, cap: int, want_stats=True, wan
     return sel, cnt, stats, gap
 
 
+def _need_kv(g: Geom, K, V):
+    dt = _store_dtype(g)
+    _need(K, kv_shape(g), dt, "K")
+    if g.kv_layout == ZHA_KV_CHUNKED:
+        if V is not None:
+            raise ValueError("V: the chunked layout holds the values in K's buffer; pass None")
+    else:
+        _need(V, kv_shape(g), dt, "V")
+
+
 def attn(g: Geom, Q, n_pos: int, K, V, sel, cnt, cap: int, O=None, scratch=None, stream=None):
-    """zha_attn; returns O [B, n_pos, H_q, d]."""
+    """zha_attn; returns O [B, n_pos, H_q, d].  Chunked layout: K is the KV buffer, V None."""
     torch = _torch()
     dt = _store_dtype(g)
     _need(Q, (g.B, n_pos, g.H_q, g.d), dt, "Q")
-    _need(K, (g.B, g.H_kv, g.T, g.d), dt, "K")
-    _need(V, (g.B, g.H_kv, g.T, g.d), dt, "V")
+    _need_kv(g, K, V)
     _need(sel, (g.B, n_pos, g.H_q, cap), torch.int32, "sel")
     _need(cnt, (g.B, n_pos, g.H_q), torch.int32, "cnt")
     if O is None:
@@ -232,11 +267,10 @@ def attn(g: Geom, Q, n_pos: int, K, V, sel, cnt, cap: int, O=None, scratch=None,
 
 
 def dense_decode(g: Geom, Q, n_pos: int, K, V, O=None, scratch=None, stream=None):
-    """zha_dense_decode; returns O [B, n_pos, H_q, d]."""
+    """zha_dense_decode; returns O [B, n_pos, H_q, d].  K, V as for attn."""
     dt = _store_dtype(g)
     _need(Q, (g.B, n_pos, g.H_q, g.d), dt, "Q")
-    _need(K, (g.B, g.H_kv, g.T, g.d), dt, "K")
-    _need(V, (g.B, g.H_kv, g.T, g.d), dt, "V")
+    _need_kv(g, K, V)
     torch = _torch()
     if O is None:
         O = torch.empty((g.B, n_pos, g.H_q, g.d), dtype=dt, device=Q.device)

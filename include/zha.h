@@ -27,8 +27,16 @@
  *   host before anything is launched (ZHA_ERR_*); nothing has been written.
  *   zha_strerror() names it.  ZHA_ERR_LAUNCH reports a failed kernel launch.
  * - Layouts are dense, row-major, head dimension fastest:
- *     K, V   [B, H_kv, T, d]      storage dtype
  *     Q, O   [B, n_pos, H_q, d]   storage dtype
+ *   and the KV cache in one of two layouts (zha_geom.kv_layout):
+ *     ZHA_KV_SPLIT    K, V  [B, H_kv, T, d] each
+ *     ZHA_KV_CHUNKED  KV    [B, H_kv, ceil(T / C), 2, C, d]: page c holds the
+ *                     keys of tokens c*C .. c*C + C - 1, then their values;
+ *                     rows of the last page past T are never read.  The
+ *                     buffer is passed as K, and V must be NULL.
+ *   The chunked layout keeps each level-1 chunk's keys and values in one
+ *   contiguous page, so the sparse gather reads 2 C d-element runs instead of
+ *   two runs of C rows in separate arrays.
  *   Query head h reads KV head h / (H_q / H_kv).  Each (b, kvh) pair owns one
  *   tree; its G = H_q / H_kv query heads share it (paper §III-B).
  * - All n_pos positions of a call attend to the same T cached keys.
@@ -52,6 +60,9 @@ extern "C" {
 /* Storage dtype of K, V, Q, O and of the stored summary keys k_hat. */
 enum { ZHA_F32 = 0, ZHA_BF16 = 1 };
 
+/* KV cache layout (see the conventions above). */
+enum { ZHA_KV_SPLIT = 0, ZHA_KV_CHUNKED = 1 };
+
 enum {
   ZHA_OK = 0,
   ZHA_ERR_NULL = -1,   /* a required pointer is NULL */
@@ -62,7 +73,8 @@ enum {
   ZHA_ERR_ALIGN = -6,  /* a buffer is not 16-byte aligned */
   ZHA_ERR_CAP = -7,    /* cap < 1 */
   ZHA_ERR_LAUNCH = -8, /* a kernel launch failed */
-  ZHA_ERR_NPOS = -9    /* n_pos < 1 */
+  ZHA_ERR_NPOS = -9,   /* n_pos < 1 */
+  ZHA_ERR_LAYOUT = -10 /* unknown kv_layout, or V given with ZHA_KV_CHUNKED */
 };
 
 typedef struct {
@@ -75,6 +87,7 @@ typedef struct {
   int32_t L;     /* tree depth */
   int32_t R;     /* reference queries per tree */
   int32_t dtype; /* ZHA_F32 or ZHA_BF16 */
+  int32_t kv_layout; /* ZHA_KV_SPLIT or ZHA_KV_CHUNKED */
 } zha_geom;
 
 /* Human-readable text for a return code. */
@@ -101,7 +114,8 @@ int zha_tree_level_offset(const zha_geom* g, int32_t level, size_t* khat_offset,
                           size_t* bhat_offset, size_t* tree_stride);
 
 /* Build every tree (paper §III-A recursive summaries; App. D-B2 baseline merge).
- *   K       device [B, H_kv, T, d] storage dtype
+ *   K       device, the keys in g->kv_layout (split: [B, H_kv, T, d]; chunked:
+ *           the KV buffer, of which only the key rows are read)
  *   qref    device [H_kv, R, d] fp32 reference queries (all zero gives the
  *           plain mean of each span's keys, with b_hat = ln(span))
  *   tree    device, zha_tree_bytes() bytes, written
@@ -166,7 +180,9 @@ int32_t zha_route_frontier_capacity(void);
  * on the same buffer race.  0 bytes means no scratch is needed. */
 int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes);
 
-/*   Q, K, V  device, layouts above
+/*   Q        device, layout above
+ *   K, V     device, the KV cache in g->kv_layout (chunked: K is the KV
+ *            buffer and V must be NULL)
  *   sel, cnt device, as written by zha_route (ascending, distinct ids < n_1)
  *   O        device [B, n_pos, H_q, d], written; rows whose cnt is negative or
  *            exceeds cap are written as NaN
@@ -181,7 +197,7 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, con
  * Dense decode baseline: O = softmax(q K^T / sqrt(d)) V over all T keys.
  * ------------------------------------------------------------------------- */
 
-/* Same scratch contract as zha_attn. */
+/* Same scratch contract as zha_attn; K and V as for zha_attn. */
 int zha_dense_decode_scratch_bytes(const zha_geom* g, int32_t n_pos, size_t* bytes);
 
 int zha_dense_decode(const zha_geom* g, const void* Q, int32_t n_pos, const void* K,

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 def test_strerror_names_every_code():
     lib = Z.load()
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10]:
         assert lib.zha_strerror(code) not in (None, b"", b"unknown error")
     assert lib.zha_strerror(-1000) == b"unknown error"
 
@@ -77,6 +77,7 @@ def test_tree_layout_matches_documented_rules(kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), -4), (dict(dtype=7), -3), (dict(H_q=6, H_kv=4), -2), (dict(C=1), -2),
     (dict(L=0), -2), (dict(R=17), -2), (dict(T=4095), -2), (dict(B=0), -2), (dict(L=17), -2),
+    (dict(kv_layout=2), -10), (dict(kv_layout=-1), -10),
 ])
 def test_invalid_geometry_is_rejected(kw, code):
     gm = g(**kw)
@@ -109,6 +110,20 @@ def test_null_and_argument_errors_before_any_launch():
                                 None) == -6
     assert lib.zha_tree_level_offset(ctypes.byref(gm), 0, ctypes.byref(n), ctypes.byref(n),
                                      ctypes.byref(n)) == -2
+    # KV layout: split needs V; chunked takes the KV buffer as K and rejects a V
+    assert lib.zha_attn(ctypes.byref(gm), buf, 1, buf, None, buf, buf, 4, buf, buf, None) == -1
+    assert lib.zha_dense_decode(ctypes.byref(gm), buf, 1, buf, None, buf, buf, None) == -1
+    gc = g(kv_layout=Z.ZHA_KV_CHUNKED)
+    assert lib.zha_attn(ctypes.byref(gc), buf, 1, buf, buf, buf, buf, 4, buf, buf, None) == -10
+    assert lib.zha_dense_decode(ctypes.byref(gc), buf, 1, buf, buf, buf, buf, None) == -10
+    assert lib.zha_attn(ctypes.byref(gc), buf, 1, None, None, buf, buf, 4, buf, buf, None) == -1
+
+
+def test_chunked_layout_shape_and_tree_layout_are_independent():
+    gs, gc = g(T=5000), g(T=5000, kv_layout=Z.ZHA_KV_CHUNKED)
+    assert Z.kv_shape(gs) == (1, 2, 5000, 128)
+    assert Z.kv_shape(gc) == (1, 2, 313, 2, 16, 128)  # ceil(5000 / 16) pages
+    assert Z.tree_bytes(gs) == Z.tree_bytes(gc)
 
 
 def test_scratch_sizes_are_consistent():

@@ -33,7 +33,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_parity(Z, g, steps, pairs=None, p=None, R=None, qref=None, check_tree=True):
+def run_parity(Z, g, steps, pairs=None, p=None, R=None, qref=None, check_tree=True,
+               chunked=False):
     import torch
     p = g.p if p is None else p
     if R is not None and R != g.R:
@@ -42,10 +43,12 @@ def run_parity(Z, g, steps, pairs=None, p=None, R=None, qref=None, check_tree=Tr
     K, V = W.make_kv(g, slices=pairs)
     qref = W.make_qref(g, K) if qref is None else qref
     Qn = W.make_query_block(g, K, steps)
-    gm = Z.geom(g)
+    gm = Z.geom(g, Z.ZHA_KV_CHUNKED if chunked else Z.ZHA_KV_SPLIT)
     n_pos = len(steps)
     cap = g.n_level(1)
     Kd, Vd, Qd = to_device(K, g.dtype), to_device(V, g.dtype), to_device(Qn, g.dtype)
+    if chunked:
+        Kd, Vd = Z.to_chunked(Kd, Vd, g.C), None
     qd = torch.from_numpy(qref).cuda()
     tree = Z.build(gm, Kd, qd)
     sel, cnt, stats, gap = Z.route(gm, tree, Qd, n_pos, p, cap)
@@ -80,9 +83,10 @@ def test_config1_tiny_fp32_all_queries(Z):
     run_parity(Z, W.CONFIGS[1], range(64))
 
 
-def test_config2_gqa_128k(Z):
-    say("config 2: GQA 128K bf16, 8 steps x 32 heads")
-    run_parity(Z, W.CONFIGS[2], range(8))
+@pytest.mark.parametrize("chunked", [False, True])
+def test_config2_gqa_128k(Z, chunked):
+    say(f"config 2: GQA 128K bf16, 8 steps x 32 heads, {'chunked' if chunked else 'split'} KV")
+    run_parity(Z, W.CONFIGS[2], range(8), chunked=chunked)
 
 
 def test_config3_deep_256k_subset(Z):
@@ -106,11 +110,20 @@ def test_other_head_dims(Z, d):
     run_parity(Z, g, range(8))
 
 
-def test_ragged_orphans_fp32_depth4(Z):
-    say("ragged T with orphan nodes at every level, fp32")
+@pytest.mark.parametrize("chunked", [False, True])
+def test_ragged_orphans_fp32_depth4(Z, chunked):
+    say(f"ragged T with orphan nodes at every level, fp32, {'chunked' if chunked else 'split'} KV")
     g = W.custom("ragged", 112, dtype=W.F32, B=2, H_q=2, H_kv=1, T=4 ** 4 * 3 + 4 ** 3 * 2 + 4 * 3 + 2,
                  C=4, L=4, p=0.8)
-    run_parity(Z, g, range(10))
+    run_parity(Z, g, range(10), chunked=chunked)
+
+
+@pytest.mark.parametrize("chunked", [False, True])
+def test_chunk_size_not_a_power_of_two(Z, chunked):
+    say(f"C = 6 (division paths), ragged tail, {'chunked' if chunked else 'split'} KV")
+    g = W.custom("c6", 117, dtype=W.BF16, B=1, H_q=8, H_kv=2, T=6 ** 4 * 2 + 6 * 5 + 4, C=6,
+                 L=4, p=0.9)
+    run_parity(Z, g, range(6), chunked=chunked)
 
 
 def test_single_level_and_wide_chunks(Z):
@@ -134,9 +147,11 @@ def test_frontier_near_capacity_low_p_variants(Z):
     run_parity(Z, W.replace(g, p=0.99, cfg_id=115), range(4))
 
 
-def test_attention_on_random_chunk_sets(Z):
+@pytest.mark.parametrize("chunked", [False, True])
+def test_attention_on_random_chunk_sets(Z, chunked):
     import torch
-    say("attention alone on random chunk sets, with sink, C_cur, overflow and invalid counts")
+    say("attention alone on random chunk sets, with sink, C_cur, overflow and invalid counts, "
+        f"{'chunked' if chunked else 'split'} KV")
     g = W.custom("attn-sets", 116, dtype=W.BF16, B=2, H_q=8, H_kv=2, T=16 * 300 + 9, C=16, L=2)
     K, V = W.make_kv(g)
     n_pos = 3
@@ -147,8 +162,10 @@ def test_attention_on_random_chunk_sets(Z):
     sel[0, :3], cnt[0] = [0, 3, 7], 3  # chunk 0 holds the sink: it must not be counted twice
     cnt[1] = 0  # only the sink and the partial chunk
     cnt[5] = -1  # a failed route
-    gm = Z.geom(g)
+    gm = Z.geom(g, Z.ZHA_KV_CHUNKED if chunked else Z.ZHA_KV_SPLIT)
     Kd, Vd, Qd = to_device(K, g.dtype), to_device(V, g.dtype), to_device(Qn, g.dtype)
+    if chunked:
+        Kd, Vd = Z.to_chunked(Kd, Vd, g.C), None
     seld = torch.from_numpy(sel.reshape(g.B, n_pos, g.H_q, cap)).cuda()
     cntd = torch.from_numpy(cnt.reshape(g.B, n_pos, g.H_q)).cuda()
     Od = Z.attn(gm, Qd, n_pos, Kd, Vd, seld, cntd, cap)
@@ -167,16 +184,18 @@ def test_attention_on_random_chunk_sets(Z):
     assert worst <= TOL[g.dtype]
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
-def test_dense_decode_matches_oracle(Z, cfg):
-    say(f"dense decode, config {cfg}")
+@pytest.mark.parametrize("cfg,chunked", [(1, False), (2, False), (2, True)])
+def test_dense_decode_matches_oracle(Z, cfg, chunked):
+    say(f"dense decode, config {cfg}, {'chunked' if chunked else 'split'} KV")
     g = W.CONFIGS[cfg]
     K, V = W.make_kv(g)
     n_pos = 2
     Qn = W.make_query_block(g, K, range(n_pos))
-    gm = Z.geom(g)
-    Od = Z.dense_decode(gm, to_device(Qn, g.dtype), n_pos, to_device(K, g.dtype),
-                        to_device(V, g.dtype))
+    gm = Z.geom(g, Z.ZHA_KV_CHUNKED if chunked else Z.ZHA_KV_SPLIT)
+    Kd, Vd = to_device(K, g.dtype), to_device(V, g.dtype)
+    if chunked:
+        Kd, Vd = Z.to_chunked(Kd, Vd, g.C), None
+    Od = Z.dense_decode(gm, to_device(Qn, g.dtype), n_pos, Kd, Vd)
     Og = from_device(Od, g.dtype)
     worst = 0.0
     for b in range(g.B):
@@ -217,6 +236,40 @@ def test_route_and_attn_are_deterministic(Z):
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
 
 
+@pytest.mark.parametrize("name", ["c6", "cfg2"])
+def test_kv_layouts_give_identical_results(Z, name):
+    import torch
+    say(f"split and chunked KV give bit-identical trees, routes and outputs ({name})")
+    if name == "c6":
+        g = W.custom("c6-id", 118, dtype=W.F32, B=2, H_q=4, H_kv=2, T=6 ** 3 * 5 + 6 * 3 + 5, C=6,
+                     L=3, p=0.85)
+        pairs = None
+    else:
+        g = W.CONFIGS[2]
+        pairs = [(0, 0), (0, 1)]
+    K, V = W.make_kv(g, slices=pairs)
+    Qn = W.make_query_block(g, K, range(3))
+    Kd, Vd, Qd = to_device(K, g.dtype), to_device(V, g.dtype), to_device(Qn, g.dtype)
+    qd = torch.from_numpy(W.make_qref(g, K)).cuda()
+    cap = g.n_level(1)
+    res = []
+    for chunked in (False, True):
+        gm = Z.geom(g, Z.ZHA_KV_CHUNKED if chunked else Z.ZHA_KV_SPLIT)
+        k, v = (Z.to_chunked(Kd, Vd, g.C), None) if chunked else (Kd, Vd)
+        tb, _ = Z.tree_bytes(gm)
+        tree = Z.build(gm, k, qd, tree=torch.zeros(tb, dtype=torch.uint8, device="cuda"))
+        sel = torch.full((g.B, 3, g.H_q, cap), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.empty((g.B, 3, g.H_q), dtype=torch.int32, device="cuda")
+        Z.route(gm, tree, Qd, 3, g.p, cap, out=(sel, cnt, None, None))
+        Oa = Z.attn(gm, Qd, 3, k, v, sel, cnt, cap)
+        Od = Z.dense_decode(gm, Qd, 3, k, v)
+        torch.cuda.synchronize()
+        res.append([x.cpu().view(torch.uint8) if x.dtype == torch.bfloat16 else x.cpu()
+                    for x in (tree, sel, cnt, Oa, Od)])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+
+
 def test_single_position_calls_match_block_call(Z):
     import torch
     say("n_pos = 1 calls equal one n_pos = 4 call (config 3 geometry, one sequence)")
@@ -243,12 +296,15 @@ def test_single_position_calls_match_block_call(Z):
 
 
 def run_full_size_sampled(Z, g, n_pos, steps, samples, seed):
-    """Full-size workload in the bench's launch configuration; oracle on sampled query heads."""
+    """Full-size workload in the bench's launch configuration (chunked KV cache);
+    oracle on sampled query heads."""
     import torch
     K, V = W.make_kv(g)
-    gm = Z.geom(g)
+    gm = Z.geom(g, Z.ZHA_KV_CHUNKED)
     cap = g.n_level(1)
-    Kd, Vd = to_device(K, g.dtype), to_device(V, g.dtype)
+    Kd = Z.to_chunked(to_device(K, g.dtype), to_device(V, g.dtype), g.C)
+    Vd = None
+    torch.cuda.empty_cache()
     tree = Z.build(gm, Kd, torch.zeros((g.H_kv, 1, g.d), device="cuda"))
     rng = np.random.default_rng(seed)
     trees = {}
