@@ -270,6 +270,44 @@ def test_kv_layouts_give_identical_results(Z, name):
         assert torch.equal(a, b)
 
 
+def test_many_head_router_shape_and_fallback_match(Z):
+    import torch
+    say("router: one 4096-head call (throughput shape, overflowing heads re-routed) equals "
+        "eight 512-head calls (latency shape)")
+    g = W.custom("wide-4096", 121, dtype=W.BF16, B=1, H_q=8, H_kv=1, T=32 ** 3 * 4, C=32, L=3,
+                 p=0.99)
+    K, _ = W.make_kv(g, want_v=False)
+    n_pos = 512
+    Qn = W.make_query_block(g, K, range(n_pos))
+    # every other position a weak query: near-uniform scores keep nearly every
+    # candidate, so those heads' level-1 frontiers outgrow 1024
+    rng = np.random.default_rng(121)
+    weak = rng.standard_normal((g.B, n_pos // 2, g.H_q, g.d)).astype(np.float32) * np.float32(0.05)
+    Qn[:, ::2] = W.f32_to_bf16_bits(weak)
+    gm = Z.geom(g)
+    Kd, Qd = to_device(K, g.dtype), to_device(Qn, g.dtype)
+    tree = Z.build(gm, Kd, torch.zeros((g.H_kv, 1, g.d), device="cuda"))
+    cap = g.n_level(1)
+    sel, cnt, stats, gap = Z.route(gm, tree, Qd, n_pos, g.p, cap)
+    parts = [Z.route(gm, tree, Qd[:, i:i + 64].contiguous(), 64, g.p, cap) for i in range(0, n_pos, 64)]
+    torch.cuda.synchronize()
+    cnt_h = cnt.cpu()
+    assert (cnt_h >= 0).all()
+    kmax = int(stats[..., 0].max())
+    say(f"  largest frontier {kmax} (the throughput shape holds 1024)")
+    assert kmax > 1024, "the case must exercise the re-routing of overflowing heads"
+    for i, (s1, c1, st1, g1) in enumerate(parts):
+        sl = slice(i * 64, (i + 1) * 64)
+        assert torch.equal(c1.cpu(), cnt_h[:, sl])
+        assert torch.equal(st1.cpu(), stats[:, sl].cpu())
+        assert torch.equal(g1.cpu(), gap[:, sl].cpu())
+        c = c1.cpu()
+        for h in range(g.H_q):
+            for t in range(64):
+                n = int(c[0, t, h])
+                assert torch.equal(s1[0, t, h, :n].cpu(), sel[0, i * 64 + t, h, :n].cpu())
+
+
 def test_single_position_calls_match_block_call(Z):
     import torch
     say("n_pos = 1 calls equal one n_pos = 4 call (config 3 geometry, one sequence)")
