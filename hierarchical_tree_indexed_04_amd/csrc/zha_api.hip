@@ -189,7 +189,8 @@ int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t
   if (n_pos < 1) return ZHA_ERR_NPOS;
   if (cap < 1) return ZHA_ERR_CAP;
   const int64_t n_heads = (int64_t)g->B * n_pos * g->H_q;
-  *bytes = (size_t)attn_scratch_layout_bytes(n_heads, g->d);
+  *bytes = (size_t)attn_scratch_layout_bytes(n_heads, (int64_t)g->B * g->H_kv, g->T, g->C, g->d,
+                                             g->dtype);
   return ZHA_OK;
 }
 
@@ -213,7 +214,9 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, con
   a.cap = cap;
   a.S = ZHA_ATTN_BLOCKS;
   a.chunked = g->kv_layout == ZHA_KV_CHUNKED;
-  const bool need_scratch = attn_scratch_layout_bytes(a.n_heads, g->d) > 0;
+  a.dtype = g->dtype;
+  const bool need_scratch =
+      attn_scratch_layout_bytes(a.n_heads, (int64_t)g->B * g->H_kv, g->T, g->C, g->d, g->dtype) > 0;
   const int kv = check_kv(g, K, V);
   if (kv) return kv;
   if (Q == nullptr || sel == nullptr || cnt == nullptr || O == nullptr ||

@@ -249,11 +249,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
   merge_partials<T, D>(part + head * (int64_t)S * (D + 2), S, O + head * D);
 }
 
+// Attention of one query head (split `split` of a.S) by one workgroup.
 template <typename T, int D, bool POW2, bool BUF>
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
-    float* __restrict__ part, AttnArgs a) {
+__device__ __forceinline__ void attend_one_head(const T* __restrict__ Q, const T* __restrict__ K,
+                                                const T* __restrict__ V,
+                                                const int32_t* __restrict__ sel,
+                                                const int32_t* __restrict__ cnt,
+                                                T* __restrict__ O, float* __restrict__ part,
+                                                const AttnArgs& a, int64_t head, int split) {
   constexpr int VEC = Vec<T>::N;
   constexpr int LPR = D / VEC;
   constexpr int RPB = kThreads / LPR;
@@ -262,8 +265,6 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
   __shared__ int32_t s_ids[kIds];
   const int tid = threadIdx.x;
   const int sub = tid % LPR, grp = tid / LPR;
-  const int64_t head = blockIdx.x;
-  const int split = blockIdx.y;
   const int c = cnt[head];
   if (c < 0 || c > a.cap) {  // overflowed or failed route: the row is NaN
     if (split == 0)
@@ -343,9 +344,17 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
     }
     if (final_round) break;
   }
-  float* phead = part + head * a.S * (int64_t)(D + 2);
-  float* prow = (a.S > 1) ? phead + split * (int64_t)(D + 2) : nullptr;
+  float* prow = (a.S > 1) ? part + (head * a.S + split) * (int64_t)(D + 2) : nullptr;
   combine_groups<T, D, RPB>(m, l, acc, grp, sub, s_m, s_l, s_acc, O + head * D, prow);
+}
+
+template <typename T, int D, bool POW2, bool BUF>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
+    float* __restrict__ part, AttnArgs a) {
+  attend_one_head<T, D, POW2, BUF>(Q, K, V, sel, cnt, O, part, a, (int64_t)blockIdx.x,
+                                   (int)blockIdx.y);
 }
 
 // |I(q)| of one query head: its chunks' tokens, the tail after the last full
@@ -615,6 +624,453 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
   }
 }
 
+// ===========================================================================
+// Block path: many query heads against the same caches (a block of positions
+// of one sequence).  Each chunk is selected by many heads there, so the work
+// is turned around: (query head, tile) pairs are bucketed per tile of CT
+// chunks, and a work item stages the selected chunks of one tile once for up
+// to kBlkQ heads and runs both products on MFMA (a query block against a leaf
+// tile is a dense contraction; unselected (head, chunk) cells are masked).
+// Each pair leaves a softmax partial; a merge launch combines the partials of
+// each head in tile order, so results do not depend on scheduling.
+// ===========================================================================
+constexpr int kBlkQ = 64;      // query heads per work item: 4 waves x 16 MFMA rows
+constexpr int kBlkGroup = 32;  // tokens per MFMA step
+constexpr int kBlkGrid = 1024; // persistent workgroups of the attention launch
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct BlkPtrs {
+  int32_t* ctrl;  // [0] pairs reserved, [1] work items
+  int32_t* qbase;  // per head: first slot, -1 past the budget, -2 failed route
+  int32_t* ntile;  // per head: pairs
+  int32_t* tcnt;   // per tile: pairs
+  int32_t* tcur;   // per tile: fill cursor
+  int32_t* toff;   // per tile: first entry (exclusive scan of tcnt)
+  int32_t* wpre;   // per tile: first work item
+  int32_t* ent;    // entries, kBlkEntryInts ints each
+  float* part;     // partials, d + 2 floats per slot
+  __device__ __host__ BlkPtrs(char* scr, const BlkLayout& L)
+      : ctrl(reinterpret_cast<int32_t*>(scr + L.off_ctrl)),
+        qbase(reinterpret_cast<int32_t*>(scr + L.off_qbase)),
+        ntile(reinterpret_cast<int32_t*>(scr + L.off_ntile)),
+        tcnt(reinterpret_cast<int32_t*>(scr + L.off_tcnt)),
+        tcur(reinterpret_cast<int32_t*>(scr + L.off_tcur)),
+        toff(reinterpret_cast<int32_t*>(scr + L.off_toff)),
+        wpre(reinterpret_cast<int32_t*>(scr + L.off_wpre)),
+        ent(reinterpret_cast<int32_t*>(scr + L.off_ent)),
+        part(reinterpret_cast<float*>(scr + L.off_part)) {}
+};
+
+__device__ __forceinline__ int64_t tree_of_head(int64_t head, const AttnArgs& a) {
+  const int h = (int)(head % a.H_q);
+  const int64_t b = head / ((int64_t)a.n_pos * a.H_q);
+  return b * a.H_kv + h / a.G;
+}
+
+__global__ __launch_bounds__(256) void blk_zero_kernel(char* scr, BlkLayout L) {
+  BlkPtrs P(scr, L);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < 16) P.ctrl[i] = 0;
+  if (i < L.NTT) {
+    P.tcnt[i] = 0;
+    P.tcur[i] = 0;
+  }
+}
+
+// A head's tiles, ascending: tile 0 when it attends the sink without chunk 0,
+// the tiles of its selected chunks, and the tile of the partial chunk n_1
+// when T is not a multiple of C.  One wave per head: count, reserve slots,
+// count pairs per tile.
+__global__ __launch_bounds__(256) void blk_count_kernel(const int32_t* __restrict__ sel,
+                                                        const int32_t* __restrict__ cnt,
+                                                        AttnArgs a, BlkLayout L, char* scr) {
+  BlkPtrs P(scr, L);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
+  if (head >= a.n_heads) return;
+  const int c = cnt[head];
+  if (c < 0 || c > a.cap) {
+    if (lane == 0) {
+      P.qbase[head] = -2;
+      P.ntile[head] = 0;
+    }
+    return;
+  }
+  const int32_t* ids = sel + head * a.cap;
+  const int CT = L.CT;
+  const bool need_sink = c == 0 || ids[0] != 0;
+  const int n1 = (int)a.n1;
+  const bool has_tail = a.T > a.n1 * a.C;
+  const int tail_tile = n1 / CT;
+  int32_t* tc = P.tcnt + tree_of_head(head, a) * L.NT;
+  for (int pass = 0; pass < 2; ++pass) {
+    int n = need_sink ? 1 : 0;
+    int cur = need_sink ? 0 : -1;
+    if (pass == 1 && need_sink && lane == 0) atomicAdd(&tc[0], 1);
+    for (int j = 0; j < c; j += kWave) {
+      const int id = j + lane < c ? ids[j + lane] : -1;
+      const int t = id >= 0 ? id / CT : -1;
+      int tp = __shfl_up(t, 1, kWave);
+      if (lane == 0) tp = cur;
+      const bool first = id >= 0 && t != tp;
+      if (pass == 0)
+        n += __popcll((unsigned long long)__ballot(first));
+      else if (first)
+        atomicAdd(&tc[t], 1);
+      cur = __shfl(t, min(kWave - 1, c - j - 1), kWave);
+    }
+    if (has_tail && cur != tail_tile) {
+      ++n;
+      if (pass == 1 && lane == 0) atomicAdd(&tc[tail_tile], 1);
+    }
+    if (pass == 0) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&P.ctrl[0], n);
+      base = __shfl(base, 0, kWave);
+      const bool ok = (int64_t)base + n <= L.P;
+      if (lane == 0) {
+        P.qbase[head] = ok ? base : -1;
+        P.ntile[head] = ok ? n : 0;
+      }
+      if (!ok) return;
+    }
+  }
+}
+
+// Exclusive scans over the tiles: first entry and first work item of each.
+__global__ __launch_bounds__(1024) void blk_scan_kernel(char* scr, BlkLayout L) {
+  BlkPtrs P(scr, L);
+  __shared__ int32_t s_c[1024], s_w[1024];
+  const int tid = threadIdx.x;
+  const int64_t seg = (L.NTT + 1023) / 1024;
+  const int64_t i0 = min(L.NTT, tid * seg), i1 = min(L.NTT, i0 + seg);
+  int sc = 0, sw = 0;
+  for (int64_t i = i0; i < i1; ++i) {
+    sc += P.tcnt[i];
+    sw += (P.tcnt[i] + kBlkQ - 1) / kBlkQ;
+  }
+  s_c[tid] = sc;
+  s_w[tid] = sw;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the 1024 segment sums
+    const int vc = tid >= off ? s_c[tid - off] : 0;
+    const int vw = tid >= off ? s_w[tid - off] : 0;
+    __syncthreads();
+    s_c[tid] += vc;
+    s_w[tid] += vw;
+    __syncthreads();
+  }
+  int rc = s_c[tid] - sc, rw = s_w[tid] - sw;
+  for (int64_t i = i0; i < i1; ++i) {
+    P.toff[i] = rc;
+    P.wpre[i] = rw;
+    rc += P.tcnt[i];
+    rw += (P.tcnt[i] + kBlkQ - 1) / kBlkQ;
+  }
+  if (tid == 1023) {
+    P.toff[L.NTT] = s_c[1023];
+    P.wpre[L.NTT] = s_w[1023];
+    P.ctrl[1] = s_w[1023];
+  }
+}
+
+// One wave per head: walk the head's tiles again (in the same order as the
+// count) and write one entry per tile: head, slot, chunk mask, sink flag.
+__global__ __launch_bounds__(256) void blk_fill_kernel(const int32_t* __restrict__ sel,
+                                                       const int32_t* __restrict__ cnt,
+                                                       AttnArgs a, BlkLayout L, char* scr) {
+  BlkPtrs P(scr, L);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
+  if (head >= a.n_heads) return;
+  const int qb = P.qbase[head];
+  if (qb < 0) return;
+  const int c = cnt[head];
+  const int32_t* ids = sel + head * a.cap;
+  const int CT = L.CT;
+  const bool need_sink = c == 0 || ids[0] != 0;
+  const int n1 = (int)a.n1;
+  const int64_t tb = tree_of_head(head, a) * L.NT;
+  int k = 0, cur = -1, flags = 0;
+  uint64_t mask = 0;
+  auto flush = [&]() {
+    if (cur >= 0) {
+      if (lane == 0) {
+        const int pos = P.toff[tb + cur] + atomicAdd(&P.tcur[tb + cur], 1);
+        int32_t* e = P.ent + (int64_t)pos * kBlkEntryInts;
+        e[0] = (int32_t)head;
+        e[1] = qb + k;
+        e[2] = (int32_t)(uint32_t)mask;
+        e[3] = (int32_t)(uint32_t)(mask >> 32);
+        e[4] = flags;
+        e[5] = 0;
+      }
+      ++k;
+    }
+  };
+  if (need_sink) {
+    cur = 0;
+    flags = 1;  // token 0 alone (chunk 0 is not selected)
+  }
+  for (int j = 0; j < c; j += kWave) {
+    const int idv = j + lane < c ? ids[j + lane] : 0;
+    const int nn = min(kWave, c - j);
+    for (int i = 0; i < nn; ++i) {
+      const int id = __builtin_amdgcn_readlane(idv, i);
+      const int t = id / CT;
+      if (t != cur) {
+        flush();
+        cur = t;
+        mask = 0;
+        flags = 0;
+      }
+      mask |= 1ull << (id - t * CT);
+    }
+  }
+  if (a.T > a.n1 * a.C) {
+    const int t = n1 / CT;
+    if (t != cur) {
+      flush();
+      cur = t;
+      mask = 0;
+      flags = 0;
+    }
+    mask |= 1ull << (n1 - t * CT);
+  }
+  flush();
+}
+
+// Work items: (tile, block of up to kBlkQ of its entries), persistent loop.
+// Per 32-token step of the tile (skipped when no head of the block selected
+// any of its chunks): the K rows and the transposed V rows go to LDS; each
+// wave (16 heads) computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (so a
+// lane holds one head's scores for 8 tokens), masks the cells its heads did
+// not select, updates the online softmax and accumulates P V with the same
+// MFMA, the 8 tokens of a lane taken as the K dimension in the order the
+// scores already sit in registers.  Operand layouts (gfx950, checked):
+// A[i][k] in lane i + 16 (k / 8), element k % 8; B[k][j] in lane j + 16 (k / 8),
+// element k % 8; D[i][j] in lane j + 16 (i / 4), element i % 4.
+template <int D, bool BUF>
+__global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict__ Q,
+                                                       const bf16_t* __restrict__ K,
+                                                       const bf16_t* __restrict__ V, AttnArgs a,
+                                                       BlkLayout L, char* scr) {
+  constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
+  constexpr int NTD = D / 16;  // 16-column tiles of O
+  constexpr int SEG = D / 8;   // 16-byte segments per row
+  constexpr int KROW = D + 8;  // padded LDS row of K (bf16 elements)
+  constexpr int VTROW = kBlkGroup + 4;  // padded LDS row of V^T (bf16 elements)
+  BlkPtrs P(scr, L);
+  __shared__ int32_t s_head[kBlkQ], s_slot[kBlkQ], s_flags[kBlkQ];
+  __shared__ unsigned long long s_mask[kBlkQ];
+  __shared__ unsigned long long s_union;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kBlkGroup * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VTROW];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const float inv = 1.0f / sqrtf((float)D);
+  const int C = a.C;
+  const int total = P.ctrl[1];
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    // Tile of work item w: the last tile u with wpre[u] <= w.
+    int64_t lo = 0, hi = L.NTT;
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (P.wpre[mid] <= w) lo = mid;
+      else hi = mid;
+    }
+    const int64_t u = lo;
+    const int e0 = P.toff[u] + (w - P.wpre[u]) * kBlkQ;
+    const int ne = min(kBlkQ, P.toff[u + 1] - e0);
+    __syncthreads();  // the previous item is done with LDS
+    if (tid == 0) s_union = 0ull;
+    if (tid < kBlkQ) {
+      if (tid < ne) {
+        const int32_t* e = P.ent + (int64_t)(e0 + tid) * kBlkEntryInts;
+        s_head[tid] = e[0];
+        s_slot[tid] = e[1];
+        s_mask[tid] = (unsigned long long)(uint32_t)e[2] | ((unsigned long long)(uint32_t)e[3] << 32);
+        s_flags[tid] = e[4];
+      } else {
+        s_head[tid] = -1;
+        s_slot[tid] = -1;
+        s_mask[tid] = 0ull;
+        s_flags[tid] = 0;
+      }
+    }
+    __syncthreads();
+    if (tid < ne) atomicOr(&s_union, s_mask[tid] | ((s_flags[tid] & 1) ? 1ull : 0ull));
+    __syncthreads();
+    const uint64_t uni = s_union;
+    const int64_t tr = u / L.NT;
+    const int chunk0 = (int)(u - tr * L.NT) * L.CT;
+    const int tok0 = chunk0 * C;
+    const int tok_end = (int)min((int64_t)(chunk0 + L.CT) * C, a.T);
+    const KvBlock<bf16_t, D, BUF> kvb(K, V, tr, a.T, C, a.chunked, tid % SEG);
+
+    // This lane's head (row li of the wave's 16): its Q slices as the B operand.
+    const int qi = wave * 16 + li;
+    const bool qvalid = qi < ne;
+    const uint64_t qmask = s_mask[qi];
+    const bool qsink = (s_flags[qi] & 1) != 0;
+    bf16x8_t qb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (qvalid) v = ld16c(Q + (int64_t)s_head[qi] * D + ks * 32 + lg * 8);
+      qb[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+    float m_i = -INFINITY, l_i = 0.f;
+    f32x4_t o[NTD];
+#pragma unroll
+    for (int n = 0; n < NTD; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int g0 = tok0; g0 < tok_end; g0 += kBlkGroup) {
+      const int gl = min(g0 + kBlkGroup, tok_end) - 1;
+      const int cf = g0 / C - chunk0, cl = gl / C - chunk0;
+      const uint64_t gbits = (cl >= 63 ? ~0ull : ((1ull << (cl + 1)) - 1)) & ~((1ull << cf) - 1);
+      if ((uni & gbits) == 0ull) continue;
+      // Stage: K rows as they are, V rows transposed (dimension-major).
+      __syncthreads();
+      for (int r = tid / SEG; r < kBlkGroup; r += 256 / SEG) {
+        const int tok = g0 + r;
+        uint4 kv, vv;
+        kvb.load(kvb.key_row(tok / C, tok % C), tok < tok_end, kv, vv);
+        const int sg = tid % SEG;
+        *reinterpret_cast<uint4*>(&s_k[r * KROW + sg * 8]) = kv;
+        const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s_vt[(sg * 8 + 2 * e) * VTROW + r] = (uint16_t)(vw[e] & 0xffffu);
+          s_vt[(sg * 8 + 2 * e + 1) * VTROW + r] = (uint16_t)(vw[e] >> 16);
+        }
+      }
+      __syncthreads();
+      // S^T = K Q^T for the two 16-token halves of the step.
+      f32x4_t st[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        st[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[(nt * 16 + li) * KROW + ks * 32 + lg * 8]);
+          st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qb[ks],
+                                                          st[nt], 0, 0, 0);
+        }
+      }
+      // Lane (li, lg) holds head li's scores for tokens nt * 16 + 4 lg + e.
+      float x[8];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tok = g0 + nt * 16 + 4 * lg + e;
+          const int ch = tok / C - chunk0;
+          const bool on = qvalid && tok < tok_end &&
+                          (((qmask >> ch) & 1ull) != 0ull || (qsink && tok == 0));
+          const float v = on ? st[nt][e] * inv : -INFINITY;
+          x[nt * 4 + e] = v;
+          mloc = fmaxf(mloc, v);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+      const float m_new = fmaxf(m_i, mloc);
+      const float mref = m_new == -INFINITY ? 0.f : m_new;
+      const float scale = __expf(m_i - mref);
+      float psum = 0.f;
+      bf16x8_t pa;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pj = __expf(x[j] - mref);
+        psum += pj;
+        pa[j] = (__bf16)pj;
+      }
+      psum += __shfl_xor(psum, 16, kWave);
+      psum += __shfl_xor(psum, 32, kWave);
+      l_i = l_i * scale + psum;
+      m_i = m_new;
+      // O rows 4 lg + e belong to heads 4 lg + e: rescale by their factors.
+      float sr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sr[e] = __shfl(scale, 4 * lg + e, kWave);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[n][e] *= sr[e];
+        // B = V in the same token order: tokens 4 lg' + (0..3) and 16 + 4 lg' + (0..3)
+        // of column n * 16 + li.
+        const uint16_t* vr = &s_vt[(n * 16 + li) * VTROW];
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * lg);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * lg);
+        const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, vb), o[n],
+                                                       0, 0, 0);
+      }
+    }
+    // Partials: O rows 4 lg + e (heads of the wave), columns n * 16 + li; m and l
+    // from the lanes of row group 0.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = wave * 16 + 4 * lg + e;
+      if (r < ne) {
+        float* pr = P.part + (int64_t)s_slot[r] * (D + 2);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) pr[n * 16 + li] = o[n][e];
+      }
+    }
+    if (lg == 0 && qvalid) {
+      float* pr = P.part + (int64_t)s_slot[qi] * (D + 2);
+      pr[D] = m_i;
+      pr[D + 1] = l_i;
+    }
+  }
+}
+
+// Per head: the merge of its pairs' partials in tile order; a head past the
+// pair budget is attended here directly; a failed route gives a NaN row.
+template <typename T, int D, bool POW2, bool BUF>
+__global__ __launch_bounds__(kThreads) void blk_merge_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
+    AttnArgs a, BlkLayout L, char* scr) {
+  BlkPtrs P(scr, L);
+  const int64_t head = blockIdx.x;
+  const int qb = P.qbase[head];
+  if (qb == -1) {
+    AttnArgs a1 = a;
+    a1.S = 1;
+    attend_one_head<T, D, POW2, BUF>(Q, K, V, sel, cnt, O, nullptr, a1, head, 0);
+  } else if (qb < 0) {
+    for (int t = threadIdx.x; t < D; t += kThreads)
+      store_elem(O + head * D, t, __int_as_float(0x7fc00000));
+  } else {
+    merge_partials<T, D>(P.part + (int64_t)qb * (D + 2), P.ntile[head], O + head * D);
+  }
+}
+
+template <typename T, int D, bool POW2, bool BUF>
+int launch_blk(const AttnArgs& a, const void* Q, const void* K, const void* V, const int32_t* sel,
+               const int32_t* cnt, void* O, void* scratch, hipStream_t s) {
+  const BlkLayout L =
+      blk_layout(a.n_heads, a.n_heads / ((int64_t)a.n_pos * a.H_q) * a.H_kv, a.T, a.C, D);
+  char* scr = reinterpret_cast<char*>(scratch);
+  const unsigned wave_blocks = (unsigned)((a.n_heads + kWaves - 1) / kWaves);
+  blk_zero_kernel<<<(unsigned)((max(L.NTT, (int64_t)16) + 255) / 256), 256, 0, s>>>(scr, L);
+  blk_count_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
+  blk_scan_kernel<<<1, 1024, 0, s>>>(scr, L);
+  blk_fill_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
+  blk_attn_kernel<D, BUF><<<kBlkGrid, 256, 0, s>>>(
+      reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K),
+      reinterpret_cast<const bf16_t*>(V), a, L, scr);
+  blk_merge_kernel<T, D, POW2, BUF><<<(unsigned)a.n_heads, kThreads, 0, s>>>(
+      reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
+      reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), a, L, scr);
+  return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
+}
+
 template <typename T, int D>
 int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
                 const int32_t* sel, const int32_t* cnt, void* O, void* scratch, hipStream_t s) {
@@ -639,12 +1095,18 @@ int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
         part, plan, cnt, a.cap, (int32_t)a.n_heads, reinterpret_cast<T*>(O));
     return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
   }
+  const bool buf =
+      kv_block_elems(a.T, a.C, D, a.chunked) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
+  if constexpr (sizeof(T) == 2 && (D == 64 || D == 128)) {
+    if (blk_eligible(a.n_heads, a.C, D, a.dtype)) {
+      if (buf) return launch_blk<T, D, true, true>(a, Q, K, V, sel, cnt, O, scratch, s);
+      return launch_blk<T, D, true, false>(a, Q, K, V, sel, cnt, O, scratch, s);
+    }
+  }
   // Many heads: one workgroup per head, written directly.
   AttnArgs a1 = a;
   a1.S = 1;
   dim3 grid((unsigned)a.n_heads, 1u);
-  const bool buf =
-      kv_block_elems(a.T, a.C, D, a.chunked) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
 #define ZHA_PART(P2, BF)                                                                    \
   attn_partial_kernel<T, D, P2, BF><<<grid, kThreads, 0, s>>>(                              \
       reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),                        \

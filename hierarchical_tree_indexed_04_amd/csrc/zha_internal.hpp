@@ -13,10 +13,63 @@ constexpr int kBalMaxHeads = 2048;       // balanced split-KV: per-head prefix h
 #define ZHA_ATTN_BLOCKS 512
 #endif
 
+// Block path of zha_attn (calls with more than kBalMaxHeads query heads):
+// (query head, tile) pairs, a tile being CT consecutive chunks of one (b, kvh)
+// cache.  Scratch: counters, per-head slot bases, per-tile counts and
+// offsets, the pair entries and one fp32 partial (d + 2) per pair, for a
+// budget of kBlkPairsPerHead pairs per query head (heads past the budget are
+// attended one head per workgroup instead).
+constexpr int kBlkPairsPerHead = 8;
+constexpr int kBlkEntryInts = 6;  // head, slot, mask lo, mask hi, flags, unused
+
+struct BlkLayout {
+  int32_t CT;  // chunks per tile (<= 64: one bit each in a 64-bit mask)
+  int32_t NT;  // tiles per (b, kvh) cache
+  int64_t NTT;  // tiles in all
+  int64_t P;    // pair budget
+  int64_t off_ctrl, off_qbase, off_ntile, off_tcnt, off_tcur, off_toff, off_wpre, off_ent,
+      off_part, total;
+};
+
+// The block path serves bf16 caches with d in {64, 128} and C in {8, 16, 32, 64}.
+inline bool blk_eligible(int64_t n_heads, int C, int d, int dtype) {
+  return n_heads > kBalMaxHeads && dtype == ZHA_BF16 && (d == 64 || d == 128) &&
+         (C == 8 || C == 16 || C == 32 || C == 64);
+}
+
+inline BlkLayout blk_layout(int64_t n_heads, int64_t n_trees, int64_t T, int C, int d) {
+  BlkLayout L{};
+  const int64_t nchunks = (T + C - 1) / C;
+  L.CT = C >= 16 ? 1024 / C : 64;
+  L.NT = (int32_t)((nchunks + L.CT - 1) / L.CT);
+  L.NTT = n_trees * L.NT;
+  L.P = n_heads * kBlkPairsPerHead + L.NTT;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  L.off_ctrl = take(64);
+  L.off_qbase = take(n_heads * 4);
+  L.off_ntile = take(n_heads * 4);
+  L.off_tcnt = take(L.NTT * 4);
+  L.off_tcur = take(L.NTT * 4);
+  L.off_toff = take((L.NTT + 1) * 4);
+  L.off_wpre = take((L.NTT + 1) * 4);
+  L.off_ent = take(L.P * kBlkEntryInts * 4);
+  L.off_part = take(L.P * (int64_t)(d + 2) * 4);
+  L.total = off;
+  return L;
+}
+
 // zha_attn scratch: with n_heads <= kBalMaxHeads, a plan (n_heads + 2 int32)
-// and (workgroups + n_heads) partials of d + 2 floats; otherwise none.
-inline int64_t attn_scratch_layout_bytes(int64_t n_heads, int d) {
-  if (n_heads > kBalMaxHeads) return 0;
+// and (workgroups + n_heads) partials of d + 2 floats; with more heads, the
+// block path's layout when it applies, else none.
+inline int64_t attn_scratch_layout_bytes(int64_t n_heads, int64_t n_trees, int64_t T, int C, int d,
+                                         int dtype) {
+  if (n_heads > kBalMaxHeads)
+    return blk_eligible(n_heads, C, d, dtype) ? blk_layout(n_heads, n_trees, T, C, d).total : 0;
   return ((n_heads + 2) * 4 + 255) / 256 * 256 + (ZHA_ATTN_BLOCKS + n_heads) * (int64_t)(d + 2) * 4;
 }
 
@@ -60,6 +113,7 @@ struct AttnArgs {
   int32_t cap;
   int32_t S;      // workgroups of the balanced split (or splits per head)
   int32_t chunked;  // ZHA_KV_CHUNKED layout
+  int32_t dtype;
 };
 
 struct DenseArgs {

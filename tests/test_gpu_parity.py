@@ -184,6 +184,55 @@ def test_attention_on_random_chunk_sets(Z, chunked):
     assert worst <= TOL[g.dtype]
 
 
+@pytest.mark.parametrize("C,chunked", [(32, False), (16, True)])
+def test_block_attention_many_heads(Z, C, chunked):
+    import torch
+    say(f"block attention (4096 query heads, C = {C}, {'chunked' if chunked else 'split'} KV): "
+        "clustered and scattered chunk sets, sink, partial chunk, failed rows, heads past the "
+        "pair budget")
+    T = C ** 3 + C * 5 + 7 if C == 32 else C ** 3 * 4 + C * 5 + 7
+    g = W.custom(f"blk{C}", 130 + C, dtype=W.BF16, B=1, H_q=8, H_kv=1, T=T, C=C, L=2, p=0.95)
+    K, V = W.make_kv(g)
+    n_pos, n_heads = 512, 4096
+    Qn = W.make_query_block(g, K, range(n_pos))
+    n1, cap, CT = g.n_level(1), 400, 1024 // C
+    rng = np.random.default_rng(500 + C)
+    sel = np.full((n_heads, cap), -1, np.int32)
+    cnt = np.zeros(n_heads, np.int32)
+    for i in range(n_heads):
+        if i % 4 == 3:  # scattered over the whole cache: many tiles per head
+            ids = rng.choice(n1, int(rng.integers(0, 300)), replace=False)
+        else:  # clustered in two neighbouring tiles
+            base = int(rng.integers(0, n1 - 2 * CT))
+            ids = base + rng.choice(2 * CT, int(rng.integers(1, 2 * CT)), replace=False)
+        if i % 16 == 0:
+            ids = np.append(ids, 0)  # chunk 0 selected: the sink is inside it
+        ids = np.unique(ids).astype(np.int32)
+        cnt[i], sel[i, :len(ids)] = len(ids), ids
+    cnt[5] = -1         # failed route
+    cnt[6] = cap + 5    # more chunks than cap: NaN row
+    gm = Z.geom(g, Z.ZHA_KV_CHUNKED if chunked else Z.ZHA_KV_SPLIT)
+    Kd, Vd, Qd = to_device(K, g.dtype), to_device(V, g.dtype), to_device(Qn, g.dtype)
+    if chunked:
+        Kd, Vd = Z.to_chunked(Kd, Vd, g.C), None
+    seld = torch.from_numpy(sel.reshape(g.B, n_pos, g.H_q, cap)).cuda()
+    cntd = torch.from_numpy(cnt.reshape(g.B, n_pos, g.H_q)).cuda()
+    Od = Z.attn(gm, Qd, n_pos, Kd, Vd, seld, cntd, cap)
+    Og = from_device(Od, g.dtype).reshape(n_heads, g.d)
+    Kf, Vf = W.to_float(K[0, 0], g.dtype), W.to_float(V[0, 0], g.dtype)
+    worst = 0.0
+    for i in range(n_heads):
+        t, h = i // g.H_q, i % g.H_q
+        if cnt[i] < 0 or cnt[i] > cap:
+            assert np.isnan(Og[i]).all(), i
+            continue
+        idx = O.token_set(sel[i, :cnt[i]], g.C, g.T)
+        o = O.attend(W.to_float(Qn[0, t, h], g.dtype), Kf, Vf, idx)
+        worst = max(worst, float(np.abs(Og[i] - o).max()))
+    say(f"  max abs err {worst:.3g} over {n_heads} heads")
+    assert worst <= TOL[g.dtype]
+
+
 @pytest.mark.parametrize("cfg,chunked", [(1, False), (2, False), (2, True)])
 def test_dense_decode_matches_oracle(Z, cfg, chunked):
     say(f"dense decode, config {cfg}, {'chunked' if chunked else 'split'} KV")
