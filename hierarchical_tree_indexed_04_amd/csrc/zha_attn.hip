@@ -636,15 +636,15 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
 // ===========================================================================
 constexpr int kBlkQ = 64;      // query heads per work item: 4 waves x 16 MFMA rows
 constexpr int kBlkGroup = 32;  // tokens per MFMA step
-constexpr int kBlkGrid = 1024; // persistent workgroups of the attention launch
+constexpr int kBlkGrid = 768;  // persistent workgroups of the attention launch (3 per CU)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct BlkPtrs {
-  int32_t* ctrl;  // [0] pairs reserved, [1] work items
-  int32_t* qbase;  // per head: first slot, -1 past the budget, -2 failed route
-  int32_t* ntile;  // per head: pairs
+  int32_t* ctrl;   // [0] work items
+  int32_t* qbase;  // per head: first slot
+  int32_t* ntile;  // per head: tiles (>= 0), -1 attended per head, -2 failed route
   int32_t* tcnt;   // per tile: pairs
   int32_t* tcur;   // per tile: fill cursor
   int32_t* toff;   // per tile: first entry (exclusive scan of tcnt)
@@ -679,10 +679,27 @@ __global__ __launch_bounds__(256) void blk_zero_kernel(char* scr, BlkLayout L) {
   }
 }
 
-// A head's tiles, ascending: tile 0 when it attends the sink without chunk 0,
-// the tiles of its selected chunks, and the tile of the partial chunk n_1
-// when T is not a multiple of C.  One wave per head: count, reserve slots,
-// count pairs per tile.
+// Walks a head's selected chunks (ascending, one wave) and calls
+// on_first(tile) in the lanes that start a new tile; returns the tile count.
+template <typename F>
+__device__ __forceinline__ int walk_tiles(const int32_t* ids, int c, int CT, F on_first) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int n = 0, cur = -1;
+  for (int j = 0; j < c; j += kWave) {
+    const int id = j + lane < c ? ids[j + lane] : -1;
+    const int t = id >= 0 ? id / CT : -1;
+    int tp = __shfl_up(t, 1, kWave);
+    if (lane == 0) tp = cur;
+    const bool first = id >= 0 && t != tp;
+    if (first) on_first(t);
+    n += __popcll((unsigned long long)__ballot(first));
+    cur = __shfl(t, min(kWave - 1, c - j - 1), kWave);
+  }
+  return n;
+}
+
+// A head's pairs are the tiles of its selected chunks, ascending (its sink and
+// partial-chunk tokens are the merge launch's).  One wave per head: count.
 __global__ __launch_bounds__(256) void blk_count_kernel(const int32_t* __restrict__ sel,
                                                         const int32_t* __restrict__ cnt,
                                                         AttnArgs a, BlkLayout L, char* scr) {
@@ -691,52 +708,69 @@ __global__ __launch_bounds__(256) void blk_count_kernel(const int32_t* __restric
   const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
   if (head >= a.n_heads) return;
   const int c = cnt[head];
-  if (c < 0 || c > a.cap) {
-    if (lane == 0) {
-      P.qbase[head] = -2;
-      P.ntile[head] = 0;
-    }
-    return;
+  int n = -2;
+  if (c >= 0 && c <= a.cap) n = walk_tiles(sel + head * a.cap, c, L.CT, [](int) {});
+  if (lane == 0) P.ntile[head] = n;
+}
+
+// One workgroup: slot bases by a prefix sum of (tiles + 1) over the heads;
+// heads whose slots would pass the budget are marked for per-head attention.
+__global__ __launch_bounds__(1024) void blk_slots_kernel(int64_t n_heads, BlkLayout L,
+                                                         char* scr) {
+  BlkPtrs P(scr, L);
+  __shared__ int64_t s_v[1024];
+  const int tid = threadIdx.x;
+  const int64_t seg = (n_heads + 1023) / 1024;
+  const int64_t i0 = min(n_heads, tid * seg), i1 = min(n_heads, i0 + seg);
+  constexpr int kReg = 32;  // segments up to kReg heads are read in one batch of loads
+  int v[kReg];
+  int64_t sum = 0;
+  if (seg <= kReg) {
+#pragma unroll
+    for (int k = 0; k < kReg; ++k) v[k] = i0 + k < i1 ? P.ntile[i0 + k] : -3;
+#pragma unroll
+    for (int k = 0; k < kReg; ++k) sum += v[k] >= 0 ? v[k] + 1 : 0;
+  } else {
+    for (int64_t i = i0; i < i1; ++i) sum += P.ntile[i] >= 0 ? P.ntile[i] + 1 : 0;
   }
-  const int32_t* ids = sel + head * a.cap;
-  const int CT = L.CT;
-  const bool need_sink = c == 0 || ids[0] != 0;
-  const int n1 = (int)a.n1;
-  const bool has_tail = a.T > a.n1 * a.C;
-  const int tail_tile = n1 / CT;
+  s_v[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int64_t x = tid >= off ? s_v[tid - off] : 0;
+    __syncthreads();
+    s_v[tid] += x;
+    __syncthreads();
+  }
+  int64_t run = s_v[tid] - sum;
+  auto assign = [&](int64_t i, int n) {
+    if (n < 0) return;
+    if (run + n + 1 > L.S) {
+      P.ntile[i] = -1;
+    } else {
+      P.qbase[i] = (int32_t)run;
+      run += n + 1;
+    }
+  };
+  if (seg <= kReg) {
+#pragma unroll
+    for (int k = 0; k < kReg; ++k)
+      if (i0 + k < i1) assign(i0 + k, v[k]);
+  } else {
+    for (int64_t i = i0; i < i1; ++i) assign(i, P.ntile[i]);
+  }
+}
+
+// Pairs per tile, for the heads that got slots.
+__global__ __launch_bounds__(256) void blk_tiles_kernel(const int32_t* __restrict__ sel,
+                                                        const int32_t* __restrict__ cnt,
+                                                        AttnArgs a, BlkLayout L, char* scr) {
+  BlkPtrs P(scr, L);
+  const int wave = threadIdx.x >> 6;
+  const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
+  if (head >= a.n_heads) return;
+  if (P.ntile[head] <= 0) return;
   int32_t* tc = P.tcnt + tree_of_head(head, a) * L.NT;
-  for (int pass = 0; pass < 2; ++pass) {
-    int n = need_sink ? 1 : 0;
-    int cur = need_sink ? 0 : -1;
-    if (pass == 1 && need_sink && lane == 0) atomicAdd(&tc[0], 1);
-    for (int j = 0; j < c; j += kWave) {
-      const int id = j + lane < c ? ids[j + lane] : -1;
-      const int t = id >= 0 ? id / CT : -1;
-      int tp = __shfl_up(t, 1, kWave);
-      if (lane == 0) tp = cur;
-      const bool first = id >= 0 && t != tp;
-      if (pass == 0)
-        n += __popcll((unsigned long long)__ballot(first));
-      else if (first)
-        atomicAdd(&tc[t], 1);
-      cur = __shfl(t, min(kWave - 1, c - j - 1), kWave);
-    }
-    if (has_tail && cur != tail_tile) {
-      ++n;
-      if (pass == 1 && lane == 0) atomicAdd(&tc[tail_tile], 1);
-    }
-    if (pass == 0) {
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&P.ctrl[0], n);
-      base = __shfl(base, 0, kWave);
-      const bool ok = (int64_t)base + n <= L.P;
-      if (lane == 0) {
-        P.qbase[head] = ok ? base : -1;
-        P.ntile[head] = ok ? n : 0;
-      }
-      if (!ok) return;
-    }
-  }
+  walk_tiles(sel + head * a.cap, cnt[head], L.CT, [&](int t) { atomicAdd(&tc[t], 1); });
 }
 
 // Exclusive scans over the tiles: first entry and first work item of each.
@@ -772,12 +806,20 @@ __global__ __launch_bounds__(1024) void blk_scan_kernel(char* scr, BlkLayout L) 
   if (tid == 1023) {
     P.toff[L.NTT] = s_c[1023];
     P.wpre[L.NTT] = s_w[1023];
-    P.ctrl[1] = s_w[1023];
+    P.ctrl[0] = s_w[1023];
   }
 }
 
+__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int off) {
+  const uint32_t lo = (uint32_t)__shfl_down((int)(uint32_t)v, off, kWave);
+  const uint32_t hi = (uint32_t)__shfl_down((int)(uint32_t)(v >> 32), off, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // One wave per head: walk the head's tiles again (in the same order as the
-// count) and write one entry per tile: head, slot, chunk mask, sink flag.
+// count) and write one entry per tile: head, slot, chunk mask.  Within a batch
+// of 64 ids, a segmented OR leaves each run of one tile's ids with its mask in
+// the run's first lane; the last run may continue into the next batch.
 __global__ __launch_bounds__(256) void blk_fill_kernel(const int32_t* __restrict__ sel,
                                                        const int32_t* __restrict__ cnt,
                                                        AttnArgs a, BlkLayout L, char* scr) {
@@ -785,61 +827,51 @@ __global__ __launch_bounds__(256) void blk_fill_kernel(const int32_t* __restrict
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
   if (head >= a.n_heads) return;
-  const int qb = P.qbase[head];
-  if (qb < 0) return;
+  if (P.ntile[head] <= 0) return;
   const int c = cnt[head];
   const int32_t* ids = sel + head * a.cap;
   const int CT = L.CT;
-  const bool need_sink = c == 0 || ids[0] != 0;
-  const int n1 = (int)a.n1;
   const int64_t tb = tree_of_head(head, a) * L.NT;
-  int k = 0, cur = -1, flags = 0;
-  uint64_t mask = 0;
-  auto flush = [&]() {
+  const int slot0 = P.qbase[head];
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  auto emit = [&](int tile, uint64_t mask, int k) {
+    const int pos = P.toff[tb + tile] + atomicAdd(&P.tcur[tb + tile], 1);
+    int32_t* e = P.ent + (int64_t)pos * kBlkEntryInts;
+    e[0] = (int32_t)head;
+    e[1] = slot0 + k;
+    e[2] = (int32_t)(uint32_t)mask;
+    e[3] = (int32_t)(uint32_t)(mask >> 32);
+  };
+  int k = 0, cur = -1;  // tiles emitted; tile carried from the previous batch
+  uint64_t carry = 0;
+  for (int j = 0; j < c; j += kWave) {
+    const bool valid = j + lane < c;
+    const int id = valid ? ids[j + lane] : 0;
+    const int t = valid ? id / CT : -1;
+    uint64_t bits = valid ? (1ull << (id - t * CT)) : 0ull;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint64_t ob = shfl_down_u64(bits, off);
+      const int ot = __shfl_down(t, off, kWave);
+      if (lane + off < kWave && ot == t) bits |= ob;
+    }
+    int tp = __shfl_up(t, 1, kWave);
+    if (lane == 0) tp = cur;
+    const bool first = valid && t != tp;
+    const uint64_t fb = __ballot(first);
+    const int t0 = __shfl(t, 0, kWave);
+    if (t0 == cur) carry |= readlane_u64(bits, 0);  // lane 0's run continues the carried tile
+    if (fb == 0ull) continue;
     if (cur >= 0) {
-      if (lane == 0) {
-        const int pos = P.toff[tb + cur] + atomicAdd(&P.tcur[tb + cur], 1);
-        int32_t* e = P.ent + (int64_t)pos * kBlkEntryInts;
-        e[0] = (int32_t)head;
-        e[1] = qb + k;
-        e[2] = (int32_t)(uint32_t)mask;
-        e[3] = (int32_t)(uint32_t)(mask >> 32);
-        e[4] = flags;
-        e[5] = 0;
-      }
+      if (lane == 0) emit(cur, carry, k);
       ++k;
     }
-  };
-  if (need_sink) {
-    cur = 0;
-    flags = 1;  // token 0 alone (chunk 0 is not selected)
+    const int last = 63 - __clzll((long long)fb);
+    if (first && lane != last) emit(t, bits, k + __popcll((unsigned long long)(fb & lt)));
+    k += __popcll((unsigned long long)fb) - 1;
+    cur = __shfl(t, last, kWave);
+    carry = readlane_u64(bits, last);
   }
-  for (int j = 0; j < c; j += kWave) {
-    const int idv = j + lane < c ? ids[j + lane] : 0;
-    const int nn = min(kWave, c - j);
-    for (int i = 0; i < nn; ++i) {
-      const int id = __builtin_amdgcn_readlane(idv, i);
-      const int t = id / CT;
-      if (t != cur) {
-        flush();
-        cur = t;
-        mask = 0;
-        flags = 0;
-      }
-      mask |= 1ull << (id - t * CT);
-    }
-  }
-  if (a.T > a.n1 * a.C) {
-    const int t = n1 / CT;
-    if (t != cur) {
-      flush();
-      cur = t;
-      mask = 0;
-      flags = 0;
-    }
-    mask |= 1ull << (n1 - t * CT);
-  }
-  flush();
+  if (cur >= 0 && lane == 0) emit(cur, carry, k);
 }
 
 // Work items: (tile, block of up to kBlkQ of its entries), persistent loop.
@@ -863,7 +895,7 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
   constexpr int KROW = D + 8;  // padded LDS row of K (bf16 elements)
   constexpr int VTROW = kBlkGroup + 4;  // padded LDS row of V^T (bf16 elements)
   BlkPtrs P(scr, L);
-  __shared__ int32_t s_head[kBlkQ], s_slot[kBlkQ], s_flags[kBlkQ];
+  __shared__ int32_t s_head[kBlkQ], s_slot[kBlkQ];
   __shared__ unsigned long long s_mask[kBlkQ];
   __shared__ unsigned long long s_union;
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kBlkGroup * KROW];
@@ -872,7 +904,7 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
   const int li = lane & 15, lg = lane >> 4;
   const float inv = 1.0f / sqrtf((float)D);
   const int C = a.C;
-  const int total = P.ctrl[1];
+  const int total = P.ctrl[0];
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     // Tile of work item w: the last tile u with wpre[u] <= w.
     int64_t lo = 0, hi = L.NTT;
@@ -892,16 +924,14 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
         s_head[tid] = e[0];
         s_slot[tid] = e[1];
         s_mask[tid] = (unsigned long long)(uint32_t)e[2] | ((unsigned long long)(uint32_t)e[3] << 32);
-        s_flags[tid] = e[4];
       } else {
         s_head[tid] = -1;
         s_slot[tid] = -1;
         s_mask[tid] = 0ull;
-        s_flags[tid] = 0;
       }
     }
     __syncthreads();
-    if (tid < ne) atomicOr(&s_union, s_mask[tid] | ((s_flags[tid] & 1) ? 1ull : 0ull));
+    if (tid < ne) atomicOr(&s_union, s_mask[tid]);
     __syncthreads();
     const uint64_t uni = s_union;
     const int64_t tr = u / L.NT;
@@ -914,7 +944,6 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
     const int qi = wave * 16 + li;
     const bool qvalid = qi < ne;
     const uint64_t qmask = s_mask[qi];
-    const bool qsink = (s_flags[qi] & 1) != 0;
     bf16x8_t qb[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -927,20 +956,37 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
 #pragma unroll
     for (int n = 0; n < NTD; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int g0 = tok0; g0 < tok_end; g0 += kBlkGroup) {
-      const int gl = min(g0 + kBlkGroup, tok_end) - 1;
-      const int cf = g0 / C - chunk0, cl = gl / C - chunk0;
-      const uint64_t gbits = (cl >= 63 ? ~0ull : ((1ull << (cl + 1)) - 1)) & ~((1ull << cf) - 1);
-      if ((uni & gbits) == 0ull) continue;
+    // 32-token steps that some head of the block selected; the rows of the
+    // next such step are loaded into registers while the current one computes.
+    constexpr int RPP = 256 / SEG;            // rows per staging pass
+    constexpr int NPASS = kBlkGroup / RPP;
+    const int sg = tid % SEG, r0 = tid / SEG;
+    auto next_step = [&](int g) {
+      for (; g < tok_end; g += kBlkGroup) {
+        const int cf = g / C - chunk0, cl = (min(g + kBlkGroup, tok_end) - 1) / C - chunk0;
+        const uint64_t bits = (cl >= 63 ? ~0ull : ((1ull << (cl + 1)) - 1)) & ~((1ull << cf) - 1);
+        if ((uni & bits) != 0ull) break;
+      }
+      return g;
+    };
+    uint4 pk[NPASS], pv[NPASS];
+    auto fetch = [&](int g) {
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const int tok = g + r0 + p * RPP;
+        kvb.load(kvb.key_row(tok / C, tok % C), tok < tok_end, pk[p], pv[p]);
+      }
+    };
+    int g0 = next_step(tok0);
+    if (g0 < tok_end) fetch(g0);
+    while (g0 < tok_end) {
       // Stage: K rows as they are, V rows transposed (dimension-major).
       __syncthreads();
-      for (int r = tid / SEG; r < kBlkGroup; r += 256 / SEG) {
-        const int tok = g0 + r;
-        uint4 kv, vv;
-        kvb.load(kvb.key_row(tok / C, tok % C), tok < tok_end, kv, vv);
-        const int sg = tid % SEG;
-        *reinterpret_cast<uint4*>(&s_k[r * KROW + sg * 8]) = kv;
-        const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const int r = r0 + p * RPP;
+        *reinterpret_cast<uint4*>(&s_k[r * KROW + sg * 8]) = pk[p];
+        const uint32_t vw[4] = {pv[p].x, pv[p].y, pv[p].z, pv[p].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           s_vt[(sg * 8 + 2 * e) * VTROW + r] = (uint16_t)(vw[e] & 0xffffu);
@@ -948,6 +994,8 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
         }
       }
       __syncthreads();
+      const int gnext = next_step(g0 + kBlkGroup);
+      if (gnext < tok_end) fetch(gnext);
       // S^T = K Q^T for the two 16-token halves of the step.
       f32x4_t st[2];
 #pragma unroll
@@ -969,8 +1017,7 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
         for (int e = 0; e < 4; ++e) {
           const int tok = g0 + nt * 16 + 4 * lg + e;
           const int ch = tok / C - chunk0;
-          const bool on = qvalid && tok < tok_end &&
-                          (((qmask >> ch) & 1ull) != 0ull || (qsink && tok == 0));
+          const bool on = qvalid && tok < tok_end && ((qmask >> ch) & 1ull) != 0ull;
           const float v = on ? st[nt][e] * inv : -INFINITY;
           x[nt * 4 + e] = v;
           mloc = fmaxf(mloc, v);
@@ -1009,6 +1056,7 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, vb), o[n],
                                                        0, 0, 0);
       }
+      g0 = gnext;
     }
     // Partials: O rows 4 lg + e (heads of the wave), columns n * 16 + li; m and l
     // from the lanes of row group 0.
@@ -1029,26 +1077,63 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
   }
 }
 
-// Per head: the merge of its pairs' partials in tile order; a head past the
-// pair budget is attended here directly; a failed route gives a NaN row.
+// Per head: the partial of its sink (when chunk 0 is not selected) and of the
+// partial chunk's tokens, then the merge of its pairs' partials in tile order
+// followed by that one; a head with too many tiles is attended here directly;
+// a failed route gives a NaN row.
 template <typename T, int D, bool POW2, bool BUF>
 __global__ __launch_bounds__(kThreads) void blk_merge_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
     AttnArgs a, BlkLayout L, char* scr) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int LPR = D / VEC;
+  constexpr int RPB = kThreads / LPR;
   BlkPtrs P(scr, L);
   const int64_t head = blockIdx.x;
-  const int qb = P.qbase[head];
-  if (qb == -1) {
+  const int n = P.ntile[head];
+  if (n == -1) {
     AttnArgs a1 = a;
     a1.S = 1;
     attend_one_head<T, D, POW2, BUF>(Q, K, V, sel, cnt, O, nullptr, a1, head, 0);
-  } else if (qb < 0) {
+    return;
+  }
+  if (n < 0) {
     for (int t = threadIdx.x; t < D; t += kThreads)
       store_elem(O + head * D, t, __int_as_float(0x7fc00000));
-  } else {
-    merge_partials<T, D>(P.part + (int64_t)qb * (D + 2), P.ntile[head], O + head * D);
+    return;
   }
+  __shared__ float s_m[RPB], s_l[RPB];
+  __shared__ float s_acc[RPB * D];
+  const int tid = threadIdx.x, sub = tid % LPR, grp = tid / LPR;
+  const int c = cnt[head];
+  const bool sink = c == 0 || sel[head * a.cap] != 0;
+  const int ntail = (int)(a.T - a.n1 * a.C);
+  const int ne = (sink ? 1 : 0) + ntail;  // extra tokens: sink, then the partial chunk
+  float* slots = P.part + (int64_t)P.qbase[head] * (D + 2);
+  if (ne > 0) {
+    const KvBlock<T, D, BUF> kvb(K, V, tree_of_head(head, a), a.T, a.C, a.chunked, sub);
+    const uint4 qv = ld16c(Q + head * D + sub * VEC);
+    const float inv = 1.0f / sqrtf((float)D);
+    float m = -INFINITY, l = 0.f, acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int base = 0; base < ne; base += RPB) {
+      const int x = base + grp;
+      const int j = sink ? x - 1 : x;  // token j of chunk n_1 (x = 0 is the sink)
+      const int row = (sink && x == 0) ? kvb.key_row(0, 0) : kvb.key_row((int)a.n1, j);
+      uint4 kv[1], vv[1];
+      kvb.load(row, x < ne, kv[0], vv[0]);
+      float sc[1];
+      const float dot = group_allreduce<LPR>(slice_dot<T>(kv[0], qv), OpAdd()) * inv;
+      sc[0] = x < ne ? dot : -INFINITY;
+      online_update<T, 1>(m, l, acc, sc, vv);
+    }
+    combine_groups<T, D, RPB>(m, l, acc, grp, sub, s_m, s_l, s_acc, nullptr,
+                              slots + (int64_t)n * (D + 2));
+    __syncthreads();  // the extra partial is read back below by other threads
+  }
+  merge_partials<T, D>(slots, n + (ne > 0 ? 1 : 0), O + head * D);
 }
 
 template <typename T, int D, bool POW2, bool BUF>
@@ -1060,6 +1145,8 @@ int launch_blk(const AttnArgs& a, const void* Q, const void* K, const void* V, c
   const unsigned wave_blocks = (unsigned)((a.n_heads + kWaves - 1) / kWaves);
   blk_zero_kernel<<<(unsigned)((max(L.NTT, (int64_t)16) + 255) / 256), 256, 0, s>>>(scr, L);
   blk_count_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
+  blk_slots_kernel<<<1, 1024, 0, s>>>(a.n_heads, L, scr);
+  blk_tiles_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
   blk_scan_kernel<<<1, 1024, 0, s>>>(scr, L);
   blk_fill_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
   blk_attn_kernel<D, BUF><<<kBlkGrid, 256, 0, s>>>(

@@ -15,18 +15,20 @@ constexpr int kBalMaxHeads = 2048;       // balanced split-KV: per-head prefix h
 
 // Block path of zha_attn (calls with more than kBalMaxHeads query heads):
 // (query head, tile) pairs, a tile being CT consecutive chunks of one (b, kvh)
-// cache.  Scratch: counters, per-head slot bases, per-tile counts and
-// offsets, the pair entries and one fp32 partial (d + 2) per pair, for a
-// budget of kBlkPairsPerHead pairs per query head (heads past the budget are
-// attended one head per workgroup instead).
-constexpr int kBlkPairsPerHead = 8;
-constexpr int kBlkEntryInts = 6;  // head, slot, mask lo, mask hi, flags, unused
+// cache.  A head takes one partial slot per tile of its selected chunks plus
+// one for its sink and partial-chunk tokens; slots are handed out by a prefix
+// sum over the heads, within a budget of kBlkSlots per head on average (heads
+// past the budget are attended one head per workgroup instead).  Scratch:
+// counters, per-head slot bases and tile counts, per-tile counts and offsets,
+// the pair entries and the fp32 partials (d + 2 each).
+constexpr int kBlkSlots = 9;
+constexpr int kBlkEntryInts = 4;  // head, slot, mask lo, mask hi
 
 struct BlkLayout {
   int32_t CT;  // chunks per tile (<= 64: one bit each in a 64-bit mask)
   int32_t NT;  // tiles per (b, kvh) cache
   int64_t NTT;  // tiles in all
-  int64_t P;    // pair budget
+  int64_t S;    // slot budget
   int64_t off_ctrl, off_qbase, off_ntile, off_tcnt, off_tcur, off_toff, off_wpre, off_ent,
       off_part, total;
 };
@@ -43,7 +45,7 @@ inline BlkLayout blk_layout(int64_t n_heads, int64_t n_trees, int64_t T, int C, 
   L.CT = C >= 16 ? 1024 / C : 64;
   L.NT = (int32_t)((nchunks + L.CT - 1) / L.CT);
   L.NTT = n_trees * L.NT;
-  L.P = n_heads * kBlkPairsPerHead + L.NTT;
+  L.S = n_heads * kBlkSlots;
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
     const int64_t o = off;
@@ -57,8 +59,8 @@ inline BlkLayout blk_layout(int64_t n_heads, int64_t n_trees, int64_t T, int C, 
   L.off_tcur = take(L.NTT * 4);
   L.off_toff = take((L.NTT + 1) * 4);
   L.off_wpre = take((L.NTT + 1) * 4);
-  L.off_ent = take(L.P * kBlkEntryInts * 4);
-  L.off_part = take(L.P * (int64_t)(d + 2) * 4);
+  L.off_ent = take(L.S * kBlkEntryInts * 4);
+  L.off_part = take(L.S * (int64_t)(d + 2) * 4);
   L.total = off;
   return L;
 }
