@@ -153,14 +153,13 @@ int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_
   if (bytes == nullptr) return ZHA_ERR_NULL;
   if (n_pos < 1) return ZHA_ERR_NPOS;
   if (cap < 1) return ZHA_ERR_CAP;
-  *bytes = 0;
+  *bytes = (size_t)route_scratch_layout_bytes((int64_t)g->B * n_pos * g->H_q);
   return ZHA_OK;
 }
 
 int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos, float p,
               int32_t* sel, int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap,
               void* scratch, void* stream) {
-  (void)scratch;
   const int rc = check_geom(g);
   if (rc) return rc;
   if (tree == nullptr || Q == nullptr || sel == nullptr || cnt == nullptr) return ZHA_ERR_NULL;
@@ -178,7 +177,8 @@ int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
   a.cap = cap;
   a.p = p;
   if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
-  return route_dispatch(a, g->dtype, g->d, tree, Q, sel, cnt, level_stats, gap,
+  if (route_scratch_layout_bytes(a.n_heads) > 0 && scratch == nullptr) return ZHA_ERR_NULL;
+  return route_dispatch(a, g->dtype, g->d, tree, Q, sel, cnt, level_stats, gap, scratch,
                         reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -7,6 +7,13 @@
 namespace zha {
 
 constexpr int kRouteFrontierMax = 4096;  // candidates per level held in LDS by the router
+constexpr int64_t kTputMinHeads = 4096;  // query heads per call for the router's throughput shape
+
+// zha_route scratch: with the throughput shape, a count and a list of the heads
+// whose frontier outgrew it.
+inline int64_t route_scratch_layout_bytes(int64_t n_heads) {
+  return n_heads >= kTputMinHeads ? (n_heads + 1) * 4 : 0;
+}
 constexpr int kBalMaxHeads = 2048;       // balanced split-KV: per-head prefix held in LDS
 
 #ifndef ZHA_ATTN_BLOCKS
@@ -166,7 +173,8 @@ inline BuildScratch build_scratch_layout(const BuildArgs& a) {
 int build_dispatch(const BuildArgs& a, int dtype, int d, const void* K, const float* qref,
                    void* tree, void* scratch, hipStream_t s);
 int route_dispatch(const RouteArgs& a, int dtype, int d, const void* tree, const void* Q,
-                   int32_t* sel, int32_t* cnt, int32_t* stats, float* gap, hipStream_t s);
+                   int32_t* sel, int32_t* cnt, int32_t* stats, float* gap, void* scratch,
+                   hipStream_t s);
 int attn_dispatch(const AttnArgs& a, int dtype, int d, const void* Q, const void* K,
                   const void* V, const int32_t* sel, const int32_t* cnt, void* O, void* scratch,
                   hipStream_t s);

@@ -51,23 +51,31 @@ constexpr int kMaxChildren = 1024;  // C <= 1024
 // a call with few query heads finishes as fast as one head walks the tree.
 // Throughput shape: 4 waves, 8 rows in flight, frontiers up to 1024 in LDS;
 // several workgroups share a CU, for calls with many query heads (a block of
-// positions).  A head whose frontier outgrows the throughput shape reports
-// cnt = -1 and is routed again by the latency shape.
+// positions).  A head whose frontier outgrows the throughput shape is listed
+// in the scratch buffer and routed again by a few persistent workgroups of the
+// latency shape.
+#ifndef ZHA_ROUTE_LAT_ROWS
+#define ZHA_ROUTE_LAT_ROWS 16
+#endif
+#ifndef ZHA_ROUTE_TPUT_ROWS
+#define ZHA_ROUTE_TPUT_ROWS 4
+#endif
 namespace lat {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kU = 16;
+constexpr int kU = ZHA_ROUTE_LAT_ROWS;
 constexpr int kFMax = kRouteFrontierMax;
 #include "zha_route_impl.inc"
 }  // namespace lat
 namespace tput {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kU = 8;
+constexpr int kU = ZHA_ROUTE_TPUT_ROWS;
 constexpr int kFMax = 1024;
 #include "zha_route_impl.inc"
 }  // namespace tput
-constexpr int64_t kTputMinHeads = 4096;  // query heads per call for the throughput shape
+// kTputMinHeads (query heads per call for the throughput shape) is in zha_internal.hpp.
+constexpr unsigned kRouteListBlocks = 256;  // persistent workgroups for the listed heads
 
 // p >= 1 keeps every candidate at every level, so S_l is all of level l and
 // S_1 is every leaf chunk 0 .. n_1 - 1 (orphans included).
@@ -92,42 +100,49 @@ __global__ __launch_bounds__(256) void route_keep_all_kernel(RouteArgs a,
   if (threadIdx.x == 0) cnt[head] = (int32_t)n1;
 }
 
+__global__ void route_zero_kernel(int32_t* fail_list) {
+  if (threadIdx.x == 0) fail_list[0] = 0;
+}
+
 template <typename T, int D, bool R1>
 void launch_route_kernels(const RouteArgs& a, const char* tree, const T* q, int32_t* sel,
-                          int32_t* cnt, int32_t* stats, float* gap, hipStream_t s) {
+                          int32_t* cnt, int32_t* stats, float* gap, int32_t* fail_list,
+                          hipStream_t s) {
   const unsigned blocks = (unsigned)a.n_heads;
   if (a.n_heads >= kTputMinHeads) {
+    route_zero_kernel<<<1, 64, 0, s>>>(fail_list);
     tput::route_kernel<T, D, tput::kFMax, R1>
-        <<<blocks, tput::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, 0);
-    // Heads whose frontier did not fit (cnt == -1) again; the others exit at once.
-    lat::route_kernel<T, D, lat::kFMax, R1>
-        <<<blocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, 1);
+        <<<blocks, tput::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, fail_list);
+    lat::route_list_kernel<T, D, lat::kFMax, R1>
+        <<<kRouteListBlocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, fail_list);
   } else {
     lat::route_kernel<T, D, lat::kFMax, R1>
-        <<<blocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, 0);
+        <<<blocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, nullptr);
   }
 }
 
 template <typename T, int D>
 int launch_route(const RouteArgs& a, const void* tree, const void* Q, int32_t* sel, int32_t* cnt,
-                 int32_t* stats, float* gap, hipStream_t s) {
+                 int32_t* stats, float* gap, void* scratch, hipStream_t s) {
   const char* tr = reinterpret_cast<const char*>(tree);
   const T* q = reinterpret_cast<const T*>(Q);
+  int32_t* fail_list = reinterpret_cast<int32_t*>(scratch);
   if (!(a.p < 1.0f))
     route_keep_all_kernel<<<(unsigned)a.n_heads, 256, 0, s>>>(a, sel, cnt, stats, gap);
   else if (a.lay.R == 1)
-    launch_route_kernels<T, D, true>(a, tr, q, sel, cnt, stats, gap, s);
+    launch_route_kernels<T, D, true>(a, tr, q, sel, cnt, stats, gap, fail_list, s);
   else
-    launch_route_kernels<T, D, false>(a, tr, q, sel, cnt, stats, gap, s);
+    launch_route_kernels<T, D, false>(a, tr, q, sel, cnt, stats, gap, fail_list, s);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
 }
 
 }  // namespace
 
 int route_dispatch(const RouteArgs& a, int dtype, int d, const void* tree, const void* Q,
-                   int32_t* sel, int32_t* cnt, int32_t* stats, float* gap, hipStream_t s) {
+                   int32_t* sel, int32_t* cnt, int32_t* stats, float* gap, void* scratch,
+                   hipStream_t s) {
 #define ZHA_ROUTE_CASE(TT, DD) \
-  if (d == DD) return launch_route<TT, DD>(a, tree, Q, sel, cnt, stats, gap, s);
+  if (d == DD) return launch_route<TT, DD>(a, tree, Q, sel, cnt, stats, gap, scratch, s);
   if (dtype == ZHA_BF16) {
     ZHA_ROUTE_CASE(bf16_t, 64)
     ZHA_ROUTE_CASE(bf16_t, 128)

@@ -139,7 +139,11 @@ int zha_build(const zha_geom* g, const void* K, const float* qref, void* tree, v
  * nodes whose parent is incomplete (paper App. E-E).
  * ------------------------------------------------------------------------- */
 
-/* Scratch bytes zha_route needs (0 is a valid answer: pass any pointer). */
+/* Scratch bytes zha_route needs: nonzero for calls of 4096 or more query heads
+ * (B * n_pos * H_q), which route most heads with a smaller-frontier launch and
+ * list there the heads whose frontier outgrew it; 0 otherwise (then any
+ * pointer, NULL included, may be passed).  Calls that overlap in time on the
+ * same buffer race. */
 int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes);
 
 /*   tree        device, built by zha_build for the same geometry
@@ -156,7 +160,8 @@ int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_
  *               index l-1, (frontier size K_l, kept count |S_l|)
  *   gap         device [B, n_pos, H_q, L] fp32 or NULL: s_(m) - s_(m+1) at
  *               each level's cut, +inf when the whole frontier is kept
- *   scratch     device, zha_route_scratch_bytes() bytes */
+ *   scratch     device, zha_route_scratch_bytes() bytes (ZHA_ERR_NULL if needed
+ *               and NULL) */
 int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos, float p,
               int32_t* sel, int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap,
               void* scratch, void* stream);

@@ -129,6 +129,7 @@ def test_chunked_layout_shape_and_tree_layout_are_independent():
 def test_scratch_sizes_are_consistent():
     gm = g(B=8, H_q=32, H_kv=4, T=262144, C=8, L=6)
     assert Z.route_scratch_bytes(gm, 1, 32768) == 0
+    assert Z.route_scratch_bytes(gm, 16, 32768) == (8 * 16 * 32 + 1) * 4  # many heads: fallback list
     a = Z.attn_scratch_bytes(gm, 1, 32768)
     assert a >= (256 + 32) * 4 * (gm.d + 2)  # plan + at least one partial per workgroup and head
     assert Z.dense_scratch_bytes(gm, 1) % (4 * (gm.d + 2)) == 0
