@@ -1077,63 +1077,77 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
   }
 }
 
-// Per head: the partial of its sink (when chunk 0 is not selected) and of the
-// partial chunk's tokens, then the merge of its pairs' partials in tile order
-// followed by that one; a head with too many tiles is attended here directly;
-// a failed route gives a NaN row.
+// One wave per head: the head's sink (when chunk 0 is not selected) and its
+// partial-chunk tokens, then the merge with its pairs' partials (in tile
+// order); a failed route gives a NaN row.  Heads with too many tiles are then
+// attended by the whole workgroup, one at a time.
 template <typename T, int D, bool POW2, bool BUF>
 __global__ __launch_bounds__(kThreads) void blk_merge_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
     AttnArgs a, BlkLayout L, char* scr) {
-  constexpr int VEC = Vec<T>::N;
-  constexpr int LPR = D / VEC;
-  constexpr int RPB = kThreads / LPR;
+  constexpr int DPL = D / kWave;  // dimensions per lane
   BlkPtrs P(scr, L);
-  const int64_t head = blockIdx.x;
-  const int n = P.ntile[head];
-  if (n == -1) {
-    AttnArgs a1 = a;
-    a1.S = 1;
-    attend_one_head<T, D, POW2, BUF>(Q, K, V, sel, cnt, O, nullptr, a1, head, 0);
-    return;
-  }
-  if (n < 0) {
-    for (int t = threadIdx.x; t < D; t += kThreads)
-      store_elem(O + head * D, t, __int_as_float(0x7fc00000));
-    return;
-  }
-  __shared__ float s_m[RPB], s_l[RPB];
-  __shared__ float s_acc[RPB * D];
-  const int tid = threadIdx.x, sub = tid % LPR, grp = tid / LPR;
-  const int c = cnt[head];
-  const bool sink = c == 0 || sel[head * a.cap] != 0;
-  const int ntail = (int)(a.T - a.n1 * a.C);
-  const int ne = (sink ? 1 : 0) + ntail;  // extra tokens: sink, then the partial chunk
-  float* slots = P.part + (int64_t)P.qbase[head] * (D + 2);
-  if (ne > 0) {
-    const KvBlock<T, D, BUF> kvb(K, V, tree_of_head(head, a), a.T, a.C, a.chunked, sub);
-    const uint4 qv = ld16c(Q + head * D + sub * VEC);
-    const float inv = 1.0f / sqrtf((float)D);
-    float m = -INFINITY, l = 0.f, acc[VEC];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
+  const int n = head < a.n_heads ? P.ntile[head] : -3;
+  if (n == -2) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-    for (int base = 0; base < ne; base += RPB) {
-      const int x = base + grp;
-      const int j = sink ? x - 1 : x;  // token j of chunk n_1 (x = 0 is the sink)
-      const int row = (sink && x == 0) ? kvb.key_row(0, 0) : kvb.key_row((int)a.n1, j);
-      uint4 kv[1], vv[1];
-      kvb.load(row, x < ne, kv[0], vv[0]);
-      float sc[1];
-      const float dot = group_allreduce<LPR>(slice_dot<T>(kv[0], qv), OpAdd()) * inv;
-      sc[0] = x < ne ? dot : -INFINITY;
-      online_update<T, 1>(m, l, acc, sc, vv);
+    for (int e = 0; e < DPL; ++e) store_elem(O + head * D, lane * DPL + e, __int_as_float(0x7fc00000));
+  } else if (n >= 0) {
+    const int c = cnt[head];
+    const bool sink = c == 0 || sel[head * a.cap] != 0;
+    const int ne = (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C);  // sink, then the partial chunk
+    const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
+    const T* Kb = K + tree_of_head(head, a) * nblk;
+    const T* Vb = a.chunked ? Kb + (int64_t)a.C * D : V + tree_of_head(head, a) * nblk;
+    const int64_t row1 = a.n1 * (a.chunked ? 2 * a.C : a.C);  // first key row of chunk n_1
+    const float inv = 1.0f / sqrtf((float)D);
+    float q[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) q[e] = load_elem(Q + head * D, lane * DPL + e);
+    float m = -INFINITY, l = 0.f, acc[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+    for (int x = 0; x < ne; ++x) {
+      const int64_t row = (sink && x == 0) ? 0 : row1 + (x - (sink ? 1 : 0));
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) part = fmaf(q[e], load_elem(Kb + row * D, lane * DPL + e), part);
+      const float sc = wave_allreduce_f32(part, OpAdd()) * inv;
+      const float mn = fmaxf(m, sc);
+      const float r = __expf(m - mn), pw = __expf(sc - mn);
+      l = l * r + pw;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pw, load_elem(Vb + row * D, lane * DPL + e), acc[e] * r);
+      m = mn;
     }
-    combine_groups<T, D, RPB>(m, l, acc, grp, sub, s_m, s_l, s_acc, nullptr,
-                              slots + (int64_t)n * (D + 2));
-    __syncthreads();  // the extra partial is read back below by other threads
+    const float* slots = P.part + (int64_t)P.qbase[head] * (D + 2);
+    float M = m;
+    for (int s = 0; s < n; ++s) M = fmaxf(M, slots[s * (D + 2) + D]);
+    const float wx = m == -INFINITY ? 0.f : __expf(m - M);
+    float num[DPL], den = wx * l;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) num[e] = wx * acc[e];
+    for (int s = 0; s < n; ++s) {
+      const float* r = slots + s * (D + 2);
+      const float ms = r[D];
+      const float w = ms == -INFINITY ? 0.f : __expf(ms - M);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) num[e] = fmaf(w, r[lane * DPL + e], num[e]);
+      den = fmaf(w, r[D + 1], den);
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) store_elem(O + head * D, lane * DPL + e, num[e] / den);
   }
-  merge_partials<T, D>(slots, n + (ne > 0 ? 1 : 0), O + head * D);
+  for (int w = 0; w < kWaves; ++w) {
+    const int64_t hh = (int64_t)blockIdx.x * kWaves + w;
+    if (hh < a.n_heads && P.ntile[hh] == -1) {
+      AttnArgs a1 = a;
+      a1.S = 1;
+      attend_one_head<T, D, POW2, BUF>(Q, K, V, sel, cnt, O, nullptr, a1, hh, 0);
+    }
+  }
 }
 
 template <typename T, int D, bool POW2, bool BUF>
@@ -1152,7 +1166,7 @@ int launch_blk(const AttnArgs& a, const void* Q, const void* K, const void* V, c
   blk_attn_kernel<D, BUF><<<kBlkGrid, 256, 0, s>>>(
       reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K),
       reinterpret_cast<const bf16_t*>(V), a, L, scr);
-  blk_merge_kernel<T, D, POW2, BUF><<<(unsigned)a.n_heads, kThreads, 0, s>>>(
+  blk_merge_kernel<T, D, POW2, BUF><<<wave_blocks, kThreads, 0, s>>>(
       reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
       reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), a, L, scr);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
