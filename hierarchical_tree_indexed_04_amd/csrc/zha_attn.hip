@@ -893,13 +893,13 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
   constexpr int NTD = D / 16;  // 16-column tiles of O
   constexpr int SEG = D / 8;   // 16-byte segments per row
   constexpr int KROW = D + 8;  // padded LDS row of K (bf16 elements)
-  constexpr int VTROW = kBlkGroup + 4;  // padded LDS row of V^T (bf16 elements)
+  constexpr int VTW = kBlkGroup / 2 + 1;  // LDS row of V^T in 32-bit words (token pairs), padded
   BlkPtrs P(scr, L);
   __shared__ int32_t s_head[kBlkQ], s_slot[kBlkQ];
   __shared__ unsigned long long s_mask[kBlkQ];
   __shared__ unsigned long long s_union;
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kBlkGroup * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VTROW];
+  __shared__ uint32_t s_vt[D * VTW];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const float inv = 1.0f / sqrtf((float)D);
@@ -958,44 +958,53 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
 
     // 32-token steps that some head of the block selected; the rows of the
     // next such step are loaded into registers while the current one computes.
-    constexpr int RPP = 256 / SEG;            // rows per staging pass
-    constexpr int NPASS = kBlkGroup / RPP;
-    const int sg = tid % SEG, r0 = tid / SEG;
+    // Staging thread (row pair rp, 16-byte segment sg) holds rows 2 rp, 2 rp + 1,
+    // so V^T is written as 32-bit words of two tokens.  C is a power of two here.
+    constexpr int NRP = kBlkGroup / 2;
+    const int sg = tid % SEG, rp = tid / SEG;
+    const bool stager = rp < NRP;
+    const int lc = a.log2C;
     auto next_step = [&](int g) {
       for (; g < tok_end; g += kBlkGroup) {
-        const int cf = g / C - chunk0, cl = (min(g + kBlkGroup, tok_end) - 1) / C - chunk0;
+        const int cf = (g >> lc) - chunk0, cl = ((min(g + kBlkGroup, tok_end) - 1) >> lc) - chunk0;
         const uint64_t bits = (cl >= 63 ? ~0ull : ((1ull << (cl + 1)) - 1)) & ~((1ull << cf) - 1);
         if ((uni & bits) != 0ull) break;
       }
       return g;
     };
-    uint4 pk[NPASS], pv[NPASS];
+    uint4 pk[2], pv[2];
     auto fetch = [&](int g) {
 #pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        const int tok = g + r0 + p * RPP;
-        kvb.load(kvb.key_row(tok / C, tok % C), tok < tok_end, pk[p], pv[p]);
+      for (int p = 0; p < 2; ++p) {
+        const int tok = g + 2 * rp + p;
+        kvb.load(kvb.key_row(tok >> lc, tok & (C - 1)), stager && tok < tok_end, pk[p], pv[p]);
       }
     };
+    const bool wave_live = wave * 16 < ne;
     int g0 = next_step(tok0);
     if (g0 < tok_end) fetch(g0);
     while (g0 < tok_end) {
       // Stage: K rows as they are, V rows transposed (dimension-major).
       __syncthreads();
+      if (stager) {
 #pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        const int r = r0 + p * RPP;
-        *reinterpret_cast<uint4*>(&s_k[r * KROW + sg * 8]) = pk[p];
-        const uint32_t vw[4] = {pv[p].x, pv[p].y, pv[p].z, pv[p].w};
+        for (int p = 0; p < 2; ++p) *reinterpret_cast<uint4*>(&s_k[(2 * rp + p) * KROW + sg * 8]) = pk[p];
+        const uint32_t v0[4] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w};
+        const uint32_t v1[4] = {pv[1].x, pv[1].y, pv[1].z, pv[1].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s_vt[(sg * 8 + 2 * e) * VTROW + r] = (uint16_t)(vw[e] & 0xffffu);
-          s_vt[(sg * 8 + 2 * e + 1) * VTROW + r] = (uint16_t)(vw[e] >> 16);
+          const int dim = sg * 8 + 2 * e;
+          s_vt[dim * VTW + rp] = (v0[e] & 0xffffu) | (v1[e] << 16);
+          s_vt[(dim + 1) * VTW + rp] = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
         }
       }
       __syncthreads();
       const int gnext = next_step(g0 + kBlkGroup);
       if (gnext < tok_end) fetch(gnext);
+      if (!wave_live) {  // this wave's 16 rows are past the block's heads
+        g0 = gnext;
+        continue;
+      }
       // S^T = K Q^T for the two 16-token halves of the step.
       f32x4_t st[2];
 #pragma unroll
@@ -1011,13 +1020,14 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
       // Lane (li, lg) holds head li's scores for tokens nt * 16 + 4 lg + e.
       float x[8];
       float mloc = -INFINITY;
+      const int nvalid = tok_end - g0;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int tok = g0 + nt * 16 + 4 * lg + e;
-          const int ch = tok / C - chunk0;
-          const bool on = qvalid && tok < tok_end && ((qmask >> ch) & 1ull) != 0ull;
+          const int t = nt * 16 + 4 * lg + e;
+          const int ch = ((g0 + t) >> lc) - chunk0;
+          const bool on = qvalid && t < nvalid && ((qmask >> ch) & 1ull) != 0ull;
           const float v = on ? st[nt][e] * inv : -INFINITY;
           x[nt * 4 + e] = v;
           mloc = fmaxf(mloc, v);
@@ -1049,10 +1059,8 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
         for (int e = 0; e < 4; ++e) o[n][e] *= sr[e];
         // B = V in the same token order: tokens 4 lg' + (0..3) and 16 + 4 lg' + (0..3)
         // of column n * 16 + li.
-        const uint16_t* vr = &s_vt[(n * 16 + li) * VTROW];
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * lg);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * lg);
-        const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        const uint32_t* vr = &s_vt[(n * 16 + li) * VTW];
+        const uint4 vb = make_uint4(vr[2 * lg], vr[2 * lg + 1], vr[8 + 2 * lg], vr[9 + 2 * lg]);
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, vb), o[n],
                                                        0, 0, 0);
       }
