@@ -75,14 +75,17 @@ int check_kv(const zha_geom* g, const void* K, const void* V) {
 }
 
 
-int dense_splits(const zha_geom* g, int32_t n_pos) {
+// Splits per dense-decode unit (and tokens per split on the matrix-core path).
+DensePlan dense_plan(const zha_geom* g, int32_t n_pos) {
+  if (dense_mfma_eligible(g->dtype, g->d))
+    return dense_mfma_plan((int64_t)g->B * g->H_kv, (int64_t)n_pos * (g->H_q / g->H_kv), g->T);
   const int64_t groups = (int64_t)g->B * n_pos * g->H_kv * (g->H_q / g->H_kv / dense_head_tile(g->H_q / g->H_kv));
   int64_t s = (4096 + groups - 1) / groups;
   const int64_t smax = (g->T + 255) / 256;
   if (s > smax) s = smax;
   if (s > 65535) s = 65535;
   if (s < 1) s = 1;
-  return (int)s;
+  return DensePlan{(int32_t)s, 0};
 }
 
 }  // namespace
@@ -235,7 +238,7 @@ int zha_dense_decode_scratch_bytes(const zha_geom* g, int32_t n_pos, size_t* byt
   if (bytes == nullptr) return ZHA_ERR_NULL;
   if (n_pos < 1) return ZHA_ERR_NPOS;
   const int64_t n_heads = (int64_t)g->B * n_pos * g->H_q;
-  *bytes = (size_t)splitkv_scratch_bytes(n_heads, dense_splits(g, n_pos), g->d);
+  *bytes = (size_t)splitkv_scratch_bytes(n_heads, dense_plan(g, n_pos).S, g->d);
   return ZHA_OK;
 }
 
@@ -251,7 +254,9 @@ int zha_dense_decode(const zha_geom* g, const void* Q, int32_t n_pos, const void
   a.H_q = g->H_q;
   a.H_kv = g->H_kv;
   a.G = g->H_q / g->H_kv;
-  a.S = dense_splits(g, n_pos);
+  const DensePlan plan = dense_plan(g, n_pos);
+  a.S = plan.S;
+  a.tps = plan.tps;
   a.C = g->C;
   a.log2C = log2_or_neg(g->C);
   a.chunked = g->kv_layout == ZHA_KV_CHUNKED;

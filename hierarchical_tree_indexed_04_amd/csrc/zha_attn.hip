@@ -189,48 +189,67 @@ __device__ __forceinline__ void online_update(float& m, float& l, float* acc, co
   m = mloc;
 }
 
-// Merge of the S split partials of one head, in split order:
-// O = sum_s e^{M_s - M} acc_s / sum_s e^{M_s - M} l_s.  Partials are read kSB
-// at a time with independent loads (one memory round trip per batch); with
-// more than kSB partials the running sums are rescaled to each batch's max.
+// Merge of S split partials (o unnormalised, m, l) of one head by the whole
+// workgroup: thread (column pair c, group g) folds partials g, g + NG, ... with
+// a running maximum (loads issued kSB at a time), then group 0 combines the NG
+// group results from LDS, in group order.  Block-uniform call (one barrier).
 template <typename T, int D>
 __device__ __forceinline__ void merge_partials(const float* part_head, int S, T* out_row) {
-  constexpr int kSB = 4;
-  const float* __restrict__ p = part_head;
-  for (int t = threadIdx.x; t < D; t += kThreads) {
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int s0 = 0; s0 < S; s0 += kSB) {
-      float ms[kSB], ls[kSB], as[kSB];
+  constexpr int NC = D / 2;           // column pairs (rows of D + 2 floats are 8-byte aligned)
+  constexpr int NG = kThreads / NC;   // partial groups
+  constexpr int kSB = 8;
+  __shared__ float s_M[NG], s_den[NG];
+  __shared__ float2 s_num[NG][NC];
+  const int c = threadIdx.x % NC, g = threadIdx.x / NC;
+  float M = -INFINITY, den = 0.f;
+  float2 num = make_float2(0.f, 0.f);
+  for (int s0 = g; s0 < S; s0 += NG * kSB) {
+    float2 ml[kSB], av[kSB];
 #pragma unroll
-      for (int j = 0; j < kSB; ++j) {
-        const int s = s0 + j;
-        if (s < S) {
-          const float* r = p + (int64_t)s * (D + 2);
-          ms[j] = r[D];
-          ls[j] = r[D + 1];
-          as[j] = r[t];
-        } else {
-          ms[j] = -INFINITY;
-          ls[j] = 0.f;
-          as[j] = 0.f;
-        }
-      }
-      float Mn = M;
-#pragma unroll
-      for (int j = 0; j < kSB; ++j) Mn = fmaxf(Mn, ms[j]);
-      if (Mn == -INFINITY) continue;
-      const float r = (M == -INFINITY) ? 0.f : __expf(M - Mn);
-      num *= r;
-      den *= r;
-#pragma unroll
-      for (int j = 0; j < kSB; ++j) {
-        const float w = (ms[j] == -INFINITY) ? 0.f : __expf(ms[j] - Mn);
-        num = fmaf(w, as[j], num);
-        den = fmaf(w, ls[j], den);
-      }
-      M = Mn;
+    for (int j = 0; j < kSB; ++j) {
+      const int s = s0 + j * NG;
+      const float* r = part_head + (int64_t)min(s, S - 1) * (D + 2);
+      ml[j] = *reinterpret_cast<const float2*>(r + D);
+      av[j] = *reinterpret_cast<const float2*>(r + 2 * c);
+      if (s >= S) ml[j].x = -INFINITY;
     }
-    store_elem(out_row, t, num / den);
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kSB; ++j) Mn = fmaxf(Mn, ml[j].x);
+    if (Mn == -INFINITY) continue;
+    const float rs = M == -INFINITY ? 0.f : __expf(M - Mn);
+    num.x *= rs;
+    num.y *= rs;
+    den *= rs;
+#pragma unroll
+    for (int j = 0; j < kSB; ++j) {
+      const float w = ml[j].x == -INFINITY ? 0.f : __expf(ml[j].x - Mn);
+      num.x = fmaf(w, av[j].x, num.x);
+      num.y = fmaf(w, av[j].y, num.y);
+      den = fmaf(w, ml[j].y, den);
+    }
+    M = Mn;
+  }
+  if (c == 0) {
+    s_M[g] = M;
+    s_den[g] = den;
+  }
+  s_num[g][c] = num;
+  __syncthreads();
+  if (g == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) Mt = fmaxf(Mt, s_M[k]);
+    float nx = 0.f, ny = 0.f, dt = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const float w = s_M[k] == -INFINITY ? 0.f : __expf(s_M[k] - Mt);
+      nx = fmaf(w, s_num[k][c].x, nx);
+      ny = fmaf(w, s_num[k][c].y, ny);
+      dt = fmaf(w, s_den[k], dt);
+    }
+    store_elem(out_row, 2 * c, nx / dt);
+    store_elem(out_row, 2 * c + 1, ny / dt);
   }
 }
 
@@ -1229,6 +1248,251 @@ int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
 }
 
+// Dense decode on the matrix cores (bf16 caches, d in {64, 128}).  S waves
+// per (KV cache, 16 query rows); wave s takes the 32-token steps s, s + S,
+// s + 2S, ... (so the grid sweeps each cache nearly in address order, which
+// measured faster than one contiguous range per wave).  The waves share
+// nothing, so the token loop has no workgroup barrier.  Per step:
+//   S^T = K Q^T with v_mfma_f32_16x16x32_bf16: K rows go from memory straight
+//   into the A operand (lane i + 16 g holds dims 32 ks + 8 g .. + 7 of token
+//   i), Q is the B operand, held for the whole range;
+//   P V with the same instruction: a lane's 8 probabilities (one query row,
+//   tokens 16 nt + 4 g + e) are its A operand, and V reaches the B operand
+//   transposed through a wave-private LDS area, as 32-bit words holding one
+//   dimension of two consecutive tokens.
+// The next step's rows are loaded before the current step computes; their
+// token indices are clamped into the cache, so every load is unconditional
+// and each wait counts exactly the loads issued after it (rows past the range
+// are masked).  The output rescale runs only when some row's maximum moved.
+// LAY: 0 split caches, 1 chunked with C a power of two, 2 chunked otherwise.
+#ifndef ZHA_DENSE_STRIDED
+#define ZHA_DENSE_STRIDED 1
+#endif
+template <int D, int LAY>
+__global__ __launch_bounds__(256) void dense_mfma_kernel(const bf16_t* __restrict__ Q,
+                                                         const bf16_t* __restrict__ K,
+                                                         const bf16_t* __restrict__ V,
+                                                         bf16_t* __restrict__ O,
+                                                         float* __restrict__ part, DenseArgs a) {
+  constexpr int KS = D / 32;   // k-steps of S^T, and 16-byte V segments per lane and row
+  constexpr int NTD = D / 16;  // 16-column tiles of O
+  constexpr int VTW = 17;      // LDS row of V^T in 32-bit words (16 token pairs), padded
+  __shared__ uint32_t s_vt[4][D * VTW];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int R = a.n_pos * a.G;  // query rows per KV cache
+  const int RT = (R + 15) >> 4;
+  const int64_t n_trees = a.n_heads / ((int64_t)a.n_pos * a.H_q) * a.H_kv;
+  const int64_t item = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave);
+  if (item >= n_trees * RT * a.S) return;  // the whole wave; no workgroup barrier follows
+  const int split = (int)(item % a.S);
+  const int64_t rest = item / a.S;
+  const int rt = (int)(rest % RT);
+  const int64_t tr = rest / RT;
+  const int64_t b = tr / a.H_kv;
+  const int kvh = (int)(tr - b * a.H_kv);
+  auto head_of = [&](int r) {
+    return (b * a.n_pos + r / a.G) * a.H_q + (int64_t)kvh * a.G + r % a.G;
+  };
+  const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
+  const char* Kc = reinterpret_cast<const char*>(K + tr * nblk);
+  const char* Vc = reinterpret_cast<const char*>(LAY != 0 ? K + tr * nblk + (int64_t)a.C * D
+                                                          : V + tr * nblk);
+  // Steps of this wave: 32-token blocks at g = gbase + i gstride, i < ns, tokens
+  // below lim.  Interleaved: the S waves of a (cache, 16 rows) take every S-th
+  // step, so the whole grid sweeps the cache nearly in address order.
+  const int T = (int)a.T;
+#if ZHA_DENSE_STRIDED
+  const int gbase = split * 32, gstride = a.S * 32, lim = T;
+  const int ns = ((T + 31) / 32 - split + a.S - 1) / a.S;
+#else
+  const int gbase = (int)(split * a.tps), gstride = 32, lim = (int)min((int64_t)gbase + a.tps, a.T);
+  const int ns = (lim - gbase + 31) / 32;
+#endif
+  // First row of the step (wave-uniform) and 32-bit byte offsets of its tokens.
+  auto row0 = [&](int g) -> int64_t {
+    if constexpr (LAY == 1) return (int64_t)g + ((g >> a.log2C) << a.log2C);
+    if constexpr (LAY == 2) return (int64_t)g + (int64_t)(g / a.C) * a.C;
+    return g;
+  };
+  auto off_of = [&](int g, int v) -> uint32_t {  // token g + v, clamped below lim
+    v = min(v, lim - 1 - g);
+    if constexpr (LAY == 1) v += (((g & (a.C - 1)) + v) >> a.log2C) << a.log2C;
+    if constexpr (LAY == 2) v += ((g % a.C) + v) / a.C * a.C;
+    return (uint32_t)v * (uint32_t)(D * 2);
+  };
+
+  // Q rows as the B operand: lane (li, lg) holds row li's dims 32 ks + 8 lg .. + 7.
+  const int qr = rt * 16 + li;
+  bf16x8_t qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (qr < R) v = ld16c(Q + head_of(qr) * D + ks * 32 + lg * 8);
+    qb[ks] = __builtin_bit_cast(bf16x8_t, v);
+  }
+
+  // V staging: lane (li, lg) holds rows 2 li and 2 li + 1 of the step, 16-byte
+  // segments lg + 4 s; K: lane (li, lg) holds row nt * 16 + li, segments lg + 4 ks.
+  uint4 kb[2 * KS], vb[2 * KS];
+  auto load_v = [&](int g) {
+    const char* vbase = Vc + row0(g) * (D * 2);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const char* vr = vbase + (off_of(g, 2 * li + p) + lg * 16);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) vb[p * KS + s] = ld16(vr + s * 64);
+    }
+  };
+  auto load_k = [&](int g) {
+    const char* kbase = Kc + row0(g) * (D * 2);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const char* kr = kbase + (off_of(g, nt * 16 + li) + lg * 16);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kb[nt * KS + ks] = ld16(kr + ks * 64);
+    }
+  };
+  uint32_t* vt = s_vt[wave];
+  auto stage_v = [&]() {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t v0[4] = {vb[s].x, vb[s].y, vb[s].z, vb[s].w};
+      const uint32_t v1[4] = {vb[KS + s].x, vb[KS + s].y, vb[KS + s].z, vb[KS + s].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int dim = (lg + 4 * s) * 8 + 2 * e;
+        vt[dim * VTW + li] = (v0[e] & 0xffffu) | (v1[e] << 16);
+        vt[(dim + 1) * VTW + li] = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
+      }
+    }
+  };
+
+  const float c2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
+  float m_i = -INFINITY, l_i = 0.f;  // m in raw score units; l summed per lane
+  f32x4_t o[NTD];
+#pragma unroll
+  for (int n = 0; n < NTD; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Step i: stage V(i); load V(i + 1); S^T from K(i); load K(i + 1) into the
+  // same registers; softmax and P V.  Loads are issued V before K, so each
+  // wait leaves the other tensor's loads in flight.  LDS accesses of one wave
+  // complete in order; the empty asm statements keep the compiler from moving
+  // them across steps.
+  load_v(gbase);
+  __builtin_amdgcn_sched_barrier(0);
+  load_k(gbase);
+  for (int i = 0; i < ns; ++i) {
+    const int g = gbase + i * gstride;
+    const int gn = i + 1 < ns ? g + gstride : g;  // past the last step: its rows again
+    asm volatile("" ::: "memory");
+    stage_v();
+    asm volatile("" ::: "memory");
+    load_v(gn);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t st[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      st[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[nt * KS + ks]),
+                                                        qb[ks], st[nt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(gn);
+    __builtin_amdgcn_sched_barrier(0);
+    const int nvalid = lim - g;
+    float x[8], mloc = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = nt * 16 + 4 * lg + e < nvalid ? st[nt][e] : -INFINITY;
+        x[nt * 4 + e] = v;
+        mloc = fmaxf(mloc, v);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    const float m_new = fmaxf(m_i, mloc);
+    if (__ballot(m_new != m_i) != 0ull) {  // some row's maximum moved: rescale
+      const float sc = m_i == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_i - m_new) * c2);
+      l_i *= sc;
+      float sr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sr[e] = __shfl(sc, 4 * lg + e, kWave);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[n][e] *= sr[e];
+      m_i = m_new;
+    }
+    const float mc = m_i == -INFINITY ? 0.f : m_i * c2;
+    bf16x8_t pa;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pj = __builtin_amdgcn_exp2f(fmaf(x[j], c2, -mc));
+      l_i += pj;
+      pa[j] = (__bf16)pj;
+    }
+#pragma unroll
+    for (int n = 0; n < NTD; ++n) {
+      const uint32_t* vr = &vt[(n * 16 + li) * VTW];
+      const uint4 w = make_uint4(vr[2 * lg], vr[2 * lg + 1], vr[8 + 2 * lg], vr[9 + 2 * lg]);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, w), o[n], 0,
+                                                     0, 0);
+    }
+  }
+
+  l_i += __shfl_xor(l_i, 16, kWave);
+  l_i += __shfl_xor(l_i, 32, kWave);
+  // O rows 4 lg + e, columns 16 n + li.
+  float lr[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lr[e] = __shfl(l_i, 4 * lg + e, kWave);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = rt * 16 + 4 * lg + e;
+    if (r >= R) continue;
+    const int64_t h = head_of(r);
+    if (a.S == 1) {
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) store_elem(O + h * D, n * 16 + li, o[n][e] / lr[e]);
+    } else {
+      float* pr = part + (h * a.S + split) * (D + 2);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) pr[n * 16 + li] = o[n][e];
+    }
+  }
+  if (a.S > 1 && lg == 0 && qr < R) {
+    float* pr = part + (head_of(qr) * a.S + split) * (D + 2);
+    pr[D] = m_i * (1.0f / sqrtf((float)D));
+    pr[D + 1] = l_i;
+  }
+}
+
+template <int D>
+int launch_dense_mfma(const DenseArgs& a, const void* Q, const void* K, const void* V, void* O,
+                      void* scratch, hipStream_t s) {
+  const int64_t n_trees = a.n_heads / ((int64_t)a.n_pos * a.H_q) * a.H_kv;
+  const int64_t items = n_trees * ((a.n_pos * a.G + 15) / 16) * a.S;
+  float* part = reinterpret_cast<float*>(scratch);
+#define ZHA_DM(LAY)                                                                   \
+  dense_mfma_kernel<D, LAY><<<(unsigned)((items + 3) / 4), 256, 0, s>>>(                \
+      reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K),           \
+      reinterpret_cast<const bf16_t*>(V), reinterpret_cast<bf16_t*>(O), part, a)
+  if (!a.chunked) ZHA_DM(0);
+  else if (a.log2C >= 0) ZHA_DM(1);
+  else ZHA_DM(2);
+#undef ZHA_DM
+  if (a.S > 1) {
+    if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
+    merge_kernel<bf16_t, D><<<(unsigned)a.n_heads, kThreads, 0, s>>>(
+        part, nullptr, 0, reinterpret_cast<bf16_t*>(O), a.S);
+  }
+  return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
+}
+
 template <typename T, int D, int GT>
 int launch_dense_gt(const DenseArgs& a, const void* Q, const void* K, const void* V, void* O,
                     void* scratch, hipStream_t s) {
@@ -1249,6 +1513,8 @@ int launch_dense_gt(const DenseArgs& a, const void* Q, const void* K, const void
 template <typename T, int D>
 int launch_dense(const DenseArgs& a, const void* Q, const void* K, const void* V, void* O,
                  void* scratch, hipStream_t s) {
+  if constexpr (sizeof(T) == 2 && (D == 64 || D == 128))
+    return launch_dense_mfma<D>(a, Q, K, V, O, scratch, s);
   const int gt = dense_head_tile(a.G);
   if (gt == 8) return launch_dense_gt<T, D, 8>(a, Q, K, V, O, scratch, s);
   if (gt == 4) return launch_dense_gt<T, D, 4>(a, Q, K, V, O, scratch, s);

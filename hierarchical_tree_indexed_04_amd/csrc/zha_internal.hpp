@@ -127,6 +127,7 @@ struct AttnArgs {
 
 struct DenseArgs {
   int64_t T;
+  int64_t tps;  // tokens per split (matrix-core path; a multiple of 32)
   int64_t n_heads;
   int32_t n_pos;
   int32_t H_q;
@@ -180,6 +181,34 @@ int attn_dispatch(const AttnArgs& a, int dtype, int d, const void* Q, const void
                   hipStream_t s);
 int dense_dispatch(const DenseArgs& a, int dtype, int d, const void* Q, const void* K,
                    const void* V, void* O, void* scratch, hipStream_t s);
+
+// Dense decode on the matrix cores (bf16, d in {64, 128}): S waves per (KV
+// cache, 16 query rows), each taking whole 32-token steps; S makes about
+// ZHA_DENSE_WAVES waves in all (two per SIMD on 256 CUs), none without a step.
+#ifndef ZHA_DENSE_WAVES
+#define ZHA_DENSE_WAVES 2048
+#endif
+inline bool dense_mfma_eligible(int dtype, int d) {
+  return dtype == ZHA_BF16 && (d == 64 || d == 128);
+}
+struct DensePlan {
+  int32_t S;    // splits per (cache, 16 rows)
+  int64_t tps;  // tokens per split
+};
+inline DensePlan dense_mfma_plan(int64_t n_trees, int64_t rows, int64_t T) {
+  const int64_t units = n_trees * ((rows + 15) / 16);
+  int64_t s = (ZHA_DENSE_WAVES + units - 1) / units;
+  const int64_t steps = (T + 31) / 32;
+  if (s > steps) s = steps;
+  if (s > 65535) s = 65535;
+  if (s < 1) s = 1;
+  // At most 2^22 tokens per split: the kernel addresses a split's rows with
+  // 32-bit byte offsets (chunked caches span twice the rows).
+  const int64_t smin = (T + (1 << 22) - 1) >> 22;
+  if (s < smin) s = smin;
+  const int64_t tps = ((T + s - 1) / s + 31) / 32 * 32;
+  return DensePlan{(int32_t)((T + tps - 1) / tps), tps};
+}
 
 // Split-KV scratch: fp32 partials [n_heads, S, d + 2] (S == 1 needs none).
 inline int64_t splitkv_scratch_bytes(int64_t n_heads, int S, int d) {

@@ -257,6 +257,37 @@ def test_dense_decode_matches_oracle(Z, cfg, chunked):
     assert worst <= TOL[g.dtype]
 
 
+@pytest.mark.parametrize("name,kw,n_pos,chunked", [
+    # d = 64, T not a multiple of 32 (a partial last step), 6 query rows per cache
+    ("d64-ragged", dict(B=2, H_q=4, H_kv=2, d=64, T=1000, C=8, L=2), 3, False),
+    # 40 query rows per cache (three 16-row tiles, the last partial), C = 6 chunked
+    ("rows40-c6", dict(B=1, H_q=8, H_kv=1, T=6 ** 3 * 7 + 5, C=6, L=3), 5, True),
+    # fewer than 32 tokens: a single split, written without partials
+    ("one-split", dict(B=1, H_q=2, H_kv=1, T=29, C=4, L=1), 1, False),
+    # G = 1, power-of-two C chunked, T past a chunk boundary
+    ("g1-c16", dict(B=3, H_q=2, H_kv=2, T=4096 + 17, C=16, L=2), 2, True),
+])
+def test_dense_decode_shapes(Z, name, kw, n_pos, chunked):
+    say(f"dense decode, {name}: {kw}, n_pos {n_pos}, {'chunked' if chunked else 'split'} KV")
+    g = W.custom(name, 130, dtype=W.BF16, p=0.9, **kw)
+    K, V = W.make_kv(g)
+    Qn = W.make_query_block(g, K, range(n_pos))
+    gm = Z.geom(g, Z.ZHA_KV_CHUNKED if chunked else Z.ZHA_KV_SPLIT)
+    Kd, Vd = to_device(K, g.dtype), to_device(V, g.dtype)
+    if chunked:
+        Kd, Vd = Z.to_chunked(Kd, Vd, g.C), None
+    Og = from_device(Z.dense_decode(gm, to_device(Qn, g.dtype), n_pos, Kd, Vd), g.dtype)
+    worst = 0.0
+    for b in range(g.B):
+        for t in range(n_pos):
+            for h in range(g.H_q):
+                o = O.dense(W.to_float(Qn[b, t, h], g.dtype), W.to_float(K[b, h // g.G], g.dtype),
+                            W.to_float(V[b, h // g.G], g.dtype))
+                worst = max(worst, float(np.abs(Og[b, t, h] - o).max()))
+    say(f"  max abs err {worst:.3g}")
+    assert worst <= TOL[g.dtype]
+
+
 def test_route_and_attn_are_deterministic(Z):
     import torch
     say("determinism: two runs are bit-identical (config 2, 4 steps)")
