@@ -718,7 +718,8 @@ __device__ __forceinline__ int walk_tiles(const int32_t* ids, int c, int CT, F o
 }
 
 // A head's pairs are the tiles of its selected chunks, ascending (its sink and
-// partial-chunk tokens are the merge launch's).  One wave per head: count.
+// partial-chunk tokens are the merge launch's).  One wave per head: count the
+// head's tiles and each tile's pairs.
 __global__ __launch_bounds__(256) void blk_count_kernel(const int32_t* __restrict__ sel,
                                                         const int32_t* __restrict__ cnt,
                                                         AttnArgs a, BlkLayout L, char* scr) {
@@ -728,104 +729,100 @@ __global__ __launch_bounds__(256) void blk_count_kernel(const int32_t* __restric
   if (head >= a.n_heads) return;
   const int c = cnt[head];
   int n = -2;
-  if (c >= 0 && c <= a.cap) n = walk_tiles(sel + head * a.cap, c, L.CT, [](int) {});
+  if (c >= 0 && c <= a.cap) {
+    int32_t* tc = P.tcnt + tree_of_head(head, a) * L.NT;
+    n = walk_tiles(sel + head * a.cap, c, L.CT, [&](int t) { atomicAdd(&tc[t], 1); });
+  }
   if (lane == 0) P.ntile[head] = n;
 }
 
-// One workgroup: slot bases by a prefix sum of (tiles + 1) over the heads;
-// heads whose slots would pass the budget are marked for per-head attention.
-__global__ __launch_bounds__(1024) void blk_slots_kernel(int64_t n_heads, BlkLayout L,
-                                                         char* scr) {
+// One launch, two workgroups.  Workgroup 0: slot bases by a prefix sum of
+// (tiles + 1) over the heads, 8192 heads at a time: coalesced loads (the next
+// chunk's issued before the current one is scanned) go through LDS, each
+// thread then sums 8 consecutive heads, one block scan per chunk.  From the
+// first head whose slots would pass the budget on, heads are marked for
+// per-head attention (their pairs stay counted and become empty entries).
+// Workgroup 1: exclusive scans over the tiles, first entry and first work item
+// of each.
+__global__ __launch_bounds__(1024) void blk_scan_kernel(int64_t n_heads, BlkLayout L, char* scr) {
   BlkPtrs P(scr, L);
-  __shared__ int64_t s_v[1024];
+  __shared__ int64_t s_v[1024], s_w[1024];
   const int tid = threadIdx.x;
-  const int64_t seg = (n_heads + 1023) / 1024;
-  const int64_t i0 = min(n_heads, tid * seg), i1 = min(n_heads, i0 + seg);
-  constexpr int kReg = 32;  // segments up to kReg heads are read in one batch of loads
-  int v[kReg];
-  int64_t sum = 0;
-  if (seg <= kReg) {
+  if (blockIdx.x == 0) {
+    constexpr int kPer = 8;
+    constexpr int kChunk = 1024 * kPer;
+    __shared__ int32_t s_c[kChunk];
+    const int lane = tid & (kWave - 1), wave = tid >> 6;
+    int v[kPer];
 #pragma unroll
-    for (int k = 0; k < kReg; ++k) v[k] = i0 + k < i1 ? P.ntile[i0 + k] : -3;
+    for (int k = 0; k < kPer; ++k) v[k] = P.ntile[min((int64_t)k * 1024 + tid, n_heads - 1)];
+    int64_t run = 0;
+    for (int64_t c0 = 0; c0 < n_heads; c0 += kChunk) {
+      __syncthreads();  // the previous chunk's reads of s_c and s_w are done
 #pragma unroll
-    for (int k = 0; k < kReg; ++k) sum += v[k] >= 0 ? v[k] + 1 : 0;
-  } else {
-    for (int64_t i = i0; i < i1; ++i) sum += P.ntile[i] >= 0 ? P.ntile[i] + 1 : 0;
-  }
-  s_v[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int64_t x = tid >= off ? s_v[tid - off] : 0;
-    __syncthreads();
-    s_v[tid] += x;
-    __syncthreads();
-  }
-  int64_t run = s_v[tid] - sum;
-  auto assign = [&](int64_t i, int n) {
-    if (n < 0) return;
-    if (run + n + 1 > L.S) {
-      P.ntile[i] = -1;
-    } else {
-      P.qbase[i] = (int32_t)run;
-      run += n + 1;
+      for (int k = 0; k < kPer; ++k) s_c[k * 1024 + tid] = v[k];
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        v[k] = P.ntile[min(c0 + kChunk + (int64_t)k * 1024 + tid, n_heads - 1)];
+      int w[kPer];
+      int64_t sum = 0;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        w[k] = c0 + tid * kPer + k < n_heads ? s_c[tid * kPer + k] : -3;
+        sum += w[k] >= 0 ? w[k] + 1 : 0;
+      }
+      const uint64_t incl = wave_incl_scan_u64((uint64_t)sum);
+      if (lane == kWave - 1) s_w[wave] = (int64_t)incl;
+      __syncthreads();
+      int64_t off = 0, tot = 0;
+#pragma unroll
+      for (int x = 0; x < 1024 / kWave; ++x) {
+        off += x < wave ? s_w[x] : 0;
+        tot += s_w[x];
+      }
+      int64_t start = run + off + (int64_t)incl - sum;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        if (w[k] < 0) continue;
+        const int64_t i = c0 + tid * kPer + k;
+        if (start + w[k] + 1 > L.S) P.ntile[i] = -1;
+        else P.qbase[i] = (int32_t)start;
+        start += w[k] + 1;
+      }
+      run += tot;
     }
-  };
-  if (seg <= kReg) {
-#pragma unroll
-    for (int k = 0; k < kReg; ++k)
-      if (i0 + k < i1) assign(i0 + k, v[k]);
-  } else {
-    for (int64_t i = i0; i < i1; ++i) assign(i, P.ntile[i]);
+    return;
   }
-}
-
-// Pairs per tile, for the heads that got slots.
-__global__ __launch_bounds__(256) void blk_tiles_kernel(const int32_t* __restrict__ sel,
-                                                        const int32_t* __restrict__ cnt,
-                                                        AttnArgs a, BlkLayout L, char* scr) {
-  BlkPtrs P(scr, L);
-  const int wave = threadIdx.x >> 6;
-  const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
-  if (head >= a.n_heads) return;
-  if (P.ntile[head] <= 0) return;
-  int32_t* tc = P.tcnt + tree_of_head(head, a) * L.NT;
-  walk_tiles(sel + head * a.cap, cnt[head], L.CT, [&](int t) { atomicAdd(&tc[t], 1); });
-}
-
-// Exclusive scans over the tiles: first entry and first work item of each.
-__global__ __launch_bounds__(1024) void blk_scan_kernel(char* scr, BlkLayout L) {
-  BlkPtrs P(scr, L);
-  __shared__ int32_t s_c[1024], s_w[1024];
-  const int tid = threadIdx.x;
   const int64_t seg = (L.NTT + 1023) / 1024;
   const int64_t i0 = min(L.NTT, tid * seg), i1 = min(L.NTT, i0 + seg);
-  int sc = 0, sw = 0;
+  int64_t sc = 0, sw = 0;
   for (int64_t i = i0; i < i1; ++i) {
     sc += P.tcnt[i];
     sw += (P.tcnt[i] + kBlkQ - 1) / kBlkQ;
   }
-  s_c[tid] = sc;
+  s_v[tid] = sc;
   s_w[tid] = sw;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the 1024 segment sums
-    const int vc = tid >= off ? s_c[tid - off] : 0;
-    const int vw = tid >= off ? s_w[tid - off] : 0;
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the 1024 run sums
+    const int64_t vc = tid >= off ? s_v[tid - off] : 0;
+    const int64_t vw = tid >= off ? s_w[tid - off] : 0;
     __syncthreads();
-    s_c[tid] += vc;
+    s_v[tid] += vc;
     s_w[tid] += vw;
     __syncthreads();
   }
-  int rc = s_c[tid] - sc, rw = s_w[tid] - sw;
+  int64_t rc = s_v[tid] - sc, rw = s_w[tid] - sw;
   for (int64_t i = i0; i < i1; ++i) {
-    P.toff[i] = rc;
-    P.wpre[i] = rw;
+    P.toff[i] = (int32_t)rc;
+    P.wpre[i] = (int32_t)rw;
     rc += P.tcnt[i];
     rw += (P.tcnt[i] + kBlkQ - 1) / kBlkQ;
   }
   if (tid == 1023) {
-    P.toff[L.NTT] = s_c[1023];
-    P.wpre[L.NTT] = s_w[1023];
-    P.ctrl[0] = s_w[1023];
+    P.toff[L.NTT] = (int32_t)s_v[1023];
+    P.wpre[L.NTT] = (int32_t)s_w[1023];
+    P.ctrl[0] = (int32_t)s_w[1023];
   }
 }
 
@@ -846,20 +843,22 @@ __global__ __launch_bounds__(256) void blk_fill_kernel(const int32_t* __restrict
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
   if (head >= a.n_heads) return;
-  if (P.ntile[head] <= 0) return;
+  const int nt = P.ntile[head];
+  if (nt == 0 || nt == -2) return;
+  const bool live = nt > 0;  // -1: past the slot budget, its pairs become empty entries
   const int c = cnt[head];
   const int32_t* ids = sel + head * a.cap;
   const int CT = L.CT;
   const int64_t tb = tree_of_head(head, a) * L.NT;
-  const int slot0 = P.qbase[head];
+  const int slot0 = live ? P.qbase[head] : 0;
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
   auto emit = [&](int tile, uint64_t mask, int k) {
     const int pos = P.toff[tb + tile] + atomicAdd(&P.tcur[tb + tile], 1);
     int32_t* e = P.ent + (int64_t)pos * kBlkEntryInts;
-    e[0] = (int32_t)head;
-    e[1] = slot0 + k;
-    e[2] = (int32_t)(uint32_t)mask;
-    e[3] = (int32_t)(uint32_t)(mask >> 32);
+    e[0] = live ? (int32_t)head : -1;
+    e[1] = live ? slot0 + k : -1;
+    e[2] = live ? (int32_t)(uint32_t)mask : 0;
+    e[3] = live ? (int32_t)(uint32_t)(mask >> 32) : 0;
   };
   int k = 0, cur = -1;  // tiles emitted; tile carried from the previous batch
   uint64_t carry = 0;
@@ -903,8 +902,11 @@ __global__ __launch_bounds__(256) void blk_fill_kernel(const int32_t* __restrict
 // scores already sit in registers.  Operand layouts (gfx950, checked):
 // A[i][k] in lane i + 16 (k / 8), element k % 8; B[k][j] in lane j + 16 (k / 8),
 // element k % 8; D[i][j] in lane j + 16 (i / 4), element i % 4.
+#ifndef ZHA_BLK_WAVES_EU
+#define ZHA_BLK_WAVES_EU 3  // waves per SIMD the register budget is held to
+#endif
 template <int D, bool BUF>
-__global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict__ Q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAVES_EU, ZHA_BLK_WAVES_EU))) void blk_attn_kernel(const bf16_t* __restrict__ Q,
                                                        const bf16_t* __restrict__ K,
                                                        const bf16_t* __restrict__ V, AttnArgs a,
                                                        BlkLayout L, char* scr) {
@@ -961,7 +963,7 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
 
     // This lane's head (row li of the wave's 16): its Q slices as the B operand.
     const int qi = wave * 16 + li;
-    const bool qvalid = qi < ne;
+    const bool qvalid = qi < ne && s_head[qi] >= 0;  // empty entries have head -1, mask 0
     const uint64_t qmask = s_mask[qi];
     bf16x8_t qb[KS];
 #pragma unroll
@@ -970,13 +972,11 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
       if (qvalid) v = ld16c(Q + (int64_t)s_head[qi] * D + ks * 32 + lg * 8);
       qb[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
-    float m_i = -INFINITY, l_i = 0.f;
     f32x4_t o[NTD];
 #pragma unroll
     for (int n = 0; n < NTD; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // 32-token steps that some head of the block selected; the rows of the
-    // next such step are loaded into registers while the current one computes.
+    // 32-token steps that some head of the block selected.
     // Staging thread (row pair rp, 16-byte segment sg) holds rows 2 rp, 2 rp + 1,
     // so V^T is written as 32-bit words of two tokens.  C is a power of two here.
     constexpr int NRP = kBlkGroup / 2;
@@ -991,20 +991,20 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
       }
       return g;
     };
-    uint4 pk[2], pv[2];
-    auto fetch = [&](int g) {
+    // Two register sets of staged rows: the next two steps are in flight while
+    // one computes.  A set past the last step loads nothing (out-of-range
+    // buffer offsets), so the loads are unconditional and every wait counts
+    // exactly the loads issued after the ones it needs.
+    uint4 ka[2], va[2], kb[2], vb[2];
+    auto fetch = [&](uint4 (&pk)[2], uint4 (&pv)[2], int g) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int tok = g + 2 * rp + p;
         kvb.load(kvb.key_row(tok >> lc, tok & (C - 1)), stager && tok < tok_end, pk[p], pv[p]);
       }
     };
-    const bool wave_live = wave * 16 < ne;
-    int g0 = next_step(tok0);
-    if (g0 < tok_end) fetch(g0);
-    while (g0 < tok_end) {
-      // Stage: K rows as they are, V rows transposed (dimension-major).
-      __syncthreads();
+    // Stage: K rows as they are, V rows transposed (dimension-major).
+    auto stage = [&](const uint4 (&pk)[2], const uint4 (&pv)[2]) {
       if (stager) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) *reinterpret_cast<uint4*>(&s_k[(2 * rp + p) * KROW + sg * 8]) = pk[p];
@@ -1017,13 +1017,10 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
           s_vt[(dim + 1) * VTW + rp] = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
         }
       }
-      __syncthreads();
-      const int gnext = next_step(g0 + kBlkGroup);
-      if (gnext < tok_end) fetch(gnext);
-      if (!wave_live) {  // this wave's 16 rows are past the block's heads
-        g0 = gnext;
-        continue;
-      }
+    };
+    const float c2 = 1.4426950408889634f * inv;  // log2(e) / sqrt(d)
+    float m_i = -INFINITY, l_i = 0.f;  // m in raw score units; l summed per lane
+    auto compute = [&](int g0) {
       // S^T = K Q^T for the two 16-token halves of the step.
       f32x4_t st[2];
 #pragma unroll
@@ -1047,50 +1044,76 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
           const int t = nt * 16 + 4 * lg + e;
           const int ch = ((g0 + t) >> lc) - chunk0;
           const bool on = qvalid && t < nvalid && ((qmask >> ch) & 1ull) != 0ull;
-          const float v = on ? st[nt][e] * inv : -INFINITY;
+          const float v = on ? st[nt][e] : -INFINITY;
           x[nt * 4 + e] = v;
           mloc = fmaxf(mloc, v);
         }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
       const float m_new = fmaxf(m_i, mloc);
-      const float mref = m_new == -INFINITY ? 0.f : m_new;
-      const float scale = __expf(m_i - mref);
-      float psum = 0.f;
+      if (__ballot(m_new != m_i) != 0ull) {  // some head's maximum moved: rescale
+        const float sc = m_i == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_i - m_new) * c2);
+        l_i *= sc;
+        // O rows 4 lg + e belong to heads 4 lg + e: rescale by their factors.
+        float sr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sr[e] = __shfl(sc, 4 * lg + e, kWave);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[n][e] *= sr[e];
+        m_i = m_new;
+      }
+      const float mc = m_i == -INFINITY ? 0.f : m_i * c2;
       bf16x8_t pa;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pj = __expf(x[j] - mref);
-        psum += pj;
+        const float pj = __builtin_amdgcn_exp2f(fmaf(x[j], c2, -mc));
+        l_i += pj;
         pa[j] = (__bf16)pj;
       }
-      psum += __shfl_xor(psum, 16, kWave);
-      psum += __shfl_xor(psum, 32, kWave);
-      l_i = l_i * scale + psum;
-      m_i = m_new;
-      // O rows 4 lg + e belong to heads 4 lg + e: rescale by their factors.
-      float sr[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sr[e] = __shfl(scale, 4 * lg + e, kWave);
 #pragma unroll
       for (int n = 0; n < NTD; ++n) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[n][e] *= sr[e];
         // B = V in the same token order: tokens 4 lg' + (0..3) and 16 + 4 lg' + (0..3)
         // of column n * 16 + li.
         const uint32_t* vr = &s_vt[(n * 16 + li) * VTW];
-        const uint4 vb = make_uint4(vr[2 * lg], vr[2 * lg + 1], vr[8 + 2 * lg], vr[9 + 2 * lg]);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, vb), o[n],
+        const uint4 w = make_uint4(vr[2 * lg], vr[2 * lg + 1], vr[8 + 2 * lg], vr[9 + 2 * lg]);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, w), o[n],
                                                        0, 0, 0);
       }
-      g0 = gnext;
+    };
+    const bool wave_live = wave * 16 < ne;
+    int g0 = next_step(tok0);
+    int g1 = next_step(g0 + kBlkGroup);
+    fetch(ka, va, g0);
+    fetch(kb, vb, g1);
+    while (g0 < tok_end) {
+      __syncthreads();
+      stage(ka, va);
+      __syncthreads();
+      int g2 = next_step(g1 + kBlkGroup);
+      fetch(ka, va, g2);
+      if (wave_live) compute(g0);  // waves past the block's heads only stage
+      g0 = g1;
+      g1 = g2;
+      if (g0 >= tok_end) break;
+      __syncthreads();
+      stage(kb, vb);
+      __syncthreads();
+      g2 = next_step(g1 + kBlkGroup);
+      fetch(kb, vb, g2);
+      if (wave_live) compute(g0);
+      g0 = g1;
+      g1 = g2;
     }
+    l_i += __shfl_xor(l_i, 16, kWave);
+    l_i += __shfl_xor(l_i, 32, kWave);
     // Partials: O rows 4 lg + e (heads of the wave), columns n * 16 + li; m and l
     // from the lanes of row group 0.
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = wave * 16 + 4 * lg + e;
-      if (r < ne) {
+      if (r < ne && s_slot[r] >= 0) {
         float* pr = P.part + (int64_t)s_slot[r] * (D + 2);
 #pragma unroll
         for (int n = 0; n < NTD; ++n) pr[n * 16 + li] = o[n][e];
@@ -1098,7 +1121,7 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
     }
     if (lg == 0 && qvalid) {
       float* pr = P.part + (int64_t)s_slot[qi] * (D + 2);
-      pr[D] = m_i;
+      pr[D] = m_i * inv;
       pr[D + 1] = l_i;
     }
   }
@@ -1106,8 +1129,8 @@ __global__ __launch_bounds__(256) void blk_attn_kernel(const bf16_t* __restrict_
 
 // One wave per head: the head's sink (when chunk 0 is not selected) and its
 // partial-chunk tokens, then the merge with its pairs' partials (in tile
-// order); a failed route gives a NaN row.  Heads with too many tiles are then
-// attended by the whole workgroup, one at a time.
+// order); a failed route gives a NaN row.  Loads that do not depend on each
+// other are issued together, and the partials kSB at a time.
 template <typename T, int D, bool POW2, bool BUF>
 __global__ __launch_bounds__(kThreads) void blk_merge_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -1117,62 +1140,114 @@ __global__ __launch_bounds__(kThreads) void blk_merge_kernel(
   BlkPtrs P(scr, L);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
-  const int n = head < a.n_heads ? P.ntile[head] : -3;
-  if (n == -2) {
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) store_elem(O + head * D, lane * DPL + e, __int_as_float(0x7fc00000));
-  } else if (n >= 0) {
+  if (head < a.n_heads) {
+    // Independent loads first: the head's counts, slot base, first chunk and query.
+    const int n = P.ntile[head];
     const int c = cnt[head];
-    const bool sink = c == 0 || sel[head * a.cap] != 0;
-    const int ne = (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C);  // sink, then the partial chunk
-    const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
-    const T* Kb = K + tree_of_head(head, a) * nblk;
-    const T* Vb = a.chunked ? Kb + (int64_t)a.C * D : V + tree_of_head(head, a) * nblk;
-    const int64_t row1 = a.n1 * (a.chunked ? 2 * a.C : a.C);  // first key row of chunk n_1
-    const float inv = 1.0f / sqrtf((float)D);
+    const int qb = P.qbase[head];  // meaningful only when n >= 0
+    const int first = sel[head * a.cap];
     float q[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) q[e] = load_elem(Q + head * D, lane * DPL + e);
-    float m = -INFINITY, l = 0.f, acc[DPL];
+    if (n == -2) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-    for (int x = 0; x < ne; ++x) {
-      const int64_t row = (sink && x == 0) ? 0 : row1 + (x - (sink ? 1 : 0));
-      float part = 0.f;
+      for (int e = 0; e < DPL; ++e) store_elem(O + head * D, lane * DPL + e, __int_as_float(0x7fc00000));
+    } else if (n >= 0) {
+      const bool sink = c == 0 || first != 0;
+      const int ne = (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C);  // sink, then the partial chunk
+      const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
+      const T* Kb = K + tree_of_head(head, a) * nblk;
+      const T* Vb = a.chunked ? Kb + (int64_t)a.C * D : V + tree_of_head(head, a) * nblk;
+      const int64_t row1 = a.n1 * (a.chunked ? 2 * a.C : a.C);  // first key row of chunk n_1
+      const float inv = 1.0f / sqrtf((float)D);
+      float m = -INFINITY, l = 0.f, acc[DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) part = fmaf(q[e], load_elem(Kb + row * D, lane * DPL + e), part);
-      const float sc = wave_allreduce_f32(part, OpAdd()) * inv;
-      const float mn = fmaxf(m, sc);
-      const float r = __expf(m - mn), pw = __expf(sc - mn);
-      l = l * r + pw;
+      for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+      for (int x = 0; x < ne; ++x) {
+        const int64_t row = (sink && x == 0) ? 0 : row1 + (x - (sink ? 1 : 0));
+        float kr[DPL], vr[DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pw, load_elem(Vb + row * D, lane * DPL + e), acc[e] * r);
-      m = mn;
+        for (int e = 0; e < DPL; ++e) {
+          kr[e] = load_elem(Kb + row * D, lane * DPL + e);
+          vr[e] = load_elem(Vb + row * D, lane * DPL + e);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) part = fmaf(q[e], kr[e], part);
+        const float sc = wave_allreduce_f32(part, OpAdd()) * inv;
+        const float mn = fmaxf(m, sc);
+        const float r = __expf(m - mn), pw = __expf(sc - mn);
+        l = l * r + pw;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pw, vr[e], acc[e] * r);
+        m = mn;
+      }
+      // The pairs' partials, kSB at a time (indices clamped: every load issues).
+      constexpr int kSB = 8;
+      const float* slots = P.part + (int64_t)qb * (D + 2);
+      float M = m, den = l, num[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) num[e] = acc[e];
+      for (int s0 = 0; s0 < n; s0 += kSB) {
+        float ms[kSB], ls[kSB], os[kSB][DPL];
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) {
+          const float* r = slots + (int64_t)min(s0 + j, n - 1) * (D + 2);
+          ms[j] = r[D];
+          ls[j] = r[D + 1];
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) os[j][e] = r[lane * DPL + e];
+          if (s0 + j >= n) ms[j] = -INFINITY;
+        }
+        float Mn = M;
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) Mn = fmaxf(Mn, ms[j]);
+        if (Mn == -INFINITY) continue;
+        const float rs = M == -INFINITY ? 0.f : __expf(M - Mn);
+        den *= rs;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) num[e] *= rs;
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) {
+          const float w = ms[j] == -INFINITY ? 0.f : __expf(ms[j] - Mn);
+          den = fmaf(w, ls[j], den);
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) num[e] = fmaf(w, os[j][e], num[e]);
+        }
+        M = Mn;
+      }
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) store_elem(O + head * D, lane * DPL + e, num[e] / den);
     }
-    const float* slots = P.part + (int64_t)P.qbase[head] * (D + 2);
-    float M = m;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, slots[s * (D + 2) + D]);
-    const float wx = m == -INFINITY ? 0.f : __expf(m - M);
-    float num[DPL], den = wx * l;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) num[e] = wx * acc[e];
-    for (int s = 0; s < n; ++s) {
-      const float* r = slots + s * (D + 2);
-      const float ms = r[D];
-      const float w = ms == -INFINITY ? 0.f : __expf(ms - M);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) num[e] = fmaf(w, r[lane * DPL + e], num[e]);
-      den = fmaf(w, r[D + 1], den);
-    }
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) store_elem(O + head * D, lane * DPL + e, num[e] / den);
   }
-  for (int w = 0; w < kWaves; ++w) {
-    const int64_t hh = (int64_t)blockIdx.x * kWaves + w;
-    if (hh < a.n_heads && P.ntile[hh] == -1) {
-      AttnArgs a1 = a;
-      a1.S = 1;
-      attend_one_head<T, D, POW2, BUF>(Q, K, V, sel, cnt, O, nullptr, a1, hh, 0);
+}
+
+// Heads past the slot budget: a few persistent workgroups find them (each
+// thread tests one head per pass, heads spread over the workgroups so that a
+// run of marked heads is shared out) and attend them one per workgroup.
+constexpr unsigned kBlkFallbackBlocks = 256;
+template <typename T, int D, bool POW2, bool BUF>
+__global__ __launch_bounds__(kThreads) void blk_fallback_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
+    AttnArgs a, BlkLayout L, char* scr) {
+  BlkPtrs P(scr, L);
+  __shared__ int64_t s_list[kThreads];
+  __shared__ int s_n;
+  AttnArgs a1 = a;
+  a1.S = 1;
+  const int tid = threadIdx.x;
+  for (int64_t base = 0; base < a.n_heads; base += (int64_t)gridDim.x * kThreads) {
+    const int64_t h = base + (int64_t)tid * gridDim.x + blockIdx.x;
+    const bool f = h < a.n_heads && P.ntile[h] == -1;
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    if (f) s_list[atomicAdd(&s_n, 1)] = h;
+    __syncthreads();
+    const int nl = s_n;
+    for (int j = 0; j < nl; ++j) {
+      attend_one_head<T, D, POW2, BUF>(Q, K, V, sel, cnt, O, nullptr, a1, s_list[j], 0);
+      __syncthreads();  // the next head reuses the LDS areas
     }
   }
 }
@@ -1186,14 +1261,15 @@ int launch_blk(const AttnArgs& a, const void* Q, const void* K, const void* V, c
   const unsigned wave_blocks = (unsigned)((a.n_heads + kWaves - 1) / kWaves);
   blk_zero_kernel<<<(unsigned)((max(L.NTT, (int64_t)16) + 255) / 256), 256, 0, s>>>(scr, L);
   blk_count_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
-  blk_slots_kernel<<<1, 1024, 0, s>>>(a.n_heads, L, scr);
-  blk_tiles_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
-  blk_scan_kernel<<<1, 1024, 0, s>>>(scr, L);
+  blk_scan_kernel<<<2, 1024, 0, s>>>(a.n_heads, L, scr);
   blk_fill_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
   blk_attn_kernel<D, BUF><<<kBlkGrid, 256, 0, s>>>(
       reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K),
       reinterpret_cast<const bf16_t*>(V), a, L, scr);
   blk_merge_kernel<T, D, POW2, BUF><<<wave_blocks, kThreads, 0, s>>>(
+      reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
+      reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), a, L, scr);
+  blk_fallback_kernel<T, D, POW2, BUF><<<kBlkFallbackBlocks, kThreads, 0, s>>>(
       reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
       reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), a, L, scr);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
