@@ -74,6 +74,12 @@ def _cb_head(item):
     return 1
 
 
+def _one_thread():
+    # One BLAS thread per worker process: `cores` is then the thread count used.
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
 def cpu_baseline(g, K, V, seconds: float, procs: int):
     """Oracle route + attention per query head of sequence 0; rate in queries/s."""
     global _CB
@@ -93,7 +99,7 @@ def cpu_baseline(g, K, V, seconds: float, procs: int):
     _CB = (g, trees, Kf, Vf)
     ctx = mp.get_context("fork")
     done = 0
-    with ctx.Pool(procs) as pool:
+    with ctx.Pool(procs, initializer=_one_thread) as pool:
         t0 = time.perf_counter()
         for _ in pool.imap_unordered(_cb_head, items, chunksize=2):
             done += 1
@@ -106,7 +112,18 @@ def cpu_baseline(g, K, V, seconds: float, procs: int):
     return {"value": heads_per_s / g.H_q, "unit": "queries/s", "cores": procs, "kind": "oracle",
             "sample": f"{done} query heads (sequence 0, decode steps in order, all {g.H_q} heads "
                       f"per step) of the same workload, fp64 NumPy route + attention, "
-                      f"{elapsed:.1f} s wall over {procs} processes; tree build excluded"}
+                      f"{elapsed:.1f} s wall over {procs} single-threaded processes; tree build "
+                      f"excluded"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ----------------------------------------------------------------------------
@@ -244,6 +261,38 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     log(f"[bench] {steps} steps: {total_ms:.3f} ms total; route {route_ms.mean() * 1e3:.1f} us, "
         f"attn {attn_ms.mean() * 1e3:.1f} us per step")
 
+    # The same steps cache-cold: 1 GiB written between steps (outside the timed
+    # region) evicts L2 and the memory-side cache; each step timed on its own.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    n_cold = min(steps, 10)
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_cold)]
+    for j in range(n_cold):
+        i = warmup + j
+        flush.fill_(j & 255)
+        evc[j][0].record()
+        if zr(*args_r[i]) != 0:
+            raise RuntimeError("zha_route failed")
+        evc[j][1].record()
+        if za(*args_a[i]) != 0:
+            raise RuntimeError("zha_attn failed")
+        evc[j][2].record()
+    torch.cuda.synchronize()
+    cold_route = np.array([e[0].elapsed_time(e[1]) for e in evc])
+    cold_attn = np.array([e[1].elapsed_time(e[2]) for e in evc])
+    log(f"[bench] {n_cold} cold steps: route {cold_route.mean() * 1e3:.1f} us, "
+        f"attn {cold_attn.mean() * 1e3:.1f} us per step")
+    # Streaming-copy bandwidth of this device (read + write bytes of a 1 GiB copy).
+    dst = torch.empty_like(flush)
+    dst.copy_(flush)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(flush)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * 5 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del flush, dst
+
     cnt_h = cnt.cpu().numpy()
     if (cnt_h[warmup:] < 0).any() or (cnt_h[warmup:] > cap).any():
         raise RuntimeError("a route overflowed the frontier capacity or the chunk-list cap")
@@ -276,7 +325,8 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
         dense_ms = d0.elapsed_time(d1) / dense_steps
         log(f"[bench] dense decode {dense_ms * 1e3:.1f} us per step")
     return {"total_ms": total_ms, "route_ms": route_ms, "attn_ms": attn_ms, "bytes": acc,
-            "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap}
+            "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap, "cold_route_ms": cold_route,
+            "cold_attn_ms": cold_attn, "copy_gbs": copy_gbs}
 
 
 def run_block_1m(reps: int = 3):
@@ -349,6 +399,102 @@ def run_block_1m(reps: int = 3):
             "hbm_frac_union": (union + route_rows) / ((r_ms + a_ms) * 1e-3) / (HBM_PEAK_GBS * 1e9)}
 
 
+CROSSOVER_T = [4096, 8192, 16384, 32768, 65536, 131072, 262144]
+
+
+def crossover_geometry(T: int):
+    """The deep-decode geometry (B=8, 32/4 heads, d=128, C=8, p=0.95, bf16) at context T, with the
+    deepest L such that C^L <= T (T / C^L top nodes)."""
+    from dataclasses import replace
+    base = W.CONFIGS[3]
+    L = 1
+    while base.C ** (L + 1) <= T:
+        L += 1
+    return replace(base, name=f"deep-decode-{T // 1024}k", T=T, L=L)
+
+
+def run_crossover(steps: int):
+    """ZHA route + attention against dense decode, one decode step per call, cache-cold (1 GiB
+    written between calls, outside the timed region), over CROSSOVER_T."""
+    import torch
+
+    from hierarchical_tree_indexed_04_amd import zha as Z
+    Z.load()
+    torch.cuda.set_device(0)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    rows = []
+    for T in CROSSOVER_T:
+        g = crossover_geometry(T)
+        K, V = W.make_kv(g)
+        Qs = np.stack([W.make_queries(g, K, i) for i in range(steps)])[:, :, None]
+        gm = Z.geom(g)
+        Kd, Vd, Qd = to_dev(torch, K, g.dtype), to_dev(torch, V, g.dtype), to_dev(torch, Qs, g.dtype)
+        del K, V
+        tree = Z.build(gm, Kd, torch.zeros((g.H_kv, g.R, g.d), dtype=torch.float32, device="cuda"))
+        cap = g.n_level(1)
+        sel = torch.empty((g.B, 1, g.H_q, cap), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((g.B, 1, g.H_q), dtype=torch.int32, device="cuda")
+        O = torch.empty((g.B, 1, g.H_q, g.d), dtype=Kd.dtype, device="cuda")
+        rsc = torch.empty(max(Z.route_scratch_bytes(gm, 1, cap), 1), dtype=torch.uint8,
+                          device="cuda")
+        asc = torch.empty(max(Z.attn_scratch_bytes(gm, 1, cap), 1), dtype=torch.uint8,
+                          device="cuda")
+        dsc = torch.empty(max(Z.dense_scratch_bytes(gm, 1), 1), dtype=torch.uint8, device="cuda")
+
+        def zha(i):
+            Z.route(gm, tree, Qd[i], 1, g.p, cap, want_stats=False, want_gap=False,
+                    out=(sel, cnt, None, None), scratch=rsc)
+            return Z.attn(gm, Qd[i], 1, Kd, Vd, sel, cnt, cap, O=O, scratch=asc)
+
+        zha(0)
+        Z.dense_decode(gm, Qd[0], 1, Kd, Vd, O=O, scratch=dsc)
+        torch.cuda.synchronize()
+        er = [[ev() for _ in range(3)] for _ in range(steps)]
+        ed = [[ev() for _ in range(2)] for _ in range(steps)]
+        toks = 0
+        for i in range(steps):
+            flush.fill_(i & 255)
+            er[i][0].record()
+            Z.route(gm, tree, Qd[i], 1, g.p, cap, want_stats=False, want_gap=False,
+                    out=(sel, cnt, None, None), scratch=rsc)
+            er[i][1].record()
+            Z.attn(gm, Qd[i], 1, Kd, Vd, sel, cnt, cap, O=O, scratch=asc)
+            er[i][2].record()
+            toks += int(cnt.sum().item()) * g.C
+            flush.fill_((i + 7) & 255)
+            ed[i][0].record()
+            Z.dense_decode(gm, Qd[i], 1, Kd, Vd, O=O, scratch=dsc)
+            ed[i][1].record()
+        torch.cuda.synchronize()
+        r_us = float(np.median([e[0].elapsed_time(e[1]) for e in er]) * 1e3)
+        a_us = float(np.median([e[1].elapsed_time(e[2]) for e in er]) * 1e3)
+        z_us = float(np.median([e[0].elapsed_time(e[2]) for e in er]) * 1e3)
+        d_us = float(np.median([e[0].elapsed_time(e[1]) for e in ed]) * 1e3)
+        row = {"T": T, "L": g.L, "top_nodes": g.n_level(g.L), "zha_us": z_us, "route_us": r_us,
+               "attn_us": a_us, "dense_us": d_us, "speedup_vs_dense": d_us / z_us,
+               "keys_attended_frac": toks / steps / (g.B * g.H_q) / T}
+        log(f"[crossover] T={T:7d} L={g.L}: zha {z_us:8.1f} us (route {r_us:6.1f}, attn "
+            f"{a_us:6.1f}), dense {d_us:8.1f} us, x{d_us / z_us:.2f}")
+        rows.append(row)
+        del Kd, Vd, Qd, tree
+        torch.cuda.empty_cache()
+    # Smallest T from which ZHA is faster at every larger T measured.
+    crossing = None
+    for k in range(len(rows)):
+        if all(r["zha_us"] < r["dense_us"] for r in rows[k:]):
+            crossing = rows[k]["T"]
+            break
+    print(json.dumps({"crossover": rows, "zha_faster_from_T": crossing,
+                      "workload": "deep-decode geometry (B=8, H_q=32/H_kv=4, d=128, C=8, p=0.95, "
+                                  "bf16), L = deepest with 8^L <= T, one decode step per call",
+                      "timing": f"median over {steps} steps, cache-cold (1 GiB written between "
+                                "calls)"}), flush=True)
+
+
 def copy_calibration():
     """One plain copy of 1 GiB: reads and writes 2^30 bytes each, for scaling HBM counters."""
     import torch
@@ -372,11 +518,16 @@ def main():
                     help="wall-time budget of the oracle baseline (0 disables)")
     ap.add_argument("--with-1m", type=int, default=1,
                     help="also time the 1M-context block workload (2048 positions routed at once)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only run the context-length sweep of ZHA against dense decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.crossover:
+        run_crossover(max(3, min(args.steps, 20)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU: the hot path has no multi-GPU mode "
@@ -396,7 +547,13 @@ def main():
         procs = max(1, min(16, os.cpu_count() or 1))
         t0 = time.perf_counter()
         cpu = cpu_baseline(g, K, V, args.cpu_seconds, procs)
-        log(f"[bench] oracle baseline {cpu['value']:.2f} queries/s ({time.perf_counter() - t0:.1f} s)")
+        one = cpu_baseline(g, K, V, max(2.0, args.cpu_seconds / 3), 1)
+        cpu["one_core_value"] = one["value"]
+        cpu["one_core_sample"] = one["sample"]
+        cpu["host_cpus"] = os.cpu_count()
+        cpu["cpu_model"] = cpu_model()
+        log(f"[bench] oracle baseline {cpu['value']:.2f} queries/s on {procs} processes, "
+            f"{one['value']:.2f} on one ({time.perf_counter() - t0:.1f} s)")
 
     r = run_gpu(g, K, V, args.steps, args.warmup, args.dense_steps)
     ms_per_step = r["total_ms"] / args.steps
@@ -433,6 +590,18 @@ def main():
         "step_bytes_union": step_union,
         "step_bytes_per_head_sum": by["attn_per_head"] + by["route"],
         "step_hbm_frac": step_union / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "query_heads_per_s": value * g.H_q,
+        "stream_copy_GBs": r["copy_gbs"],
+        "attn_frac_of_copy": achieved / r["copy_gbs"],
+        "cold": {"route_us": float(r["cold_route_ms"].mean() * 1e3),
+                 "attn_us": float(r["cold_attn_ms"].mean() * 1e3),
+                 "us_per_step": float((r["cold_route_ms"] + r["cold_attn_ms"]).mean() * 1e3),
+                 "queries_per_s": g.B / float((r["cold_route_ms"] + r["cold_attn_ms"]).mean()
+                                              * 1e-3),
+                 "step_hbm_frac": step_union / float((r["cold_route_ms"] + r["cold_attn_ms"]).mean()
+                                                     * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                 "steps": int(len(r["cold_route_ms"])),
+                 "how": "1 GiB written between steps, outside the timed region"},
         "tokens_per_head": by["tokens_per_head"],
         "keys_attended_frac": by["tokens_per_head"] / g.T,
         "build_ms": r["build_ms"],

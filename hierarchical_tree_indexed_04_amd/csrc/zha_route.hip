@@ -49,29 +49,41 @@ constexpr int kMaxChildren = 1024;  // C <= 1024
 // Two launch shapes of the same kernel.  Latency shape: 8 waves, 16 rows in
 // flight per lane, frontiers up to kRouteFrontierMax; one workgroup per CU, so
 // a call with few query heads finishes as fast as one head walks the tree.
-// Throughput shape: 4 waves, 8 rows in flight, frontiers up to 1024 in LDS;
-// several workgroups share a CU, for calls with many query heads (a block of
-// positions).  A head whose frontier outgrows the throughput shape is listed
-// in the scratch buffer and routed again by a few persistent workgroups of the
-// latency shape.
+// Throughput shape: ZHA_ROUTE_TPUT_THREADS threads, ZHA_ROUTE_TPUT_ROWS rows in
+// flight per lane, frontiers up to ZHA_ROUTE_TPUT_FMAX in LDS; many workgroups
+// share a CU, for calls with many query heads (a block of positions), so more
+// heads are in flight.  A head whose frontier outgrows the throughput shape is
+// listed in the scratch buffer and routed again by a few persistent workgroups
+// of the latency shape.
 #ifndef ZHA_ROUTE_LAT_ROWS
 #define ZHA_ROUTE_LAT_ROWS 16
 #endif
 #ifndef ZHA_ROUTE_TPUT_ROWS
 #define ZHA_ROUTE_TPUT_ROWS 4
 #endif
+#ifndef ZHA_ROUTE_TPUT_THREADS
+#define ZHA_ROUTE_TPUT_THREADS 128
+#endif
+#ifndef ZHA_ROUTE_TPUT_FMAX
+#define ZHA_ROUTE_TPUT_FMAX 768
+#endif
+#ifndef ZHA_ROUTE_TPUT_EU
+#define ZHA_ROUTE_TPUT_EU 1
+#endif
 namespace lat {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kU = ZHA_ROUTE_LAT_ROWS;
 constexpr int kFMax = kRouteFrontierMax;
+constexpr int kMinWavesEU = 1;
 #include "zha_route_impl.inc"
 }  // namespace lat
 namespace tput {
-constexpr int kThreads = 256;
+constexpr int kThreads = ZHA_ROUTE_TPUT_THREADS;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kU = ZHA_ROUTE_TPUT_ROWS;
-constexpr int kFMax = 1024;
+constexpr int kFMax = ZHA_ROUTE_TPUT_FMAX;
+constexpr int kMinWavesEU = ZHA_ROUTE_TPUT_EU;
 #include "zha_route_impl.inc"
 }  // namespace tput
 // kTputMinHeads (query heads per call for the throughput shape) is in zha_internal.hpp.
