@@ -49,8 +49,8 @@ constexpr int kMaxChildren = 1024;  // C <= 1024
 // Two launch shapes of the same kernel.  Latency shape: 8 waves, 16 rows in
 // flight per lane, frontiers up to kRouteFrontierMax; one workgroup per CU, so
 // a call with few query heads finishes as fast as one head walks the tree.
-// Throughput shape: ZHA_ROUTE_TPUT_THREADS threads, ZHA_ROUTE_TPUT_ROWS rows in
-// flight per lane, frontiers up to ZHA_ROUTE_TPUT_FMAX in LDS; many workgroups
+// Throughput shape: ZHA_ROUTE_TPUT_THREADS threads, ZHA_ROUTE_TPUT_ROWS 16-byte
+// loads in flight per lane, frontiers up to ZHA_ROUTE_TPUT_FMAX in LDS; many workgroups
 // share a CU, for calls with many query heads (a block of positions), so more
 // heads are in flight.  A head whose frontier outgrows the throughput shape is
 // listed in the scratch buffer and routed again by a few persistent workgroups

@@ -64,18 +64,18 @@ struct OpMin {
   }
 };
 
-// All-reduce inside aligned groups of W lanes (W = 8, 16, 32 or 64); every
-// lane of a group gets the group's result.
+// All-reduce inside aligned groups of W lanes (W = 2, 4, 8, 16, 32 or 64);
+// every lane of a group gets the group's result.
 template <int W, typename Op>
 __device__ __forceinline__ float group_allreduce(float v, Op op) {
-  static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
   if constexpr (W == 8) {
     v = op(v, dpp_f32<kDppRowHalfMirror>(v));
-  } else {
+  } else if constexpr (W >= 16) {
     v = op(v, dpp_f32<kDppRowRor8>(v));
     v = op(v, dpp_f32<kDppRowRor4>(v));
   }
-  v = op(v, dpp_f32<kDppQpXor2>(v));
+  if constexpr (W >= 4) v = op(v, dpp_f32<kDppQpXor2>(v));
   v = op(v, dpp_f32<kDppQpXor1>(v));
   if constexpr (W >= 32) v = op(v, __shfl_xor(v, 16, kWave));
   if constexpr (W == 64) v = op(v, __shfl_xor(v, 32, kWave));
