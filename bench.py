@@ -92,7 +92,7 @@ def cpu_baseline(g, K, V, seconds: float, procs: int):
         Vf[kvh] = W.to_float(V[0, kvh], g.dtype)
         trees[kvh] = O.build_tree(Kf[kvh].astype(np.float64), np.zeros((1, g.d)), g.C, g.L, g.dtype)
     items = []
-    for step in range(1024):
+    for step in range(8192):
         Q = W.make_queries(g, K, step)
         for h in range(g.H_q):
             items.append((W.to_float(Q[0, h], g.dtype), h // g.G))

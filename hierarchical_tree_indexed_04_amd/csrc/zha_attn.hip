@@ -31,7 +31,7 @@ namespace {
 
 constexpr int kThreads = 256;
 #ifndef ZHA_ATTN_ROWS
-#define ZHA_ATTN_ROWS 8
+#define ZHA_ATTN_ROWS 4
 #endif
 #ifndef ZHA_DENSE_ROWS
 #define ZHA_DENSE_ROWS 4
@@ -107,6 +107,15 @@ struct KvBlock {
   }
   uint32_t vdelta, sub16;
   __device__ __forceinline__ int key_row(int chunk, int j) const { return chunk * cs + j; }
+  // K or V row alone (the same rules as load).
+  __device__ __forceinline__ uint4 load_k(int row, bool live) const {
+    if (BUF) return bld16(rk, live ? (uint32_t)row * kRow + sub16 : kBufNone);
+    return live ? ld16(k + (size_t)(uint32_t)row * kRow) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __device__ __forceinline__ uint4 load_v(int row, bool live) const {
+    if (BUF) return bld16(rv, live ? (uint32_t)row * kRow + sub16 + vdelta : kBufNone);
+    return live ? ld16(v + (size_t)(uint32_t)row * kRow) : make_uint4(0u, 0u, 0u, 0u);
+  }
   __device__ __forceinline__ void load(int row, bool live, uint4& kv, uint4& vv) const {
     if (BUF) {
       // Straight-line: a slot without a row reads nothing and gets zeros.
@@ -499,11 +508,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
         for (int i = tid; i <= lc - fc; i += kThreads) s_ids[i] = ids[fc + i];
         __syncthreads();
       }
-      for (int base = xr; base < xe; base += RPB * kUA) {
-        // Key row of every slot first: the chunk-id reads from LDS are
-        // unconditional (clamped in bounds, one wait for all of them), so
-        // the 2 kUA row loads below issue back to back.
-        int row[kUA];
+      // Each tensor's rows of the next batch are loaded as soon as its rows of
+      // the current batch have been read: K(i + 1) right after the scores of
+      // batch i, V(i + 1) right after its softmax update.  Past the round's
+      // end a batch loads nothing (slots without a row use out-of-range buffer
+      // offsets), so the loads stay unconditional and each wait counts exactly
+      // the loads issued after it.  The next batch's key rows (which need
+      // branches) are computed first, so the loads and the arithmetic form one
+      // straight-line block; the empty asm statements keep them in order.
+      auto rows_of = [&](int base, int (&row)[kUA]) {
+        // Chunk ids from LDS for every slot first (clamped in bounds, one wait).
 #pragma unroll
         for (int u = 0; u < kUA; ++u) {
           const int x = base + u * RPB + grp;
@@ -523,19 +537,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
           const int j = x < ct ? x - ci * Cc : (is_sink ? 0 : e - (sink ? 1 : 0));
           row[u] = kvb.key_row(chunk, j);
         }
-        uint4 kv[kUA], vv[kUA];
+      };
+      constexpr int kStep = RPB * kUA;
+      int row[kUA];
+      uint4 kv[kUA], vv[kUA];
+      rows_of(xr, row);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < kUA; ++u) kvb.load(row[u], base + u * RPB + grp < xe, kv[u], vv[u]);
-        // Keep all 2 kUA loads ahead of the arithmetic (the scheduler would
-        // otherwise delay some V loads to reuse K's registers).
-        __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < kUA; ++u) kv[u] = kvb.load_k(row[u], xr + u * RPB + grp < xe);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kUA; ++u) vv[u] = kvb.load_v(row[u], xr + u * RPB + grp < xe);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      for (int base = xr; base < xe; base += kStep) {
+        const int nb = base + kStep;
+        rows_of(nb, row);
+        asm volatile("" ::: "memory");
         float sc[kUA];
 #pragma unroll
         for (int u = 0; u < kUA; ++u) {
           const float dot = group_allreduce<LPR>(slice_dot<T>(kv[u], qv), OpAdd()) * inv;
           sc[u] = (base + u * RPB + grp < xe) ? dot : -INFINITY;
         }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kUA; ++u) kv[u] = kvb.load_k(row[u], nb + u * RPB + grp < xe);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
         online_update<T, kUA>(m, l, acc, sc, vv);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kUA; ++u) vv[u] = kvb.load_v(row[u], nb + u * RPB + grp < xe);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
       }
       xr = xe;
     }
