@@ -702,6 +702,7 @@ struct BlkPtrs {
   int32_t* ctrl;   // [0] work items
   int32_t* qbase;  // per head: first slot
   int32_t* ntile;  // per head: tiles (>= 0), -1 attended per head, -2 failed route
+  int64_t* wsum;   // per workgroup of the count launch (4 heads): slots wanted
   int32_t* tcnt;   // per tile: pairs
   int32_t* tcur;   // per tile: fill cursor
   int32_t* toff;   // per tile: first entry (exclusive scan of tcnt)
@@ -712,6 +713,7 @@ struct BlkPtrs {
       : ctrl(reinterpret_cast<int32_t*>(scr + L.off_ctrl)),
         qbase(reinterpret_cast<int32_t*>(scr + L.off_qbase)),
         ntile(reinterpret_cast<int32_t*>(scr + L.off_ntile)),
+        wsum(reinterpret_cast<int64_t*>(scr + L.off_wsum)),
         tcnt(reinterpret_cast<int32_t*>(scr + L.off_tcnt)),
         tcur(reinterpret_cast<int32_t*>(scr + L.off_tcur)),
         toff(reinterpret_cast<int32_t*>(scr + L.off_toff)),
@@ -736,14 +738,23 @@ __global__ __launch_bounds__(256) void blk_zero_kernel(char* scr, BlkLayout L) {
   }
 }
 
+// The merge launch gives each query head a group of kGL lanes (four heads per
+// wave): its work per head is short, and one wave per head took several
+// rounds of resident waves.  (The count and fill launches keep a wave per
+// head: with kGL-lane groups, their cross-lane shuffles per batch of ids cost
+// more than the rounds saved.)
+constexpr int kGL = 16;
+constexpr int kHPW = kWave / kGL;  // heads per wave
+
 // Walks a head's selected chunks (ascending, one wave) and calls
 // on_first(tile) in the lanes that start a new tile; returns the tile count.
 template <typename F>
-__device__ __forceinline__ int walk_tiles(const int32_t* ids, int c, int CT, F on_first) {
+__device__ __forceinline__ int walk_tiles(const int32_t* ids, int c, int CT, int id0, F on_first) {
   const int lane = threadIdx.x & (kWave - 1);
   int n = 0, cur = -1;
   for (int j = 0; j < c; j += kWave) {
-    const int id = j + lane < c ? ids[j + lane] : -1;
+    // id0: the first batch, loaded by the caller together with c.
+    const int id = j + lane < c ? (j == 0 ? id0 : ids[j + lane]) : -1;
     const int t = id >= 0 ? id / CT : -1;
     int tp = __shfl_up(t, 1, kWave);
     if (lane == 0) tp = cur;
@@ -761,74 +772,95 @@ __device__ __forceinline__ int walk_tiles(const int32_t* ids, int c, int CT, F o
 __global__ __launch_bounds__(256) void blk_count_kernel(const int32_t* __restrict__ sel,
                                                         const int32_t* __restrict__ cnt,
                                                         AttnArgs a, BlkLayout L, char* scr) {
+  __shared__ int32_t s_n[kWaves];
   BlkPtrs P(scr, L);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
-  if (head >= a.n_heads) return;
-  const int c = cnt[head];
-  int n = -2;
-  if (c >= 0 && c <= a.cap) {
-    int32_t* tc = P.tcnt + tree_of_head(head, a) * L.NT;
-    n = walk_tiles(sel + head * a.cap, c, L.CT, [&](int t) { atomicAdd(&tc[t], 1); });
+  int n = -3;
+  if (head < a.n_heads) {
+    // The count and the first batch of ids load together (index clamped to the list).
+    const int c = cnt[head];
+    const int id0 = sel[head * a.cap + min(lane, a.cap - 1)];
+    n = -2;
+    if (c >= 0 && c <= a.cap) {
+      int32_t* tc = P.tcnt + tree_of_head(head, a) * L.NT;
+      n = walk_tiles(sel + head * a.cap, c, L.CT, id0, [&](int t) { atomicAdd(&tc[t], 1); });
+    }
+    if (lane == 0) P.ntile[head] = n;
   }
-  if (lane == 0) P.ntile[head] = n;
+  // Slots this workgroup's heads want (tiles + 1 each), for the prefix sum.
+  if (lane == 0) s_n[wave] = n >= 0 ? n + 1 : 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t w = 0;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) w += s_n[x];
+    P.wsum[blockIdx.x] = w;
+  }
 }
 
-// One launch, two workgroups.  Workgroup 0: slot bases by a prefix sum of
-// (tiles + 1) over the heads, 8192 heads at a time: coalesced loads (the next
-// chunk's issued before the current one is scanned) go through LDS, each
-// thread then sums 8 consecutive heads, one block scan per chunk.  From the
-// first head whose slots would pass the budget on, heads are marked for
-// per-head attention (their pairs stay counted and become empty entries).
-// Workgroup 1: exclusive scans over the tiles, first entry and first work item
-// of each.
+// Prefix sums, one launch.  Workgroups 0 .. nq-1: slot bases by a prefix sum
+// of (tiles + 1) over the heads, 8192 heads each: the slots of the heads before
+// its range come from the count launch's per-workgroup sums; its own range
+// goes through LDS in coalesced loads, each thread then sums 8 consecutive
+// heads, one block scan.  From the first head whose slots would pass the
+// budget on, heads are marked for per-head attention (their pairs stay
+// counted and become empty entries).  The last workgroup: exclusive scans over
+// the tiles, first entry and first work item of each.
+constexpr int kScanPer = 8;
+constexpr int kScanChunk = 1024 * kScanPer;  // heads per workgroup of the scan launch
 __global__ __launch_bounds__(1024) void blk_scan_kernel(int64_t n_heads, BlkLayout L, char* scr) {
   BlkPtrs P(scr, L);
   __shared__ int64_t s_v[1024], s_w[1024];
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0) {
-    constexpr int kPer = 8;
-    constexpr int kChunk = 1024 * kPer;
-    __shared__ int32_t s_c[kChunk];
-    const int lane = tid & (kWave - 1), wave = tid >> 6;
-    int v[kPer];
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  if (blockIdx.x + 1 < gridDim.x) {
+    __shared__ int32_t s_c[kScanChunk];
+    const int64_t c0 = (int64_t)blockIdx.x * kScanChunk;
+    // This range's values, loaded first (coalesced, unconditional).
+    int v[kScanPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) v[k] = P.ntile[min((int64_t)k * 1024 + tid, n_heads - 1)];
+    for (int k = 0; k < kScanPer; ++k) v[k] = P.ntile[min(c0 + (int64_t)k * 1024 + tid, n_heads - 1)];
+    // Slots of the heads before the range: the count launch's sums of 4 heads.
+    const int64_t nw = c0 / kWaves;
+    int64_t before = 0;
+    for (int64_t i0 = 0; i0 < nw; i0 += 8 * 1024) {  // 8 loads in flight per thread
+      int64_t x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = P.wsum[min(i0 + u * 1024 + tid, nw - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) before += i0 + u * 1024 + tid < nw ? x[u] : 0;
+    }
+    before = (int64_t)wave_sum_u64_bcast((uint64_t)before);
+    if (lane == 0) s_w[wave] = before;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) s_c[k * 1024 + tid] = v[k];
+    __syncthreads();
     int64_t run = 0;
-    for (int64_t c0 = 0; c0 < n_heads; c0 += kChunk) {
-      __syncthreads();  // the previous chunk's reads of s_c and s_w are done
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) s_c[k * 1024 + tid] = v[k];
-      __syncthreads();
+    for (int x = 0; x < 1024 / kWave; ++x) run += s_w[x];
+    int w[kScanPer];
+    int64_t sum = 0;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k)
-        v[k] = P.ntile[min(c0 + kChunk + (int64_t)k * 1024 + tid, n_heads - 1)];
-      int w[kPer];
-      int64_t sum = 0;
+    for (int k = 0; k < kScanPer; ++k) {
+      w[k] = c0 + tid * kScanPer + k < n_heads ? s_c[tid * kScanPer + k] : -3;
+      sum += w[k] >= 0 ? w[k] + 1 : 0;
+    }
+    __syncthreads();  // s_w is reused
+    const uint64_t incl = wave_incl_scan_u64((uint64_t)sum);
+    if (lane == kWave - 1) s_w[wave] = (int64_t)incl;
+    __syncthreads();
+    int64_t off = 0;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        w[k] = c0 + tid * kPer + k < n_heads ? s_c[tid * kPer + k] : -3;
-        sum += w[k] >= 0 ? w[k] + 1 : 0;
-      }
-      const uint64_t incl = wave_incl_scan_u64((uint64_t)sum);
-      if (lane == kWave - 1) s_w[wave] = (int64_t)incl;
-      __syncthreads();
-      int64_t off = 0, tot = 0;
+    for (int x = 0; x < 1024 / kWave; ++x) off += x < wave ? s_w[x] : 0;
+    int64_t start = run + off + (int64_t)incl - sum;
 #pragma unroll
-      for (int x = 0; x < 1024 / kWave; ++x) {
-        off += x < wave ? s_w[x] : 0;
-        tot += s_w[x];
-      }
-      int64_t start = run + off + (int64_t)incl - sum;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        if (w[k] < 0) continue;
-        const int64_t i = c0 + tid * kPer + k;
-        if (start + w[k] + 1 > L.S) P.ntile[i] = -1;
-        else P.qbase[i] = (int32_t)start;
-        start += w[k] + 1;
-      }
-      run += tot;
+    for (int k = 0; k < kScanPer; ++k) {
+      if (w[k] < 0) continue;
+      const int64_t i = c0 + tid * kScanPer + k;
+      if (start + w[k] + 1 > L.S) P.ntile[i] = -1;
+      else P.qbase[i] = (int32_t)start;
+      start += w[k] + 1;
     }
     return;
   }
@@ -864,32 +896,33 @@ __global__ __launch_bounds__(1024) void blk_scan_kernel(int64_t n_heads, BlkLayo
   }
 }
 
-__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int off) {
-  const uint32_t lo = (uint32_t)__shfl_down((int)(uint32_t)v, off, kWave);
-  const uint32_t hi = (uint32_t)__shfl_down((int)(uint32_t)(v >> 32), off, kWave);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // One wave per head: walk the head's tiles again (in the same order as the
-// count) and write one entry per tile: head, slot, chunk mask.  Within a batch
-// of 64 ids, a segmented OR leaves each run of one tile's ids with its mask in
-// the run's first lane; the last run may continue into the next batch.
+// count) and write one entry per tile: head, slot, chunk mask.  In a batch of
+// 64 ids the runs of one tile are numbered by the lanes that start them; each
+// lane ORs its chunk's bit into its run's mask in LDS (a per-wave array, in
+// order within the wave), and the run's first lane emits it.  The last run may
+// continue into the next batch: its mask is carried in the array's last slot.
 __global__ __launch_bounds__(256) void blk_fill_kernel(const int32_t* __restrict__ sel,
                                                        const int32_t* __restrict__ cnt,
                                                        AttnArgs a, BlkLayout L, char* scr) {
+  __shared__ unsigned long long s_run[kWaves][kWave + 1];
   BlkPtrs P(scr, L);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
-  if (head >= a.n_heads) return;
+  if (head >= a.n_heads) return;  // the whole wave: nothing below synchronises waves
+  // Independent loads together: tile count, chunk count, slot base, first ids.
   const int nt = P.ntile[head];
+  const int c = cnt[head];
+  const int qb = P.qbase[head];
+  const int32_t* ids = sel + head * a.cap;
+  const int id0 = ids[min(lane, a.cap - 1)];
   if (nt == 0 || nt == -2) return;
   const bool live = nt > 0;  // -1: past the slot budget, its pairs become empty entries
-  const int c = cnt[head];
-  const int32_t* ids = sel + head * a.cap;
   const int CT = L.CT;
   const int64_t tb = tree_of_head(head, a) * L.NT;
-  const int slot0 = live ? P.qbase[head] : 0;
+  const int slot0 = live ? qb : 0;
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  unsigned long long* rm = s_run[wave];
   auto emit = [&](int tile, uint64_t mask, int k) {
     const int pos = P.toff[tb + tile] + atomicAdd(&P.tcur[tb + tile], 1);
     int32_t* e = P.ent + (int64_t)pos * kBlkEntryInts;
@@ -898,36 +931,39 @@ __global__ __launch_bounds__(256) void blk_fill_kernel(const int32_t* __restrict
     e[2] = live ? (int32_t)(uint32_t)mask : 0;
     e[3] = live ? (int32_t)(uint32_t)(mask >> 32) : 0;
   };
+  if (lane == 0) rm[kWave] = 0ull;
   int k = 0, cur = -1;  // tiles emitted; tile carried from the previous batch
-  uint64_t carry = 0;
   for (int j = 0; j < c; j += kWave) {
     const bool valid = j + lane < c;
-    const int id = valid ? ids[j + lane] : 0;
+    const int id = valid ? (j == 0 ? id0 : ids[j + lane]) : 0;
     const int t = valid ? id / CT : -1;
-    uint64_t bits = valid ? (1ull << (id - t * CT)) : 0ull;
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint64_t ob = shfl_down_u64(bits, off);
-      const int ot = __shfl_down(t, off, kWave);
-      if (lane + off < kWave && ot == t) bits |= ob;
-    }
     int tp = __shfl_up(t, 1, kWave);
     if (lane == 0) tp = cur;
     const bool first = valid && t != tp;
     const uint64_t fb = __ballot(first);
-    const int t0 = __shfl(t, 0, kWave);
-    if (t0 == cur) carry |= readlane_u64(bits, 0);  // lane 0's run continues the carried tile
-    if (fb == 0ull) continue;
-    if (cur >= 0) {
-      if (lane == 0) emit(cur, carry, k);
-      ++k;
+    // Run of this lane: starts at or below it, minus one (-1: the carried run).
+    const int r = __popcll((unsigned long long)(fb & (lt | (1ull << lane)))) - 1;
+    rm[lane] = 0ull;
+    asm volatile("" ::: "memory");
+    if (valid) atomicOr(&rm[r < 0 ? kWave : r], 1ull << (id - t * CT));
+    asm volatile("" ::: "memory");
+    if (fb != 0ull) {
+      if (cur >= 0) {
+        if (lane == 0) emit(cur, rm[kWave], k);
+        ++k;
+      }
+      const int last = 63 - __clzll((long long)fb);
+      const int nrun = __popcll((unsigned long long)fb);
+      if (first && lane != last) emit(t, rm[r], k + r);
+      k += nrun - 1;
+      cur = __builtin_amdgcn_readlane(t, last);
+      asm volatile("" ::: "memory");
+      const unsigned long long lm = rm[nrun - 1];
+      asm volatile("" ::: "memory");
+      if (lane == 0) rm[kWave] = lm;
     }
-    const int last = 63 - __clzll((long long)fb);
-    if (first && lane != last) emit(t, bits, k + __popcll((unsigned long long)(fb & lt)));
-    k += __popcll((unsigned long long)fb) - 1;
-    cur = __shfl(t, last, kWave);
-    carry = readlane_u64(bits, last);
   }
-  if (cur >= 0 && lane == 0) emit(cur, carry, k);
+  if (cur >= 0 && lane == 0) emit(cur, rm[kWave], k);
 }
 
 // Work items: (tile, block of up to kBlkQ of its entries), persistent loop.
@@ -1071,21 +1107,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
                                                           st[nt], 0, 0, 0);
         }
       }
-      // Lane (li, lg) holds head li's scores for tokens nt * 16 + 4 lg + e.
+      // Lane (li, lg) holds head li's scores for tokens nt * 16 + 4 lg + e.  A
+      // step starts on a chunk boundary (g0 is a multiple of 32 and C <= 64 is
+      // a power of two >= 8), so the lane's 4 tokens of each half share a
+      // chunk: two mask bits per lane, from one shift of the head's mask.
       float x[8];
       float mloc = -INFINITY;
       const int nvalid = tok_end - g0;
+      const uint32_t smask = qvalid ? (uint32_t)(qmask >> ((g0 >> lc) - chunk0)) : 0u;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt) {
+        const bool on = ((smask >> ((nt * 16 + 4 * lg) >> lc)) & 1u) != 0u;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = nt * 16 + 4 * lg + e;
-          const int ch = ((g0 + t) >> lc) - chunk0;
-          const bool on = qvalid && t < nvalid && ((qmask >> ch) & 1ull) != 0ull;
-          const float v = on ? st[nt][e] : -INFINITY;
+          const float v = (on & (t < nvalid)) ? st[nt][e] : -INFINITY;
           x[nt * 4 + e] = v;
           mloc = fmaxf(mloc, v);
         }
+      }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
       const float m_new = fmaxf(m_i, mloc);
@@ -1165,98 +1205,104 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
   }
 }
 
-// One wave per head: the head's sink (when chunk 0 is not selected) and its
-// partial-chunk tokens, then the merge with its pairs' partials (in tile
-// order); a failed route gives a NaN row.  Loads that do not depend on each
-// other are issued together, and the partials kSB at a time.
+// kGL lanes per head (four heads per wave): the head's sink (when chunk 0 is
+// not selected) and its partial-chunk tokens, then the merge with its pairs'
+// partials (in tile order); a failed route gives a NaN row.  Loads that do not
+// depend on each other are issued together, and the partials kSB at a time.
 template <typename T, int D, bool POW2, bool BUF>
 __global__ __launch_bounds__(kThreads) void blk_merge_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
     AttnArgs a, BlkLayout L, char* scr) {
-  constexpr int DPL = D / kWave;  // dimensions per lane
+  constexpr int DPL = D / kGL;  // dimensions per lane
   BlkPtrs P(scr, L);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
-  if (head < a.n_heads) {
-    // Independent loads first: the head's counts, slot base, first chunk and query.
-    const int n = P.ntile[head];
-    const int c = cnt[head];
-    const int qb = P.qbase[head];  // meaningful only when n >= 0
-    const int first = sel[head * a.cap];
-    float q[DPL];
+  const int gl = lane & (kGL - 1), gg = lane / kGL;
+  const int64_t head = ((int64_t)blockIdx.x * kWaves + wave) * kHPW + gg;
+  const bool hv = head < a.n_heads;
+  const int64_t hh = hv ? head : 0;
+  // Independent loads first: the head's counts, slot base, first chunk and query.
+  const int n = hv ? P.ntile[hh] : -3;
+  const int c = cnt[hh];
+  const int qb = P.qbase[hh];  // meaningful only when n >= 0
+  const int first = sel[hh * a.cap];
+  float q[DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) q[e] = load_elem(Q + head * D, lane * DPL + e);
-    if (n == -2) {
+  for (int e = 0; e < DPL; ++e) q[e] = load_elem(Q + hh * D, gl * DPL + e);
+  // Every lane of the wave runs the same number of steps (shuffles below).
+  const bool sink = n >= 0 && (c == 0 || first != 0);
+  const int ne = n >= 0 ? (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C) : 0;
+  const int ne_max = (int)wave_allreduce_u64((uint64_t)ne, OpMax());
+  const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
+  const T* Kb = K + tree_of_head(hh, a) * nblk;
+  const T* Vb = a.chunked ? Kb + (int64_t)a.C * D : V + tree_of_head(hh, a) * nblk;
+  const int64_t row1 = a.n1 * (a.chunked ? 2 * a.C : a.C);  // first key row of chunk n_1
+  const float inv = 1.0f / sqrtf((float)D);
+  float m = -INFINITY, l = 0.f, acc[DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) store_elem(O + head * D, lane * DPL + e, __int_as_float(0x7fc00000));
-    } else if (n >= 0) {
-      const bool sink = c == 0 || first != 0;
-      const int ne = (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C);  // sink, then the partial chunk
-      const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
-      const T* Kb = K + tree_of_head(head, a) * nblk;
-      const T* Vb = a.chunked ? Kb + (int64_t)a.C * D : V + tree_of_head(head, a) * nblk;
-      const int64_t row1 = a.n1 * (a.chunked ? 2 * a.C : a.C);  // first key row of chunk n_1
-      const float inv = 1.0f / sqrtf((float)D);
-      float m = -INFINITY, l = 0.f, acc[DPL];
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  for (int x = 0; x < ne_max; ++x) {
+    const bool on = x < ne;
+    const int64_t row = !on ? 0 : (sink && x == 0) ? 0 : row1 + (x - (sink ? 1 : 0));
+    float kr[DPL], vr[DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-      for (int x = 0; x < ne; ++x) {
-        const int64_t row = (sink && x == 0) ? 0 : row1 + (x - (sink ? 1 : 0));
-        float kr[DPL], vr[DPL];
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-          kr[e] = load_elem(Kb + row * D, lane * DPL + e);
-          vr[e] = load_elem(Vb + row * D, lane * DPL + e);
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) part = fmaf(q[e], kr[e], part);
-        const float sc = wave_allreduce_f32(part, OpAdd()) * inv;
-        const float mn = fmaxf(m, sc);
-        const float r = __expf(m - mn), pw = __expf(sc - mn);
-        l = l * r + pw;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pw, vr[e], acc[e] * r);
-        m = mn;
-      }
-      // The pairs' partials, kSB at a time (indices clamped: every load issues).
-      constexpr int kSB = 8;
-      const float* slots = P.part + (int64_t)qb * (D + 2);
-      float M = m, den = l, num[DPL];
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) num[e] = acc[e];
-      for (int s0 = 0; s0 < n; s0 += kSB) {
-        float ms[kSB], ls[kSB], os[kSB][DPL];
-#pragma unroll
-        for (int j = 0; j < kSB; ++j) {
-          const float* r = slots + (int64_t)min(s0 + j, n - 1) * (D + 2);
-          ms[j] = r[D];
-          ls[j] = r[D + 1];
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) os[j][e] = r[lane * DPL + e];
-          if (s0 + j >= n) ms[j] = -INFINITY;
-        }
-        float Mn = M;
-#pragma unroll
-        for (int j = 0; j < kSB; ++j) Mn = fmaxf(Mn, ms[j]);
-        if (Mn == -INFINITY) continue;
-        const float rs = M == -INFINITY ? 0.f : __expf(M - Mn);
-        den *= rs;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) num[e] *= rs;
-#pragma unroll
-        for (int j = 0; j < kSB; ++j) {
-          const float w = ms[j] == -INFINITY ? 0.f : __expf(ms[j] - Mn);
-          den = fmaf(w, ls[j], den);
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) num[e] = fmaf(w, os[j][e], num[e]);
-        }
-        M = Mn;
-      }
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) store_elem(O + head * D, lane * DPL + e, num[e] / den);
+    for (int e = 0; e < DPL; ++e) {
+      kr[e] = load_elem(Kb + row * D, gl * DPL + e);
+      vr[e] = load_elem(Vb + row * D, gl * DPL + e);
     }
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) part = fmaf(q[e], kr[e], part);
+    const float sc = on ? group_allreduce<kGL>(part, OpAdd()) * inv : -INFINITY;
+    if (on) {
+      const float mn = fmaxf(m, sc);
+      const float r = __expf(m - mn), pw = __expf(sc - mn);
+      l = l * r + pw;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pw, vr[e], acc[e] * r);
+      m = mn;
+    }
+  }
+  if (n == -2) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) store_elem(O + head * D, gl * DPL + e, __int_as_float(0x7fc00000));
+  } else if (n >= 0) {
+    // The pairs' partials, kSB at a time (indices clamped: every load issues).
+    constexpr int kSB = 8;
+    const float* slots = P.part + (int64_t)qb * (D + 2);
+    float M = m, den = l, num[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) num[e] = acc[e];
+    for (int s0 = 0; s0 < n; s0 += kSB) {
+      float ms[kSB], ls[kSB], os[kSB][DPL];
+#pragma unroll
+      for (int j = 0; j < kSB; ++j) {
+        const float* r = slots + (int64_t)min(s0 + j, n - 1) * (D + 2);
+        ms[j] = r[D];
+        ls[j] = r[D + 1];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) os[j][e] = r[gl * DPL + e];
+        if (s0 + j >= n) ms[j] = -INFINITY;
+      }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < kSB; ++j) Mn = fmaxf(Mn, ms[j]);
+      if (Mn == -INFINITY) continue;
+      const float rs = M == -INFINITY ? 0.f : __expf(M - Mn);
+      den *= rs;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) num[e] *= rs;
+#pragma unroll
+      for (int j = 0; j < kSB; ++j) {
+        const float w = ms[j] == -INFINITY ? 0.f : __expf(ms[j] - Mn);
+        den = fmaf(w, ls[j], den);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) num[e] = fmaf(w, os[j][e], num[e]);
+      }
+      M = Mn;
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) store_elem(O + head * D, gl * DPL + e, num[e] / den);
   }
 }
 
@@ -1297,14 +1343,16 @@ int launch_blk(const AttnArgs& a, const void* Q, const void* K, const void* V, c
       blk_layout(a.n_heads, a.n_heads / ((int64_t)a.n_pos * a.H_q) * a.H_kv, a.T, a.C, D);
   char* scr = reinterpret_cast<char*>(scratch);
   const unsigned wave_blocks = (unsigned)((a.n_heads + kWaves - 1) / kWaves);
+  const unsigned group_blocks = (unsigned)((a.n_heads + kWaves * kHPW - 1) / (kWaves * kHPW));
   blk_zero_kernel<<<(unsigned)((max(L.NTT, (int64_t)16) + 255) / 256), 256, 0, s>>>(scr, L);
   blk_count_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
-  blk_scan_kernel<<<2, 1024, 0, s>>>(a.n_heads, L, scr);
+  blk_scan_kernel<<<(unsigned)((a.n_heads + kScanChunk - 1) / kScanChunk + 1), 1024, 0, s>>>(
+      a.n_heads, L, scr);
   blk_fill_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
   blk_attn_kernel<D, BUF><<<kBlkGrid, 256, 0, s>>>(
       reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K),
       reinterpret_cast<const bf16_t*>(V), a, L, scr);
-  blk_merge_kernel<T, D, POW2, BUF><<<wave_blocks, kThreads, 0, s>>>(
+  blk_merge_kernel<T, D, POW2, BUF><<<group_blocks, kThreads, 0, s>>>(
       reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
       reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), a, L, scr);
   blk_fallback_kernel<T, D, POW2, BUF><<<kBlkFallbackBlocks, kThreads, 0, s>>>(

@@ -36,8 +36,8 @@ struct BlkLayout {
   int32_t NT;  // tiles per (b, kvh) cache
   int64_t NTT;  // tiles in all
   int64_t S;    // slot budget
-  int64_t off_ctrl, off_qbase, off_ntile, off_tcnt, off_tcur, off_toff, off_wpre, off_ent,
-      off_part, total;
+  int64_t off_ctrl, off_qbase, off_ntile, off_wsum, off_tcnt, off_tcur, off_toff, off_wpre,
+      off_ent, off_part, total;
 };
 
 // The block path serves bf16 caches with d in {64, 128} and C in {8, 16, 32, 64}.
@@ -62,6 +62,7 @@ inline BlkLayout blk_layout(int64_t n_heads, int64_t n_trees, int64_t T, int C, 
   L.off_ctrl = take(64);
   L.off_qbase = take(n_heads * 4);
   L.off_ntile = take(n_heads * 4);
+  L.off_wsum = take((n_heads + 3) / 4 * 8);  // slots per workgroup of the count launch
   L.off_tcnt = take(L.NTT * 4);
   L.off_tcur = take(L.NTT * 4);
   L.off_toff = take((L.NTT + 1) * 4);
