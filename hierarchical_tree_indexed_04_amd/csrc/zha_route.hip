@@ -70,8 +70,11 @@ constexpr int kMaxChildren = 1024;  // C <= 1024
 #ifndef ZHA_ROUTE_TPUT_EU
 #define ZHA_ROUTE_TPUT_EU 1
 #endif
+#ifndef ZHA_ROUTE_LAT_THREADS
+#define ZHA_ROUTE_LAT_THREADS 512
+#endif
 namespace lat {
-constexpr int kThreads = 512;
+constexpr int kThreads = ZHA_ROUTE_LAT_THREADS;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kU = ZHA_ROUTE_LAT_ROWS;
 constexpr int kFMax = kRouteFrontierMax;

@@ -102,6 +102,15 @@ def test_reference_queries_r4(Z):
     run_parity(Z, g, range(6))
 
 
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_reference_queries_r16(Z, dtype):
+    # The pages' main geometry: 16 tangents per node, the max over them scores a node.
+    say(f"R=16 random reference queries ({dtype}), C=16 L=3, a ragged tail")
+    g = W.custom("r16", 111, dtype=dtype, B=1, H_q=8, H_kv=2, T=16 ** 3 * 2 + 16 * 3 + 7, C=16,
+                 L=3, p=0.9, R=16)
+    run_parity(Z, g, range(4))
+
+
 @pytest.mark.parametrize("d", [64, 256])
 def test_other_head_dims(Z, d):
     say(f"head dim {d}")
