@@ -324,9 +324,47 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
         torch.cuda.synchronize()
         dense_ms = d0.elapsed_time(d1) / dense_steps
         log(f"[bench] dense decode {dense_ms * 1e3:.1f} us per step")
+    maint = decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch)
     return {"total_ms": total_ms, "route_ms": route_ms, "attn_ms": attn_ms, "bytes": acc,
             "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap, "cold_route_ms": cold_route,
-            "cold_attn_ms": cold_attn, "copy_gbs": copy_gbs}
+            "cold_attn_ms": cold_attn, "copy_gbs": copy_gbs, "maintenance": maint}
+
+
+def decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch, reps: int = 200):
+    """Tree-maintenance cost of decode (the paper App. D-B2, amortized decode tree cost):
+    t_summ(1) is a zha_tree_update whose appended token completes one leaf per tree, t_full one
+    that completes a node at every level; t_merge(1) = (t_full - t_summ) / (L - 1).  The amortized
+    cost per decoded token is t_summ / C + t_merge * sum_{l=2..L} C^-l.  The updates rewrite nodes
+    that already hold the same values, so the tree stays valid."""
+    import torch
+    C, L, T = g.C, g.L, g.T
+    t_leaf = (T // C) * C
+    if L > 1 and t_leaf % (C * C) == 0:
+        t_leaf -= C
+    t_top = (T // C ** L) * C ** L
+
+    def timed(t_new):
+        gt = Z.with_length(gm, t_new)
+        Z.tree_update(gt, t_new - 1, Kd, qref, tree, bscratch)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            Z.tree_update(gt, t_new - 1, Kd, qref, tree, bscratch)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    t_summ = timed(t_leaf)
+    t_full = timed(t_top)
+    t_merge = (t_full - t_summ) / (L - 1) if L > 1 else 0.0
+    amort = t_summ / C + t_merge * sum(C ** -l for l in range(2, L + 1))
+    log(f"[bench] decode maintenance: one leaf per tree {t_summ:.1f} us, a node at all {L} levels "
+        f"{t_full:.1f} us; amortized {amort:.2f} us per decoded token")
+    return {"t_summ_us": t_summ, "t_full_update_us": t_full, "t_merge_us": t_merge,
+            "amortized_us_per_token": amort,
+            "how": f"mean of {reps} back-to-back zha_tree_update calls, {g.B * g.H_kv} trees; "
+                   "amortized = t_summ / C + t_merge * sum over l = 2..L of C^-l"}
 
 
 def run_block_1m(reps: int = 3):
@@ -605,6 +643,8 @@ def main():
         "tokens_per_head": by["tokens_per_head"],
         "keys_attended_frac": by["tokens_per_head"] / g.T,
         "build_ms": r["build_ms"],
+        "decode_maintenance": dict(r["maintenance"], frac_of_step=r["maintenance"][
+            "amortized_us_per_token"] / (ms_per_step * 1e3)),
         "dense_ms_per_step": r["dense_ms"],
         "speedup_vs_dense": (r["dense_ms"] / ms_per_step) if r["dense_ms"] else None,
         "at_1m": run_block_1m() if args.with_1m else None,

@@ -20,6 +20,7 @@ int check_geom(const zha_geom* g) {
   if (g->C < 2 || g->C > 1024 || g->L < 1 || g->L > kMaxLevels || g->R < 1 || g->R > 16)
     return ZHA_ERR_GEOM;
   if (g->T < 1 || g->T >= ((int64_t)1 << 31)) return ZHA_ERR_GEOM;
+  if (g->T_cap != 0 && (g->T_cap < g->T || g->T_cap >= ((int64_t)1 << 31))) return ZHA_ERR_GEOM;
   if (g->kv_layout != ZHA_KV_SPLIT && g->kv_layout != ZHA_KV_CHUNKED) return ZHA_ERR_LAYOUT;
   int64_t span = 1;
   for (int l = 0; l < g->L; ++l) {
@@ -28,6 +29,9 @@ int check_geom(const zha_geom* g) {
   }
   return ZHA_OK;
 }
+
+// Token capacity: the strides of the KV cache, the tree and the build scratch.
+int64_t capacity(const zha_geom* g) { return g->T_cap != 0 ? g->T_cap : g->T; }
 
 TreeLayout make_layout(const zha_geom* g) {
   TreeLayout lay{};
@@ -39,14 +43,15 @@ TreeLayout make_layout(const zha_geom* g) {
   for (int l = 1; l <= g->L; ++l) {
     span *= g->C;
     lay.n[l] = g->T / span;
+    lay.ncap[l] = capacity(g) / span;
   }
   for (int l = 1; l <= g->L; ++l) {
     lay.khat[l] = off;
-    off += align256(lay.n[l] * g->R * g->d * es);
+    off += align256(lay.ncap[l] * g->R * g->d * es);
   }
   for (int l = 1; l <= g->L; ++l) {
     lay.bhat[l] = off;
-    off += align256(lay.n[l] * g->R * 4);
+    off += align256(lay.ncap[l] * g->R * 4);
   }
   lay.stride = off;
   return lay;
@@ -60,6 +65,7 @@ BuildArgs make_build_args(const zha_geom* g) {
   a.d = g->d;
   a.chunked = g->kv_layout == ZHA_KV_CHUNKED;
   a.T = g->T;
+  a.Tc = capacity(g);
   return a;
 }
 
@@ -148,6 +154,27 @@ int zha_build(const zha_geom* g, const void* K, const float* qref, void* tree, v
                         reinterpret_cast<hipStream_t>(stream));
 }
 
+int zha_tree_update(const zha_geom* g, int64_t T_old, const void* K, const float* qref,
+                    void* tree, void* scratch, void* stream) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (T_old < 0 || T_old > g->T) return ZHA_ERR_GEOM;
+  BuildArgs a = make_build_args(g);
+  int64_t span = 1;
+  for (int l = 1; l <= g->L; ++l) {
+    span *= g->C;
+    a.lo[l] = T_old / span;  // nodes already summarised at the old length
+  }
+  const bool need_scratch = build_scratch_layout(a).total > 0;
+  if (K == nullptr || qref == nullptr || tree == nullptr || (need_scratch && scratch == nullptr))
+    return ZHA_ERR_NULL;
+  if (!aligned16(K) || !aligned16(qref) || !aligned16(tree) ||
+      (need_scratch && !aligned16(scratch)))
+    return ZHA_ERR_ALIGN;
+  return build_dispatch(a, g->dtype, g->d, K, qref, tree, scratch,
+                        reinterpret_cast<hipStream_t>(stream));
+}
+
 int32_t zha_route_frontier_capacity(void) { return kRouteFrontierMax; }
 
 int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes) {
@@ -206,6 +233,7 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, con
   if (cap < 1) return ZHA_ERR_CAP;
   AttnArgs a{};
   a.T = g->T;
+  a.Tc = capacity(g);
   a.n_heads = (int64_t)g->B * n_pos * g->H_q;
   a.n1 = g->T / g->C;
   a.n_pos = n_pos;
@@ -249,6 +277,7 @@ int zha_dense_decode(const zha_geom* g, const void* Q, int32_t n_pos, const void
   if (n_pos < 1) return ZHA_ERR_NPOS;
   DenseArgs a{};
   a.T = g->T;
+  a.Tc = capacity(g);
   a.n_heads = (int64_t)g->B * n_pos * g->H_q;
   a.n_pos = n_pos;
   a.H_q = g->H_q;

@@ -303,7 +303,7 @@ __device__ __forceinline__ void attend_one_head(const T* __restrict__ Q, const T
   const int64_t b = head / ((int64_t)a.n_pos * a.H_q);
   const int64_t tr = b * a.H_kv + h / a.G;
   const int32_t* ids = sel + head * a.cap;
-  const KvBlock<T, D, BUF> kvb(K, V, tr, a.T, a.C, a.chunked, sub);
+  const KvBlock<T, D, BUF> kvb(K, V, tr, a.Tc, a.C, a.chunked, sub);
 
   // This split's chunks, plus (last split) the sink when chunk 0 is not selected
   // and C_cur.  Token positions and ids fit in 31 bits (T < 2^31).
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
     const int hq = (int)(h % a.H_q);
     const int64_t b = h / ((int64_t)a.n_pos * a.H_q);
     const int64_t tr = b * a.H_kv + hq / a.G;
-    const KvBlock<T, D, BUF> kvb(K, V, tr, a.T, a.C, a.chunked, sub);
+    const KvBlock<T, D, BUF> kvb(K, V, tr, a.Tc, a.C, a.chunked, sub);
     const uint4 qv = ld16c(Q + (int64_t)h * D + sub * VEC);
     const int Cc = a.C, log2C = a.log2C;
     const int ct = c * Cc;  // chunk tokens come first, then the extras
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
   const int64_t head0 = bt * a.H_q + (int64_t)kvh * a.G + tile * GT;
   // Key row of token t: t (split) or t + (t / C) C (chunked pages of C key
   // rows then C value rows, the value row C rows further).
-  const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
+  const int64_t nblk = kv_block_elems(a.Tc, a.C, D, a.chunked);
   const T* Kt = K + (b * a.H_kv + kvh) * nblk;
   const T* Vt = a.chunked ? Kt + (int64_t)a.C * D : V + (b * a.H_kv + kvh) * nblk;
   const int64_t t0 = (a.T * split) / a.S, t1 = (a.T * (split + 1)) / a.S;
@@ -1033,7 +1033,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
     const int chunk0 = (int)(u - tr * L.NT) * L.CT;
     const int tok0 = chunk0 * C;
     const int tok_end = (int)min((int64_t)(chunk0 + L.CT) * C, a.T);
-    const KvBlock<bf16_t, D, BUF> kvb(K, V, tr, a.T, C, a.chunked, tid % SEG);
+    const KvBlock<bf16_t, D, BUF> kvb(K, V, tr, a.Tc, C, a.chunked, tid % SEG);
 
     // This lane's head (row li of the wave's 16): its Q slices as the B operand.
     const int qi = wave * 16 + li;
@@ -1233,7 +1233,7 @@ __global__ __launch_bounds__(kThreads) void blk_merge_kernel(
   const bool sink = n >= 0 && (c == 0 || first != 0);
   const int ne = n >= 0 ? (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C) : 0;
   const int ne_max = (int)wave_allreduce_u64((uint64_t)ne, OpMax());
-  const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
+  const int64_t nblk = kv_block_elems(a.Tc, a.C, D, a.chunked);
   const T* Kb = K + tree_of_head(hh, a) * nblk;
   const T* Vb = a.chunked ? Kb + (int64_t)a.C * D : V + tree_of_head(hh, a) * nblk;
   const int64_t row1 = a.n1 * (a.chunked ? 2 * a.C : a.C);  // first key row of chunk n_1
@@ -1369,7 +1369,7 @@ int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) +
                                            align256((a.n_heads + 2) * 4));
     const bool buf =
-        kv_block_elems(a.T, a.C, D, a.chunked) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
+        kv_block_elems(a.Tc, a.C, D, a.chunked) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
 #define ZHA_BAL(P2, BF)                                                                    \
   attn_balanced_kernel<T, D, P2, BF><<<(unsigned)a.S, kThreads, 0, s>>>(                  \
       reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),                       \
@@ -1386,7 +1386,7 @@ int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
     return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
   }
   const bool buf =
-      kv_block_elems(a.T, a.C, D, a.chunked) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
+      kv_block_elems(a.Tc, a.C, D, a.chunked) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
   if constexpr (sizeof(T) == 2 && (D == 64 || D == 128)) {
     if (blk_eligible(a.n_heads, a.C, D, a.dtype)) {
       if (buf) return launch_blk<T, D, true, true>(a, Q, K, V, sel, cnt, O, scratch, s);
@@ -1456,7 +1456,7 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(const bf16_t* __restric
   auto head_of = [&](int r) {
     return (b * a.n_pos + r / a.G) * a.H_q + (int64_t)kvh * a.G + r % a.G;
   };
-  const int64_t nblk = kv_block_elems(a.T, a.C, D, a.chunked);
+  const int64_t nblk = kv_block_elems(a.Tc, a.C, D, a.chunked);
   const char* Kc = reinterpret_cast<const char*>(K + tr * nblk);
   const char* Vc = reinterpret_cast<const char*>(LAY != 0 ? K + tr * nblk + (int64_t)a.C * D
                                                           : V + tr * nblk);

@@ -13,6 +13,13 @@
 //
 // One wave per node; lane l owns dims [l*DPL, l*DPL + DPL).  References are
 // processed one at a time (the chunk's keys are re-read from cache).
+//
+// Each launch summarises the nodes [lo_l, n_l) of a level: lo_l = 0 for a
+// full build; during decode (§III-A, App. D-B2: a summary is written once,
+// when the last token of its span arrives) lo_l = n_l at the previous length,
+// so only the spans completed since are visited.  Rows are strided by the
+// level's capacity nc_l, so the tree and the fp64 scratch stay in place as the
+// cache grows.
 
 #include "zha_internal.hpp"
 
@@ -34,17 +41,18 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
   constexpr int DPL = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t node = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t n1 = a.lay.n[1];
-  if (node >= (int64_t)a.n_trees * n1) return;
-  const int64_t tr = node / n1;
-  const int64_t i = node - tr * n1;
+  const int64_t lo = a.lo[1];
+  const int64_t nn = a.lay.n[1] - lo;  // nodes to summarise per tree
+  if (node >= (int64_t)a.n_trees * nn) return;
+  const int64_t tr = node / nn;
+  const int64_t i = lo + (node - tr * nn);
   const int kvh = (int)(tr % a.H_kv);
   const int C = a.lay.C;
   const int R = a.lay.R;
   const double inv_sqrt_d = 1.0 / sqrt((double)D);
   // Chunk i's C keys are consecutive rows in both layouts; only the chunk's
   // first row differs (chunked: each page holds C key rows, then C value rows).
-  const T* keys = K + tr * kv_block_elems(a.T, C, D, a.chunked) +
+  const T* keys = K + tr * kv_block_elems(a.Tc, C, D, a.chunked) +
                   i * (int64_t)C * (a.chunked ? 2 : 1) * D;
   T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
   float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
@@ -92,7 +100,7 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
     for (int e = 0; e < DPL; ++e) store_elem64(khat, row * D + lane * DPL + e, acc[e]);
     if (lane == 0) bhat[row] = (float)b;
     if (sF != nullptr) {
-      const int64_t srow = tr * n1 * R + row;
+      const int64_t srow = tr * a.lay.ncap[1] * R + row;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) sK[srow * D + lane * DPL + e] = acc[e];
       if (lane == 0) sF[srow] = F;
@@ -110,19 +118,20 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qr
                                                     int level) {
   constexpr int DPL = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t np = a.lay.n[level];
-  const int64_t nc = a.lay.n[level - 1];
+  const int64_t lo = a.lo[level];
+  const int64_t nn = a.lay.n[level] - lo;  // nodes to merge per tree
   const int64_t node = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (node >= (int64_t)a.n_trees * np) return;
-  const int64_t tr = node / np;
-  const int64_t i = node - tr * np;
+  if (node >= (int64_t)a.n_trees * nn) return;
+  const int64_t tr = node / nn;
+  const int64_t i = lo + (node - tr * nn);
   const int kvh = (int)(tr % a.H_kv);
   const int C = a.lay.C;
   const int R = a.lay.R;
   const double inv_sqrt_d = 1.0 / sqrt((double)D);
   T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[level]);
   float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[level]);
-  const int64_t child0 = tr * nc + i * C;  // first child's row (per reference block)
+  // First child's scratch row (per reference block).
+  const int64_t child0 = tr * a.lay.ncap[level - 1] + i * C;
 
   for (int r = 0; r < R; ++r) {
     // Maximum child log-mass.
@@ -158,7 +167,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qr
     for (int e = 0; e < DPL; ++e) store_elem64(khat, row * D + lane * DPL + e, acc[e]);
     if (lane == 0) bhat[row] = (float)b;
     if (pF != nullptr) {
-      const int64_t prow = (tr * np + i) * R + r;
+      const int64_t prow = (tr * a.lay.ncap[level] + i) * R + r;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) pK[prow * D + lane * DPL + e] = acc[e];
       if (lane == 0) pF[prow] = F;
@@ -174,8 +183,8 @@ static int launch_build(const BuildArgs& a, const void* K, const float* qref, vo
   auto F = [&](int l) { return reinterpret_cast<double*>(base + sc.F[l]); };
   auto Kp = [&](int l) { return reinterpret_cast<double*>(base + sc.K[l]); };
   const int L = a.lay.L;
-  {
-    const int64_t nodes = (int64_t)a.n_trees * a.lay.n[1];
+  if (a.lay.n[1] > a.lo[1]) {
+    const int64_t nodes = (int64_t)a.n_trees * (a.lay.n[1] - a.lo[1]);
     const unsigned blocks = (unsigned)((nodes + 3) / 4);
     leaf_kernel<T, D><<<blocks, 256, 0, s>>>(reinterpret_cast<const T*>(K), qref,
                                              reinterpret_cast<char*>(tree),
@@ -183,7 +192,8 @@ static int launch_build(const BuildArgs& a, const void* K, const float* qref, vo
     if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
   }
   for (int l = 2; l <= L; ++l) {
-    const int64_t nodes = (int64_t)a.n_trees * a.lay.n[l];
+    if (a.lay.n[l] == a.lo[l]) continue;  // no span of this level completed
+    const int64_t nodes = (int64_t)a.n_trees * (a.lay.n[l] - a.lo[l]);
     const unsigned blocks = (unsigned)((nodes + 3) / 4);
     merge_kernel<T, D><<<blocks, 256, 0, s>>>(qref, reinterpret_cast<char*>(tree), F(l - 1),
                                               Kp(l - 1), l < L ? F(l) : nullptr,

@@ -20,7 +20,8 @@ struct TreeLayout {
   int32_t R;
   int32_t C;
   int64_t stride;
-  int64_t n[kMaxLevels + 1];     // n[l], l = 1..L (n[0] unused)
+  int64_t n[kMaxLevels + 1];     // n[l], l = 1..L (n[0] unused): nodes of the T cached tokens
+  int64_t ncap[kMaxLevels + 1];  // rows of capacity per level (offsets and strides)
   int64_t khat[kMaxLevels + 1];  // byte offset of k_hat_l
   int64_t bhat[kMaxLevels + 1];  // byte offset of b_hat_l
 };

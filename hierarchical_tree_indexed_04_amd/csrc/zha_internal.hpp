@@ -90,9 +90,12 @@ struct BuildArgs {
   int32_t d;
   int32_t chunked;  // ZHA_KV_CHUNKED layout
   int64_t T;
+  int64_t Tc;                    // token capacity (strides)
+  int64_t lo[kMaxLevels + 1];    // first node of each level to summarise (0 for a build)
 };
 
-// fp64 F [n_trees, n_l, R] and k_hat [n_trees, n_l, R, d] for levels 1..L-1.
+// fp64 F [n_trees, nc_l, R] and k_hat [n_trees, nc_l, R, d] for levels 1..L-1
+// (nc_l: rows of capacity).
 struct BuildScratch {
   int64_t F[kMaxLevels + 1];
   int64_t K[kMaxLevels + 1];
@@ -112,6 +115,7 @@ struct RouteArgs {
 
 struct AttnArgs {
   int64_t T;
+  int64_t Tc;       // token capacity (KV strides)
   int64_t n_heads;  // B * n_pos * H_q
   int64_t n1;       // full leaf chunks
   int32_t n_pos;
@@ -128,6 +132,7 @@ struct AttnArgs {
 
 struct DenseArgs {
   int64_t T;
+  int64_t Tc;   // token capacity (KV strides)
   int64_t tps;  // tokens per split (matrix-core path; a multiple of 32)
   int64_t n_heads;
   int32_t n_pos;
@@ -163,9 +168,9 @@ inline BuildScratch build_scratch_layout(const BuildArgs& a) {
   int64_t off = 0;
   for (int l = 1; l < a.lay.L; ++l) {
     s.F[l] = off;
-    off += align256((int64_t)a.n_trees * a.lay.n[l] * a.lay.R * 8);
+    off += align256((int64_t)a.n_trees * a.lay.ncap[l] * a.lay.R * 8);
     s.K[l] = off;
-    off += align256((int64_t)a.n_trees * a.lay.n[l] * a.lay.R * a.d * 8);
+    off += align256((int64_t)a.n_trees * a.lay.ncap[l] * a.lay.R * a.d * 8);
   }
   s.total = off;
   return s;

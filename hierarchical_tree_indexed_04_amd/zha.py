@@ -31,7 +31,7 @@ class Geom(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("T", ctypes.c_int64), ("C", ctypes.c_int32),
                 ("L", ctypes.c_int32), ("R", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("kv_layout", ctypes.c_int32)]
+                ("kv_layout", ctypes.c_int32), ("T_cap", ctypes.c_int64)]
 
 
 _GP = ctypes.POINTER(Geom)
@@ -43,6 +43,7 @@ SIGNATURES = {
     "zha_tree_bytes": (ctypes.c_int, [_GP, _c_size_p, _c_size_p]),
     "zha_tree_level_offset": (ctypes.c_int, [_GP, _I32, _c_size_p, _c_size_p, _c_size_p]),
     "zha_build": (ctypes.c_int, [_GP, _VP, _VP, _VP, _VP, _VP]),
+    "zha_tree_update": (ctypes.c_int, [_GP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP]),
     "zha_route_scratch_bytes": (ctypes.c_int, [_GP, _I32, _I32, _c_size_p]),
     "zha_route": (ctypes.c_int, [_GP, _VP, _VP, _I32, ctypes.c_float, _VP, _VP, _I32, _VP, _VP,
                                  _VP, _VP]),
@@ -84,19 +85,33 @@ def _check(rc: int, where: str):
         raise ZhaError(rc, where)
 
 
-def geom(g, kv_layout: int = ZHA_KV_SPLIT) -> Geom:
-    """zha_geom from any object with B, H_q, H_kv, d, T, C, L, R and dtype ('f32'/'bf16')."""
+def geom(g, kv_layout: int = ZHA_KV_SPLIT, T_cap: int = 0) -> Geom:
+    """zha_geom from any object with B, H_q, H_kv, d, T, C, L, R and dtype ('f32'/'bf16');
+    T_cap > 0 lays the KV cache and the tree out for T_cap tokens (T of them valid)."""
     dt = g.dtype
     if isinstance(dt, str):
         dt = ZHA_BF16 if dt == "bf16" else ZHA_F32
-    return Geom(g.B, g.H_q, g.H_kv, g.d, g.T, g.C, g.L, g.R, dt, kv_layout)
+    return Geom(g.B, g.H_q, g.H_kv, g.d, g.T, g.C, g.L, g.R, dt, kv_layout, T_cap)
+
+
+def with_length(g: Geom, T: int) -> Geom:
+    """The same geometry and capacity holding T tokens (the capacity is pinned
+    to the current length when none was set)."""
+    return Geom(g.B, g.H_q, g.H_kv, g.d, T, g.C, g.L, g.R, g.dtype, g.kv_layout,
+                g.T_cap if g.T_cap else g.T)
+
+
+def capacity(g: Geom) -> int:
+    return g.T_cap if g.T_cap else g.T
 
 
 def kv_shape(g: Geom):
-    """Shape of K (and V) in the split layout, or of the KV buffer in the chunked one."""
+    """Shape of K (and V) in the split layout, or of the KV buffer in the chunked one
+    (capacity rows; the first T are the cached tokens)."""
+    tc = capacity(g)
     if g.kv_layout == ZHA_KV_CHUNKED:
-        return (g.B, g.H_kv, -(-g.T // g.C), 2, g.C, g.d)
-    return (g.B, g.H_kv, g.T, g.d)
+        return (g.B, g.H_kv, -(-tc // g.C), 2, g.C, g.d)
+    return (g.B, g.H_kv, tc, g.d)
 
 
 def tree_bytes(g: Geom):
@@ -213,6 +228,20 @@ def build(g: Geom, K, qref, tree=None, scratch=None, stream=None):
         scratch = _bytes(sb, K.device)
     _check(load().zha_build(ctypes.byref(g), _ptr(K), _ptr(qref), _ptr(tree), _ptr(scratch),
                             _stream(stream)), "zha_build")
+    return tree
+
+
+def tree_update(g: Geom, T_old: int, K, qref, tree, scratch, stream=None):
+    """zha_tree_update: extend a tree built for T_old tokens to g.T tokens in place.
+    ``tree`` and ``scratch`` are the buffers of the earlier build or update."""
+    torch = _torch()
+    _need(K, kv_shape(g), _store_dtype(g), "K")
+    _need(qref, (g.H_kv, g.R, g.d), torch.float32, "qref")
+    tb, sb = tree_bytes(g)
+    if tree.numel() * tree.element_size() < tb or (sb and scratch.numel() * scratch.element_size() < sb):
+        raise ValueError("tree_update: tree or scratch smaller than the layout needs")
+    _check(load().zha_tree_update(ctypes.byref(g), int(T_old), _ptr(K), _ptr(qref), _ptr(tree),
+                                  _ptr(scratch), _stream(stream)), "zha_tree_update")
     return tree
 
 

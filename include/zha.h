@@ -28,12 +28,13 @@
  *   zha_strerror() names it.  ZHA_ERR_LAUNCH reports a failed kernel launch.
  * - Layouts are dense, row-major, head dimension fastest:
  *     Q, O   [B, n_pos, H_q, d]   storage dtype
- *   and the KV cache in one of two layouts (zha_geom.kv_layout):
- *     ZHA_KV_SPLIT    K, V  [B, H_kv, T, d] each
- *     ZHA_KV_CHUNKED  KV    [B, H_kv, ceil(T / C), 2, C, d]: page c holds the
+ *   and the KV cache in one of two layouts (zha_geom.kv_layout), with Tc =
+ *   zha_geom.T_cap (or T when T_cap is 0) token rows per (b, kvh):
+ *     ZHA_KV_SPLIT    K, V  [B, H_kv, Tc, d] each
+ *     ZHA_KV_CHUNKED  KV    [B, H_kv, ceil(Tc / C), 2, C, d]: page c holds the
  *                     keys of tokens c*C .. c*C + C - 1, then their values;
- *                     rows of the last page past T are never read.  The
- *                     buffer is passed as K, and V must be NULL.
+ *                     rows past T are never read.  The buffer is passed as
+ *                     K, and V must be NULL.
  *   The chunked layout keeps each level-1 chunk's keys and values in one
  *   contiguous page, so the sparse gather reads 2 C d-element runs instead of
  *   two runs of C rows in separate arrays.
@@ -45,7 +46,17 @@
  * level 1 nodes are chunks of C consecutive keys, a level-l node has the C
  * level-(l-1) nodes below it as children.  Requirements: B, H_q, H_kv >= 1,
  * H_q % H_kv == 0, d in {64, 128, 256}, 2 <= C <= 1024, 1 <= L <= 16,
- * 1 <= R <= 16, n_L >= 1 (T >= C^L), T < 2^31.
+ * 1 <= R <= 16, n_L >= 1 (T >= C^L), T < 2^31, and T_cap == 0 or
+ * T <= T_cap < 2^31.
+ *
+ * Capacity (T_cap): the strides of the KV cache, of the tree blob and of the
+ * build scratch follow Tc (T_cap, or T when it is 0); every count follows T.
+ * A cache allocated for Tc tokens, and its tree, can then grow token by token
+ * in place during decode: append the token's K/V rows, call zha_tree_update
+ * with the old and new T, and route and attend with the new T (paper §III-A
+ * and App. D-B2: a leaf is summarised when its chunk completes, a parent when
+ * its last child completes; the route adds the nodes whose parent is not
+ * complete yet, App. E-E).
  */
 #ifndef ZHA_H
 #define ZHA_H
@@ -88,6 +99,7 @@ typedef struct {
   int32_t R;     /* reference queries per tree */
   int32_t dtype; /* ZHA_F32 or ZHA_BF16 */
   int32_t kv_layout; /* ZHA_KV_SPLIT or ZHA_KV_CHUNKED */
+  int64_t T_cap; /* token capacity of the KV cache and tree layout; 0 means T */
 } zha_geom;
 
 /* Human-readable text for a return code. */
@@ -97,9 +109,10 @@ const char* zha_strerror(int code);
  * Tree blob
  *
  * For each (b, kvh), at byte offset (b * H_kv + kvh) * tree_stride, the tree
- * holds for every level l = 1..L:
- *   k_hat_l [n_l, R, d]  storage dtype, at khat_offset(l)
- *   b_hat_l [n_l, R]     fp32,          at bhat_offset(l)
+ * holds for every level l = 1..L (nc_l = floor(Tc / C^l) rows of capacity, the
+ * first n_l of them valid):
+ *   k_hat_l [nc_l, R, d]  storage dtype, at khat_offset(l)
+ *   b_hat_l [nc_l, R]     fp32,          at bhat_offset(l)
  * Every array starts on a 256-byte boundary.  k_hat_{l,i,r} is the tangent
  * summary of node i for reference r, rounded to nearest-even from the exact
  * value; b_hat is the matching bias rounded to fp32 (paper §III-A: t_r(q) =
@@ -118,14 +131,30 @@ int zha_tree_level_offset(const zha_geom* g, int32_t level, size_t* khat_offset,
  *           the KV buffer, of which only the key rows are read)
  *   qref    device [H_kv, R, d] fp32 reference queries (all zero gives the
  *           plain mean of each span's keys, with b_hat = ln(span))
- *   tree    device, zha_tree_bytes() bytes, written
- *   scratch device, build_scratch_bytes, clobbered
+ *   tree    device, zha_tree_bytes() bytes, written (the n_l valid rows)
+ *   scratch device, build_scratch_bytes: receives the fp64 summaries of
+ *           levels 1..L-1, which zha_tree_update reads (keep it with the tree)
  * Leaves: F = LSE_j(q_r . k_j / sqrt(d)), k_hat = softmax-weighted key mean,
  * b_hat = F - q_r . k_hat / sqrt(d).  Parents, per reference: F_P = LSE_c F_c,
  * k_hat_P = sum_c exp(F_c - F_P) k_hat_c.  Accumulation is fp64, so the stored
  * copies are the correctly rounded values of the exact summaries. */
 int zha_build(const zha_geom* g, const void* K, const float* qref, void* tree, void* scratch,
               void* stream);
+
+/* Extend trees built (or updated) for T_old tokens to g->T tokens, in place
+ * (decode-time maintenance, paper §III-A / App. D-B2: the nodes whose spans
+ * completed between T_old and T are summarised; nothing else is touched).
+ *   T_old   0 <= T_old <= g->T; the tree and scratch hold the result of a
+ *           zha_build or zha_tree_update for T_old tokens with this same
+ *           geometry otherwise (T_old == 0: nothing built yet)
+ *   K, qref, tree, scratch as for zha_build (same buffers: scratch carries the
+ *           fp64 child summaries the new parents are merged from)
+ * Leaves [n_1(T_old), n_1(T)) are summarised and, at every level l >= 2, the
+ * parents [n_l(T_old), n_l(T)) are merged from their children, so the result
+ * is bit-identical to zha_build at T.  Returns ZHA_ERR_GEOM for T_old outside
+ * [0, T]. */
+int zha_tree_update(const zha_geom* g, int64_t T_old, const void* K, const float* qref,
+                    void* tree, void* scratch, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Routing (paper §III-C; summary page "Routing")

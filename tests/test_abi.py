@@ -31,7 +31,7 @@ def g(**kw):
 def test_library_exports_every_declared_function():
     lib = Z.load()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Z.SIGNATURES)
@@ -45,7 +45,8 @@ def test_strerror_names_every_code():
 
 
 def expected_layout(gm, es):
-    n = [None] + [gm.T // gm.C ** l for l in range(1, gm.L + 1)]
+    tc = gm.T_cap or gm.T  # rows of capacity follow the capacity, not the length
+    n = [None] + [tc // gm.C ** l for l in range(1, gm.L + 1)]
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
     off, khat, bhat = 0, {}, {}
     for l in range(1, gm.L + 1):
@@ -57,7 +58,8 @@ def expected_layout(gm, es):
     return khat, bhat, off
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(dtype=Z.ZHA_F32, R=3, T=5000), dict(C=8, L=6, T=8 ** 6 + 77)])
+@pytest.mark.parametrize("kw", [dict(), dict(dtype=Z.ZHA_F32, R=3, T=5000), dict(C=8, L=6, T=8 ** 6 + 77),
+                                dict(T=4096, T_cap=70000), dict(dtype=Z.ZHA_F32, T=5000, T_cap=5001)])
 def test_tree_layout_matches_documented_rules(kw):
     gm = g(**kw)
     es = 2 if gm.dtype == Z.ZHA_BF16 else 4
@@ -68,8 +70,9 @@ def test_tree_layout_matches_documented_rules(kw):
         assert Z.level_offset(gm, l) == (khat[l], bhat[l], stride)
     # build scratch: fp64 F and k_hat for levels 1..L-1
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = sum(a256(gm.B * gm.H_kv * (gm.T // gm.C ** l) * gm.R * 8)
-               + a256(gm.B * gm.H_kv * (gm.T // gm.C ** l) * gm.R * gm.d * 8)
+    tc = gm.T_cap or gm.T
+    want = sum(a256(gm.B * gm.H_kv * (tc // gm.C ** l) * gm.R * 8)
+               + a256(gm.B * gm.H_kv * (tc // gm.C ** l) * gm.R * gm.d * 8)
                for l in range(1, gm.L))
     assert sb == want
 
@@ -78,6 +81,7 @@ def test_tree_layout_matches_documented_rules(kw):
     (dict(d=96), -4), (dict(dtype=7), -3), (dict(H_q=6, H_kv=4), -2), (dict(C=1), -2),
     (dict(L=0), -2), (dict(R=17), -2), (dict(T=4095), -2), (dict(B=0), -2), (dict(L=17), -2),
     (dict(kv_layout=2), -10), (dict(kv_layout=-1), -10),
+    (dict(T_cap=4095), -2), (dict(T_cap=-1), -2), (dict(T_cap=1 << 31), -2),
 ])
 def test_invalid_geometry_is_rejected(kw, code):
     gm = g(**kw)
@@ -108,6 +112,12 @@ def test_null_and_argument_errors_before_any_launch():
     assert lib.zha_dense_decode(ctypes.byref(gm), buf, 0, buf, buf, buf, buf, None) == -9
     assert lib.zha_dense_decode(ctypes.byref(gm), ctypes.c_void_p(24), 1, buf, buf, buf, buf,
                                 None) == -6
+    # tree update: the old length must lie in [0, T]; pointers as for zha_build
+    for t_old in (-1, gm.T + 1):
+        assert lib.zha_tree_update(ctypes.byref(gm), t_old, buf, buf, buf, buf, None) == -2
+    assert lib.zha_tree_update(ctypes.byref(gm), 0, None, buf, buf, buf, None) == -1
+    assert lib.zha_tree_update(ctypes.byref(gm), gm.T, buf, buf, buf, None, None) == -1
+    assert lib.zha_tree_update(ctypes.byref(gm), 5, buf, buf, ctypes.c_void_p(40), buf, None) == -6
     assert lib.zha_tree_level_offset(ctypes.byref(gm), 0, ctypes.byref(n), ctypes.byref(n),
                                      ctypes.byref(n)) == -2
     # KV layout: split needs V; chunked takes the KV buffer as K and rejects a V
@@ -124,6 +134,23 @@ def test_chunked_layout_shape_and_tree_layout_are_independent():
     assert Z.kv_shape(gs) == (1, 2, 5000, 128)
     assert Z.kv_shape(gc) == (1, 2, 313, 2, 16, 128)  # ceil(5000 / 16) pages
     assert Z.tree_bytes(gs) == Z.tree_bytes(gc)
+
+
+def test_capacity_sets_strides_and_length_sets_nothing_else():
+    # Layout (tree offsets, scratch sizes, KV shape) depends on the capacity only,
+    # so a cache and tree laid out once stay valid as the length grows.
+    base = dict(T_cap=20000, C=16, L=3)
+    sizes = {Z.tree_bytes(g(T=t, **base)) for t in (4096, 5000, 19999, 20000)}
+    offs = {Z.level_offset(g(T=t, **base), 2) for t in (4096, 5000, 20000)}
+    assert len(sizes) == 1 and len(offs) == 1
+    assert Z.tree_bytes(g(T=20000)) == sizes.pop()
+    assert Z.kv_shape(g(T=4096, T_cap=20000)) == (1, 2, 20000, 128)
+    assert Z.kv_shape(g(T=4096, T_cap=20000, kv_layout=Z.ZHA_KV_CHUNKED)) == (1, 2, 1250, 2, 16, 128)
+    g2 = Z.with_length(g(T=4096), 4100)
+    assert (g2.T, g2.T_cap) == (4100, 4096) and Z.tree_bytes(Z.with_length(g(T=4096), 4096))
+    # with_length keeps the capacity, and a length beyond it is rejected
+    n = ctypes.c_size_t()
+    assert Z.load().zha_tree_bytes(ctypes.byref(g2), ctypes.byref(n), ctypes.byref(n)) == -2
 
 
 def test_scratch_sizes_are_consistent():

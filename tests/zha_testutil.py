@@ -29,9 +29,10 @@ def from_device(t, dtype: str) -> np.ndarray:
     return t.float().cpu().numpy()
 
 
-def unpack_tree(Z, g: W.Geometry, tree_np: np.ndarray, b: int, kvh: int):
-    """Level arrays (k_hat [n, R, d] float, b_hat [n, R] float32) of one tree from the blob."""
-    gm = Z.geom(g)
+def unpack_tree(Z, g: W.Geometry, tree_np: np.ndarray, b: int, kvh: int, gm=None):
+    """Level arrays (k_hat [n, R, d] float, b_hat [n, R] float32) of one tree from the blob;
+    ``gm`` gives the layout when it has a capacity beyond g.T."""
+    gm = Z.geom(g) if gm is None else gm
     out = []
     for ell in range(1, g.L + 1):
         ko, bo, stride = Z.level_offset(gm, ell)
@@ -103,11 +104,11 @@ def oracle_trees(g: W.Geometry, K: np.ndarray, qref: np.ndarray, pairs):
     return trees
 
 
-def tree_mismatch(Z, g, tree_np, trees):
+def tree_mismatch(Z, g, tree_np, trees, gm=None):
     """Counts of stored k_hat / b_hat entries where the device tree differs from the oracle's."""
     bad_k = bad_b = total = 0
     for (b, kvh), t in trees.items():
-        levels = unpack_tree(Z, g, tree_np, b, kvh)
+        levels = unpack_tree(Z, g, tree_np, b, kvh, gm)
         for ell, (k, bh) in enumerate(levels, start=1):
             lv = t.levels[ell - 1]
             bad_k += int(np.count_nonzero(k.astype(np.float64) != lv.k_store))
