@@ -343,14 +343,22 @@ def decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch, reps: int = 200):
         t_leaf -= C
     t_top = (T // C ** L) * C ** L
 
+    import ctypes
+    lib = Z.load()
+    vp = ctypes.c_void_p
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+
     def timed(t_new):
         gt = Z.with_length(gm, t_new)
-        Z.tree_update(gt, t_new - 1, Kd, qref, tree, bscratch)
+        Z.tree_update(gt, t_new - 1, Kd, qref, tree, bscratch)  # checked once through the binding
         torch.cuda.synchronize()
+        args = (ctypes.byref(gt), ctypes.c_int64(t_new - 1), vp(Kd.data_ptr()),
+                vp(qref.data_ptr()), vp(tree.data_ptr()), vp(bscratch.data_ptr()), stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            Z.tree_update(gt, t_new - 1, Kd, qref, tree, bscratch)
+            if lib.zha_tree_update(*args) != 0:
+                raise RuntimeError("zha_tree_update failed")
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
@@ -363,7 +371,7 @@ def decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch, reps: int = 200):
         f"{t_full:.1f} us; amortized {amort:.2f} us per decoded token")
     return {"t_summ_us": t_summ, "t_full_update_us": t_full, "t_merge_us": t_merge,
             "amortized_us_per_token": amort,
-            "how": f"mean of {reps} back-to-back zha_tree_update calls, {g.B * g.H_kv} trees; "
+            "how": f"mean of {reps} back-to-back zha_tree_update C-ABI calls, {g.B * g.H_kv} trees; "
                    "amortized = t_summ / C + t_merge * sum over l = 2..L of C^-l"}
 
 

@@ -22,11 +22,6 @@ int check_geom(const zha_geom* g) {
   if (g->T < 1 || g->T >= ((int64_t)1 << 31)) return ZHA_ERR_GEOM;
   if (g->T_cap != 0 && (g->T_cap < g->T || g->T_cap >= ((int64_t)1 << 31))) return ZHA_ERR_GEOM;
   if (g->kv_layout != ZHA_KV_SPLIT && g->kv_layout != ZHA_KV_CHUNKED) return ZHA_ERR_LAYOUT;
-  int64_t span = 1;
-  for (int l = 0; l < g->L; ++l) {
-    span *= g->C;
-    if (span > g->T) return ZHA_ERR_GEOM;  // n_L >= 1 needs T >= C^L
-  }
   return ZHA_OK;
 }
 

@@ -315,7 +315,7 @@ __device__ __forceinline__ void attend_one_head(const T* __restrict__ Q, const T
   bool sink = false;
   const int n1 = (int)a.n1;
   if (split == a.S - 1) {
-    sink = (c == 0) || (ids[0] != 0);
+    sink = n1 > 0 && ((c == 0) || (ids[0] != 0));  // with no full chunk, C_cur holds token 0
     n_extra = (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C);
   }
   const int ntok = ct + n_extra;
@@ -386,10 +386,11 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
 }
 
 // |I(q)| of one query head: its chunks' tokens, the tail after the last full
-// chunk and the sink when chunk 0 is not selected; 0 for a failed route.
+// chunk and the sink when chunk 0 is not selected (and exists: with no full
+// chunk the tail starts at token 0); 0 for a failed route.
 __device__ __forceinline__ int head_tokens(int c, int first_id, const AttnArgs& a) {
   if (c < 0 || c > a.cap) return 0;
-  const int sink = (c == 0 || first_id != 0) ? 1 : 0;
+  const int sink = (a.n1 > 0 && (c == 0 || first_id != 0)) ? 1 : 0;
   return c * a.C + (int)(a.T - a.n1 * a.C) + sink;
 }
 
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
     const int x0 = (int)max(lo, (int64_t)P0) - P0, x1 = (int)min(hi, (int64_t)P1) - P0;
     const int c = cnt[h];
     const int32_t* ids = sel + (int64_t)h * a.cap;
-    const bool sink = (c == 0) || (ids[0] != 0);
+    const bool sink = a.n1 > 0 && ((c == 0) || (ids[0] != 0));
     const int hq = (int)(h % a.H_q);
     const int64_t b = h / ((int64_t)a.n_pos * a.H_q);
     const int64_t tr = b * a.H_kv + hq / a.G;
@@ -1230,7 +1231,7 @@ __global__ __launch_bounds__(kThreads) void blk_merge_kernel(
 #pragma unroll
   for (int e = 0; e < DPL; ++e) q[e] = load_elem(Q + hh * D, gl * DPL + e);
   // Every lane of the wave runs the same number of steps (shuffles below).
-  const bool sink = n >= 0 && (c == 0 || first != 0);
+  const bool sink = n >= 0 && a.n1 > 0 && (c == 0 || first != 0);
   const int ne = n >= 0 ? (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C) : 0;
   const int ne_max = (int)wave_allreduce_u64((uint64_t)ne, OpMax());
   const int64_t nblk = kv_block_elems(a.Tc, a.C, D, a.chunked);

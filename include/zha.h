@@ -46,8 +46,12 @@
  * level 1 nodes are chunks of C consecutive keys, a level-l node has the C
  * level-(l-1) nodes below it as children.  Requirements: B, H_q, H_kv >= 1,
  * H_q % H_kv == 0, d in {64, 128, 256}, 2 <= C <= 1024, 1 <= L <= 16,
- * 1 <= R <= 16, n_L >= 1 (T >= C^L), T < 2^31, and T_cap == 0 or
- * T <= T_cap < 2^31.
+ * 1 <= R <= 16, 1 <= T < 2^31, and T_cap == 0 or T <= T_cap < 2^31.
+ * A context shorter than C^L leaves the upper levels empty (n_l = 0): an
+ * empty level keeps nothing and every node of the level below joins that
+ * level's frontier as a node without a complete parent (App. E-E), so the
+ * walk is the one through a tree of depth max {l : n_l >= 1}; with T < C no
+ * chunk is complete and I(q) is every cached token.
  *
  * Capacity (T_cap): the strides of the KV cache, of the tree blob and of the
  * build scratch follow Tc (T_cap, or T when it is 0); every count follows T.

@@ -79,7 +79,7 @@ def test_tree_layout_matches_documented_rules(kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), -4), (dict(dtype=7), -3), (dict(H_q=6, H_kv=4), -2), (dict(C=1), -2),
-    (dict(L=0), -2), (dict(R=17), -2), (dict(T=4095), -2), (dict(B=0), -2), (dict(L=17), -2),
+    (dict(L=0), -2), (dict(R=17), -2), (dict(T=0), -2), (dict(B=0), -2), (dict(L=17), -2),
     (dict(kv_layout=2), -10), (dict(kv_layout=-1), -10),
     (dict(T_cap=4095), -2), (dict(T_cap=-1), -2), (dict(T_cap=1 << 31), -2),
 ])
@@ -134,6 +134,18 @@ def test_chunked_layout_shape_and_tree_layout_are_independent():
     assert Z.kv_shape(gs) == (1, 2, 5000, 128)
     assert Z.kv_shape(gc) == (1, 2, 313, 2, 16, 128)  # ceil(5000 / 16) pages
     assert Z.tree_bytes(gs) == Z.tree_bytes(gc)
+
+
+def test_short_contexts_have_empty_upper_levels():
+    # T < C^L is valid (a decode context that has not filled the top level yet):
+    # the empty levels take no bytes unless a capacity reserves them.
+    for T in (1, 15, 16, 255, 4095):
+        gm = g(T=T)
+        tb, sb = Z.tree_bytes(gm)
+        expect = expected_layout(gm, 2)[2] * gm.B * gm.H_kv
+        assert tb == expect
+    assert Z.tree_bytes(g(T=1))[0] == 0
+    assert Z.tree_bytes(g(T=1, T_cap=4096)) == Z.tree_bytes(g(T=4096))
 
 
 def test_capacity_sets_strides_and_length_sets_nothing_else():

@@ -78,7 +78,7 @@ def check_length(Z, g, gm, cache, tree, qref, T, n_pos, p, steps_seed):
     assert bad_k == 0 and bad_b == 0, (T, bad_k, bad_b, total)
     Qn = W.make_query_block(gT, cache.K[:, :, :T], range(steps_seed, steps_seed + n_pos))
     Qd = to_device(Qn, g.dtype)
-    cap = gT.n_level(1)
+    cap = max(gT.n_level(1), 1)
     sel, cnt, stats, _ = Z.route(gm, tree, Qd, n_pos, p, cap)
     Od = Z.attn(gm, Qd, n_pos, cache.Kd, cache.Vd, sel, cnt, cap)
     Dd = Z.dense_decode(gm, Qd, n_pos, cache.Kd, cache.Vd)
@@ -168,3 +168,49 @@ def test_update_from_zero_equals_build(Z):
     Z.tree_update(gm, g.T, cache.Kd, qd, t_upd, torch.empty((sb,), dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(t_build, t_upd)
+
+
+@pytest.mark.parametrize("dtype,chunked", [(W.BF16, False), (W.F32, True)])
+def test_decode_from_one_token(Z, dtype, chunked):
+    # Every length from 1 to past C^L, one token per step: no full chunk (I(q)
+    # is every token), then empty upper levels, then the first top node.
+    import torch
+    C, L, T_end = 4, 3, 4 ** 3 + 9
+    say(f"decode from one token: {dtype}, {'chunked' if chunked else 'split'} KV, T 1 -> {T_end}")
+    g = W.custom("dec1", 170, dtype=dtype, B=1, H_q=4, H_kv=2, T=T_end, C=C, L=L, p=0.8, R=2)
+    K, V = W.make_kv(g)
+    qref = W.make_qref(g, K)
+    qd = torch.from_numpy(qref).cuda()
+    cache = Cache(Z, g, K, V, T_end, chunked)
+    layout = Z.ZHA_KV_CHUNKED if chunked else Z.ZHA_KV_SPLIT
+    cache.append(0, 1)
+    gm = Z.geom(W.replace(g, T=1), layout, T_cap=T_end)
+    tb, sb = Z.tree_bytes(gm)
+    tree = torch.full((tb,), 0xFF, dtype=torch.uint8, device="cuda")
+    scratch = torch.empty((sb,), dtype=torch.uint8, device="cuda")
+    Z.build(gm, cache.Kd, qd, tree, scratch)
+    check_length(Z, g, gm, cache, tree, qref, 1, 2, 0.8, 0)
+    for T in range(2, T_end + 1):
+        cache.append(T - 1, T)
+        gm = Z.with_length(gm, T)
+        Z.tree_update(gm, T - 1, cache.Kd, qd, tree, scratch)
+        par, _ = check_length(Z, g, gm, cache, tree, qref, T, 2, 0.8, 7 * T)
+    say(f"  {T_end} lengths exact; last: {par.summary()}")
+
+
+@pytest.mark.parametrize("T,dtype", [(5, W.BF16), (8 * 3 + 2, W.BF16), (70, W.BF16), (70, W.F32)])
+def test_short_context_many_heads(Z, T, dtype):
+    # 4120 query heads: the router's throughput shape, and the block attention
+    # path (bf16) or one workgroup per head (fp32), on a tree with empty upper
+    # levels (C^L = 512 > T).
+    import torch
+    say(f"short context T={T} ({dtype}), 1030 positions x 4 heads")
+    g = W.custom("short", 171, dtype=dtype, B=1, H_q=4, H_kv=1, T=T, C=8, L=3, p=0.9, R=1)
+    K, V = W.make_kv(g)
+    qref = W.make_qref(g, K)
+    cache = Cache(Z, g, K, V, T, False)
+    cache.append(0, T)
+    gm = Z.geom(g)
+    tree = Z.build(gm, cache.Kd, torch.from_numpy(qref).cuda())
+    par, _ = check_length(Z, g, gm, cache, tree, qref, T, 1030, 0.9, 0)
+    say(f"  {par.summary()}")

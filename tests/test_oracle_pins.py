@@ -301,6 +301,43 @@ def test_route_adds_orphan_nodes_to_frontier():
     assert 9 in list(r.S1)
 
 
+@pytest.mark.parametrize("T", [64, 65, 100, 511])
+def test_route_with_empty_upper_levels_equals_the_shallower_tree(T):
+    # A decode context shorter than C^L: the levels with no full node are empty,
+    # keep nothing, and every node below them joins the next frontier as an
+    # orphan, so the walk equals the one through the tree of depth
+    # L(T) = max {l : n_l >= 1}, level for level.
+    C, L, d = 8, 4, 16
+    keys = rng(306).standard_normal((T, d))
+    qref = rng(307).standard_normal((2, d))
+    deep = O.build_tree(keys, qref, C, L, O.F64)
+    Ls = max(ell for ell in range(1, L + 1) if T // C ** ell >= 1)
+    shallow = O.build_tree(keys, qref, C, Ls, O.F64)
+    for i in range(6):
+        q = 2 * rng(308 + i).standard_normal(d)
+        a, b = O.route(deep, q, 0.8), O.route(shallow, q, 0.8)
+        assert a.K[Ls:] == [0] * (L - Ls) and all(len(S) == 0 for S in a.S[Ls:])
+        assert a.K[:Ls] == b.K
+        for x, y in zip(a.S[:Ls], b.S):
+            np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("T", [1, 2, 7])
+def test_context_shorter_than_a_chunk_is_dense_attention(T):
+    # No leaf chunk is complete: I(q) is C_cur = every cached token (token 0
+    # included once), so the output is full attention whatever p is.
+    C, L, d = 8, 2, 16
+    g = rng(309)
+    K, V = g.standard_normal((T, d)), g.standard_normal((T, d))
+    tree = O.build_tree(K, np.zeros((1, d)), C, L, O.F32)
+    for p in (0.3, 0.95, 1.0):
+        q = 3 * g.standard_normal(d)
+        r, o = O.zha_head(tree, q, K, V, p)
+        assert r.K == [0, 0] and len(r.S1) == 0
+        np.testing.assert_array_equal(O.token_set(r.S1, C, T), np.arange(T))
+        np.testing.assert_allclose(o, O.dense(q, K, V), rtol=0, atol=1e-14)
+
+
 # ----------------------------------------------------------------------------
 # Attention
 # ----------------------------------------------------------------------------
