@@ -32,6 +32,11 @@ design notes of the repository):
   biases b_hat to fp32; merges use the unrounded fp64 child values.
 * Token 0 (the sink) and the tokens after the last complete leaf chunk are
   always attended; the sink is a set union, never counted twice.
+* RoPE re-anchoring (paper §III-B, reference queries): token t sits at position
+  t; a node's reference queries are rotated to the last position of its span;
+  the rotation pairs dim k with dim k + dims/2 (k < dims/2) at angle
+  position * theta_k, with the theta_k given (the model's frequencies), and
+  leaves dims >= dims unrotated.
 
 Fragility (reported, used by parity tests): a level's cut is fragile when
 (G) m < K and the score gap s_(m) - s_(m+1) is below EPS = 1e-3, or (M) a
@@ -107,48 +112,93 @@ def chunk_log_mass(q, keys) -> float:
     return float(m + math.log(np.exp(s - m).sum()))
 
 
+def rope_rotate(x, pos, dims: int, theta):
+    """Rotary position embedding (RoFormer rotation) of vectors x [..., d] to positions pos.
+
+    pos: a scalar or one position per leading index of x ([n] for x [n, ...]).  For
+    k < dims/2, the pair (x_k, x_{k + dims/2}) is rotated by the angle pos * theta_k; dims
+    from `dims` on are left as they are.  dims = 0 returns x unchanged.
+    """
+    x = np.array(x, dtype=np.float64)
+    if dims == 0:
+        return x
+    h = dims // 2
+    theta = np.asarray(theta, np.float64).reshape(h)
+    pos = np.asarray(pos, np.float64)
+    ang = pos.reshape(pos.shape + (1,) * (x.ndim - 1 - pos.ndim) + (1,)) * theta
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :h].copy(), x[..., h:dims].copy()
+    x[..., :h] = a * c - b * s
+    x[..., h:dims] = a * s + b * c
+    return x
+
+
+def node_references(qref, ell: int, n: int, C: int, rope):
+    """Reference queries [n, R, d] of the first n nodes of level ell: the shared qref [R, d],
+    or with rope = (dims, theta) qref rotated to the last position of each node's span,
+    (i + 1) C^ell - 1 (paper §III-B)."""
+    qref = np.asarray(qref, np.float64)
+    q = np.broadcast_to(qref, (n,) + qref.shape).copy()
+    if rope is None or rope[0] == 0:
+        return q
+    last = (np.arange(n, dtype=np.float64) + 1) * float(C) ** ell - 1
+    return rope_rotate(q, last, rope[0], rope[1])
+
+
 def leaf_summaries(keys, qref):
     """Tangent summaries of leaf chunks.
 
-    keys: [n, C, d] (n chunks of C raw keys), qref: [R, d].
+    keys: [n, C, d] (n chunks of C raw keys), qref: [R, d] shared by all chunks, or [n, R, d]
+    one set per chunk (rotated references).
     For each chunk and reference r (summary page "Tree Construction"; paper §III-A):
       s_j = q_r . k_j / sqrt(d),  F = LSE_j s_j,
       k_hat = sum_j softmax_j(s) k_j,  b_hat = F - q_r . k_hat / sqrt(d).
     Returns F [n, R], k_hat [n, R, d], b_hat [n, R], all fp64.
     """
     keys = np.asarray(keys, np.float64)
+    n, _, d = keys.shape
     qref = np.asarray(qref, np.float64)
-    d = keys.shape[-1]
-    s = np.einsum("ncd,rd->nrc", keys, qref) / math.sqrt(d)  # [n, R, C]
+    if qref.ndim == 2:
+        qref = np.broadcast_to(qref, (n,) + qref.shape)
+    s = np.einsum("ncd,nrd->nrc", keys, qref) / math.sqrt(d)  # [n, R, C]
     m = s.max(axis=-1, keepdims=True)
     w = np.exp(s - m)
     Z = w.sum(axis=-1)  # [n, R]
     F = m[..., 0] + np.log(Z)
     k_hat = np.einsum("nrc,ncd->nrd", w, keys) / Z[..., None]
-    b_hat = F - np.einsum("nrd,rd->nr", k_hat, qref) / math.sqrt(d)
+    b_hat = F - np.einsum("nrd,nrd->nr", k_hat, qref) / math.sqrt(d)
     return F, k_hat, b_hat
 
 
-def merge_summaries(F_child, k_child, qref):
+def merge_summaries(F_child, k_child, qref, q_child=None):
     """Parent summaries from C children each (paper App. D-B2 baseline stable-state merge).
 
-    F_child: [n, C, R], k_child: [n, C, R, d].  Per reference r, independently:
+    F_child: [n, C, R], k_child: [n, C, R, d]; qref: the parents' references, [R, d] shared
+    or [n, R, d].  Per reference r, independently:
       F_P = LSE_c F_c,  k_hat_P = sum_c exp(F_c - F_P) k_hat_c,
       b_hat_P = F_P - q_r . k_hat_P / sqrt(d).
     The sum is evaluated the way App. D-B2 keeps its statistics, a maximum m and a weight sum
     Z = sum_c exp(F_c - m): k_hat_P = sum_c exp(F_c - m) k_hat_c / Z and F_P = m + ln Z (the
     same quantity; with equal child masses every weight is exactly 1).
+    With q_child [n, C, R, d] (children summarised at their own rotated references), every
+    child's log-mass is first moved to the parent's reference (paper §III-B re-anchoring):
+      F_c <- F_c + <k_hat_c, q_P - q_c> / sqrt(d).
     """
     F_child = np.asarray(F_child, np.float64)
     k_child = np.asarray(k_child, np.float64)
+    n, C, R, d = k_child.shape
     qref = np.asarray(qref, np.float64)
-    d = k_child.shape[-1]
+    if qref.ndim == 2:
+        qref = np.broadcast_to(qref, (n,) + qref.shape)
+    if q_child is not None:
+        dq = qref[:, None, :, :] - np.asarray(q_child, np.float64)  # [n, C, R, d]
+        F_child = F_child + np.einsum("ncrd,ncrd->ncr", k_child, dq) / math.sqrt(d)
     m = F_child.max(axis=1, keepdims=True)  # [n, 1, R]
     e = np.exp(F_child - m)  # [n, C, R]
     Z = e.sum(axis=1)  # [n, R]
     F_P = m[:, 0, :] + np.log(Z)
     k_P = np.einsum("ncr,ncrd->nrd", e, k_child) / Z[..., None]
-    b_P = F_P - np.einsum("nrd,rd->nr", k_P, qref) / math.sqrt(d)
+    b_P = F_P - np.einsum("nrd,nrd->nr", k_P, qref) / math.sqrt(d)
     return F_P, k_P, b_P
 
 
@@ -177,27 +227,35 @@ class Tree:
         return self.levels[ell - 1].F.shape[0]
 
 
-def build_tree(keys, qref, C: int, L: int, dtype: str) -> Tree:
+def build_tree(keys, qref, C: int, L: int, dtype: str, rope=None) -> Tree:
     """Full tree over one KV head's keys [T, d] (paper §III-A: recursive summaries).
 
     Level 1 has n_1 = floor(T / C) chunk summaries; level ell has n_ell = floor(T / C^ell)
-    nodes, each built from its C children at level ell - 1.
+    nodes, each built from its C children at level ell - 1.  rope = (dims, theta) summarises
+    every node at its rotated references and re-anchors children to their parent's (paper
+    §III-B); None (or dims 0) uses the shared references everywhere.
     """
     keys = np.asarray(keys, np.float64)
     T, d = keys.shape
     qref = np.asarray(qref, np.float64).reshape(-1, d)
+    R = qref.shape[0]
+    roped = rope is not None and rope[0] != 0
     bias_dtype = F64 if dtype == F64 else F32
     tree = Tree(C=C, T=T, d=d, dtype=dtype)
     n1 = T // C
-    F, k, b = leaf_summaries(keys[: n1 * C].reshape(n1, C, d), qref)
+    q1 = node_references(qref, 1, n1, C, rope)
+    F, k, b = leaf_summaries(keys[: n1 * C].reshape(n1, C, d), q1)
     tree.levels.append(Level(F, k, b, round_to_store(k, dtype), round_to_store(b, bias_dtype)))
+    q_prev = q1
     for ell in range(2, L + 1):
         prev = tree.levels[-1]
         n = T // C ** ell
-        R = qref.shape[0]
+        q_ell = node_references(qref, ell, n, C, rope)
+        q_child = q_prev[: n * C].reshape(n, C, R, d) if roped else None
         F, k, b = merge_summaries(prev.F[: n * C].reshape(n, C, R),
-                                  prev.k_hat[: n * C].reshape(n, C, R, d), qref)
+                                  prev.k_hat[: n * C].reshape(n, C, R, d), q_ell, q_child)
         tree.levels.append(Level(F, k, b, round_to_store(k, dtype), round_to_store(b, bias_dtype)))
+        q_prev = q_ell
     return tree
 
 

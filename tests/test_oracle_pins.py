@@ -153,6 +153,119 @@ def test_stored_copies_are_rounded_from_fp64():
 
 
 # ----------------------------------------------------------------------------
+# RoPE re-anchoring (paper §III-B: references rotated to each node's last
+# position; children moved to the parent's reference before the merge)
+# ----------------------------------------------------------------------------
+
+def rope_theta(dims, base=10000.0):
+    return base ** (-np.arange(dims // 2, dtype=np.float64) * 2.0 / dims)
+
+
+def rotate_complex(x, pos, dims, theta):
+    # The same rotation written as complex multiplication: z_k = x_k + i x_{k+h}.
+    h = dims // 2
+    z = (x[..., :h] + 1j * x[..., h:dims]) * np.exp(1j * pos * theta)
+    out = np.array(x, dtype=np.float64)
+    out[..., :h], out[..., h:dims] = z.real, z.imag
+    return out
+
+
+def test_rope_rotation_is_a_complex_phase_and_a_group():
+    d, dims = 16, 12
+    th = rope_theta(dims)
+    x = rng(500).standard_normal((3, d))
+    for pos in (0, 1, 7, 12345, 2 ** 30 + 3):
+        r = O.rope_rotate(x, pos, dims, th)
+        np.testing.assert_allclose(r, rotate_complex(x, pos, dims, th), rtol=0, atol=1e-9)
+        np.testing.assert_array_equal(r[..., dims:], x[..., dims:])  # unrotated tail
+        np.testing.assert_allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(x, axis=-1),
+                                   rtol=1e-13)
+    np.testing.assert_array_equal(O.rope_rotate(x, 0, dims, th), x)
+    np.testing.assert_allclose(O.rope_rotate(O.rope_rotate(x, 40, dims, th), 2, dims, th),
+                               O.rope_rotate(x, 42, dims, th), rtol=0, atol=1e-12)
+    # relative positions: <R(a) q, R(b) k> depends on a - b only
+    q, k = x[0], x[1]
+    v1 = O.rope_rotate(q, 100, dims, th) @ O.rope_rotate(k, 60, dims, th)
+    v2 = O.rope_rotate(q, 47, dims, th) @ O.rope_rotate(k, 7, dims, th)
+    assert abs(v1 - v2) < 1e-12
+    # per-row positions
+    rows = O.rope_rotate(x, np.array([3, 5, 9]), dims, th)
+    for i, pos in enumerate((3, 5, 9)):
+        np.testing.assert_allclose(rows[i], rotate_complex(x[i], pos, dims, th), atol=1e-12)
+
+
+def test_rope_with_zero_frequencies_or_zero_reference_is_the_plain_tree():
+    C, L, d, T = 4, 3, 8, 4 ** 3 * 2 + 9
+    keys = rng(501).standard_normal((T, d))
+    qref = rng(502).standard_normal((3, d))
+    plain = O.build_tree(keys, qref, C, L, O.F64)
+    flat = O.build_tree(keys, qref, C, L, O.F64, rope=(d, np.zeros(d // 2)))
+    for a, b in zip(plain.levels, flat.levels):
+        np.testing.assert_array_equal(a.k_hat, b.k_hat)
+        np.testing.assert_array_equal(a.b_hat, b.b_hat)
+    z0 = O.build_tree(keys, np.zeros((1, d)), C, L, O.F64)
+    z1 = O.build_tree(keys, np.zeros((1, d)), C, L, O.F64, rope=(d, rope_theta(d)))
+    for a, b in zip(z0.levels, z1.levels):
+        np.testing.assert_array_equal(a.k_hat, b.k_hat)
+        np.testing.assert_array_equal(a.b_hat, b.b_hat)
+
+
+def test_rope_leaf_tangent_touches_the_log_mass_at_the_chunk_end():
+    C, L, d, dims = 8, 1, 16, 8
+    th = rope_theta(dims, 50.0)
+    T = C * 6
+    keys = 2 * rng(503).standard_normal((T, d))
+    qref = 2 * rng(504).standard_normal((2, d))
+    tree = O.build_tree(keys, qref, C, L, O.F64, rope=(dims, th))
+    lv = tree.levels[0]
+    g = rng(505)
+    for i in range(T // C):
+        chunk = keys[i * C:(i + 1) * C]
+        for r in range(2):
+            qc = rotate_complex(qref[r], (i + 1) * C - 1, dims, th)
+            t = lambda q: q @ lv.k_hat[i, r] / math.sqrt(d) + lv.b_hat[i, r]  # noqa: E731
+            assert abs(t(qc) - O.chunk_log_mass(qc, chunk)) < 1e-12
+            # a lower bound everywhere, strictly below at the chunk's first position
+            for _ in range(5):
+                q = qc + g.standard_normal(d)
+                assert t(q) <= O.chunk_log_mass(q, chunk) + 1e-12
+            q0 = rotate_complex(qref[r], i * C, dims, th)
+            assert t(q0) < O.chunk_log_mass(q0, chunk) - 1e-9
+
+
+def test_rope_parent_is_the_tangent_of_its_childrens_tangents_at_its_reference():
+    # Re-anchoring moves each child's tangent to the parent's rotated reference:
+    # the parent's tangent there equals LSE over the children's tangents, its
+    # gradient is their softmax-weighted k_hat, and it stays below the exact
+    # log-mass of the parent's span.
+    C, L, d, dims = 4, 3, 16, 16
+    th = rope_theta(dims, 30.0)
+    T = C ** L * 2 + 5
+    keys = 2 * rng(506).standard_normal((T, d))
+    qref = 2 * rng(507).standard_normal((2, d))
+    tree = O.build_tree(keys, qref, C, L, O.F64, rope=(dims, th))
+    g = rng(508)
+    for ell in (2, 3):
+        par, ch = tree.levels[ell - 1], tree.levels[ell - 2]
+        span = C ** ell
+        for i in range(par.F.shape[0]):
+            for r in range(2):
+                qP = rotate_complex(qref[r], (i + 1) * span - 1, dims, th)
+                kids = range(i * C, (i + 1) * C)
+                tc = np.array([qP @ ch.k_hat[c, r] / math.sqrt(d) + ch.b_hat[c, r] for c in kids])
+                lse = tc.max() + math.log(np.exp(tc - tc.max()).sum())
+                tP = qP @ par.k_hat[i, r] / math.sqrt(d) + par.b_hat[i, r]
+                assert abs(tP - lse) < 1e-11
+                w = np.exp(tc - lse)
+                np.testing.assert_allclose(par.k_hat[i, r], w @ ch.k_hat[list(kids), r],
+                                           rtol=0, atol=1e-11)
+                for _ in range(3):
+                    q = qP + g.standard_normal(d)
+                    exact = O.chunk_log_mass(q, keys[i * span:(i + 1) * span])
+                    assert q @ par.k_hat[i, r] / math.sqrt(d) + par.b_hat[i, r] <= exact + 1e-12
+
+
+# ----------------------------------------------------------------------------
 # Top-p primitive
 # ----------------------------------------------------------------------------
 
