@@ -353,7 +353,7 @@ def decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch, reps: int = 200):
         Z.tree_update(gt, t_new - 1, Kd, qref, tree, bscratch)  # checked once through the binding
         torch.cuda.synchronize()
         args = (ctypes.byref(gt), ctypes.c_int64(t_new - 1), vp(Kd.data_ptr()),
-                vp(qref.data_ptr()), vp(tree.data_ptr()), vp(bscratch.data_ptr()), stream)
+                vp(qref.data_ptr()), None, vp(tree.data_ptr()), vp(bscratch.data_ptr()), stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):

@@ -64,6 +64,18 @@ BuildArgs make_build_args(const zha_geom* g) {
   return a;
 }
 
+// Rotated references: validates and copies the frequencies into the arguments.
+int set_rope(const zha_geom* g, const zha_rope* rope, BuildArgs& a) {
+  a.rope_dims = 0;
+  if (rope == nullptr || rope->dims == 0) return ZHA_OK;
+  if (rope->dims < 0 || (rope->dims & 1) || rope->dims > g->d || rope->reserved != 0 ||
+      rope->theta == nullptr)
+    return ZHA_ERR_ROPE;
+  a.rope_dims = rope->dims;
+  for (int k = 0; k < rope->dims / 2; ++k) a.theta[k] = rope->theta[k];
+  return ZHA_OK;
+}
+
 int log2_or_neg(int C) { return (C & (C - 1)) == 0 ? __builtin_ctz((unsigned)C) : -1; }
 
 // K and V pointers per layout: split needs both, chunked takes the KV buffer
@@ -106,6 +118,7 @@ const char* zha_strerror(int code) {
     case ZHA_ERR_LAUNCH: return "kernel launch failed";
     case ZHA_ERR_NPOS: return "n_pos must be >= 1";
     case ZHA_ERR_LAYOUT: return "unknown kv_layout, or V given with the chunked layout";
+    case ZHA_ERR_ROPE: return "rope: dims must be even and in [0, d], with theta given";
     default: return "unknown error";
   }
 }
@@ -134,11 +147,13 @@ int zha_tree_level_offset(const zha_geom* g, int32_t level, size_t* khat_offset,
   return ZHA_OK;
 }
 
-int zha_build(const zha_geom* g, const void* K, const float* qref, void* tree, void* scratch,
-              void* stream) {
+int zha_build(const zha_geom* g, const void* K, const float* qref, const zha_rope* rope,
+              void* tree, void* scratch, void* stream) {
   const int rc = check_geom(g);
   if (rc) return rc;
-  const BuildArgs a = make_build_args(g);
+  BuildArgs a = make_build_args(g);
+  const int rr = set_rope(g, rope, a);
+  if (rr) return rr;
   const bool need_scratch = build_scratch_layout(a).total > 0;
   if (K == nullptr || qref == nullptr || tree == nullptr || (need_scratch && scratch == nullptr))
     return ZHA_ERR_NULL;
@@ -150,11 +165,13 @@ int zha_build(const zha_geom* g, const void* K, const float* qref, void* tree, v
 }
 
 int zha_tree_update(const zha_geom* g, int64_t T_old, const void* K, const float* qref,
-                    void* tree, void* scratch, void* stream) {
+                    const zha_rope* rope, void* tree, void* scratch, void* stream) {
   const int rc = check_geom(g);
   if (rc) return rc;
   if (T_old < 0 || T_old > g->T) return ZHA_ERR_GEOM;
   BuildArgs a = make_build_args(g);
+  const int rr = set_rope(g, rope, a);
+  if (rr) return rr;
   int64_t span = 1;
   for (int l = 1; l <= g->L; ++l) {
     span *= g->C;

@@ -14,6 +14,12 @@
 // One wave per node; lane l owns dims [l*DPL, l*DPL + DPL).  References are
 // processed one at a time (the chunk's keys are re-read from cache).
 //
+// With RoPE (§III-B, reference queries) every node is summarised at its
+// references rotated to the last position of its span, and a merge first
+// moves each child to the parent's reference: the child's log-mass there is
+// its tangent, b_hat_c + q_P . k_hat_c / sqrt(d) (equal to the pages' F_c +
+// <k_hat_c, q_P - q_c> / sqrt(d)), so the scratch keeps b_hat_c in place of F_c.
+//
 // Each launch summarises the nodes [lo_l, n_l) of a level: lo_l = 0 for a
 // full build; during decode (§III-A, App. D-B2: a summary is written once,
 // when the last token of its span arrives) lo_l = n_l at the previous length,
@@ -30,6 +36,28 @@ __device__ __forceinline__ void load_row_f64(const T* row, int lane, double* out
   constexpr int DPL = D / kWave;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) out[e] = (double)load_elem(row, lane * DPL + e);
+}
+
+// This lane's dims of reference row qr for a node whose span ends at position
+// pos: rotated by pos * theta_j in the pairs (j, j + dims/2), or as given.
+template <int D>
+__device__ __forceinline__ void node_reference(const float* __restrict__ qr, int lane,
+                                               const BuildArgs& a, double pos, double* q) {
+  constexpr int DPL = D / kWave;
+  const int dims = a.rope_dims, h = dims >> 1;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const int k = lane * DPL + e;
+    double x = (double)qr[k];
+    if (k < dims) {
+      const int j = k < h ? k : k - h;
+      const double y = (double)qr[k < h ? k + h : k - h];
+      double sn, cs;
+      sincos(pos * a.theta[j], &sn, &cs);
+      x = k < h ? x * cs - y * sn : y * sn + x * cs;
+    }
+    q[e] = x;
+  }
 }
 
 template <typename T, int D>
@@ -57,10 +85,10 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
   T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
   float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
 
+  const double pos = (double)((i + 1) * C - 1);  // the chunk's last position
   for (int r = 0; r < R; ++r) {
     double q[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) q[e] = (double)qref[((int64_t)kvh * R + r) * D + lane * DPL + e];
+    node_reference<D>(qref + ((int64_t)kvh * R + r) * D, lane, a, pos, q);
     // First key read: the maximum score of the chunk.
     double m = -INFINITY;
     for (int j = 0; j < C; ++j) {
@@ -103,12 +131,12 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
       const int64_t srow = tr * a.lay.ncap[1] * R + row;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) sK[srow * D + lane * DPL + e] = acc[e];
-      if (lane == 0) sF[srow] = F;
+      if (lane == 0) sF[srow] = a.rope_dims ? b : F;
     }
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qref,
                                                     char* __restrict__ tree,
                                                     const double* __restrict__ cF,
@@ -132,19 +160,41 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qr
   float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[level]);
   // First child's scratch row (per reference block).
   const int64_t child0 = tr * a.lay.ncap[level - 1] + i * C;
+  // Children's log-masses at the parent's rotated reference (one wave's row).
+  __shared__ double s_f[ROPE ? 4 : 1][ROPE ? 1024 : 1];
+  double* fw = s_f[ROPE ? (threadIdx.x >> 6) : 0];
+  double span = 1.0;
+  for (int l = 0; l < level; ++l) span *= C;
+  const double pos = (double)(i + 1) * span - 1.0;  // the node's last position
 
   for (int r = 0; r < R; ++r) {
+    double qp[DPL];
+    node_reference<D>(qref + ((int64_t)kvh * R + r) * D, lane, a, pos, qp);
     // Maximum child log-mass.
     double m = -INFINITY;
-    for (int c = lane; c < C; c += kWave) m = fmax(m, cF[(child0 + c) * R + r]);
-    m = group_max64<kWave>(m);
+    if constexpr (ROPE) {
+      for (int c = 0; c < C; ++c) {
+        const double* krow = cK + ((child0 + c) * R + r) * D + lane * DPL;
+        double part = 0.0;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) part = fma(qp[e], krow[e], part);
+        const double f = cF[(child0 + c) * R + r] + group_sum64<kWave>(part) * inv_sqrt_d;
+        fw[c] = f;  // every lane holds f; the row is read back by this wave only
+        m = fmax(m, f);
+      }
+    } else {
+      for (int c = lane; c < C; c += kWave) m = fmax(m, cF[(child0 + c) * R + r]);
+      m = group_max64<kWave>(m);
+    }
     // Weight sum and rescaled sum of the children's summaries, children in order.
     double Z = 0.0;
     double acc[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
     for (int c0 = 0; c0 < C; c0 += kWave) {
-      const double e_mine = (c0 + lane < C) ? exp(cF[(child0 + c0 + lane) * R + r] - m) : 0.0;
+      const double f_mine =
+          c0 + lane < C ? (ROPE ? fw[c0 + lane] : cF[(child0 + c0 + lane) * R + r]) : 0.0;
+      const double e_mine = (c0 + lane < C) ? exp(f_mine - m) : 0.0;
       const int cn = min(kWave, C - c0);
       for (int c = 0; c < cn; ++c) {
         const double w = __shfl(e_mine, c, kWave);
@@ -159,7 +209,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qr
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
       acc[e] = acc[e] / Z;
-      part = fma((double)qref[((int64_t)kvh * R + r) * D + lane * DPL + e], acc[e], part);
+      part = fma(qp[e], acc[e], part);
     }
     const double b = F - group_sum64<kWave>(part) * inv_sqrt_d;
     const int64_t row = i * R + r;
@@ -170,7 +220,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qr
       const int64_t prow = (tr * a.lay.ncap[level] + i) * R + r;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) pK[prow * D + lane * DPL + e] = acc[e];
-      if (lane == 0) pF[prow] = F;
+      if (lane == 0) pF[prow] = ROPE ? b : F;
     }
   }
 }
@@ -195,9 +245,16 @@ static int launch_build(const BuildArgs& a, const void* K, const float* qref, vo
     if (a.lay.n[l] == a.lo[l]) continue;  // no span of this level completed
     const int64_t nodes = (int64_t)a.n_trees * (a.lay.n[l] - a.lo[l]);
     const unsigned blocks = (unsigned)((nodes + 3) / 4);
-    merge_kernel<T, D><<<blocks, 256, 0, s>>>(qref, reinterpret_cast<char*>(tree), F(l - 1),
-                                              Kp(l - 1), l < L ? F(l) : nullptr,
-                                              l < L ? Kp(l) : nullptr, a, l);
+    if (a.rope_dims)
+      merge_kernel<T, D, true><<<blocks, 256, 0, s>>>(qref, reinterpret_cast<char*>(tree),
+                                                      F(l - 1), Kp(l - 1),
+                                                      l < L ? F(l) : nullptr,
+                                                      l < L ? Kp(l) : nullptr, a, l);
+    else
+      merge_kernel<T, D, false><<<blocks, 256, 0, s>>>(qref, reinterpret_cast<char*>(tree),
+                                                       F(l - 1), Kp(l - 1),
+                                                       l < L ? F(l) : nullptr,
+                                                       l < L ? Kp(l) : nullptr, a, l);
     if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
   }
   return ZHA_OK;

@@ -92,10 +92,14 @@ struct BuildArgs {
   int64_t T;
   int64_t Tc;                    // token capacity (strides)
   int64_t lo[kMaxLevels + 1];    // first node of each level to summarise (0 for a build)
+  int32_t rope_dims;             // rotated dims of the references (0: none)
+  double theta[128];             // their angular frequencies (rope_dims / 2 used)
 };
 
 // fp64 F [n_trees, nc_l, R] and k_hat [n_trees, nc_l, R, d] for levels 1..L-1
-// (nc_l: rows of capacity).
+// (nc_l: rows of capacity).  With rotated references the F slot holds the fp64
+// bias b_hat instead: a child's log-mass at its parent's reference is then its
+// tangent there, b_hat_c + q_P . k_hat_c / sqrt(d).
 struct BuildScratch {
   int64_t F[kMaxLevels + 1];
   int64_t K[kMaxLevels + 1];

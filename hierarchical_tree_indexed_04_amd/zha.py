@@ -20,7 +20,7 @@ ZHA_KV_CHUNKED = 1
 ERRORS = {
     -1: "ZHA_ERR_NULL", -2: "ZHA_ERR_GEOM", -3: "ZHA_ERR_DTYPE", -4: "ZHA_ERR_DIM",
     -5: "ZHA_ERR_P", -6: "ZHA_ERR_ALIGN", -7: "ZHA_ERR_CAP", -8: "ZHA_ERR_LAUNCH",
-    -9: "ZHA_ERR_NPOS", -10: "ZHA_ERR_LAYOUT",
+    -9: "ZHA_ERR_NPOS", -10: "ZHA_ERR_LAYOUT", -11: "ZHA_ERR_ROPE",
 }
 
 # Every function the header declares, with its ctypes signature.
@@ -34,7 +34,13 @@ class Geom(ctypes.Structure):
                 ("kv_layout", ctypes.c_int32), ("T_cap", ctypes.c_int64)]
 
 
+class Rope(ctypes.Structure):
+    _fields_ = [("dims", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("theta", ctypes.POINTER(ctypes.c_double))]
+
+
 _GP = ctypes.POINTER(Geom)
+_RP = ctypes.POINTER(Rope)
 _VP = ctypes.c_void_p
 _I32 = ctypes.c_int32
 
@@ -42,8 +48,8 @@ SIGNATURES = {
     "zha_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "zha_tree_bytes": (ctypes.c_int, [_GP, _c_size_p, _c_size_p]),
     "zha_tree_level_offset": (ctypes.c_int, [_GP, _I32, _c_size_p, _c_size_p, _c_size_p]),
-    "zha_build": (ctypes.c_int, [_GP, _VP, _VP, _VP, _VP, _VP]),
-    "zha_tree_update": (ctypes.c_int, [_GP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP]),
+    "zha_build": (ctypes.c_int, [_GP, _VP, _VP, _RP, _VP, _VP, _VP]),
+    "zha_tree_update": (ctypes.c_int, [_GP, ctypes.c_int64, _VP, _VP, _RP, _VP, _VP, _VP]),
     "zha_route_scratch_bytes": (ctypes.c_int, [_GP, _I32, _I32, _c_size_p]),
     "zha_route": (ctypes.c_int, [_GP, _VP, _VP, _I32, ctypes.c_float, _VP, _VP, _I32, _VP, _VP,
                                  _VP, _VP]),
@@ -216,8 +222,26 @@ class Workspace:
     dense_scratch: object = None
 
 
-def build(g: Geom, K, qref, tree=None, scratch=None, stream=None):
-    """zha_build; returns the tree blob (uint8 tensor)."""
+def rope(dims: int, theta):
+    """zha_rope for `dims` rotated dims with angular frequencies theta (dims / 2 values);
+    returns (struct, backing array): keep both alive for the call."""
+    import numpy as np
+    th = np.ascontiguousarray(theta, dtype=np.float64).reshape(-1)
+    if th.size != dims // 2:
+        raise ValueError(f"rope: {th.size} frequencies for {dims} dims")
+    return Rope(dims, 0, th.ctypes.data_as(ctypes.POINTER(ctypes.c_double))), th
+
+
+def _rope_ref(r):
+    if r is None:
+        return None
+    if isinstance(r, tuple) and len(r) == 2 and isinstance(r[0], Rope):
+        return ctypes.byref(r[0])
+    raise TypeError("rope: pass the value returned by zha.rope(dims, theta)")
+
+
+def build(g: Geom, K, qref, tree=None, scratch=None, stream=None, rope=None):
+    """zha_build; returns the tree blob (uint8 tensor).  rope: zha.rope(dims, theta) or None."""
     torch = _torch()
     _need(K, kv_shape(g), _store_dtype(g), "K")
     _need(qref, (g.H_kv, g.R, g.d), torch.float32, "qref")
@@ -226,12 +250,12 @@ def build(g: Geom, K, qref, tree=None, scratch=None, stream=None):
         tree = _bytes(tb, K.device)
     if scratch is None:
         scratch = _bytes(sb, K.device)
-    _check(load().zha_build(ctypes.byref(g), _ptr(K), _ptr(qref), _ptr(tree), _ptr(scratch),
-                            _stream(stream)), "zha_build")
+    _check(load().zha_build(ctypes.byref(g), _ptr(K), _ptr(qref), _rope_ref(rope), _ptr(tree),
+                            _ptr(scratch), _stream(stream)), "zha_build")
     return tree
 
 
-def tree_update(g: Geom, T_old: int, K, qref, tree, scratch, stream=None):
+def tree_update(g: Geom, T_old: int, K, qref, tree, scratch, stream=None, rope=None):
     """zha_tree_update: extend a tree built for T_old tokens to g.T tokens in place.
     ``tree`` and ``scratch`` are the buffers of the earlier build or update."""
     torch = _torch()
@@ -240,8 +264,9 @@ def tree_update(g: Geom, T_old: int, K, qref, tree, scratch, stream=None):
     tb, sb = tree_bytes(g)
     if tree.numel() * tree.element_size() < tb or (sb and scratch.numel() * scratch.element_size() < sb):
         raise ValueError("tree_update: tree or scratch smaller than the layout needs")
-    _check(load().zha_tree_update(ctypes.byref(g), int(T_old), _ptr(K), _ptr(qref), _ptr(tree),
-                                  _ptr(scratch), _stream(stream)), "zha_tree_update")
+    _check(load().zha_tree_update(ctypes.byref(g), int(T_old), _ptr(K), _ptr(qref),
+                                  _rope_ref(rope), _ptr(tree), _ptr(scratch), _stream(stream)),
+           "zha_tree_update")
     return tree
 
 

@@ -89,7 +89,8 @@ enum {
   ZHA_ERR_CAP = -7,    /* cap < 1 */
   ZHA_ERR_LAUNCH = -8, /* a kernel launch failed */
   ZHA_ERR_NPOS = -9,   /* n_pos < 1 */
-  ZHA_ERR_LAYOUT = -10 /* unknown kv_layout, or V given with ZHA_KV_CHUNKED */
+  ZHA_ERR_LAYOUT = -10, /* unknown kv_layout, or V given with ZHA_KV_CHUNKED */
+  ZHA_ERR_ROPE = -11    /* rope->dims odd, negative or > d, or theta NULL */
 };
 
 typedef struct {
@@ -105,6 +106,23 @@ typedef struct {
   int32_t kv_layout; /* ZHA_KV_SPLIT or ZHA_KV_CHUNKED */
   int64_t T_cap; /* token capacity of the KV cache and tree layout; 0 means T */
 } zha_geom;
+
+/* Rotary position embedding of the model, for re-anchoring the tree's
+ * reference queries (paper §III-B, reference queries).  Token t sits at
+ * position t.  A node's references are rotated to the last position of its
+ * span, (i + 1) C^l - 1: for k < dims / 2 the pair (q_k, q_{k + dims/2}) turns
+ * by the angle position * theta[k] (a RoFormer rotation in rotate-half
+ * pairing); dims from `dims` on are not rotated.  Before a merge each child's
+ * log-mass is moved to the parent's reference, F_c + <k_hat_c, q_P - q_c> /
+ * sqrt(d), which is the child's tangent evaluated at q_P.
+ *   dims   even, 0 <= dims <= d (0: no rotation)
+ *   theta  host, dims / 2 angular frequencies in radians per position; read
+ *          during the call only */
+typedef struct {
+  int32_t dims;
+  int32_t reserved; /* must be 0 */
+  const double* theta;
+} zha_rope;
 
 /* Human-readable text for a return code. */
 const char* zha_strerror(int code);
@@ -135,6 +153,9 @@ int zha_tree_level_offset(const zha_geom* g, int32_t level, size_t* khat_offset,
  *           the KV buffer, of which only the key rows are read)
  *   qref    device [H_kv, R, d] fp32 reference queries (all zero gives the
  *           plain mean of each span's keys, with b_hat = ln(span))
+ *   rope    host, NULL (or dims 0) for shared references; else every node is
+ *           summarised at its rotated references and children are re-anchored
+ *           to the parent's (zha_rope above).  ZHA_ERR_ROPE if invalid.
  *   tree    device, zha_tree_bytes() bytes, written (the n_l valid rows)
  *   scratch device, build_scratch_bytes: receives the fp64 summaries of
  *           levels 1..L-1, which zha_tree_update reads (keep it with the tree)
@@ -142,8 +163,8 @@ int zha_tree_level_offset(const zha_geom* g, int32_t level, size_t* khat_offset,
  * b_hat = F - q_r . k_hat / sqrt(d).  Parents, per reference: F_P = LSE_c F_c,
  * k_hat_P = sum_c exp(F_c - F_P) k_hat_c.  Accumulation is fp64, so the stored
  * copies are the correctly rounded values of the exact summaries. */
-int zha_build(const zha_geom* g, const void* K, const float* qref, void* tree, void* scratch,
-              void* stream);
+int zha_build(const zha_geom* g, const void* K, const float* qref, const zha_rope* rope,
+              void* tree, void* scratch, void* stream);
 
 /* Extend trees built (or updated) for T_old tokens to g->T tokens, in place
  * (decode-time maintenance, paper §III-A / App. D-B2: the nodes whose spans
@@ -151,14 +172,15 @@ int zha_build(const zha_geom* g, const void* K, const float* qref, void* tree, v
  *   T_old   0 <= T_old <= g->T; the tree and scratch hold the result of a
  *           zha_build or zha_tree_update for T_old tokens with this same
  *           geometry otherwise (T_old == 0: nothing built yet)
- *   K, qref, tree, scratch as for zha_build (same buffers: scratch carries the
- *           fp64 child summaries the new parents are merged from)
+ *   K, qref, rope, tree, scratch as for zha_build (the same rope as the
+ *           build; scratch carries the fp64 child summaries the new parents
+ *           are merged from)
  * Leaves [n_1(T_old), n_1(T)) are summarised and, at every level l >= 2, the
  * parents [n_l(T_old), n_l(T)) are merged from their children, so the result
  * is bit-identical to zha_build at T.  Returns ZHA_ERR_GEOM for T_old outside
  * [0, T]. */
 int zha_tree_update(const zha_geom* g, int64_t T_old, const void* K, const float* qref,
-                    void* tree, void* scratch, void* stream);
+                    const zha_rope* rope, void* tree, void* scratch, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Routing (paper §III-C; summary page "Routing")

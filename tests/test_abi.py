@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 def test_strerror_names_every_code():
     lib = Z.load()
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11]:
         assert lib.zha_strerror(code) not in (None, b"", b"unknown error")
     assert lib.zha_strerror(-1000) == b"unknown error"
 
@@ -95,8 +95,21 @@ def test_null_and_argument_errors_before_any_launch():
     buf = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation
     n = ctypes.c_size_t()
     assert lib.zha_tree_bytes(None, ctypes.byref(n), ctypes.byref(n)) == -1
-    assert lib.zha_build(ctypes.byref(gm), None, buf, buf, buf, None) == -1
-    assert lib.zha_build(ctypes.byref(gm), ctypes.c_void_p(17), buf, buf, buf, None) == -6
+    assert lib.zha_build(ctypes.byref(gm), None, buf, None, buf, buf, None) == -1
+    assert lib.zha_build(ctypes.byref(gm), ctypes.c_void_p(17), buf, None, buf, buf, None) == -6
+    # rope: even dims in [0, d], frequencies given, reserved field zero
+    th = (ctypes.c_double * 64)()
+    tp = ctypes.cast(th, ctypes.POINTER(ctypes.c_double))
+    for r in (Z.Rope(3, 0, tp), Z.Rope(-2, 0, tp), Z.Rope(130, 0, tp), Z.Rope(8, 0, None),
+              Z.Rope(8, 1, tp)):
+        assert lib.zha_build(ctypes.byref(gm), buf, buf, ctypes.byref(r), buf, buf, None) == -11
+        assert lib.zha_tree_update(ctypes.byref(gm), 0, buf, buf, ctypes.byref(r), buf, buf,
+                                   None) == -11
+    # a valid rope passes validation (the call then fails on the NULL keys)
+    r = Z.Rope(128, 0, tp)
+    assert lib.zha_build(ctypes.byref(gm), None, buf, ctypes.byref(r), buf, buf, None) == -1
+    assert lib.zha_build(ctypes.byref(gm), None, buf, ctypes.byref(Z.Rope(0, 0, None)), buf,
+                         buf, None) == -1
     # p outside (0, 1]
     for p in (0.0, -0.5, 1.5, math.nan):
         assert lib.zha_route(ctypes.byref(gm), buf, buf, 1, p, buf, buf, 4, None, None, None,
@@ -114,10 +127,11 @@ def test_null_and_argument_errors_before_any_launch():
                                 None) == -6
     # tree update: the old length must lie in [0, T]; pointers as for zha_build
     for t_old in (-1, gm.T + 1):
-        assert lib.zha_tree_update(ctypes.byref(gm), t_old, buf, buf, buf, buf, None) == -2
-    assert lib.zha_tree_update(ctypes.byref(gm), 0, None, buf, buf, buf, None) == -1
-    assert lib.zha_tree_update(ctypes.byref(gm), gm.T, buf, buf, buf, None, None) == -1
-    assert lib.zha_tree_update(ctypes.byref(gm), 5, buf, buf, ctypes.c_void_p(40), buf, None) == -6
+        assert lib.zha_tree_update(ctypes.byref(gm), t_old, buf, buf, None, buf, buf, None) == -2
+    assert lib.zha_tree_update(ctypes.byref(gm), 0, None, buf, None, buf, buf, None) == -1
+    assert lib.zha_tree_update(ctypes.byref(gm), gm.T, buf, buf, None, buf, None, None) == -1
+    assert lib.zha_tree_update(ctypes.byref(gm), 5, buf, buf, None, ctypes.c_void_p(40), buf,
+                               None) == -6
     assert lib.zha_tree_level_offset(ctypes.byref(gm), 0, ctypes.byref(n), ctypes.byref(n),
                                      ctypes.byref(n)) == -2
     # KV layout: split needs V; chunked takes the KV buffer as K and rejects a V

@@ -96,11 +96,12 @@ def compare_head(par: Parity, r: O.Route, sel_row: np.ndarray, cnt: int, stats: 
             par.out_bad.append((tag, err))
 
 
-def oracle_trees(g: W.Geometry, K: np.ndarray, qref: np.ndarray, pairs):
+def oracle_trees(g: W.Geometry, K: np.ndarray, qref: np.ndarray, pairs, rope=None):
+    """Oracle trees per (b, kvh); rope = (dims, theta) or None."""
     trees = {}
     for b, kvh in pairs:
         keys = W.to_float(K[b, kvh], g.dtype).astype(np.float64)
-        trees[(b, kvh)] = O.build_tree(keys, qref[kvh], g.C, g.L, g.dtype)
+        trees[(b, kvh)] = O.build_tree(keys, qref[kvh], g.C, g.L, g.dtype, rope=rope)
     return trees
 
 
