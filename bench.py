@@ -229,10 +229,11 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     stream = vp(torch.cuda.current_stream().cuda_stream)
     tree_p, k_p, v_p = vp(tree.data_ptr()), vp(Kd.data_ptr()), vp(Vd.data_ptr())
     rs_p, as_p = vp(rscratch.data_ptr()), vp(ascratch.data_ptr())
-    args_r = [(gref, tree_p, vp(Qd[i].data_ptr()), 1, ctypes.c_float(g.p), vp(sel[i].data_ptr()),
+    args_r = [(gref, tree_p, vp(Qd[i].data_ptr()), 1, None, ctypes.c_float(g.p),
+               vp(sel[i].data_ptr()),
                vp(cnt[i].data_ptr()), cap, vp(stats[i].data_ptr()), None, rs_p, stream)
               for i in range(n)]
-    args_a = [(gref, vp(Qd[i].data_ptr()), 1, k_p, v_p, vp(sel[i].data_ptr()),
+    args_a = [(gref, vp(Qd[i].data_ptr()), 1, None, k_p, v_p, vp(sel[i].data_ptr()),
                vp(cnt[i].data_ptr()), cap, vp(O[i].data_ptr()), as_p, stream) for i in range(n)]
     zr, za = lib.zha_route, lib.zha_attn
 
@@ -541,6 +542,102 @@ def run_crossover(steps: int):
                                 "calls)"}), flush=True)
 
 
+def run_prefill(block: int, reps: int):
+    """Causal prefill of the 128K GQA workload (B=1, H_q=32/H_kv=4, d=128, T=131072, C=32,
+    L=3, p=0.95): every cached token is also a query seeing the tokens up to itself (ctx_len =
+    t + 1), routed and attended in calls of `block` positions over a tree built once on the
+    prompt.  Queries 3 k_j + N(0, 0.3^2) with j uniform over the visible tokens, drawn on the
+    device from a seeded generator."""
+    import torch
+
+    from hierarchical_tree_indexed_04_amd import zha as Z
+    Z.load()
+    torch.cuda.set_device(0)
+    g = W.CONFIGS[2]
+    K, V = W.make_kv(g)
+    gm = Z.geom(g)
+    Kd, Vd = to_dev(torch, K, g.dtype), to_dev(torch, V, g.dtype)
+    del K, V
+    T = g.T
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20240)
+    t = torch.arange(T, device="cuda")
+    j = torch.minimum((torch.rand((T, g.H_q), generator=gen, device="cuda")
+                       * (t[:, None] + 1)).long(), t[:, None])
+    kvh = (torch.arange(g.H_q, device="cuda") // g.G)[None, :]
+    Qd = (3.0 * Kd[0][kvh, j].float() + 0.3 * torch.randn((T, g.H_q, g.d), generator=gen,
+                                                            device="cuda")).to(Kd.dtype)[None]
+    ctx = (t + 1).to(torch.int32)[None].contiguous()
+    del j
+    qref = torch.zeros((g.H_kv, g.R, g.d), dtype=torch.float32, device="cuda")
+    tb, sb = Z.tree_bytes(gm)
+    tree = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    bsc = torch.empty(max(sb, 1), dtype=torch.uint8, device="cuda")
+    cap = 1024
+    sel = torch.empty((1, block, g.H_q, cap), dtype=torch.int32, device="cuda")
+    cnt_all = torch.empty((1, T, g.H_q), dtype=torch.int32, device="cuda")
+    O = torch.empty((1, T, g.H_q, g.d), dtype=Kd.dtype, device="cuda")
+    rsc = torch.empty(max(Z.route_scratch_bytes(gm, block, cap), 1), dtype=torch.uint8,
+                      device="cuda")
+    asc = torch.empty(max(Z.attn_scratch_bytes(gm, block, cap), 1), dtype=torch.uint8,
+                      device="cuda")
+    starts = list(range(0, T, block))
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def prefill(evs=None):
+        Z.build(gm, Kd, qref, tree, bsc)
+        if evs:
+            evs[0].record()
+        for i, t0 in enumerate(starts):
+            n = min(block, T - t0)
+            Qb, cb = Qd[:, t0:t0 + n], ctx[:, t0:t0 + n]
+            sb_, cnt = sel[:, :n], cnt_all[:, t0:t0 + n]
+            Z.route(gm, tree, Qb, n, g.p, cap, want_stats=False, want_gap=False,
+                    out=(sb_, cnt, None, None), scratch=rsc, ctx_len=cb)
+            if evs:
+                evs[1 + 2 * i].record()
+            Z.attn(gm, Qb, n, Kd, Vd, sb_, cnt, cap, O=O[:, t0:t0 + n], scratch=asc, ctx_len=cb)
+            if evs:
+                evs[2 + 2 * i].record()
+
+    prefill()
+    torch.cuda.synchronize()
+    c = cnt_all.cpu().numpy()
+    if (c < 0).any() or (c > cap).any():
+        raise RuntimeError("prefill: a route overflowed the frontier capacity or the list cap")
+    if not torch.isfinite(O).all():
+        raise RuntimeError("prefill: non-finite output")
+    tail = (np.arange(1, T + 1) % g.C)[None, :, None]
+    toks = c.astype(np.int64) * g.C + tail  # + the sink when chunk 0 is not selected
+    e_start, e_end = ev(), ev()
+    totals, builds, routes, attns = [], [], [], []
+    for _ in range(reps):
+        evs = [ev() for _ in range(1 + 2 * len(starts))]
+        e_start.record()
+        prefill(evs)
+        e_end.record()
+        torch.cuda.synchronize()
+        totals.append(e_start.elapsed_time(e_end))
+        builds.append(e_start.elapsed_time(evs[0]))
+        routes.append(sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(starts))))
+        attns.append(sum(evs[2 * i + 1].elapsed_time(evs[2 * i + 2]) for i in range(len(starts))))
+    tot, b_ms, r_ms, a_ms = (float(np.median(x)) for x in (totals, builds, routes, attns))
+    log(f"[prefill] {T} tokens in {len(starts)} calls of {block}: {tot:.2f} ms (build {b_ms:.2f}, "
+        f"route {r_ms:.2f}, attn {a_ms:.2f}); {T / (tot * 1e-3) / 1e6:.2f} M tokens/s")
+    print(json.dumps({
+        "prefill": {"tokens_per_s": T / (tot * 1e-3), "ms": tot, "build_ms": b_ms,
+                    "route_ms": r_ms, "attn_ms": a_ms, "calls": len(starts),
+                    "positions_per_call": block, "cap": cap,
+                    "keys_attended_frac_mean": float(np.mean(toks / np.arange(1, T + 1)[None, :, None])),
+                    "tokens_per_query_head_mean": float(toks.mean())},
+        "workload": f"causal prefill of {g.name}: B={g.B}, H_q={g.H_q}/H_kv={g.H_kv}, d={g.d}, "
+                    f"T={T}, C={g.C}, L={g.L}, p={g.p}, bf16; query at position t sees t + 1 tokens",
+        "timing": f"median of {reps} full prefills (tree build + every call), HIP events"}),
+        flush=True)
+
+
 def copy_calibration():
     """One plain copy of 1 GiB: reads and writes 2^30 bytes each, for scaling HBM counters."""
     import torch
@@ -566,6 +663,9 @@ def main():
                     help="also time the 1M-context block workload (2048 positions routed at once)")
     ap.add_argument("--crossover", action="store_true",
                     help="only run the context-length sweep of ZHA against dense decode")
+    ap.add_argument("--prefill", type=int, default=0, metavar="BLOCK",
+                    help="only run a causal prefill of the 128K workload in calls of BLOCK "
+                         "positions")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -574,6 +674,9 @@ def main():
         return
     if args.crossover:
         run_crossover(max(3, min(args.steps, 20)))
+        return
+    if args.prefill:
+        run_prefill(args.prefill, max(1, min(args.steps, 5)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU: the hot path has no multi-GPU mode "

@@ -25,6 +25,9 @@ int check_geom(const zha_geom* g) {
   return ZHA_OK;
 }
 
+// C^l, saturated past 2^40 (any span above 2^31 > T leaves its level empty).
+int64_t next_span(int64_t span, int C) { return span > ((int64_t)1 << 40) ? span : span * C; }
+
 // Token capacity: the strides of the KV cache, the tree and the build scratch.
 int64_t capacity(const zha_geom* g) { return g->T_cap != 0 ? g->T_cap : g->T; }
 
@@ -36,7 +39,7 @@ TreeLayout make_layout(const zha_geom* g) {
   const int64_t es = g->dtype == ZHA_BF16 ? 2 : 4;
   int64_t span = 1, off = 0;
   for (int l = 1; l <= g->L; ++l) {
-    span *= g->C;
+    span = next_span(span, g->C);
     lay.n[l] = g->T / span;
     lay.ncap[l] = capacity(g) / span;
   }
@@ -174,7 +177,7 @@ int zha_tree_update(const zha_geom* g, int64_t T_old, const void* K, const float
   if (rr) return rr;
   int64_t span = 1;
   for (int l = 1; l <= g->L; ++l) {
-    span *= g->C;
+    span = next_span(span, g->C);
     a.lo[l] = T_old / span;  // nodes already summarised at the old length
   }
   const bool need_scratch = build_scratch_layout(a).total > 0;
@@ -199,7 +202,8 @@ int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_
   return ZHA_OK;
 }
 
-int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos, float p,
+int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
+              const int32_t* ctx_len, float p,
               int32_t* sel, int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap,
               void* scratch, void* stream) {
   const int rc = check_geom(g);
@@ -211,6 +215,10 @@ int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
   if (!aligned16(tree) || !aligned16(Q)) return ZHA_ERR_ALIGN;
   RouteArgs a{};
   a.lay = make_layout(g);
+  a.T = g->T;
+  a.ctx = ctx_len;
+  a.span[0] = 1;
+  for (int l = 1; l <= g->L; ++l) a.span[l] = next_span(a.span[l - 1], g->C);
   a.n_heads = (int64_t)g->B * n_pos * g->H_q;
   a.n_pos = n_pos;
   a.H_q = g->H_q;
@@ -236,7 +244,8 @@ int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t
   return ZHA_OK;
 }
 
-int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, const void* V,
+int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx_len,
+             const void* K, const void* V,
              const int32_t* sel, const int32_t* cnt, int32_t cap, void* O, void* scratch,
              void* stream) {
   const int rc = check_geom(g);
@@ -246,6 +255,7 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, con
   AttnArgs a{};
   a.T = g->T;
   a.Tc = capacity(g);
+  a.ctx = ctx_len;
   a.n_heads = (int64_t)g->B * n_pos * g->H_q;
   a.n1 = g->T / g->C;
   a.n_pos = n_pos;

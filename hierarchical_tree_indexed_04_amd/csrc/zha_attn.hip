@@ -293,7 +293,8 @@ __device__ __forceinline__ void attend_one_head(const T* __restrict__ Q, const T
   __shared__ int32_t s_ids[kIds];
   const int tid = threadIdx.x;
   const int sub = tid % LPR, grp = tid / LPR;
-  const int c = cnt[head];
+  const int64_t Th = visible_len(a, head);  // tokens this head may see
+  const int c = Th < 0 ? -1 : cnt[head];
   if (c < 0 || c > a.cap) {  // overflowed or failed route: the row is NaN
     if (split == 0)
       for (int t = tid; t < D; t += kThreads) store_elem(O + head * D, t, __int_as_float(0x7fc00000));
@@ -313,10 +314,10 @@ __device__ __forceinline__ void attend_one_head(const T* __restrict__ Q, const T
   const int ct = (c1 - c0) * Cc;  // chunk tokens come first, then the extras
   int n_extra = 0;
   bool sink = false;
-  const int n1 = (int)a.n1;
+  const int n1 = (int)(Th / Cc);  // full chunks within the visible tokens
   if (split == a.S - 1) {
     sink = n1 > 0 && ((c == 0) || (ids[0] != 0));  // with no full chunk, C_cur holds token 0
-    n_extra = (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C);
+    n_extra = (sink ? 1 : 0) + (int)(Th - (int64_t)n1 * Cc);
   }
   const int ntok = ct + n_extra;
 
@@ -388,10 +389,11 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
 // |I(q)| of one query head: its chunks' tokens, the tail after the last full
 // chunk and the sink when chunk 0 is not selected (and exists: with no full
 // chunk the tail starts at token 0); 0 for a failed route.
-__device__ __forceinline__ int head_tokens(int c, int first_id, const AttnArgs& a) {
-  if (c < 0 || c > a.cap) return 0;
-  const int sink = (a.n1 > 0 && (c == 0 || first_id != 0)) ? 1 : 0;
-  return c * a.C + (int)(a.T - a.n1 * a.C) + sink;
+__device__ __forceinline__ int head_tokens(int c, int first_id, int64_t Th, const AttnArgs& a) {
+  if (c < 0 || c > a.cap || Th < 0) return 0;
+  const int64_t n1 = Th / a.C;
+  const int sink = (n1 > 0 && (c == 0 || first_id != 0)) ? 1 : 0;
+  return c * a.C + (int)(Th - n1 * a.C) + sink;
 }
 
 // Balanced split-KV over all heads of the call: workgroup w owns tokens
@@ -422,21 +424,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
 
   // 1. Prefix of per-head token counts (thread tid owns heads [tid E, tid E + E)).
   int cv[kE], fv[kE];
+  int64_t lv[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
     const int h = tid * E + e;
     cv[e] = -1;
     fv[e] = 0;
+    lv[e] = -1;
     if (e < E && h < nh) {
       cv[e] = cnt[h];
       fv[e] = sel[(int64_t)h * a.cap];  // read even when unused: the buffer has it
+      lv[e] = visible_len(a, h);
     }
   }
   uint32_t tv[kE];
   uint32_t run = 0;
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
-    tv[e] = (e < E && tid * E + e < nh) ? (uint32_t)head_tokens(cv[e], fv[e], a) : 0u;
+    tv[e] = (e < E && tid * E + e < nh) ? (uint32_t)head_tokens(cv[e], fv[e], lv[e], a) : 0u;
     run += tv[e];
   }
   const uint32_t incl = wave_incl_scan_u32(run);
@@ -486,7 +491,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
     const int x0 = (int)max(lo, (int64_t)P0) - P0, x1 = (int)min(hi, (int64_t)P1) - P0;
     const int c = cnt[h];
     const int32_t* ids = sel + (int64_t)h * a.cap;
-    const bool sink = a.n1 > 0 && ((c == 0) || (ids[0] != 0));
+    const int64_t Th = visible_len(a, h);  // valid: the head has tokens
+    const int n1 = (int)(Th / a.C);
+    const bool sink = n1 > 0 && ((c == 0) || (ids[0] != 0));
     const int hq = (int)(h % a.H_q);
     const int64_t b = h / ((int64_t)a.n_pos * a.H_q);
     const int64_t tr = b * a.H_kv + hq / a.G;
@@ -494,7 +501,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
     const uint4 qv = ld16c(Q + (int64_t)h * D + sub * VEC);
     const int Cc = a.C, log2C = a.log2C;
     const int ct = c * Cc;  // chunk tokens come first, then the extras
-    const int n1 = (int)a.n1;
     float m = -INFINITY, l = 0.f, acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
@@ -590,12 +596,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ plan,
-    const int32_t* __restrict__ cnt, int32_t cap, int32_t nh, T* __restrict__ O) {
+    const int32_t* __restrict__ cnt, AttnArgs a, T* __restrict__ O) {
   const int h = blockIdx.x;
+  const int cap = a.cap, nh = (int)a.n_heads;
   // Independent loads, issued together.
   const int c = cnt[h];
+  const int64_t Th = visible_len(a, h);
   const int64_t P0 = plan[h], P1 = plan[h + 1], W = plan[nh + 1];
-  if (c < 0 || c > cap) {  // failed or overflowed route: NaN row
+  if (c < 0 || c > cap || Th < 0) {  // failed or overflowed route: NaN row
     for (int t = threadIdx.x; t < D; t += kThreads)
       store_elem(O + (int64_t)h * D, t, __int_as_float(0x7fc00000));
     return;
@@ -780,7 +788,7 @@ __global__ __launch_bounds__(256) void blk_count_kernel(const int32_t* __restric
   int n = -3;
   if (head < a.n_heads) {
     // The count and the first batch of ids load together (index clamped to the list).
-    const int c = cnt[head];
+    const int c = visible_len(a, head) < 0 ? -1 : cnt[head];
     const int id0 = sel[head * a.cap + min(lane, a.cap - 1)];
     n = -2;
     if (c >= 0 && c <= a.cap) {
@@ -1231,13 +1239,15 @@ __global__ __launch_bounds__(kThreads) void blk_merge_kernel(
 #pragma unroll
   for (int e = 0; e < DPL; ++e) q[e] = load_elem(Q + hh * D, gl * DPL + e);
   // Every lane of the wave runs the same number of steps (shuffles below).
-  const bool sink = n >= 0 && a.n1 > 0 && (c == 0 || first != 0);
-  const int ne = n >= 0 ? (sink ? 1 : 0) + (int)(a.T - a.n1 * a.C) : 0;
+  const int64_t Th = visible_len(a, hh);  // valid when n >= 0
+  const int64_t n1 = Th / a.C;
+  const bool sink = n >= 0 && n1 > 0 && (c == 0 || first != 0);
+  const int ne = n >= 0 ? (sink ? 1 : 0) + (int)(Th - n1 * a.C) : 0;
   const int ne_max = (int)wave_allreduce_u64((uint64_t)ne, OpMax());
   const int64_t nblk = kv_block_elems(a.Tc, a.C, D, a.chunked);
   const T* Kb = K + tree_of_head(hh, a) * nblk;
   const T* Vb = a.chunked ? Kb + (int64_t)a.C * D : V + tree_of_head(hh, a) * nblk;
-  const int64_t row1 = a.n1 * (a.chunked ? 2 * a.C : a.C);  // first key row of chunk n_1
+  const int64_t row1 = n1 * (a.chunked ? 2 * a.C : a.C);  // first key row of chunk n_1
   const float inv = 1.0f / sqrtf((float)D);
   float m = -INFINITY, l = 0.f, acc[DPL];
 #pragma unroll
@@ -1383,7 +1393,7 @@ int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
 #undef ZHA_BAL
     if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
     merge_balanced_kernel<T, D><<<(unsigned)a.n_heads, kThreads, 0, s>>>(
-        part, plan, cnt, a.cap, (int32_t)a.n_heads, reinterpret_cast<T*>(O));
+        part, plan, cnt, a, reinterpret_cast<T*>(O));
     return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
   }
   const bool buf =

@@ -108,6 +108,9 @@ struct BuildScratch {
 
 struct RouteArgs {
   TreeLayout lay;
+  int64_t T;
+  int64_t span[kMaxLevels + 1];  // C^l: tokens under a level-l node
+  const int32_t* ctx;  // visible length per position [B, n_pos] (device), or null: all T
   int64_t n_heads;  // B * n_pos * H_q
   int32_t n_pos;
   int32_t H_q;
@@ -117,9 +120,19 @@ struct RouteArgs {
   float p;
 };
 
+// Tokens visible to query head h (of B * n_pos * H_q): its position's entry
+// of ctx, or T; -1 when the entry is outside [1, T] (the head then fails).
+template <typename A>
+__device__ __forceinline__ int64_t visible_len(const A& a, int64_t h) {
+  if (a.ctx == nullptr) return a.T;
+  const int64_t v = a.ctx[h / a.H_q];
+  return (v >= 1 && v <= a.T) ? v : -1;
+}
+
 struct AttnArgs {
   int64_t T;
   int64_t Tc;       // token capacity (KV strides)
+  const int32_t* ctx;  // visible length per position [B, n_pos] (device), or null: all T
   int64_t n_heads;  // B * n_pos * H_q
   int64_t n1;       // full leaf chunks
   int32_t n_pos;

@@ -100,15 +100,21 @@ __global__ __launch_bounds__(256) void route_keep_all_kernel(RouteArgs a,
                                                                   int32_t* __restrict__ stats,
                                                                   float* __restrict__ gapo) {
   const int64_t head = blockIdx.x;
-  const int64_t n1 = a.lay.n[1];
+  const int64_t Th = visible_len(a, head);
+  if (Th < 0) {  // invalid visible length: a failed route
+    if (threadIdx.x == 0) cnt[head] = -1;
+    return;
+  }
+  auto n_at = [&](int l) -> int64_t { return a.ctx == nullptr ? a.lay.n[l] : Th / a.span[l]; };
+  const int64_t n1 = n_at(1);
   const int64_t lim = n1 < a.cap ? n1 : a.cap;
   for (int64_t j = threadIdx.x; j < lim; j += blockDim.x) sel[head * a.cap + j] = (int32_t)j;
   if (threadIdx.x < a.lay.L) {
     const int l = threadIdx.x + 1;
     const int64_t o = head * a.lay.L + (l - 1);
     if (stats != nullptr) {
-      stats[2 * o] = (int32_t)a.lay.n[l];
-      stats[2 * o + 1] = (int32_t)a.lay.n[l];
+      stats[2 * o] = (int32_t)n_at(l);
+      stats[2 * o + 1] = (int32_t)n_at(l);
     }
     if (gapo != nullptr) gapo[o] = INFINITY;
   }

@@ -51,11 +51,11 @@ SIGNATURES = {
     "zha_build": (ctypes.c_int, [_GP, _VP, _VP, _RP, _VP, _VP, _VP]),
     "zha_tree_update": (ctypes.c_int, [_GP, ctypes.c_int64, _VP, _VP, _RP, _VP, _VP, _VP]),
     "zha_route_scratch_bytes": (ctypes.c_int, [_GP, _I32, _I32, _c_size_p]),
-    "zha_route": (ctypes.c_int, [_GP, _VP, _VP, _I32, ctypes.c_float, _VP, _VP, _I32, _VP, _VP,
-                                 _VP, _VP]),
+    "zha_route": (ctypes.c_int, [_GP, _VP, _VP, _I32, _VP, ctypes.c_float, _VP, _VP, _I32, _VP,
+                                 _VP, _VP, _VP]),
     "zha_route_frontier_capacity": (ctypes.c_int32, []),
     "zha_attn_scratch_bytes": (ctypes.c_int, [_GP, _I32, _I32, _c_size_p]),
-    "zha_attn": (ctypes.c_int, [_GP, _VP, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "zha_attn": (ctypes.c_int, [_GP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
     "zha_dense_decode_scratch_bytes": (ctypes.c_int, [_GP, _I32, _c_size_p]),
     "zha_dense_decode": (ctypes.c_int, [_GP, _VP, _I32, _VP, _VP, _VP, _VP, _VP]),
 }
@@ -270,11 +270,18 @@ def tree_update(g: Geom, T_old: int, K, qref, tree, scratch, stream=None, rope=N
     return tree
 
 
+def _need_ctx(g: Geom, ctx_len, n_pos: int):
+    if ctx_len is not None:
+        _need(ctx_len, (g.B, n_pos), _torch().int32, "ctx_len")
+
+
 def route(g: Geom, tree, Q, n_pos: int, p: float, cap: int, want_stats=True, want_gap=True,
-          out=None, scratch=None, stream=None):
-    """zha_route; returns (sel, cnt, stats or None, gap or None)."""
+          out=None, scratch=None, stream=None, ctx_len=None):
+    """zha_route; returns (sel, cnt, stats or None, gap or None).  ctx_len: int32 [B, n_pos]
+    tokens visible to each position (causal prefill: t + 1), or None for all T."""
     torch = _torch()
     _need(Q, (g.B, n_pos, g.H_q, g.d), _store_dtype(g), "Q")
+    _need_ctx(g, ctx_len, n_pos)
     dev = Q.device
     if out is None:
         sel = torch.empty((g.B, n_pos, g.H_q, cap), dtype=torch.int32, device=dev)
@@ -287,7 +294,8 @@ def route(g: Geom, tree, Q, n_pos: int, p: float, cap: int, want_stats=True, wan
         sel, cnt, stats, gap = out
     if scratch is None:
         scratch = _bytes(route_scratch_bytes(g, n_pos, cap), dev)
-    _check(load().zha_route(ctypes.byref(g), _ptr(tree), _ptr(Q), n_pos, float(p), _ptr(sel),
+    _check(load().zha_route(ctypes.byref(g), _ptr(tree), _ptr(Q), n_pos, _ptr(ctx_len),
+                            float(p), _ptr(sel),
                             _ptr(cnt), cap, _ptr(stats), _ptr(gap), _ptr(scratch),
                             _stream(stream)), "zha_route")
     return sel, cnt, stats, gap
@@ -303,11 +311,14 @@ def _need_kv(g: Geom, K, V):
         _need(V, kv_shape(g), dt, "V")
 
 
-def attn(g: Geom, Q, n_pos: int, K, V, sel, cnt, cap: int, O=None, scratch=None, stream=None):
-    """zha_attn; returns O [B, n_pos, H_q, d].  Chunked layout: K is the KV buffer, V None."""
+def attn(g: Geom, Q, n_pos: int, K, V, sel, cnt, cap: int, O=None, scratch=None, stream=None,
+         ctx_len=None):
+    """zha_attn; returns O [B, n_pos, H_q, d].  Chunked layout: K is the KV buffer, V None.
+    ctx_len: the same visible lengths as given to route (or None)."""
     torch = _torch()
     dt = _store_dtype(g)
     _need(Q, (g.B, n_pos, g.H_q, g.d), dt, "Q")
+    _need_ctx(g, ctx_len, n_pos)
     _need_kv(g, K, V)
     _need(sel, (g.B, n_pos, g.H_q, cap), torch.int32, "sel")
     _need(cnt, (g.B, n_pos, g.H_q), torch.int32, "cnt")
@@ -315,7 +326,8 @@ def attn(g: Geom, Q, n_pos: int, K, V, sel, cnt, cap: int, O=None, scratch=None,
         O = torch.empty((g.B, n_pos, g.H_q, g.d), dtype=dt, device=Q.device)
     if scratch is None:
         scratch = _bytes(attn_scratch_bytes(g, n_pos, cap), Q.device)
-    _check(load().zha_attn(ctypes.byref(g), _ptr(Q), n_pos, _ptr(K), _ptr(V), _ptr(sel),
+    _check(load().zha_attn(ctypes.byref(g), _ptr(Q), n_pos, _ptr(ctx_len), _ptr(K), _ptr(V),
+                           _ptr(sel),
                            _ptr(cnt), cap, _ptr(O), _ptr(scratch), _stream(stream)), "zha_attn")
     return O
 

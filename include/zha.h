@@ -203,6 +203,14 @@ int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_
 
 /*   tree        device, built by zha_build for the same geometry
  *   Q           device [B, n_pos, H_q, d] storage dtype
+ *   ctx_len     device [B, n_pos] int32 or NULL: tokens visible to each
+ *               position (NULL: all T).  A position seeing T_t tokens routes
+ *               through the nodes complete within them, n_l(T_t) =
+ *               floor(T_t / C^l), with orphans taken relative to T_t; causal
+ *               prefill passes T_t = t + 1 for the token at cache position t
+ *               (paper §V, Q(T) = T: every query sees the nodes completed
+ *               before it and its own partial chunk).  A value outside [1, T]
+ *               fails that position: cnt = -1, level_stats and gap unwritten.
  *   p           top-p threshold in (0, 1]
  *   sel         device [B, n_pos, H_q, cap] int32, written: the level-1 chunk
  *               ids of S_1 in ascending order; entries past min(cnt, cap) are
@@ -217,7 +225,8 @@ int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_
  *               each level's cut, +inf when the whole frontier is kept
  *   scratch     device, zha_route_scratch_bytes() bytes (ZHA_ERR_NULL if needed
  *               and NULL) */
-int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos, float p,
+int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
+              const int32_t* ctx_len, float p,
               int32_t* sel, int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap,
               void* scratch, void* stream);
 
@@ -227,10 +236,11 @@ int32_t zha_route_frontier_capacity(void);
 /* ---------------------------------------------------------------------------
  * Sparse attention (summary page "Routing": I(q) and o(q))
  *
- * For query head h at position t, the attended token set is
- *   I = {0} U {c*C .. c*C + C - 1 : c in sel[.., :cnt]} U [n_1*C, T)
- * (token 0 is the attention sink, counted once; the tail after the last full
- * chunk is the current partial chunk) and
+ * For query head h at position t, seeing T_t tokens (ctx_len, else T), the
+ * attended token set is
+ *   I = {0} U {c*C .. c*C + C - 1 : c in sel[.., :cnt]} U [n_1*C, T_t)
+ * with n_1 = floor(T_t / C) (token 0 is the attention sink, counted once; the
+ * tail after the last full chunk is the current partial chunk) and
  *   O = sum_{j in I} softmax_j(q . k_j / sqrt(d)) v_j
  * computed with fp32 arithmetic and rounded nearest-even to the storage dtype.
  * ------------------------------------------------------------------------- */
@@ -241,6 +251,8 @@ int32_t zha_route_frontier_capacity(void);
 int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes);
 
 /*   Q        device, layout above
+ *   ctx_len  device [B, n_pos] int32 or NULL, as for zha_route (the same
+ *            array); a value outside [1, T] gives a NaN row
  *   K, V     device, the KV cache in g->kv_layout (chunked: K is the KV
  *            buffer and V must be NULL)
  *   sel, cnt device, as written by zha_route (ascending, distinct ids < n_1)
@@ -249,7 +261,8 @@ int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t
  *   scratch  device, zha_attn_scratch_bytes() bytes
  * Split partials are merged in split order, so results do not depend on
  * scheduling. */
-int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const void* K, const void* V,
+int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx_len,
+             const void* K, const void* V,
              const int32_t* sel, const int32_t* cnt, int32_t cap, void* O, void* scratch,
              void* stream);
 

@@ -112,16 +112,16 @@ def test_null_and_argument_errors_before_any_launch():
                          buf, None) == -1
     # p outside (0, 1]
     for p in (0.0, -0.5, 1.5, math.nan):
-        assert lib.zha_route(ctypes.byref(gm), buf, buf, 1, p, buf, buf, 4, None, None, None,
+        assert lib.zha_route(ctypes.byref(gm), buf, buf, 1, None, p, buf, buf, 4, None, None, None,
                              None) == -5
-    assert lib.zha_route(ctypes.byref(gm), buf, buf, 1, 0.9, buf, buf, 0, None, None, None,
+    assert lib.zha_route(ctypes.byref(gm), buf, buf, 1, None, 0.9, buf, buf, 0, None, None, None,
                          None) == -7
-    assert lib.zha_route(ctypes.byref(gm), buf, buf, 0, 0.9, buf, buf, 4, None, None, None,
+    assert lib.zha_route(ctypes.byref(gm), buf, buf, 0, None, 0.9, buf, buf, 4, None, None, None,
                          None) == -9
-    assert lib.zha_route(ctypes.byref(gm), None, buf, 1, 0.9, buf, buf, 4, None, None, None,
+    assert lib.zha_route(ctypes.byref(gm), None, buf, 1, None, 0.9, buf, buf, 4, None, None, None,
                          None) == -1
-    assert lib.zha_attn(ctypes.byref(gm), buf, 1, buf, buf, None, buf, 4, buf, buf, None) == -1
-    assert lib.zha_attn(ctypes.byref(gm), buf, 1, buf, buf, buf, buf, 0, buf, buf, None) == -7
+    assert lib.zha_attn(ctypes.byref(gm), buf, 1, None, buf, buf, None, buf, 4, buf, buf, None) == -1
+    assert lib.zha_attn(ctypes.byref(gm), buf, 1, None, buf, buf, buf, buf, 0, buf, buf, None) == -7
     assert lib.zha_dense_decode(ctypes.byref(gm), buf, 0, buf, buf, buf, buf, None) == -9
     assert lib.zha_dense_decode(ctypes.byref(gm), ctypes.c_void_p(24), 1, buf, buf, buf, buf,
                                 None) == -6
@@ -135,12 +135,12 @@ def test_null_and_argument_errors_before_any_launch():
     assert lib.zha_tree_level_offset(ctypes.byref(gm), 0, ctypes.byref(n), ctypes.byref(n),
                                      ctypes.byref(n)) == -2
     # KV layout: split needs V; chunked takes the KV buffer as K and rejects a V
-    assert lib.zha_attn(ctypes.byref(gm), buf, 1, buf, None, buf, buf, 4, buf, buf, None) == -1
+    assert lib.zha_attn(ctypes.byref(gm), buf, 1, None, buf, None, buf, buf, 4, buf, buf, None) == -1
     assert lib.zha_dense_decode(ctypes.byref(gm), buf, 1, buf, None, buf, buf, None) == -1
     gc = g(kv_layout=Z.ZHA_KV_CHUNKED)
-    assert lib.zha_attn(ctypes.byref(gc), buf, 1, buf, buf, buf, buf, 4, buf, buf, None) == -10
+    assert lib.zha_attn(ctypes.byref(gc), buf, 1, None, buf, buf, buf, buf, 4, buf, buf, None) == -10
     assert lib.zha_dense_decode(ctypes.byref(gc), buf, 1, buf, buf, buf, buf, None) == -10
-    assert lib.zha_attn(ctypes.byref(gc), buf, 1, None, None, buf, buf, 4, buf, buf, None) == -1
+    assert lib.zha_attn(ctypes.byref(gc), buf, 1, None, None, None, buf, buf, 4, buf, buf, None) == -1
 
 
 def test_chunked_layout_shape_and_tree_layout_are_independent():
