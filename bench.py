@@ -485,6 +485,7 @@ def run_crossover(steps: int):
         cap = g.n_level(1)
         sel = torch.empty((g.B, 1, g.H_q, cap), dtype=torch.int32, device="cuda")
         cnt = torch.empty((g.B, 1, g.H_q), dtype=torch.int32, device="cuda")
+        stats = torch.empty((g.B, 1, g.H_q, g.L, 2), dtype=torch.int32, device="cuda")
         O = torch.empty((g.B, 1, g.H_q, g.d), dtype=Kd.dtype, device="cuda")
         rsc = torch.empty(max(Z.route_scratch_bytes(gm, 1, cap), 1), dtype=torch.uint8,
                           device="cuda")
@@ -494,7 +495,7 @@ def run_crossover(steps: int):
 
         def zha(i):
             Z.route(gm, tree, Qd[i], 1, g.p, cap, want_stats=False, want_gap=False,
-                    out=(sel, cnt, None, None), scratch=rsc)
+                    out=(sel, cnt, stats, None), scratch=rsc)
             return Z.attn(gm, Qd[i], 1, Kd, Vd, sel, cnt, cap, O=O, scratch=asc)
 
         zha(0)
@@ -503,15 +504,21 @@ def run_crossover(steps: int):
         er = [[ev() for _ in range(3)] for _ in range(steps)]
         ed = [[ev() for _ in range(2)] for _ in range(steps)]
         toks = 0
+        k_lv, s_lv, k0_union = np.zeros(g.L), np.zeros(g.L), 0.0
         for i in range(steps):
             flush.fill_(i & 255)
             er[i][0].record()
             Z.route(gm, tree, Qd[i], 1, g.p, cap, want_stats=False, want_gap=False,
-                    out=(sel, cnt, None, None), scratch=rsc)
+                    out=(sel, cnt, stats, None), scratch=rsc)
             er[i][1].record()
             Z.attn(gm, Qd[i], 1, Kd, Vd, sel, cnt, cap, O=O, scratch=asc)
             er[i][2].record()
             toks += int(cnt.sum().item()) * g.C
+            st = stats.cpu().numpy().reshape(-1, g.L, 2)
+            k_lv += st[:, :, 0].mean(axis=0) / steps
+            s_lv += st[:, :, 1].mean(axis=0) / steps
+            k0_union += step_bytes(g, sel.cpu().numpy(), cnt.cpu().numpy(),
+                                   stats.cpu().numpy())["attn_union"] / steps
             flush.fill_((i + 7) & 255)
             ed[i][0].record()
             Z.dense_decode(gm, Qd[i], 1, Kd, Vd, O=O, scratch=dsc)
@@ -523,7 +530,10 @@ def run_crossover(steps: int):
         d_us = float(np.median([e[0].elapsed_time(e[1]) for e in ed]) * 1e3)
         row = {"T": T, "L": g.L, "top_nodes": g.n_level(g.L), "zha_us": z_us, "route_us": r_us,
                "attn_us": a_us, "dense_us": d_us, "speedup_vs_dense": d_us / z_us,
-               "keys_attended_frac": toks / steps / (g.B * g.H_q) / T}
+               "keys_attended_frac": toks / steps / (g.B * g.H_q) / T,
+               "frontier_per_level": [float(x) for x in k_lv],  # K_l, level 1 first
+               "kept_per_level": [float(x) for x in s_lv],
+               "attn_union_bytes": float(k0_union)}
         log(f"[crossover] T={T:7d} L={g.L}: zha {z_us:8.1f} us (route {r_us:6.1f}, attn "
             f"{a_us:6.1f}), dense {d_us:8.1f} us, x{d_us / z_us:.2f}")
         rows.append(row)
