@@ -716,6 +716,7 @@ struct BlkPtrs {
   int32_t* tcur;   // per tile: fill cursor
   int32_t* toff;   // per tile: first entry (exclusive scan of tcnt)
   int32_t* wpre;   // per tile: first work item
+  int32_t* wbase;  // per (workgroup of the per-tile launches, tile): first entry in the tile
   int32_t* ent;    // entries, kBlkEntryInts ints each
   float* part;     // partials, d + 2 floats per slot
   __device__ __host__ BlkPtrs(char* scr, const BlkLayout& L)
@@ -727,6 +728,7 @@ struct BlkPtrs {
         tcur(reinterpret_cast<int32_t*>(scr + L.off_tcur)),
         toff(reinterpret_cast<int32_t*>(scr + L.off_toff)),
         wpre(reinterpret_cast<int32_t*>(scr + L.off_wpre)),
+        wbase(reinterpret_cast<int32_t*>(scr + L.off_wbase)),
         ent(reinterpret_cast<int32_t*>(scr + L.off_ent)),
         part(reinterpret_cast<float*>(scr + L.off_part)) {}
 };
@@ -737,142 +739,295 @@ __device__ __forceinline__ int64_t tree_of_head(int64_t head, const AttnArgs& a)
   return b * a.H_kv + h / a.G;
 }
 
-__global__ __launch_bounds__(256) void blk_zero_kernel(char* scr, BlkLayout L) {
-  BlkPtrs P(scr, L);
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < 16) P.ctrl[i] = 0;
-  if (i < L.NTT) {
-    P.tcnt[i] = 0;
-    P.tcur[i] = 0;
-  }
-}
-
 // The merge launch gives each query head a group of kGL lanes (four heads per
 // wave): its work per head is short, and one wave per head took several
-// rounds of resident waves.  (The count and fill launches keep a wave per
-// head: with kGL-lane groups, their cross-lane shuffles per batch of ids cost
-// more than the rounds saved.)
+// rounds of resident waves.
 constexpr int kGL = 16;
 constexpr int kHPW = kWave / kGL;  // heads per wave
 
-// Walks a head's selected chunks (ascending, one wave) and calls
-// on_first(tile) in the lanes that start a new tile; returns the tile count.
+// The bookkeeping launches give each query head one lane.  A head of at most
+// kWave chunk ids is walked by its lane with every id load issued at once (the
+// loads are independent, so the lane waits once): each run of ids in one tile
+// is handed to f(tile, mask of its chunks within the tile, run index).
+// Returns the number of runs (tiles).  CT = 2^lct chunks per tile.
 template <typename F>
-__device__ __forceinline__ int walk_tiles(const int32_t* ids, int c, int CT, int id0, F on_first) {
-  const int lane = threadIdx.x & (kWave - 1);
+__device__ __forceinline__ int short_runs(const int32_t* __restrict__ ids, int c, int lct, F f) {
+  int v[kWave];
+#pragma unroll
+  for (int u = 0; u < kWave; ++u) v[u] = u < c ? ids[u] : -1;
   int n = 0, cur = -1;
-  for (int j = 0; j < c; j += kWave) {
-    // id0: the first batch, loaded by the caller together with c.
-    const int id = j + lane < c ? (j == 0 ? id0 : ids[j + lane]) : -1;
-    const int t = id >= 0 ? id / CT : -1;
-    int tp = __shfl_up(t, 1, kWave);
-    if (lane == 0) tp = cur;
-    const bool first = id >= 0 && t != tp;
-    if (first) on_first(t);
-    n += __popcll((unsigned long long)__ballot(first));
-    cur = __shfl(t, min(kWave - 1, c - j - 1), kWave);
+  uint64_t mask = 0;
+#pragma unroll
+  for (int u = 0; u < kWave; ++u) {
+    if (v[u] < 0) continue;
+    const int t = v[u] >> lct;
+    if (t != cur) {
+      if (cur >= 0) {
+        f(cur, mask, n);
+        ++n;
+      }
+      cur = t;
+      mask = 0;
+    }
+    mask |= 1ull << (v[u] - (t << lct));
+  }
+  if (cur >= 0) {
+    f(cur, mask, n);
+    ++n;
   }
   return n;
 }
 
-// A head's pairs are the tiles of its selected chunks, ascending (its sink and
-// partial-chunk tokens are the merge launch's).  One wave per head: count the
-// head's tiles and each tile's pairs.
-__global__ __launch_bounds__(256) void blk_count_kernel(const int32_t* __restrict__ sel,
-                                                        const int32_t* __restrict__ cnt,
-                                                        AttnArgs a, BlkLayout L, char* scr) {
-  __shared__ int32_t s_n[kWaves];
-  BlkPtrs P(scr, L);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
-  int n = -3;
-  if (head < a.n_heads) {
-    // The count and the first batch of ids load together (index clamped to the list).
-    const int c = visible_len(a, head) < 0 ? -1 : cnt[head];
-    const int id0 = sel[head * a.cap + min(lane, a.cap - 1)];
-    n = -2;
-    if (c >= 0 && c <= a.cap) {
-      int32_t* tc = P.tcnt + tree_of_head(head, a) * L.NT;
-      n = walk_tiles(sel + head * a.cap, c, L.CT, id0, [&](int t) { atomicAdd(&tc[t], 1); });
-    }
-    if (lane == 0) P.ntile[head] = n;
-  }
-  // Slots this workgroup's heads want (tiles + 1 each), for the prefix sum.
-  if (lane == 0) s_n[wave] = n >= 0 ? n + 1 : 0;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t w = 0;
+// The same walk by a whole wave for one head (c and ids uniform), for heads of
+// more than kWave ids: lane i takes id j + i of each batch of 64; the lanes
+// that start a tile's run are found by ballot, each lane ORs its chunk's bit
+// into its run's mask in LDS (rm: kWave + 1 words of this wave; the last
+// slot carries a run into the next batch), and the run's first lane calls
+// emit(tile, mask, run index).  Returns the number of runs.
+template <typename F>
+__device__ __forceinline__ int wave_runs(const int32_t* __restrict__ ids, int c, int lct,
+                                         unsigned long long* rm, F emit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  if (lane == 0) rm[kWave] = 0ull;
+  int k = 0, cur = -1;  // runs emitted; tile carried from the previous batch
+  int pre[4];           // ids of the next four batches, loaded together
+  for (int j = 0; j < c; j += kWave) {
+    const int q = (j / kWave) & 3;
+    if (q == 0) {
 #pragma unroll
-    for (int x = 0; x < kWaves; ++x) w += s_n[x];
-    P.wsum[blockIdx.x] = w;
+      for (int u = 0; u < 4; ++u) pre[u] = j + u * kWave + lane < c ? ids[j + u * kWave + lane] : 0;
+    }
+    const bool valid = j + lane < c;
+    const int id = q == 0 ? pre[0] : q == 1 ? pre[1] : q == 2 ? pre[2] : pre[3];
+    const int t = valid ? id >> lct : -1;
+    int tp = __shfl_up(t, 1, kWave);
+    if (lane == 0) tp = cur;
+    const bool first = valid && t != tp;
+    const uint64_t fb = __ballot(first);
+    // Run of this lane: starts at or below it, minus one (-1: the carried run).
+    const int r = __popcll((unsigned long long)(fb & (lt | (1ull << lane)))) - 1;
+    rm[lane] = 0ull;
+    asm volatile("" ::: "memory");
+    if (valid) atomicOr(&rm[r < 0 ? kWave : r], 1ull << (id - (t << lct)));
+    asm volatile("" ::: "memory");
+    if (fb != 0ull) {
+      if (cur >= 0) {
+        if (lane == 0) emit(cur, (uint64_t)rm[kWave], k);
+        ++k;
+      }
+      const int last = 63 - __clzll((long long)fb);
+      const int nrun = __popcll((unsigned long long)fb);
+      if (first && lane != last) emit(t, (uint64_t)rm[r], k + r);
+      k += nrun - 1;
+      cur = __builtin_amdgcn_readlane(t, last);
+      asm volatile("" ::: "memory");
+      const unsigned long long lm = rm[nrun - 1];
+      asm volatile("" ::: "memory");
+      if (lane == 0) rm[kWave] = lm;
+    }
+  }
+  if (cur >= 0) {
+    if (lane == 0) emit(cur, (uint64_t)rm[kWave], k);
+    ++k;
+  }
+  return k;
+}
+
+// Runs of every lane's head: heads of at most kWave ids by their own lane,
+// longer ones by the whole wave, one after another.  Per lane: its head, the
+// head's id count c (c < 0: no head) and one more value aux of the head;
+// emit(head, aux, tile, mask, run index) is called in the head's own lane for
+// the short heads and in a lane of the wave for the long ones.  All lanes of
+// the wave must call it together.  Returns the lane's head's run count.
+template <typename F>
+__device__ __forceinline__ int head_runs(const int32_t* __restrict__ sel, int64_t head, int c,
+                                         int aux, int cap, int lct, unsigned long long* rm,
+                                         F emit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int n = 0;
+  if (c > 0 && c <= kWave)
+    n = short_runs(sel + head * cap, c, lct,
+                   [&](int t, uint64_t m, int k) { emit(head, aux, t, m, k); });
+  uint64_t longs = __ballot(c > kWave);
+  while (longs != 0ull) {
+    const int src = __ffsll((unsigned long long)longs) - 1;
+    longs &= longs - 1;
+    const int64_t hh = ((int64_t)__builtin_amdgcn_readlane((int)(head >> 32), src) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)head, src);
+    const int hc = __builtin_amdgcn_readlane(c, src);
+    const int ha = __builtin_amdgcn_readlane(aux, src);
+    const int nn = wave_runs(sel + hh * cap, hc, lct, rm,
+                             [&](int t, uint64_t m, int k) { emit(hh, ha, t, m, k); });
+    if (lane == src) n = nn;
+  }
+  return n;
+}
+
+constexpr int kLaneHeads = 128;     // query heads per workgroup of the lane-per-head launches
+constexpr int kHeadsPerWave = 8;    // of them per wave: lanes 0..7 (a wave walks long heads alone)
+constexpr int kLaneWaves = kLaneHeads / kHeadsPerWave;
+constexpr int kLaneThreads = kLaneWaves * kWave;
+constexpr int kBlkLdsTiles = 4096;  // tiles of one cache that an LDS histogram covers
+
+// Item i of cache tr, the caches' heads taken (position, query head of the
+// group) in order: the launches that count and fill per tile give each
+// workgroup heads of one cache, so its tiles aggregate in LDS.
+__device__ __forceinline__ int64_t tree_item_head(int64_t tr, int64_t i, const AttnArgs& a) {
+  const int64_t b = tr / a.H_kv;
+  const int kvh = (int)(tr - b * a.H_kv);
+  const int64_t pos = i / a.G;
+  const int g = (int)(i - pos * a.G);
+  return (b * a.n_pos + pos) * a.H_q + (int64_t)kvh * a.G + g;
+}
+
+// A head's pairs are the tiles of its selected chunks, ascending (its sink and
+// partial-chunk tokens are the merge launch's).  One lane per head, heads in
+// order: the head's tile count, and the slots each workgroup's heads want
+// (tiles + 1 each) for the prefix sum.  Also clears the tile counters and
+// cursors and the control words for the launches that follow.
+__global__ __launch_bounds__(kLaneThreads) void blk_count_kernel(const int32_t* __restrict__ sel,
+                                                                 const int32_t* __restrict__ cnt,
+                                                                 AttnArgs a, BlkLayout L,
+                                                                 char* scr) {
+  __shared__ uint64_t s_w[kLaneWaves];
+  __shared__ unsigned long long s_run[kLaneWaves][kWave + 1];
+  BlkPtrs P(scr, L);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  for (int64_t i = (int64_t)blockIdx.x * kLaneThreads + tid; i < L.NTT;
+       i += (int64_t)gridDim.x * kLaneThreads) {
+    P.tcnt[i] = 0;
+    P.tcur[i] = 0;
+  }
+  if (blockIdx.x == 0 && tid < 16) P.ctrl[tid] = 0;
+  const int64_t head = (int64_t)blockIdx.x * kLaneHeads + wave * kHeadsPerWave + lane;
+  const bool hv = lane < kHeadsPerWave && head < a.n_heads;
+  int c = -1;
+  if (hv) {
+    c = visible_len(a, head) < 0 ? -1 : cnt[head];
+    if (c > a.cap) c = -1;
+  }
+  int n = head_runs(sel, hv ? head : 0, c, 0, a.cap, L.lct, s_run[wave],
+                    [](int64_t, int, int, uint64_t, int) {});
+  if (c < 0) n = -2;
+  if (hv) P.ntile[head] = n;
+  const uint64_t w = wave_sum_u64_bcast(hv && n >= 0 ? (uint64_t)(n + 1) : 0ull);
+  if (lane == 0) s_w[wave] = w;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t t = 0;
+#pragma unroll
+    for (int x = 0; x < kLaneWaves; ++x) t += s_w[x];
+    P.wsum[blockIdx.x] = (int64_t)t;
   }
 }
 
-// Prefix sums, one launch.  Workgroups 0 .. nq-1: slot bases by a prefix sum
-// of (tiles + 1) over the heads, 8192 heads each: the slots of the heads before
-// its range come from the count launch's per-workgroup sums; its own range
-// goes through LDS in coalesced loads, each thread then sums 8 consecutive
-// heads, one block scan.  From the first head whose slots would pass the
-// budget on, heads are marked for per-head attention (their pairs stay
-// counted and become empty entries).  The last workgroup: exclusive scans over
-// the tiles, first entry and first work item of each.
+// Slot bases, one launch of workgroups of 8192 heads: the slots of the heads
+// before its range come from the count launch's per-workgroup sums; its own
+// range goes through LDS in coalesced loads, each thread then sums 8
+// consecutive heads, one block scan.  From the first head whose slots would
+// pass the budget on, heads are marked for per-head attention (ntile = -1):
+// they take no slots and no pairs.
 constexpr int kScanPer = 8;
 constexpr int kScanChunk = 1024 * kScanPer;  // heads per workgroup of the scan launch
 __global__ __launch_bounds__(1024) void blk_scan_kernel(int64_t n_heads, BlkLayout L, char* scr) {
   BlkPtrs P(scr, L);
-  __shared__ int64_t s_v[1024], s_w[1024];
+  __shared__ int64_t s_w[1024 / kWave];
+  __shared__ int32_t s_c[kScanChunk];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid >> 6;
-  if (blockIdx.x + 1 < gridDim.x) {
-    __shared__ int32_t s_c[kScanChunk];
-    const int64_t c0 = (int64_t)blockIdx.x * kScanChunk;
-    // This range's values, loaded first (coalesced, unconditional).
-    int v[kScanPer];
+  const int64_t c0 = (int64_t)blockIdx.x * kScanChunk;
+  // This range's values, loaded first (coalesced, unconditional).
+  int v[kScanPer];
 #pragma unroll
-    for (int k = 0; k < kScanPer; ++k) v[k] = P.ntile[min(c0 + (int64_t)k * 1024 + tid, n_heads - 1)];
-    // Slots of the heads before the range: the count launch's sums of 4 heads.
-    const int64_t nw = c0 / kWaves;
-    int64_t before = 0;
-    for (int64_t i0 = 0; i0 < nw; i0 += 8 * 1024) {  // 8 loads in flight per thread
-      int64_t x[8];
+  for (int k = 0; k < kScanPer; ++k) v[k] = P.ntile[min(c0 + (int64_t)k * 1024 + tid, n_heads - 1)];
+  // Slots of the heads before the range: the count launch's sums of kLaneHeads heads.
+  const int64_t nw = c0 / kLaneHeads;
+  int64_t before = 0;
+  for (int64_t i0 = 0; i0 < nw; i0 += 8 * 1024) {  // 8 loads in flight per thread
+    int64_t x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = P.wsum[min(i0 + u * 1024 + tid, nw - 1)];
+    for (int u = 0; u < 8; ++u) x[u] = P.wsum[min(i0 + u * 1024 + tid, nw - 1)];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) before += i0 + u * 1024 + tid < nw ? x[u] : 0;
-    }
-    before = (int64_t)wave_sum_u64_bcast((uint64_t)before);
-    if (lane == 0) s_w[wave] = before;
-#pragma unroll
-    for (int k = 0; k < kScanPer; ++k) s_c[k * 1024 + tid] = v[k];
-    __syncthreads();
-    int64_t run = 0;
-#pragma unroll
-    for (int x = 0; x < 1024 / kWave; ++x) run += s_w[x];
-    int w[kScanPer];
-    int64_t sum = 0;
-#pragma unroll
-    for (int k = 0; k < kScanPer; ++k) {
-      w[k] = c0 + tid * kScanPer + k < n_heads ? s_c[tid * kScanPer + k] : -3;
-      sum += w[k] >= 0 ? w[k] + 1 : 0;
-    }
-    __syncthreads();  // s_w is reused
-    const uint64_t incl = wave_incl_scan_u64((uint64_t)sum);
-    if (lane == kWave - 1) s_w[wave] = (int64_t)incl;
-    __syncthreads();
-    int64_t off = 0;
-#pragma unroll
-    for (int x = 0; x < 1024 / kWave; ++x) off += x < wave ? s_w[x] : 0;
-    int64_t start = run + off + (int64_t)incl - sum;
-#pragma unroll
-    for (int k = 0; k < kScanPer; ++k) {
-      if (w[k] < 0) continue;
-      const int64_t i = c0 + tid * kScanPer + k;
-      if (start + w[k] + 1 > L.S) P.ntile[i] = -1;
-      else P.qbase[i] = (int32_t)start;
-      start += w[k] + 1;
-    }
-    return;
+    for (int u = 0; u < 8; ++u) before += i0 + u * 1024 + tid < nw ? x[u] : 0;
   }
+  before = (int64_t)wave_sum_u64_bcast((uint64_t)before);
+  if (lane == 0) s_w[wave] = before;
+#pragma unroll
+  for (int k = 0; k < kScanPer; ++k) s_c[k * 1024 + tid] = v[k];
+  __syncthreads();
+  int64_t run = 0;
+#pragma unroll
+  for (int x = 0; x < 1024 / kWave; ++x) run += s_w[x];
+  int w[kScanPer];
+  int64_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < kScanPer; ++k) {
+    w[k] = c0 + tid * kScanPer + k < n_heads ? s_c[tid * kScanPer + k] : -3;
+    sum += w[k] >= 0 ? w[k] + 1 : 0;
+  }
+  __syncthreads();  // s_w is reused
+  const uint64_t incl = wave_incl_scan_u64((uint64_t)sum);
+  if (lane == kWave - 1) s_w[wave] = (int64_t)incl;
+  __syncthreads();
+  int64_t off = 0;
+#pragma unroll
+  for (int x = 0; x < 1024 / kWave; ++x) off += x < wave ? s_w[x] : 0;
+  int64_t start = run + off + (int64_t)incl - sum;
+#pragma unroll
+  for (int k = 0; k < kScanPer; ++k) {
+    if (w[k] < 0) continue;
+    const int64_t i = c0 + tid * kScanPer + k;
+    if (start + w[k] + 1 > L.S) P.ntile[i] = -1;
+    else P.qbase[i] = (int32_t)start;
+    start += w[k] + 1;
+  }
+}
+
+// Pairs per tile, over the heads that have slots.  Eight heads per wave, the
+// workgroup's heads all of one cache: its pairs per tile are counted in LDS,
+// then one global add per tile touched, whose old value is the workgroup's
+// first place in the tile's entries (kept for the fill launch); caches of more
+// than kBlkLdsTiles tiles add per pair.
+__global__ __launch_bounds__(kLaneThreads) void blk_tcount_kernel(
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, AttnArgs a, BlkLayout L,
+    char* scr) {
+  __shared__ int32_t s_h[kBlkLdsTiles];
+  __shared__ unsigned long long s_run[kLaneWaves][kWave + 1];
+  BlkPtrs P(scr, L);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int64_t per_tree = (int64_t)a.n_pos * a.G;
+  const int64_t wpt = (per_tree + kLaneHeads - 1) / kLaneHeads;
+  const int64_t tr = blockIdx.x / wpt;
+  const int64_t i = (blockIdx.x - tr * wpt) * kLaneHeads + wave * kHeadsPerWave + lane;
+  const bool hv = lane < kHeadsPerWave && i < per_tree;
+  const bool lds = L.NT <= kBlkLdsTiles;
+  int32_t* tc = P.tcnt + tr * L.NT;
+  if (lds) {
+    for (int t = tid; t < L.NT; t += kLaneThreads) s_h[t] = 0;
+    __syncthreads();
+  }
+  const int64_t head = hv ? tree_item_head(tr, i, a) : 0;
+  const int c = (hv && P.ntile[head] >= 0) ? cnt[head] : -1;
+  head_runs(sel, head, c, 0, a.cap, L.lct, s_run[wave],
+            [&](int64_t, int, int t, uint64_t, int) {
+              if (lds) atomicAdd(&s_h[t], 1);
+              else atomicAdd(&tc[t], 1);
+            });
+  if (lds) {
+    __syncthreads();
+    int32_t* wb = P.wbase + (int64_t)blockIdx.x * L.NT;
+    for (int t = tid; t < L.NT; t += kLaneThreads)
+      if (s_h[t] != 0) wb[t] = atomicAdd(&tc[t], s_h[t]);
+  }
+}
+
+// Exclusive scans over the tiles: first entry and first work item of each
+// (one workgroup), and the number of work items.
+__global__ __launch_bounds__(1024) void blk_tscan_kernel(BlkLayout L, char* scr) {
+  BlkPtrs P(scr, L);
+  __shared__ int64_t s_v[1024], s_w[1024];
+  const int tid = threadIdx.x;
   const int64_t seg = (L.NTT + 1023) / 1024;
   const int64_t i0 = min(L.NTT, tid * seg), i1 = min(L.NTT, i0 + seg);
   int64_t sc = 0, sw = 0;
@@ -905,74 +1060,50 @@ __global__ __launch_bounds__(1024) void blk_scan_kernel(int64_t n_heads, BlkLayo
   }
 }
 
-// One wave per head: walk the head's tiles again (in the same order as the
-// count) and write one entry per tile: head, slot, chunk mask.  In a batch of
-// 64 ids the runs of one tile are numbered by the lanes that start them; each
-// lane ORs its chunk's bit into its run's mask in LDS (a per-wave array, in
-// order within the wave), and the run's first lane emits it.  The last run may
-// continue into the next batch: its mask is carried in the array's last slot.
-__global__ __launch_bounds__(256) void blk_fill_kernel(const int32_t* __restrict__ sel,
-                                                       const int32_t* __restrict__ cnt,
-                                                       AttnArgs a, BlkLayout L, char* scr) {
-  __shared__ unsigned long long s_run[kWaves][kWave + 1];
+// One entry per (head with slots, tile): head, slot, 64-bit mask of the
+// head's chunks in the tile.  The same heads per workgroup as the tile count
+// launch: each pair takes the next place of the workgroup's range of its tile
+// (first place from the tile count launch) from an LDS counter.  Caches of
+// more than kBlkLdsTiles tiles take places one by one from a global cursor.
+__global__ __launch_bounds__(kLaneThreads) void blk_fill_kernel(const int32_t* __restrict__ sel,
+                                                                const int32_t* __restrict__ cnt,
+                                                                AttnArgs a, BlkLayout L,
+                                                                char* scr) {
+  __shared__ int32_t s_h[kBlkLdsTiles];  // places taken per tile
+  __shared__ int32_t s_b[kBlkLdsTiles];  // first place of the workgroup's range
+  __shared__ unsigned long long s_run[kLaneWaves][kWave + 1];
   BlkPtrs P(scr, L);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int64_t head = (int64_t)blockIdx.x * kWaves + wave;
-  if (head >= a.n_heads) return;  // the whole wave: nothing below synchronises waves
-  // Independent loads together: tile count, chunk count, slot base, first ids.
-  const int nt = P.ntile[head];
-  const int c = cnt[head];
-  const int qb = P.qbase[head];
-  const int32_t* ids = sel + head * a.cap;
-  const int id0 = ids[min(lane, a.cap - 1)];
-  if (nt == 0 || nt == -2) return;
-  const bool live = nt > 0;  // -1: past the slot budget, its pairs become empty entries
-  const int CT = L.CT;
-  const int64_t tb = tree_of_head(head, a) * L.NT;
-  const int slot0 = live ? qb : 0;
-  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-  unsigned long long* rm = s_run[wave];
-  auto emit = [&](int tile, uint64_t mask, int k) {
-    const int pos = P.toff[tb + tile] + atomicAdd(&P.tcur[tb + tile], 1);
-    int32_t* e = P.ent + (int64_t)pos * kBlkEntryInts;
-    e[0] = live ? (int32_t)head : -1;
-    e[1] = live ? slot0 + k : -1;
-    e[2] = live ? (int32_t)(uint32_t)mask : 0;
-    e[3] = live ? (int32_t)(uint32_t)(mask >> 32) : 0;
-  };
-  if (lane == 0) rm[kWave] = 0ull;
-  int k = 0, cur = -1;  // tiles emitted; tile carried from the previous batch
-  for (int j = 0; j < c; j += kWave) {
-    const bool valid = j + lane < c;
-    const int id = valid ? (j == 0 ? id0 : ids[j + lane]) : 0;
-    const int t = valid ? id / CT : -1;
-    int tp = __shfl_up(t, 1, kWave);
-    if (lane == 0) tp = cur;
-    const bool first = valid && t != tp;
-    const uint64_t fb = __ballot(first);
-    // Run of this lane: starts at or below it, minus one (-1: the carried run).
-    const int r = __popcll((unsigned long long)(fb & (lt | (1ull << lane)))) - 1;
-    rm[lane] = 0ull;
-    asm volatile("" ::: "memory");
-    if (valid) atomicOr(&rm[r < 0 ? kWave : r], 1ull << (id - t * CT));
-    asm volatile("" ::: "memory");
-    if (fb != 0ull) {
-      if (cur >= 0) {
-        if (lane == 0) emit(cur, rm[kWave], k);
-        ++k;
-      }
-      const int last = 63 - __clzll((long long)fb);
-      const int nrun = __popcll((unsigned long long)fb);
-      if (first && lane != last) emit(t, rm[r], k + r);
-      k += nrun - 1;
-      cur = __builtin_amdgcn_readlane(t, last);
-      asm volatile("" ::: "memory");
-      const unsigned long long lm = rm[nrun - 1];
-      asm volatile("" ::: "memory");
-      if (lane == 0) rm[kWave] = lm;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int64_t per_tree = (int64_t)a.n_pos * a.G;
+  const int64_t wpt = (per_tree + kLaneHeads - 1) / kLaneHeads;
+  const int64_t tr = blockIdx.x / wpt;
+  const int64_t i = (blockIdx.x - tr * wpt) * kLaneHeads + wave * kHeadsPerWave + lane;
+  const bool hv = lane < kHeadsPerWave && i < per_tree;
+  const bool lds = L.NT <= kBlkLdsTiles;
+  const int64_t tb = tr * L.NT;
+  const int64_t head = hv ? tree_item_head(tr, i, a) : 0;
+  const bool live = hv && P.ntile[head] >= 0;
+  const int c = live ? cnt[head] : -1;
+  const int qb = live ? P.qbase[head] : 0;
+  if (lds) {
+    // Places of tiles this workgroup does not touch are never read.
+    const int32_t* wb = P.wbase + (int64_t)blockIdx.x * L.NT;
+    for (int t = tid; t < L.NT; t += kLaneThreads) {
+      s_h[t] = 0;
+      s_b[t] = P.toff[tb + t] + wb[t];
     }
+    __syncthreads();
   }
-  if (cur >= 0 && lane == 0) emit(cur, rm[kWave], k);
+  head_runs(sel, head, c, qb, a.cap, L.lct, s_run[wave],
+            [&](int64_t h, int q, int t, uint64_t mask, int k) {
+              const int pos = lds ? s_b[t] + atomicAdd(&s_h[t], 1)
+                                  : P.toff[tb + t] + atomicAdd(&P.tcur[tb + t], 1);
+              int32_t* e = P.ent + (int64_t)pos * kBlkEntryInts;
+              e[0] = (int32_t)h;
+              e[1] = q + k;
+              e[2] = (int32_t)(uint32_t)mask;
+              e[3] = (int32_t)(uint32_t)(mask >> 32);
+            });
 }
 
 // Work items: (tile, block of up to kBlkQ of its entries), persistent loop.
@@ -1353,13 +1484,17 @@ int launch_blk(const AttnArgs& a, const void* Q, const void* K, const void* V, c
   const BlkLayout L =
       blk_layout(a.n_heads, a.n_heads / ((int64_t)a.n_pos * a.H_q) * a.H_kv, a.T, a.C, D);
   char* scr = reinterpret_cast<char*>(scratch);
-  const unsigned wave_blocks = (unsigned)((a.n_heads + kWaves - 1) / kWaves);
+  const unsigned lane_blocks = (unsigned)((a.n_heads + kLaneHeads - 1) / kLaneHeads);
+  const int64_t n_trees = a.n_heads / ((int64_t)a.n_pos * a.H_q) * a.H_kv;
+  const unsigned tree_blocks =
+      (unsigned)(n_trees * (((int64_t)a.n_pos * a.G + kLaneHeads - 1) / kLaneHeads));
   const unsigned group_blocks = (unsigned)((a.n_heads + kWaves * kHPW - 1) / (kWaves * kHPW));
-  blk_zero_kernel<<<(unsigned)((max(L.NTT, (int64_t)16) + 255) / 256), 256, 0, s>>>(scr, L);
-  blk_count_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
-  blk_scan_kernel<<<(unsigned)((a.n_heads + kScanChunk - 1) / kScanChunk + 1), 1024, 0, s>>>(
+  blk_count_kernel<<<lane_blocks, kLaneThreads, 0, s>>>(sel, cnt, a, L, scr);
+  blk_scan_kernel<<<(unsigned)((a.n_heads + kScanChunk - 1) / kScanChunk), 1024, 0, s>>>(
       a.n_heads, L, scr);
-  blk_fill_kernel<<<wave_blocks, 256, 0, s>>>(sel, cnt, a, L, scr);
+  blk_tcount_kernel<<<tree_blocks, kLaneThreads, 0, s>>>(sel, cnt, a, L, scr);
+  blk_tscan_kernel<<<1, 1024, 0, s>>>(L, scr);
+  blk_fill_kernel<<<tree_blocks, kLaneThreads, 0, s>>>(sel, cnt, a, L, scr);
   blk_attn_kernel<D, BUF><<<kBlkGrid, 256, 0, s>>>(
       reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K),
       reinterpret_cast<const bf16_t*>(V), a, L, scr);

@@ -40,7 +40,7 @@ __device__ __forceinline__ void load_row_f64(const T* row, int lane, double* out
 
 // This lane's dims of reference row qr for a node whose span ends at position
 // pos: rotated by pos * theta_j in the pairs (j, j + dims/2), or as given.
-template <int D>
+template <int D, bool ROPE>
 __device__ __forceinline__ void node_reference(const float* __restrict__ qr, int lane,
                                                const BuildArgs& a, double pos, double* q) {
   constexpr int DPL = D / kWave;
@@ -49,7 +49,7 @@ __device__ __forceinline__ void node_reference(const float* __restrict__ qr, int
   for (int e = 0; e < DPL; ++e) {
     const int k = lane * DPL + e;
     double x = (double)qr[k];
-    if (k < dims) {
+    if (ROPE && k < dims) {
       const int j = k < h ? k : k - h;
       const double y = (double)qr[k < h ? k + h : k - h];
       double sn, cs;
@@ -60,7 +60,7 @@ __device__ __forceinline__ void node_reference(const float* __restrict__ qr, int
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
                                                    const float* __restrict__ qref,
                                                    char* __restrict__ tree,
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
   const double pos = (double)((i + 1) * C - 1);  // the chunk's last position
   for (int r = 0; r < R; ++r) {
     double q[DPL];
-    node_reference<D>(qref + ((int64_t)kvh * R + r) * D, lane, a, pos, q);
+    node_reference<D, ROPE>(qref + ((int64_t)kvh * R + r) * D, lane, a, pos, q);
     // First key read: the maximum score of the chunk.
     double m = -INFINITY;
     for (int j = 0; j < C; ++j) {
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
       const int64_t srow = tr * a.lay.ncap[1] * R + row;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) sK[srow * D + lane * DPL + e] = acc[e];
-      if (lane == 0) sF[srow] = a.rope_dims ? b : F;
+      if (lane == 0) sF[srow] = ROPE ? b : F;
     }
   }
 }
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qr
 
   for (int r = 0; r < R; ++r) {
     double qp[DPL];
-    node_reference<D>(qref + ((int64_t)kvh * R + r) * D, lane, a, pos, qp);
+    node_reference<D, ROPE>(qref + ((int64_t)kvh * R + r) * D, lane, a, pos, qp);
     // Maximum child log-mass.
     double m = -INFINITY;
     if constexpr (ROPE) {
@@ -236,9 +236,14 @@ static int launch_build(const BuildArgs& a, const void* K, const float* qref, vo
   if (a.lay.n[1] > a.lo[1]) {
     const int64_t nodes = (int64_t)a.n_trees * (a.lay.n[1] - a.lo[1]);
     const unsigned blocks = (unsigned)((nodes + 3) / 4);
-    leaf_kernel<T, D><<<blocks, 256, 0, s>>>(reinterpret_cast<const T*>(K), qref,
-                                             reinterpret_cast<char*>(tree),
-                                             L > 1 ? F(1) : nullptr, L > 1 ? Kp(1) : nullptr, a);
+    if (a.rope_dims)
+      leaf_kernel<T, D, true><<<blocks, 256, 0, s>>>(
+          reinterpret_cast<const T*>(K), qref, reinterpret_cast<char*>(tree),
+          L > 1 ? F(1) : nullptr, L > 1 ? Kp(1) : nullptr, a);
+    else
+      leaf_kernel<T, D, false><<<blocks, 256, 0, s>>>(
+          reinterpret_cast<const T*>(K), qref, reinterpret_cast<char*>(tree),
+          L > 1 ? F(1) : nullptr, L > 1 ? Kp(1) : nullptr, a);
     if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
   }
   for (int l = 2; l <= L; ++l) {

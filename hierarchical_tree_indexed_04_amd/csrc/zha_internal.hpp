@@ -25,7 +25,8 @@ constexpr int kBalMaxHeads = 2048;       // balanced split-KV: per-head prefix h
 // cache.  A head takes one partial slot per tile of its selected chunks plus
 // one for its sink and partial-chunk tokens; slots are handed out by a prefix
 // sum over the heads, within a budget of kBlkSlots per head on average (heads
-// past the budget are attended one head per workgroup instead).  Scratch:
+// past the budget are attended one head per workgroup instead and take no
+// pairs, so the entries never outnumber the slots).  Scratch:
 // counters, per-head slot bases and tile counts, per-tile counts and offsets,
 // the pair entries and the fp32 partials (d + 2 each).
 constexpr int kBlkSlots = 9;
@@ -33,11 +34,12 @@ constexpr int kBlkEntryInts = 4;  // head, slot, mask lo, mask hi
 
 struct BlkLayout {
   int32_t CT;  // chunks per tile (<= 64: one bit each in a 64-bit mask)
+  int32_t lct;  // log2(CT)
   int32_t NT;  // tiles per (b, kvh) cache
   int64_t NTT;  // tiles in all
   int64_t S;    // slot budget
   int64_t off_ctrl, off_qbase, off_ntile, off_wsum, off_tcnt, off_tcur, off_toff, off_wpre,
-      off_ent, off_part, total;
+      off_wbase, off_ent, off_part, total;
 };
 
 // The block path serves bf16 caches with d in {64, 128} and C in {8, 16, 32, 64}.
@@ -50,6 +52,7 @@ inline BlkLayout blk_layout(int64_t n_heads, int64_t n_trees, int64_t T, int C, 
   BlkLayout L{};
   const int64_t nchunks = (T + C - 1) / C;
   L.CT = C >= 16 ? 1024 / C : 64;
+  L.lct = __builtin_ctz((unsigned)L.CT);
   L.NT = (int32_t)((nchunks + L.CT - 1) / L.CT);
   L.NTT = n_trees * L.NT;
   L.S = n_heads * kBlkSlots;
@@ -62,11 +65,15 @@ inline BlkLayout blk_layout(int64_t n_heads, int64_t n_trees, int64_t T, int C, 
   L.off_ctrl = take(64);
   L.off_qbase = take(n_heads * 4);
   L.off_ntile = take(n_heads * 4);
-  L.off_wsum = take((n_heads + 3) / 4 * 8);  // slots per workgroup of the count launch
+  L.off_wsum = take((n_heads + 127) / 128 * 8);  // slots per workgroup of the count launch
   L.off_tcnt = take(L.NTT * 4);
   L.off_tcur = take(L.NTT * 4);
   L.off_toff = take((L.NTT + 1) * 4);
   L.off_wpre = take((L.NTT + 1) * 4);
+  // Per workgroup of the per-tile launches (128 heads of one cache), its first
+  // entry within each tile's range.
+  const int64_t per_tree = n_heads / n_trees;
+  L.off_wbase = take(n_trees * ((per_tree + 127) / 128) * L.NT * 4);
   L.off_ent = take(L.S * kBlkEntryInts * 4);
   L.off_part = take(L.S * (int64_t)(d + 2) * 4);
   L.total = off;

@@ -242,6 +242,40 @@ def test_block_attention_many_heads(Z, C, chunked):
     assert worst <= TOL[g.dtype]
 
 
+def test_block_attention_most_heads_past_the_budget(Z):
+    # Every head scattered over ~30 of the cache's 33 tiles: ~34 slots wanted per
+    # head against a budget of 9, so three quarters of the heads are attended one
+    # per workgroup and only the others' pairs become entries.
+    import torch
+    say("block attention, 4096 heads scattered over most tiles (slot budget exceeded)")
+    C = 32
+    g = W.custom("blk-over", 140, dtype=W.BF16, B=1, H_q=8, H_kv=1, T=C ** 3 + C * 5 + 7, C=C,
+                 L=2, p=0.95)
+    K, V = W.make_kv(g)
+    n_pos, n_heads = 512, 4096
+    Qn = W.make_query_block(g, K, range(n_pos))
+    n1, cap = g.n_level(1), 320
+    rng = np.random.default_rng(640)
+    sel = np.full((n_heads, cap), -1, np.int32)
+    cnt = np.zeros(n_heads, np.int32)
+    for i in range(n_heads):
+        ids = np.unique(rng.choice(n1, int(rng.integers(100, 300)), replace=False)).astype(np.int32)
+        cnt[i], sel[i, :len(ids)] = len(ids), ids
+    gm = Z.geom(g)
+    Kd, Vd, Qd = to_device(K, g.dtype), to_device(V, g.dtype), to_device(Qn, g.dtype)
+    seld = torch.from_numpy(sel.reshape(g.B, n_pos, g.H_q, cap)).cuda()
+    cntd = torch.from_numpy(cnt.reshape(g.B, n_pos, g.H_q)).cuda()
+    Og = from_device(Z.attn(gm, Qd, n_pos, Kd, Vd, seld, cntd, cap), g.dtype).reshape(n_heads, g.d)
+    Kf, Vf = W.to_float(K[0, 0], g.dtype), W.to_float(V[0, 0], g.dtype)
+    worst = 0.0
+    for i in range(n_heads):
+        t, h = i // g.H_q, i % g.H_q
+        o = O.attend(W.to_float(Qn[0, t, h], g.dtype), Kf, Vf, O.token_set(sel[i, :cnt[i]], C, g.T))
+        worst = max(worst, float(np.abs(Og[i] - o).max()))
+    say(f"  max abs err {worst:.3g} over {n_heads} heads")
+    assert worst <= TOL[g.dtype]
+
+
 @pytest.mark.parametrize("cfg,chunked", [(1, False), (2, False), (2, True)])
 def test_dense_decode_matches_oracle(Z, cfg, chunked):
     say(f"dense decode, config {cfg}, {'chunked' if chunked else 'split'} KV")
