@@ -435,6 +435,9 @@ def run_block_1m(reps: int = 3):
         union += int(mark.sum()) * g.C * 2 * g.d * g.elem_bytes
     per_head = int(c.sum()) * g.C * 2 * g.d * g.elem_bytes
     route_rows = int(stats.cpu().numpy()[..., 0].sum()) * (g.d * g.elem_bytes + 4)
+    # Summary rows touched by some head: at most the whole tree (the heads'
+    # frontiers overlap; their per-head sum counts shared rows many times).
+    route_union = min(route_rows, tb)
     b_ms, r_ms, a_ms = (float(np.median(x)) for x in (tb_ms, tr_ms, ta_ms))
     log(f"[bench] 1M block: build {b_ms:.3f} ms, route {r_ms:.3f} ms, attn {a_ms:.3f} ms")
     return {"workload": f"{g.name}: B={g.B}, H_q={g.H_q}/H_kv={g.H_kv}, d={g.d}, T={g.T}, C={g.C}, "
@@ -442,8 +445,12 @@ def run_block_1m(reps: int = 3):
             "queries_per_s": n_pos / ((r_ms + a_ms) * 1e-3),
             "queries_per_s_with_build": n_pos / ((b_ms + r_ms + a_ms) * 1e-3),
             "build_ms": b_ms, "route_ms": r_ms, "attn_ms": a_ms,
-            "bytes_union": union + route_rows, "bytes_per_head_sum": per_head + route_rows,
-            "hbm_frac_union": (union + route_rows) / ((r_ms + a_ms) * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+            "bytes_union": union + route_union, "bytes_kv_union": union,
+            "bytes_route_rows_per_head_sum": route_rows, "bytes_tree": tb,
+            "bytes_per_head_sum": per_head + route_rows,
+            "hbm_frac_union": (union + route_union) / ((r_ms + a_ms) * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "how_union": "K/V rows of the chunks selected by any head of a KV group, plus the "
+                         "summary rows touched (at most the tree's bytes)"}
 
 
 CROSSOVER_T = [4096, 8192, 16384, 32768, 65536, 131072, 262144]
@@ -747,6 +754,9 @@ def main():
         "route_us": route_us,
         "attn_us": attn_us,
         "step_bytes_union": step_union,
+        "step_bytes_how": "attention: K/V rows of the union of chunks over each KV group's heads, "
+                          "plus q, o and chunk lists; routing: each query head's frontier summary "
+                          "rows (heads of a group share many of them, so this overcounts HBM)",
         "step_bytes_per_head_sum": by["attn_per_head"] + by["route"],
         "step_hbm_frac": step_union / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "query_heads_per_s": value * g.H_q,
