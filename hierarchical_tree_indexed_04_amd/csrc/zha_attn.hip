@@ -702,7 +702,10 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
 // ===========================================================================
 constexpr int kBlkQ = 64;      // query heads per work item: 4 waves x 16 MFMA rows
 constexpr int kBlkGroup = 32;  // tokens per MFMA step
-constexpr int kBlkGrid = 768;  // persistent workgroups of the attention launch (3 per CU)
+#ifndef ZHA_BLK_GRID
+#define ZHA_BLK_GRID 768
+#endif
+constexpr int kBlkGrid = ZHA_BLK_GRID;  // persistent workgroups of the attention launch (3 per CU)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

@@ -89,31 +89,45 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
   for (int r = 0; r < R; ++r) {
     double q[DPL];
     node_reference<D, ROPE>(qref + ((int64_t)kvh * R + r) * D, lane, a, pos, q);
+    // Rows are read kB at a time, every load of a batch issued before the
+    // first is used (one memory latency per batch, not per row); the
+    // arithmetic runs row by row in order.
+    constexpr int kB = 8;
     // First key read: the maximum score of the chunk.
     double m = -INFINITY;
-    for (int j = 0; j < C; ++j) {
-      double k[DPL];
-      load_row_f64<T, D>(keys + (int64_t)j * D, lane, k);
-      double part = 0.0;
+    for (int j0 = 0; j0 < C; j0 += kB) {
+      double k[kB][DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) part = fma(q[e], k[e], part);
-      m = fmax(m, group_sum64<kWave>(part) * inv_sqrt_d);
+      for (int u = 0; u < kB; ++u) load_row_f64<T, D>(keys + (int64_t)min(j0 + u, C - 1) * D, lane, k[u]);
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (j0 + u >= C) break;
+        double part = 0.0;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) part = fma(q[e], k[u][e], part);
+        m = fmax(m, group_sum64<kWave>(part) * inv_sqrt_d);
+      }
     }
     // Second key read: weights exp(s - m), their sum and the weighted key sum.
     double Z = 0.0;
     double acc[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
-    for (int j = 0; j < C; ++j) {
-      double k[DPL];
-      load_row_f64<T, D>(keys + (int64_t)j * D, lane, k);
-      double part = 0.0;
+    for (int j0 = 0; j0 < C; j0 += kB) {
+      double k[kB][DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) part = fma(q[e], k[e], part);
-      const double w = exp(group_sum64<kWave>(part) * inv_sqrt_d - m);
-      Z += w;
+      for (int u = 0; u < kB; ++u) load_row_f64<T, D>(keys + (int64_t)min(j0 + u, C - 1) * D, lane, k[u]);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = fma(w, k[e], acc[e]);
+      for (int u = 0; u < kB; ++u) {
+        if (j0 + u >= C) break;
+        double part = 0.0;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) part = fma(q[e], k[u][e], part);
+        const double w = exp(group_sum64<kWave>(part) * inv_sqrt_d - m);
+        Z += w;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fma(w, k[u][e], acc[e]);
+      }
     }
     const double F = m + log(Z);
     double part = 0.0;
@@ -196,12 +210,25 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qr
           c0 + lane < C ? (ROPE ? fw[c0 + lane] : cF[(child0 + c0 + lane) * R + r]) : 0.0;
       const double e_mine = (c0 + lane < C) ? exp(f_mine - m) : 0.0;
       const int cn = min(kWave, C - c0);
-      for (int c = 0; c < cn; ++c) {
-        const double w = __shfl(e_mine, c, kWave);
-        Z += w;
-        const double* krow = cK + ((child0 + c0 + c) * R + r) * D + lane * DPL;
+      // Children's rows kB at a time, all loads of a batch issued first; the
+      // sums run child by child in order.
+      constexpr int kB = 8;
+      for (int cb = 0; cb < cn; cb += kB) {
+        double kr[kB][DPL];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fma(w, krow[e], acc[e]);
+        for (int u = 0; u < kB; ++u) {
+          const double* krow = cK + ((child0 + c0 + min(cb + u, cn - 1)) * R + r) * D + lane * DPL;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) kr[u][e] = krow[e];
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          if (cb + u >= cn) break;
+          const double w = __shfl(e_mine, cb + u, kWave);
+          Z += w;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[e] = fma(w, kr[u][e], acc[e]);
+        }
       }
     }
     const double F = m + log(Z);
