@@ -111,6 +111,22 @@ def test_reference_queries_r16(Z, dtype):
     run_parity(Z, g, range(4))
 
 
+@pytest.mark.parametrize("name,kw,chunked", [
+    # sixteen levels of a binary tree, a ragged tail
+    ("c2-l16", dict(dtype=W.BF16, B=1, H_q=4, H_kv=1, T=2 ** 16 + 3, C=2, L=16, p=0.9), False),
+    # fp32, d = 256, three reference queries, chunked KV with C = 5
+    ("f32-d256-r3", dict(dtype=W.F32, B=2, H_q=4, H_kv=2, d=256, T=5 ** 4 * 3 + 5 * 2 + 4, C=5,
+                         L=4, p=0.9, R=3), True),
+    # the widest chunk: 1024 children per node
+    ("c1024", dict(dtype=W.BF16, B=1, H_q=8, H_kv=2, T=1024 * 1024 * 2 + 1024 * 3 + 11, C=1024,
+                   L=2, p=0.95), False),
+])
+def test_extreme_geometries(Z, name, kw, chunked):
+    say(f"geometry {name}: {kw}, {'chunked' if chunked else 'split'} KV")
+    g = W.custom(name, 190, **kw)
+    run_parity(Z, g, range(3), chunked=chunked)
+
+
 @pytest.mark.parametrize("d", [64, 256])
 def test_other_head_dims(Z, d):
     say(f"head dim {d}")
