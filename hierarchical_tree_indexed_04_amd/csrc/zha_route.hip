@@ -49,23 +49,25 @@ constexpr int kMaxChildren = 1024;  // C <= 1024
 // Two launch shapes of the same kernel.  Latency shape: 8 waves, 16 rows in
 // flight per lane, frontiers up to kRouteFrontierMax; one workgroup per CU, so
 // a call with few query heads finishes as fast as one head walks the tree.
-// Throughput shape: ZHA_ROUTE_TPUT_THREADS threads, ZHA_ROUTE_TPUT_ROWS 16-byte
-// loads in flight per lane, frontiers up to ZHA_ROUTE_TPUT_FMAX in LDS; many workgroups
-// share a CU, for calls with many query heads (a block of positions), so more
-// heads are in flight.  A head whose frontier outgrows the throughput shape is
+// Throughput shape: ZHA_ROUTE_TPUT_THREADS threads (one wave: no barrier between
+// waves, no work repeated per wave), ZHA_ROUTE_TPUT_ROWS 16-byte loads in flight
+// per lane, frontiers up to ZHA_ROUTE_TPUT_FMAX in LDS; many workgroups share a
+// CU, for calls with many query heads (a block of positions), so more heads are
+// in flight (measured on the 1M block: 241 us against 255 us with two waves and
+// 768 candidates; causal prefill at 128K: 23.2 against 27.3 ms of routing).  A head whose frontier outgrows the throughput shape is
 // listed in the scratch buffer and routed again by a few persistent workgroups
 // of the latency shape.
 #ifndef ZHA_ROUTE_LAT_ROWS
 #define ZHA_ROUTE_LAT_ROWS 16
 #endif
 #ifndef ZHA_ROUTE_TPUT_ROWS
-#define ZHA_ROUTE_TPUT_ROWS 4
+#define ZHA_ROUTE_TPUT_ROWS 8
 #endif
 #ifndef ZHA_ROUTE_TPUT_THREADS
-#define ZHA_ROUTE_TPUT_THREADS 128
+#define ZHA_ROUTE_TPUT_THREADS 64
 #endif
 #ifndef ZHA_ROUTE_TPUT_FMAX
-#define ZHA_ROUTE_TPUT_FMAX 768
+#define ZHA_ROUTE_TPUT_FMAX 512
 #endif
 #ifndef ZHA_ROUTE_TPUT_EU
 #define ZHA_ROUTE_TPUT_EU 1
