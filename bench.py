@@ -210,7 +210,8 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     build_ms = eb0.elapsed_time(eb1)
     log(f"[bench] tree build {build_ms:.2f} ms ({tb / 1e6:.1f} MB tree)")
 
-    cap = min(g.n_level(1), 8192)
+    # Chunk-list capacity: every leaf chunk when the lists of all steps fit in 2 GiB.
+    cap = g.n_level(1) if n * g.B * g.H_q * g.n_level(1) * 4 <= (2 << 30) else 8192
     sel = torch.empty((n, g.B, 1, g.H_q, cap), dtype=torch.int32, device="cuda")
     cnt = torch.empty((n, g.B, 1, g.H_q), dtype=torch.int32, device="cuda")
     stats = torch.empty((n, g.B, 1, g.H_q, g.L, 2), dtype=torch.int32, device="cuda")

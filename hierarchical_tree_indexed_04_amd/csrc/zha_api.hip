@@ -198,7 +198,7 @@ int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_
   if (bytes == nullptr) return ZHA_ERR_NULL;
   if (n_pos < 1) return ZHA_ERR_NPOS;
   if (cap < 1) return ZHA_ERR_CAP;
-  *bytes = (size_t)route_scratch_layout_bytes((int64_t)g->B * n_pos * g->H_q);
+  *bytes = (size_t)route_scratch_layout((int64_t)g->B * n_pos * g->H_q, capacity(g) / g->C).bytes;
   return ZHA_OK;
 }
 
@@ -227,7 +227,9 @@ int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
   a.cap = cap;
   a.p = p;
   if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
-  if (route_scratch_layout_bytes(a.n_heads) > 0 && scratch == nullptr) return ZHA_ERR_NULL;
+  const RouteScratch rs = route_scratch_layout(a.n_heads, a.lay.ncap[1]);
+  if (rs.bytes > 0 && scratch == nullptr) return ZHA_ERR_NULL;
+  if (rs.bytes > 0 && !aligned16(scratch)) return ZHA_ERR_ALIGN;
   return route_dispatch(a, g->dtype, g->d, tree, Q, sel, cnt, level_stats, gap, scratch,
                         reinterpret_cast<hipStream_t>(stream));
 }

@@ -8,11 +8,39 @@ namespace zha {
 
 constexpr int kRouteFrontierMax = 4096;  // candidates per level held in LDS by the router
 constexpr int64_t kTputMinHeads = 4096;  // query heads per call for the router's throughput shape
+constexpr int kRouteSpillBlocks = 8;     // workgroups routing heads whose frontier outgrew the LDS
 
-// zha_route scratch: with the throughput shape, a count and a list of the heads
-// whose frontier outgrew it.
-inline int64_t route_scratch_layout_bytes(int64_t n_heads) {
-  return n_heads >= kTputMinHeads ? (n_heads + 1) * 4 : 0;
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+// zha_route scratch (byte offsets, -1 where absent).
+//   list1  throughput shape (n_heads >= kTputMinHeads): a count and the heads
+//          whose frontier outgrew its LDS, routed again by the latency shape.
+//   list2  trees whose level 1 can hold more than kRouteFrontierMax nodes
+//          (n1c, at capacity): the heads whose frontier outgrew the latency
+//          shape's LDS, as a count and a list after list1, or as one flag per
+//          head (written by every head, so nothing is cleared beforehand) when
+//          the latency shape routes the whole call.
+//   ws     with list2: per spill workgroup, a frontier of n1c candidates in
+//          device memory (two id arrays and the scores, 12 bytes each).
+struct RouteScratch {
+  int64_t list1 = -1, list2 = -1, ws = -1, ws_stride = 0, bytes = 0;
+};
+inline RouteScratch route_scratch_layout(int64_t n_heads, int64_t n1c) {
+  RouteScratch s;
+  int64_t off = 0;
+  if (n_heads >= kTputMinHeads) {
+    s.list1 = off;
+    off += align256((n_heads + 1) * 4);
+  }
+  if (n1c > kRouteFrontierMax) {
+    s.list2 = off;
+    off += align256((n_heads + 1) * 4);
+    s.ws_stride = align256(n1c * 12);
+    s.ws = off;
+    off += s.ws_stride * kRouteSpillBlocks;
+  }
+  s.bytes = off;
+  return s;
 }
 constexpr int kBalMaxHeads = 2048;       // balanced split-KV: per-head prefix held in LDS
 
@@ -175,7 +203,6 @@ __host__ __device__ inline int64_t kv_block_elems(int64_t T, int C, int d, bool 
   return chunked ? (T + C - 1) / C * 2 * C * (int64_t)d : T * (int64_t)d;
 }
 
-inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 // Query heads per dense-decode workgroup: the largest of 8, 4, 2, 1 dividing G.
 #ifndef ZHA_DENSE_MAX_TILE

@@ -56,7 +56,10 @@ constexpr int kMaxChildren = 1024;  // C <= 1024
 // in flight (measured on the 1M block: 241 us against 255 us with two waves and
 // 768 candidates; causal prefill at 128K: 23.2 against 27.3 ms of routing).  A head whose frontier outgrows the throughput shape is
 // listed in the scratch buffer and routed again by a few persistent workgroups
-// of the latency shape.
+// of the latency shape.  A head that outgrows the latency shape's frontier as
+// well (trees with more than kRouteFrontierMax level-1 nodes) is routed again
+// with its frontier in device memory, by kRouteSpillBlocks workgroups that each
+// own n_1 candidates of the scratch buffer: routes never fail for size.
 #ifndef ZHA_ROUTE_LAT_ROWS
 #define ZHA_ROUTE_LAT_ROWS 16
 #endif
@@ -123,24 +126,44 @@ __global__ __launch_bounds__(256) void route_keep_all_kernel(RouteArgs a,
   if (threadIdx.x == 0) cnt[head] = (int32_t)n1;
 }
 
-__global__ void route_zero_kernel(int32_t* fail_list) {
-  if (threadIdx.x == 0) fail_list[0] = 0;
+__global__ void route_zero_kernel(int32_t* list1, int32_t* list2) {
+  if (threadIdx.x == 0) {
+    list1[0] = 0;
+    if (list2 != nullptr) list2[0] = 0;
+  }
 }
 
+// Launch sequence.  Many heads: the throughput shape, then the latency shape
+// on the heads it listed, then (trees whose level 1 can outgrow the latency
+// shape's LDS) the device-memory frontier on the heads listed again.  Few
+// heads: the latency shape, then the device-memory frontier on the heads it
+// flagged.
 template <typename T, int D, bool R1>
 void launch_route_kernels(const RouteArgs& a, const char* tree, const T* q, int32_t* sel,
-                          int32_t* cnt, int32_t* stats, float* gap, int32_t* fail_list,
+                          int32_t* cnt, int32_t* stats, float* gap, char* scratch,
                           hipStream_t s) {
+  const RouteScratch rs = route_scratch_layout(a.n_heads, a.lay.ncap[1]);
+  int32_t* list1 = rs.list1 < 0 ? nullptr : reinterpret_cast<int32_t*>(scratch + rs.list1);
+  int32_t* list2 = rs.list2 < 0 ? nullptr : reinterpret_cast<int32_t*>(scratch + rs.list2);
+  char* ws = rs.ws < 0 ? nullptr : scratch + rs.ws;
   const unsigned blocks = (unsigned)a.n_heads;
   if (a.n_heads >= kTputMinHeads) {
-    route_zero_kernel<<<1, 64, 0, s>>>(fail_list);
+    route_zero_kernel<<<1, 64, 0, s>>>(list1, list2);
     tput::route_kernel<T, D, tput::kFMax, R1>
-        <<<blocks, tput::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, fail_list);
-    lat::route_list_kernel<T, D, lat::kFMax, R1>
-        <<<kRouteListBlocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, fail_list);
+        <<<blocks, tput::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, list1, nullptr);
+    lat::route_list_kernel<T, D, lat::kFMax, R1><<<kRouteListBlocks, lat::kThreads, 0, s>>>(
+        tree, q, a, sel, cnt, stats, gap, list1, list2);
+    if (list2 != nullptr)
+      lat::route_spill_kernel<T, D, lat::kFMax, R1, false>
+          <<<kRouteSpillBlocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, list2, ws,
+                                                       rs.ws_stride);
   } else {
     lat::route_kernel<T, D, lat::kFMax, R1>
-        <<<blocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, nullptr);
+        <<<blocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, nullptr, list2);
+    if (list2 != nullptr)
+      lat::route_spill_kernel<T, D, lat::kFMax, R1, true>
+          <<<kRouteSpillBlocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, list2, ws,
+                                                       rs.ws_stride);
   }
 }
 
@@ -149,13 +172,13 @@ int launch_route(const RouteArgs& a, const void* tree, const void* Q, int32_t* s
                  int32_t* stats, float* gap, void* scratch, hipStream_t s) {
   const char* tr = reinterpret_cast<const char*>(tree);
   const T* q = reinterpret_cast<const T*>(Q);
-  int32_t* fail_list = reinterpret_cast<int32_t*>(scratch);
+  char* sc = reinterpret_cast<char*>(scratch);
   if (!(a.p < 1.0f))
     route_keep_all_kernel<<<(unsigned)a.n_heads, 256, 0, s>>>(a, sel, cnt, stats, gap);
   else if (a.lay.R == 1)
-    launch_route_kernels<T, D, true>(a, tr, q, sel, cnt, stats, gap, fail_list, s);
+    launch_route_kernels<T, D, true>(a, tr, q, sel, cnt, stats, gap, sc, s);
   else
-    launch_route_kernels<T, D, false>(a, tr, q, sel, cnt, stats, gap, fail_list, s);
+    launch_route_kernels<T, D, false>(a, tr, q, sel, cnt, stats, gap, sc, s);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
 }
 

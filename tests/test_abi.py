@@ -180,9 +180,20 @@ def test_capacity_sets_strides_and_length_sets_nothing_else():
 
 
 def test_scratch_sizes_are_consistent():
+    # n_1 = 4096: every frontier fits the router's on-chip capacity
+    small = g(B=8, H_q=32, H_kv=4, T=32768, C=8, L=5)
+    assert Z.frontier_capacity() == 4096
+    assert Z.route_scratch_bytes(small, 1, 4096) == 0
+    assert Z.route_scratch_bytes(small, 16, 4096) >= (8 * 16 * 32 + 1) * 4  # many heads: re-route list
+    # n_1 = 32768: frontiers of up to n_1 candidates in device memory (ids twice, scores)
     gm = g(B=8, H_q=32, H_kv=4, T=262144, C=8, L=6)
-    assert Z.route_scratch_bytes(gm, 1, 32768) == 0
-    assert Z.route_scratch_bytes(gm, 16, 32768) == (8 * 16 * 32 + 1) * 4  # many heads: fallback list
+    few = Z.route_scratch_bytes(gm, 1, 32768)
+    assert few >= 12 * 32768 + 256 * 4
+    many = Z.route_scratch_bytes(gm, 16, 32768)
+    assert many >= few + (8 * 16 * 32 + 1) * 4
+    # sized for the capacity, so the same at every length up to it
+    assert Z.route_scratch_bytes(g(B=8, H_q=32, H_kv=4, T=5000, T_cap=262144, C=8, L=6), 1,
+                                 32768) == few
     a = Z.attn_scratch_bytes(gm, 1, 32768)
     assert a >= (256 + 32) * 4 * (gm.d + 2)  # plan + at least one partial per workgroup and head
     assert Z.dense_scratch_bytes(gm, 1) % (4 * (gm.d + 2)) == 0
