@@ -297,7 +297,7 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
 
     cnt_h = cnt.cpu().numpy()
     if (cnt_h[warmup:] < 0).any() or (cnt_h[warmup:] > cap).any():
-        raise RuntimeError("a route overflowed the frontier capacity or the chunk-list cap")
+        raise RuntimeError("a route failed (cnt < 0) or its count exceeds the chunk-list cap")
     sel_h = sel.cpu().numpy()
     stats_h = stats.cpu().numpy()
     acc = {"attn_union": 0, "attn_per_head": 0, "route": 0, "tokens_per_head": 0.0}
@@ -628,7 +628,7 @@ def run_prefill(block: int, reps: int):
     torch.cuda.synchronize()
     c = cnt_all.cpu().numpy()
     if (c < 0).any() or (c > cap).any():
-        raise RuntimeError("prefill: a route overflowed the frontier capacity or the list cap")
+        raise RuntimeError("prefill: a route failed (cnt < 0) or its count exceeds the list cap")
     if not torch.isfinite(O).all():
         raise RuntimeError("prefill: non-finite output")
     tail = (np.arange(1, T + 1) % g.C)[None, :, None]

@@ -8,22 +8,19 @@ namespace zha {
 
 constexpr int kRouteFrontierMax = 4096;  // candidates per level held in LDS by the router
 constexpr int64_t kTputMinHeads = 4096;  // query heads per call for the router's throughput shape
-constexpr int kRouteSpillBlocks = 8;     // workgroups routing heads whose frontier outgrew the LDS
+constexpr int kRouteSpillBlocks = 8;     // device-memory frontier slots for heads that outgrow the LDS
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 // zha_route scratch (byte offsets, -1 where absent).
 //   list1  throughput shape (n_heads >= kTputMinHeads): a count and the heads
 //          whose frontier outgrew its LDS, routed again by the latency shape.
-//   list2  trees whose level 1 can hold more than kRouteFrontierMax nodes
-//          (n1c, at capacity): the heads whose frontier outgrew the latency
-//          shape's LDS, as a count and a list after list1, or as one flag per
-//          head (written by every head, so nothing is cleared beforehand) when
-//          the latency shape routes the whole call.
-//   ws     with list2: per spill workgroup, a frontier of n1c candidates in
-//          device memory (two id arrays and the scores, 12 bytes each).
+//   ws     trees whose level 1 can hold more than kRouteFrontierMax nodes (n1c,
+//          at capacity): kRouteSpillBlocks slots, each a frontier of n1c
+//          candidates in device memory (two id arrays and the scores, 12 bytes
+//          per candidate), for the heads that outgrow the latency shape's LDS.
 struct RouteScratch {
-  int64_t list1 = -1, list2 = -1, ws = -1, ws_stride = 0, bytes = 0;
+  int64_t list1 = -1, ws = -1, ws_stride = 0, bytes = 0;
 };
 inline RouteScratch route_scratch_layout(int64_t n_heads, int64_t n1c) {
   RouteScratch s;
@@ -33,8 +30,6 @@ inline RouteScratch route_scratch_layout(int64_t n_heads, int64_t n1c) {
     off += align256((n_heads + 1) * 4);
   }
   if (n1c > kRouteFrontierMax) {
-    s.list2 = off;
-    off += align256((n_heads + 1) * 4);
     s.ws_stride = align256(n1c * 12);
     s.ws = off;
     off += s.ws_stride * kRouteSpillBlocks;

@@ -46,6 +46,10 @@ namespace {
 #endif
 constexpr int kMaxChildren = 1024;  // C <= 1024
 
+// Device-memory frontier slots in use (1) or free (0): zero when the code
+// object loads, and every holder frees its slot before its kernel ends.
+__device__ int32_t g_route_spill_lock[kRouteSpillBlocks];
+
 // Two launch shapes of the same kernel.  Latency shape: 8 waves, 16 rows in
 // flight per lane, frontiers up to kRouteFrontierMax; one workgroup per CU, so
 // a call with few query heads finishes as fast as one head walks the tree.
@@ -58,8 +62,9 @@ constexpr int kMaxChildren = 1024;  // C <= 1024
 // listed in the scratch buffer and routed again by a few persistent workgroups
 // of the latency shape.  A head that outgrows the latency shape's frontier as
 // well (trees with more than kRouteFrontierMax level-1 nodes) is routed again
-// with its frontier in device memory, by kRouteSpillBlocks workgroups that each
-// own n_1 candidates of the scratch buffer: routes never fail for size.
+// by the same workgroup with its frontier in device memory, in one of
+// kRouteSpillBlocks slots of n_1 candidates in the scratch buffer: routes never
+// fail for size.
 #ifndef ZHA_ROUTE_LAT_ROWS
 #define ZHA_ROUTE_LAT_ROWS 16
 #endif
@@ -84,6 +89,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kU = ZHA_ROUTE_LAT_ROWS;
 constexpr int kFMax = kRouteFrontierMax;
 constexpr int kMinWavesEU = 1;
+constexpr bool kSpillInPlace = true;
 #include "zha_route_impl.inc"
 }  // namespace lat
 namespace tput {
@@ -92,6 +98,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kU = ZHA_ROUTE_TPUT_ROWS;
 constexpr int kFMax = ZHA_ROUTE_TPUT_FMAX;
 constexpr int kMinWavesEU = ZHA_ROUTE_TPUT_EU;
+constexpr bool kSpillInPlace = false;  // overflowing heads are listed for the latency shape
 #include "zha_route_impl.inc"
 }  // namespace tput
 // kTputMinHeads (query heads per call for the throughput shape) is in zha_internal.hpp.
@@ -126,44 +133,31 @@ __global__ __launch_bounds__(256) void route_keep_all_kernel(RouteArgs a,
   if (threadIdx.x == 0) cnt[head] = (int32_t)n1;
 }
 
-__global__ void route_zero_kernel(int32_t* list1, int32_t* list2) {
-  if (threadIdx.x == 0) {
-    list1[0] = 0;
-    if (list2 != nullptr) list2[0] = 0;
-  }
+__global__ void route_zero_kernel(int32_t* list) {
+  if (threadIdx.x == 0) list[0] = 0;
 }
 
 // Launch sequence.  Many heads: the throughput shape, then the latency shape
-// on the heads it listed, then (trees whose level 1 can outgrow the latency
-// shape's LDS) the device-memory frontier on the heads listed again.  Few
-// heads: the latency shape, then the device-memory frontier on the heads it
-// flagged.
+// on the heads it listed.  Few heads: the latency shape alone.  The latency
+// shape routes a head that outgrows its LDS again in place, with a
+// device-memory frontier (trees whose level 1 can outgrow the LDS).
 template <typename T, int D, bool R1>
 void launch_route_kernels(const RouteArgs& a, const char* tree, const T* q, int32_t* sel,
                           int32_t* cnt, int32_t* stats, float* gap, char* scratch,
                           hipStream_t s) {
   const RouteScratch rs = route_scratch_layout(a.n_heads, a.lay.ncap[1]);
   int32_t* list1 = rs.list1 < 0 ? nullptr : reinterpret_cast<int32_t*>(scratch + rs.list1);
-  int32_t* list2 = rs.list2 < 0 ? nullptr : reinterpret_cast<int32_t*>(scratch + rs.list2);
   char* ws = rs.ws < 0 ? nullptr : scratch + rs.ws;
   const unsigned blocks = (unsigned)a.n_heads;
   if (a.n_heads >= kTputMinHeads) {
-    route_zero_kernel<<<1, 64, 0, s>>>(list1, list2);
-    tput::route_kernel<T, D, tput::kFMax, R1>
-        <<<blocks, tput::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, list1, nullptr);
+    route_zero_kernel<<<1, 64, 0, s>>>(list1);
+    tput::route_kernel<T, D, tput::kFMax, R1><<<blocks, tput::kThreads, 0, s>>>(
+        tree, q, a, sel, cnt, stats, gap, list1, nullptr, 0);
     lat::route_list_kernel<T, D, lat::kFMax, R1><<<kRouteListBlocks, lat::kThreads, 0, s>>>(
-        tree, q, a, sel, cnt, stats, gap, list1, list2);
-    if (list2 != nullptr)
-      lat::route_spill_kernel<T, D, lat::kFMax, R1, false>
-          <<<kRouteSpillBlocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, list2, ws,
-                                                       rs.ws_stride);
+        tree, q, a, sel, cnt, stats, gap, list1, ws, rs.ws_stride);
   } else {
-    lat::route_kernel<T, D, lat::kFMax, R1>
-        <<<blocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, nullptr, list2);
-    if (list2 != nullptr)
-      lat::route_spill_kernel<T, D, lat::kFMax, R1, true>
-          <<<kRouteSpillBlocks, lat::kThreads, 0, s>>>(tree, q, a, sel, cnt, stats, gap, list2, ws,
-                                                       rs.ws_stride);
+    lat::route_kernel<T, D, lat::kFMax, R1><<<blocks, lat::kThreads, 0, s>>>(
+        tree, q, a, sel, cnt, stats, gap, nullptr, ws, rs.ws_stride);
   }
 }
 

@@ -194,11 +194,17 @@ int zha_tree_update(const zha_geom* g, int64_t T_old, const void* K, const float
  * nodes whose parent is incomplete (paper App. E-E).
  * ------------------------------------------------------------------------- */
 
-/* Scratch bytes zha_route needs: nonzero for calls of 4096 or more query heads
- * (B * n_pos * H_q), which route most heads with a smaller-frontier launch and
- * list there the heads whose frontier outgrew it; 0 otherwise (then any
- * pointer, NULL included, may be passed).  Calls that overlap in time on the
- * same buffer race. */
+/* Scratch bytes zha_route needs (0: any pointer, NULL included, may be passed):
+ *   - calls of 4096 or more query heads (B * n_pos * H_q) route most heads
+ *     with a smaller-frontier launch and list there the heads whose frontier
+ *     outgrew it: (heads + 1) int32;
+ *   - trees whose level 1 can hold more than zha_route_frontier_capacity()
+ *     nodes (n_1 at the capacity T_cap, else T): a head whose frontier
+ *     outgrows the on-chip capacity is routed again with its frontier in
+ *     device memory, in one of 8 slots of 12 * n_1 bytes (ids and scores;
+ *     about 100 MB at 2^24 tokens with C = 16).
+ * The size depends on the capacity, not on T, so one buffer serves every
+ * length up to it.  Calls that overlap in time on the same buffer race. */
 int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes);
 
 /*   tree        device, built by zha_build for the same geometry
@@ -217,8 +223,7 @@ int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_
  *               left untouched
  *   cnt         device [B, n_pos, H_q] int32, written: |S_1|, the true count
  *               even when it exceeds cap (then sel holds the cap lowest ids);
- *               -1 if a frontier exceeded the router's capacity
- *               (zha_route_frontier_capacity())
+ *               -1 for a position whose ctx_len entry is invalid
  *   level_stats device [B, n_pos, H_q, L, 2] int32 or NULL: for level l at
  *               index l-1, (frontier size K_l, kept count |S_l|)
  *   gap         device [B, n_pos, H_q, L] fp32 or NULL: s_(m) - s_(m+1) at
@@ -230,7 +235,9 @@ int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
               int32_t* sel, int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap,
               void* scratch, void* stream);
 
-/* Largest frontier (candidates at one level of one query head) zha_route handles. */
+/* Largest frontier (candidates at one level of one query head) that zha_route
+ * holds on chip; larger ones go through the scratch buffer (slower, same
+ * result). */
 int32_t zha_route_frontier_capacity(void);
 
 /* ---------------------------------------------------------------------------
