@@ -107,16 +107,19 @@ def test_device_memory_frontier_matches_oracle(Z, name, kw, chunked):
     check_heads(g, K, V, Qn, trees, sel, cnt, stats, from_device(Od, g.dtype), heads)
 
 
-def test_device_memory_frontier_many_heads(Z):
+@pytest.mark.parametrize("dtype,R,chunked", [(W.BF16, 1, False), (W.F32, 2, True)])
+def test_device_memory_frontier_many_heads(Z, dtype, R, chunked):
     # 4096 query heads: the throughput shape lists every weak head, the latency
-    # shape lists them again, and the device-memory frontier routes them.
+    # shape's list kernel outgrows its LDS on them too and routes them again
+    # with the device-memory frontier.
     import torch
-    g = W.custom("wide-many", 181, dtype=W.BF16, B=1, H_q=8, H_kv=1, C=16, L=2,
-                 T=16 * 16 * 300 + 37, R=1, p=0.99)
+    g = W.custom("wide-many", 181, dtype=dtype, B=1, H_q=8, H_kv=1, C=16, L=2,
+                 T=16 * 16 * 300 + 37, R=R, p=0.99)
     n_pos = 512
-    say(f"many heads: {n_pos} positions x {g.H_q} heads, n_1={g.n_level(1)}, every 8th position weak")
+    say(f"many heads ({dtype}, R={R}): {n_pos} positions x {g.H_q} heads, n_1={g.n_level(1)}, "
+        f"every 8th position weak")
     K, V = W.make_kv(g)
-    gm, Kd, Vd, tree, qref = build(Z, g, K, V, False)
+    gm, Kd, Vd, tree, qref = build(Z, g, K, V, chunked)
     Qn = W.make_query_block(g, K, range(n_pos))
     weak = list(range(0, n_pos, 8))
     weaken(g, Qn, weak, 181)
