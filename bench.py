@@ -178,6 +178,12 @@ def to_dev(torch, a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
+def layer_count(layer_bytes: int) -> int:
+    """Synthetic layers the timed decode steps cycle through: at least 4, and
+    enough for 4 GiB of caches and trees in all (at most 16)."""
+    return int(min(16, max(4, -(-(4 << 30) // layer_bytes))))
+
+
 def run_gpu(g, K, V, steps, warmup, dense_steps):
     import torch
 
@@ -210,6 +216,18 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     build_ms = eb0.elapsed_time(eb1)
     log(f"[bench] tree build {build_ms:.2f} ms ({tb / 1e6:.1f} MB tree)")
 
+    # Decode visits every layer's cache and tree in turn, so a layer's rows are
+    # long gone from L2 and the 256 MB memory-side cache when its next step
+    # comes.  The timed steps do the same: step i uses layer i mod n_layers, each
+    # layer its own copy of K, V and the tree in HBM, with at least 4 GiB of them
+    # in all.
+    n_layers = layer_count(Kd.numel() * 2 * Kd.element_size() + tb)
+    layers = [(Kd, Vd, tree)]
+    for _ in range(n_layers - 1):
+        layers.append((Kd.clone(), Vd.clone(), tree.clone()))
+    torch.cuda.synchronize()
+    log(f"[bench] steps cycle through {n_layers} layers' caches and trees")
+
     # Chunk-list capacity: every leaf chunk when the lists of all steps fit in 2 GiB.
     cap = g.n_level(1) if n * g.B * g.H_q * g.n_level(1) * 4 <= (2 << 30) else 8192
     sel = torch.empty((n, g.B, 1, g.H_q, cap), dtype=torch.int32, device="cuda")
@@ -228,14 +246,15 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     gref = ctypes.byref(gm)
     vp = ctypes.c_void_p
     stream = vp(torch.cuda.current_stream().cuda_stream)
-    tree_p, k_p, v_p = vp(tree.data_ptr()), vp(Kd.data_ptr()), vp(Vd.data_ptr())
+    lp = [(vp(t.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr())) for (k, v, t) in layers]
     rs_p, as_p = vp(rscratch.data_ptr()), vp(ascratch.data_ptr())
-    args_r = [(gref, tree_p, vp(Qd[i].data_ptr()), 1, None, ctypes.c_float(g.p),
+    args_r = [(gref, lp[i % n_layers][0], vp(Qd[i].data_ptr()), 1, None, ctypes.c_float(g.p),
                vp(sel[i].data_ptr()),
                vp(cnt[i].data_ptr()), cap, vp(stats[i].data_ptr()), None, rs_p, stream)
               for i in range(n)]
-    args_a = [(gref, vp(Qd[i].data_ptr()), 1, None, k_p, v_p, vp(sel[i].data_ptr()),
-               vp(cnt[i].data_ptr()), cap, vp(O[i].data_ptr()), as_p, stream) for i in range(n)]
+    args_a = [(gref, vp(Qd[i].data_ptr()), 1, None, lp[i % n_layers][1], lp[i % n_layers][2],
+               vp(sel[i].data_ptr()), vp(cnt[i].data_ptr()), cap, vp(O[i].data_ptr()), as_p,
+               stream) for i in range(n)]
     zr, za = lib.zha_route, lib.zha_attn
 
     def step(i):
@@ -293,7 +312,8 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     c1.record()
     torch.cuda.synchronize()
     copy_gbs = 2 * 5 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del flush, dst
+    del flush, dst, layers
+    torch.cuda.empty_cache()
 
     cnt_h = cnt.cpu().numpy()
     if (cnt_h[warmup:] < 0).any() or (cnt_h[warmup:] > cap).any():
@@ -329,7 +349,8 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     maint = decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch)
     return {"total_ms": total_ms, "route_ms": route_ms, "attn_ms": attn_ms, "bytes": acc,
             "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap, "cold_route_ms": cold_route,
-            "cold_attn_ms": cold_attn, "copy_gbs": copy_gbs, "maintenance": maint}
+            "cold_attn_ms": cold_attn, "copy_gbs": copy_gbs, "maintenance": maint,
+            "n_layers": n_layers}
 
 
 def decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch, reps: int = 200):
@@ -749,7 +770,8 @@ def main():
         "dtype": g.dtype,
         "data": "synthetic",
         "config": {"workload": f"{g.name}: B={g.B}, H_q={g.H_q}/H_kv={g.H_kv}, d={g.d}, T={g.T}, "
-                               f"C={g.C}, L={g.L}, R={g.R}, p={g.p}, one decode step per call",
+                               f"C={g.C}, L={g.L}, R={g.R}, p={g.p}, one decode step per call, "
+                               f"steps cycling through {r['n_layers']} layers' KV caches and trees",
                    "global_batch": g.B, "seq_len": g.T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm",
                      "kernel": "zha_attn call (attn_balanced_kernel + merge_balanced_kernel)",
