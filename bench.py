@@ -261,45 +261,49 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
         if zr(*args_r[i]) != 0 or za(*args_a[i]) != 0:
             raise RuntimeError("launch failed")
 
+    def timed(calls):
+        """Device time of the given launches, back to back, between two events."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for fn, a in calls:
+            if fn(*a) != 0:
+                raise RuntimeError("launch failed")
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
-    torch.cuda.synchronize()
-    ev[0].record()
-    for j in range(steps):
-        i = warmup + j
-        if zr(*args_r[i]) != 0:
-            raise RuntimeError("zha_route failed")
-        ev[2 * j + 1].record()
-        if za(*args_a[i]) != 0:
-            raise RuntimeError("zha_attn failed")
-        ev[2 * j + 2].record()
-    torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[2 * steps])
-    route_ms = np.array([ev[2 * j].elapsed_time(ev[2 * j + 1]) for j in range(steps)])
-    attn_ms = np.array([ev[2 * j + 1].elapsed_time(ev[2 * j + 2]) for j in range(steps)])
-    log(f"[bench] {steps} steps: {total_ms:.3f} ms total; route {route_ms.mean() * 1e3:.1f} us, "
-        f"attn {attn_ms.mean() * 1e3:.1f} us per step")
+    # The timed steps: route + attention per step, no event between them (an
+    # event recorded between two launches costs the stream ~3.5 us).
+    timed_ids = range(warmup, warmup + steps)
+    total_ms = timed([c for i in timed_ids for c in ((zr, args_r[i]), (za, args_a[i]))])
+    # The split, each call kind timed back to back over the same steps (the
+    # attention calls reuse the routes computed above).
+    route_ms = np.full(steps, timed([(zr, args_r[i]) for i in timed_ids]) / steps)
+    attn_ms = np.full(steps, timed([(za, args_a[i]) for i in timed_ids]) / steps)
+    log(f"[bench] {steps} steps: {total_ms:.3f} ms total ({total_ms / steps * 1e3:.1f} us per step); "
+        f"route alone {route_ms.mean() * 1e3:.1f} us, attn alone {attn_ms.mean() * 1e3:.1f} us per call")
 
-    # The same steps cache-cold: 1 GiB written between steps (outside the timed
-    # region) evicts L2 and the memory-side cache; each step timed on its own.
+    # The same calls fully cache-cold: 1 GiB written before each call (outside
+    # its timing) evicts L2 and the memory-side cache; each call between two
+    # events of its own.
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     n_cold = min(steps, 10)
-    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_cold)]
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_cold)]
     for j in range(n_cold):
         i = warmup + j
-        flush.fill_(j & 255)
-        evc[j][0].record()
-        if zr(*args_r[i]) != 0:
-            raise RuntimeError("zha_route failed")
-        evc[j][1].record()
-        if za(*args_a[i]) != 0:
-            raise RuntimeError("zha_attn failed")
-        evc[j][2].record()
+        for k, (fn, a) in enumerate(((zr, args_r[i]), (za, args_a[i]))):
+            flush.fill_((2 * j + k) & 255)
+            evc[j][2 * k].record()
+            if fn(*a) != 0:
+                raise RuntimeError("launch failed")
+            evc[j][2 * k + 1].record()
     torch.cuda.synchronize()
     cold_route = np.array([e[0].elapsed_time(e[1]) for e in evc])
-    cold_attn = np.array([e[1].elapsed_time(e[2]) for e in evc])
+    cold_attn = np.array([e[2].elapsed_time(e[3]) for e in evc])
     log(f"[bench] {n_cold} cold steps: route {cold_route.mean() * 1e3:.1f} us, "
         f"attn {cold_attn.mean() * 1e3:.1f} us per step")
     # Streaming-copy bandwidth of this device (read + write bytes of a 1 GiB copy).
@@ -797,7 +801,8 @@ def main():
                  "step_hbm_frac": step_union / float((r["cold_route_ms"] + r["cold_attn_ms"]).mean()
                                                      * 1e-3) / (HBM_PEAK_GBS * 1e9),
                  "steps": int(len(r["cold_route_ms"])),
-                 "how": "1 GiB written between steps, outside the timed region"},
+                 "how": "1 GiB written before each route and each attention call, outside its "
+                        "timing; each call between two events of its own"},
         "tokens_per_head": by["tokens_per_head"],
         "keys_attended_frac": by["tokens_per_head"] / g.T,
         "build_ms": r["build_ms"],
