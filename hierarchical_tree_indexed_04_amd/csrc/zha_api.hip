@@ -226,6 +226,7 @@ int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
   a.G = g->H_q / g->H_kv;
   a.cap = cap;
   a.p = p;
+  a.cdiv = (uint32_t)(((1ull << 32) + (uint64_t)g->C - 1) / (uint64_t)g->C);
   if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
   const RouteScratch rs = route_scratch_layout(a.n_heads, a.lay.ncap[1]);
   if (rs.bytes > 0 && scratch == nullptr) return ZHA_ERR_NULL;

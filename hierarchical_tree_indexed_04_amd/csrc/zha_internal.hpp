@@ -148,6 +148,7 @@ struct RouteArgs {
   int32_t G;
   int32_t cap;
   float p;
+  uint32_t cdiv;  // ceil(2^32 / C): floor(x / C) = umulhi(x, cdiv) for 0 <= x < 2^16
 };
 
 // Tokens visible to query head h (of B * n_pos * H_q): its position's entry
