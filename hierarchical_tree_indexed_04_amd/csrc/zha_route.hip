@@ -50,21 +50,22 @@ constexpr int kMaxChildren = 1024;  // C <= 1024
 // object loads, and every holder frees its slot before its kernel ends.
 __device__ int32_t g_route_spill_lock[kRouteSpillBlocks];
 
-// Two launch shapes of the same kernel.  Latency shape: 8 waves, 16 rows in
+// Launch shapes of the same kernel body.  Latency shape: 8 waves, 16 rows in
 // flight per lane, frontiers up to kRouteFrontierMax; one workgroup per CU, so
 // a call with few query heads finishes as fast as one head walks the tree.
-// Throughput shape: ZHA_ROUTE_TPUT_THREADS threads (one wave: no barrier between
-// waves, no work repeated per wave), ZHA_ROUTE_TPUT_ROWS 16-byte loads in flight
-// per lane, frontiers up to ZHA_ROUTE_TPUT_FMAX in LDS; many workgroups share a
-// CU, for calls with many query heads (a block of positions), so more heads are
-// in flight (measured on the 1M block: 241 us against 255 us with two waves and
-// 768 candidates; causal prefill at 128K: 23.2 against 27.3 ms of routing).  A head whose frontier outgrows the throughput shape is
-// listed in the scratch buffer and routed again by a few persistent workgroups
-// of the latency shape.  A head that outgrows the latency shape's frontier as
-// well (trees with more than kRouteFrontierMax level-1 nodes) is routed again
-// by the same workgroup with its frontier in device memory, in one of
-// kRouteSpillBlocks slots of n_1 candidates in the scratch buffer: routes never
-// fail for size.
+// Throughput shape: ZHA_ROUTE_TPUT_THREADS threads (one wave: no barrier
+// between waves, no work repeated per wave), ZHA_ROUTE_TPUT_ROWS 16-byte loads
+// in flight per lane, frontiers up to ZHA_ROUTE_TPUT_FMAX in LDS; many
+// workgroups share a CU, for calls with many query heads (a block of
+// positions), so more heads are in flight (measured on the 1M block: 241 us
+// against 255 us with two waves and 768 candidates; causal prefill at 128K:
+// 23.2 against 27.3 ms of routing).  A head whose frontier outgrows the
+// throughput shape is listed in the scratch buffer and routed again by
+// persistent workgroups with the latency shape's frontier capacity (4 waves
+// each, two per CU).  A head that outgrows that frontier as well (trees with
+// more than kRouteFrontierMax level-1 nodes) is routed again by the same
+// workgroup with its frontier in device memory, in one of kRouteSpillBlocks
+// slots of n_1 candidates in the scratch buffer: routes never fail for size.
 #ifndef ZHA_ROUTE_LAT_ROWS
 #define ZHA_ROUTE_LAT_ROWS 16
 #endif
@@ -101,8 +102,21 @@ constexpr int kMinWavesEU = ZHA_ROUTE_TPUT_EU;
 constexpr bool kSpillInPlace = false;  // overflowing heads are listed for the latency shape
 #include "zha_route_impl.inc"
 }  // namespace tput
+// Re-routing shape for the heads the throughput shape lists: the latency
+// shape's frontier capacity with 4 waves, so two workgroups share a CU and
+// twice as many listed heads are in flight (1M block: 265 listed heads, list
+// pass 33 -> ~24 us).
+namespace lst {
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kU = ZHA_ROUTE_LAT_ROWS;
+constexpr int kFMax = kRouteFrontierMax;
+constexpr int kMinWavesEU = 1;
+constexpr bool kSpillInPlace = true;
+#include "zha_route_impl.inc"
+}  // namespace lst
 // kTputMinHeads (query heads per call for the throughput shape) is in zha_internal.hpp.
-constexpr unsigned kRouteListBlocks = 256;  // persistent workgroups for the listed heads
+constexpr unsigned kRouteListBlocks = 512;  // persistent workgroups for the listed heads (2 per CU)
 
 // p >= 1 keeps every candidate at every level, so S_l is all of level l and
 // S_1 is every leaf chunk 0 .. n_1 - 1 (orphans included).
@@ -153,7 +167,7 @@ void launch_route_kernels(const RouteArgs& a, const char* tree, const T* q, int3
     route_zero_kernel<<<1, 64, 0, s>>>(list1);
     tput::route_kernel<T, D, tput::kFMax, R1><<<blocks, tput::kThreads, 0, s>>>(
         tree, q, a, sel, cnt, stats, gap, list1, nullptr, 0);
-    lat::route_list_kernel<T, D, lat::kFMax, R1><<<kRouteListBlocks, lat::kThreads, 0, s>>>(
+    lst::route_list_kernel<T, D, lst::kFMax, R1><<<kRouteListBlocks, lst::kThreads, 0, s>>>(
         tree, q, a, sel, cnt, stats, gap, list1, ws, rs.ws_stride);
   } else {
     lat::route_kernel<T, D, lat::kFMax, R1><<<blocks, lat::kThreads, 0, s>>>(
