@@ -198,3 +198,15 @@ def test_scratch_sizes_are_consistent():
     assert a >= (256 + 32) * 4 * (gm.d + 2)  # plan + at least one partial per workgroup and head
     assert Z.dense_scratch_bytes(gm, 1) % (4 * (gm.d + 2)) == 0
     assert Z.frontier_capacity() >= 1024
+
+
+def test_child_index_by_multiply_high_is_exact():
+    # The router's child expansion takes a parent index floor(x / C) as the high
+    # word of x * ceil(2^32 / C) (zha_route's cdiv argument); exact for every x
+    # the expansion meets (x < 2^16) and every chunk size (2 <= C <= 1024).
+    import numpy as np
+    x = np.arange(1 << 16, dtype=np.uint64)
+    for C in range(2, 1025):
+        magic = np.uint64(((1 << 32) + C - 1) // C)
+        assert magic < (1 << 32)
+        assert np.array_equal((x * magic) >> np.uint64(32), x // np.uint64(C)), C
