@@ -90,7 +90,8 @@ def cpu_baseline(g, K, V, seconds: float, procs: int):
     for kvh in range(g.H_kv):
         Kf[kvh] = W.to_float(K[0, kvh], g.dtype)
         Vf[kvh] = W.to_float(V[0, kvh], g.dtype)
-        trees[kvh] = O.build_tree(Kf[kvh].astype(np.float64), np.zeros((1, g.d)), g.C, g.L, g.dtype)
+        trees[kvh] = O.build_tree(Kf[kvh].astype(np.float64), reference_queries(g, K)[kvh],
+                                  g.C, g.L, g.dtype)
     items = []
     for step in range(8192):
         Q = W.make_queries(g, K, step)
@@ -184,6 +185,14 @@ def layer_count(layer_bytes: int) -> int:
     return int(min(16, max(4, -(-(4 << 30) // layer_bytes))))
 
 
+def reference_queries(g, K):
+    """[H_kv, R, d] fp32: the zero reference for R = 1 (tangents are the span means), else R
+    reference queries per KV head drawn like queries from the head's keys."""
+    if g.R == 1:
+        return np.zeros((g.H_kv, 1, g.d), np.float32)
+    return W.make_qref(g, K)
+
+
 def run_gpu(g, K, V, steps, warmup, dense_steps):
     import torch
 
@@ -198,7 +207,7 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     t0 = time.perf_counter()
     Kd, Vd = to_dev(torch, K, g.dtype), to_dev(torch, V, g.dtype)
     Qd = to_dev(torch, Qs, g.dtype)
-    qref = torch.zeros((g.H_kv, g.R, g.d), dtype=torch.float32, device="cuda")
+    qref = torch.from_numpy(reference_queries(g, K)).cuda()
     torch.cuda.synchronize()
     log(f"[bench] upload {Kd.numel() * 2 * Kd.element_size() / 1e9:.2f} GB: "
         f"{time.perf_counter() - t0:.1f} s")
@@ -706,6 +715,9 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle baseline (0 disables)")
+    ap.add_argument("--refs", type=int, default=0, metavar="R",
+                    help="reference queries per KV head (0: the workload's own R = 1 with the zero "
+                         "reference; R > 1 draws them like queries)")
     ap.add_argument("--with-1m", type=int, default=1,
                     help="also time the 1M-context block workload (2048 positions routed at once)")
     ap.add_argument("--crossover", action="store_true",
@@ -730,6 +742,8 @@ def main():
             "(run with --gpus 1)")
         sys.exit(2)
     g = W.CONFIGS[args.config]
+    if args.refs > 0:
+        g = W.replace(g, R=args.refs)
     if g.block:
         log("the chunked-query block workload is not a decode-step benchmark yet")
         sys.exit(2)

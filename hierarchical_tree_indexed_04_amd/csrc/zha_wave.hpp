@@ -120,6 +120,25 @@ __device__ __forceinline__ float wave_max_f32_bcast(float v) {
   return unord_f32((uint32_t)__builtin_amdgcn_readlane((int)u, kWave - 1));
 }
 
+// Maximum of integer images over aligned groups of W lanes (W = 2 .. 64), DPP
+// only.  For W <= 16 every lane of a group holds the group's maximum; for W = 32
+// and 64, the row_bcast steps carry it into the group's last 16-lane row only.
+template <int W>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t u) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  if constexpr (W == 8) {
+    u = max(u, dpp_u32<kDppRowHalfMirror>(u, u));
+  } else if constexpr (W >= 16) {
+    u = max(u, dpp_u32<kDppRowRor8>(u, u));
+    u = max(u, dpp_u32<kDppRowRor4>(u, u));
+  }
+  if constexpr (W >= 4) u = max(u, dpp_u32<kDppQpXor2>(u, u));
+  u = max(u, dpp_u32<kDppQpXor1>(u, u));
+  if constexpr (W >= 32) u = max(u, dpp_u32<kDppRowBcast15, 0xA>(u, u));
+  if constexpr (W == 64) u = max(u, dpp_u32<kDppRowBcast31, 0xC>(u, u));
+  return u;
+}
+
 // Whole-wave sum of a 64-bit value (uniform result), same pattern.
 __device__ __forceinline__ uint64_t wave_sum_u64_bcast(uint64_t v) {
   v = row_allreduce_u64(v, OpAdd());
