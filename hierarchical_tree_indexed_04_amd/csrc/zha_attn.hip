@@ -1386,26 +1386,41 @@ __global__ __launch_bounds__(kThreads) void blk_merge_kernel(
   float m = -INFINITY, l = 0.f, acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  for (int x = 0; x < ne_max; ++x) {
-    const bool on = x < ne;
-    const int64_t row = !on ? 0 : (sink && x == 0) ? 0 : row1 + (x - (sink ? 1 : 0));
-    float kr[DPL], vr[DPL];
+  // The sink and partial-chunk tokens, kXB at a time: every row load of a
+  // batch issues before the first is used (causal prefill has up to C of them
+  // per head); the online update still takes the tokens one by one, in order.
+  constexpr int kXB = 4;
+  for (int x0 = 0; x0 < ne_max; x0 += kXB) {
+    float kr[kXB][DPL], vr[kXB][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      kr[e] = load_elem(Kb + row * D, gl * DPL + e);
-      vr[e] = load_elem(Vb + row * D, gl * DPL + e);
+    for (int u = 0; u < kXB; ++u) {
+      const int x = x0 + u;
+      const bool on = x < ne;
+      const int64_t row = !on ? 0 : (sink && x == 0) ? 0 : row1 + (x - (sink ? 1 : 0));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        kr[u][e] = load_elem(Kb + row * D, gl * DPL + e);
+        vr[u][e] = load_elem(Vb + row * D, gl * DPL + e);
+      }
     }
-    float part = 0.f;
+    float sc[kXB];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) part = fmaf(q[e], kr[e], part);
-    const float sc = on ? group_allreduce<kGL>(part, OpAdd()) * inv : -INFINITY;
-    if (on) {
-      const float mn = fmaxf(m, sc);
-      const float r = __expf(m - mn), pw = __expf(sc - mn);
-      l = l * r + pw;
+    for (int u = 0; u < kXB; ++u) {
+      float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pw, vr[e], acc[e] * r);
-      m = mn;
+      for (int e = 0; e < DPL; ++e) part = fmaf(q[e], kr[u][e], part);
+      sc[u] = x0 + u < ne_max ? group_allreduce<kGL>(part, OpAdd()) * inv : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kXB; ++u) {
+      if (x0 + u < ne) {
+        const float mn = fmaxf(m, sc[u]);
+        const float r = __expf(m - mn), pw = __expf(sc[u] - mn);
+        l = l * r + pw;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pw, vr[u][e], acc[e] * r);
+        m = mn;
+      }
     }
   }
   if (n == -2) {
