@@ -102,6 +102,27 @@ def test_reference_queries_r4(Z):
     run_parity(Z, g, range(6))
 
 
+# The R tangent scores of a node are combined by a maximum over the lane group
+# holding its R rows (R LPR lanes, LPR = lanes per row: 4 for bf16 d = 128, 8 for
+# fp32 d = 128 and bf16 d = 256, 2 for bf16 d = 64), or through LDS atomics when
+# R is not a power of two or R LPR > 64.  One case per group width and both
+# fallbacks.
+@pytest.mark.parametrize("dtype,d,R", [
+    (W.BF16, 64, 2),    # 4 lanes
+    (W.BF16, 128, 2),   # 8 lanes
+    (W.BF16, 128, 8),   # 32 lanes
+    (W.F32, 128, 4),    # 32 lanes
+    (W.F32, 128, 8),    # 64 lanes
+    (W.BF16, 128, 3),   # not a power of two: atomics
+    (W.BF16, 256, 16),  # 128 lanes: atomics
+])
+def test_reference_queries_tangent_groups(Z, dtype, d, R):
+    say(f"R={R} reference queries, {dtype}, d={d}")
+    g = W.custom(f"rg{R}-{d}", 112, dtype=dtype, B=1, H_q=4, H_kv=2, d=d,
+                 T=8 ** 3 * 3 + 8 * 5 + 3, C=8, L=3, p=0.9, R=R)
+    run_parity(Z, g, range(3))
+
+
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 def test_reference_queries_r16(Z, dtype):
     # The pages' main geometry: 16 tangents per node, the max over them scores a node.
