@@ -579,3 +579,119 @@ def test_zero_reference_tree_stores_correctly_rounded_exact_means():
         np.testing.assert_array_equal(tree.levels[ell - 1].k_store[:, 0], O.round_to_bf16(exact))
         np.testing.assert_array_equal(tree.levels[ell - 1].b_store[:, 0],
                                       np.float64(np.float32(math.log(span))))
+
+
+# ----------------------------------------------------------------------------
+# Several reference queries: a node's score is the maximum over its R tangents
+# (paper §III-A; summary page "Tree Construction")
+# ----------------------------------------------------------------------------
+
+def _tree_levels_for_reference(keys, qref_row, C, L):
+    """Stored (k_hat, b_hat) of every level of a one-reference tree (R = 1)."""
+    t = O.build_tree(keys, qref_row[None, :], C, L, O.F64)
+    return [(lv.k_store, lv.b_store) for lv in t.levels]
+
+
+@pytest.mark.parametrize("slot", [0, 2, 4])
+def test_scores_with_the_query_among_the_references_are_exact_span_log_masses(slot):
+    # Every tangent lies below the convex log-mass F(q) of its span and the one
+    # taken at q touches it, so with q among the R references the maximum over
+    # the tangents is exactly F(q) at every node of every level.  A sum, a mean
+    # or one fixed tangent of the R would not be.
+    C, L, d, R = 4, 3, 16, 5
+    T = C ** L * 2 + C * 3 + 1
+    g = rng(600 + slot)
+    keys = g.standard_normal((T, d)) * 1.5
+    q = 3 * keys[int(g.integers(T))] + 0.3 * g.standard_normal(d)
+    qref = 2 * g.standard_normal((R, d))
+    qref[slot] = q
+    tree = O.build_tree(keys, qref, C, L, O.F64)
+    for ell in range(1, L + 1):
+        lv = tree.levels[ell - 1]
+        n = lv.F.shape[0]
+        s = O.node_scores(q, lv.k_store, lv.b_store)
+        exact = _exact_log_mass(q, keys, C ** ell, range(n))
+        np.testing.assert_allclose(s, exact, rtol=0, atol=1e-11)
+
+
+def test_scores_are_the_largest_single_reference_score():
+    # A node's score with R references equals the largest of the scores the same
+    # node gets in the R one-reference trees (where the score is that reference's
+    # tangent alone, itself pinned against the exact log-mass above).
+    C, L, d, R = 4, 3, 16, 4
+    T = C ** L * 2 + 7
+    g = rng(610)
+    keys = g.standard_normal((T, d)) * 1.5
+    qref = 2 * g.standard_normal((R, d))
+    tree = O.build_tree(keys, qref, C, L, O.F64)
+    single = [_tree_levels_for_reference(keys, qref[r], C, L) for r in range(R)]
+    for q in 3 * g.standard_normal((6, d)):
+        for ell in range(1, L + 1):
+            lv = tree.levels[ell - 1]
+            s = O.node_scores(q, lv.k_store, lv.b_store)
+            per_ref = np.stack([O.node_scores(q, *single[r][ell - 1]) for r in range(R)])
+            np.testing.assert_allclose(s, per_ref.max(axis=0), rtol=0, atol=1e-12)
+            # the maximum is attained, and strictly above some other tangent
+            assert (per_ref.min(axis=0) < s - 1e-9).any()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_route_with_the_query_among_several_references_is_exact_hierarchical_topp(seed):
+    # R = 3 with q as the middle reference: the route must be top-p over the
+    # exact span masses at every level, as with q as the only reference.
+    C, L, d, R = 4, 3, 16, 3
+    T = C ** L * 2
+    g = rng(620 + seed)
+    keys = g.standard_normal((T, d)) * 1.5
+    q = 3 * keys[g.integers(T)] + 0.3 * g.standard_normal(d)
+    qref = 3 * g.standard_normal((R, d))
+    qref[1] = q
+    p = 0.9
+    tree = O.build_tree(keys, qref, C, L, O.F64)
+    r = O.route(tree, q, p)
+    frontier = list(range(T // C ** L))
+    for ell in range(L, 0, -1):
+        lm = _exact_log_mass(q, keys, C ** ell, frontier)
+        order = sorted(range(len(frontier)), key=lambda i: (-lm[i], frontier[i]))
+        w = np.exp(lm - lm.max())
+        acc, S = 0.0, []
+        for i in order:
+            acc += w[i]
+            S.append(frontier[i])
+            if acc >= np.float32(p) * w.sum():
+                break
+        if r.fragile[ell - 1]:
+            return
+        assert sorted(S) == list(r.S[ell - 1]), f"level {ell}"
+        frontier = [c for i in sorted(S) for c in range(i * C, i * C + C)]
+
+
+def test_route_with_several_references_differs_from_the_first_reference_alone():
+    # The case above is not decided by the first reference: routing with the
+    # first reference only selects a different leaf set on these inputs.
+    C, L, d = 4, 3, 16
+    T = C ** L * 2
+    g = rng(620)
+    keys = g.standard_normal((T, d)) * 1.5
+    q = 3 * keys[g.integers(T)] + 0.3 * g.standard_normal(d)
+    qref = 3 * g.standard_normal((3, d))
+    qref[1] = q
+    full = O.route(O.build_tree(keys, qref, C, L, O.F64), q, 0.9)
+    first = O.route(O.build_tree(keys, qref[:1], C, L, O.F64), q, 0.9)
+    assert list(full.S1) != list(first.S1)
+
+
+# ----------------------------------------------------------------------------
+# p is the fp32 value the library receives
+# ----------------------------------------------------------------------------
+
+def test_cut_uses_the_fp32_value_of_p():
+    # fp32(0.3) = 0.300000011920928955... is above 0.3.  Over ten equal scores
+    # W_m / Z = m / 10 exactly, so the first prefix reaching fp32(0.3) is m = 4,
+    # while the real number 0.3 (or its fp64 value, whose product with 10
+    # rounds to 3) would stop at m = 3.  fp32(0.7) = 0.69999998807907... is
+    # below 0.7: m = 7 either way.
+    assert float(np.float32(0.3)) > 0.3
+    assert O.topp_cut(np.zeros(10), np.arange(10), 0.3).m == 4
+    assert O.topp_cut(np.zeros(10), np.arange(10), 0.7).m == 7
+    assert O.topp_cut(np.zeros(10), np.arange(10), float(np.float32(0.3))).m == 4
