@@ -43,7 +43,6 @@ constexpr int kUA = ZHA_ATTN_ROWS;   // K/V rows in flight per lane (sparse)
 constexpr int kUD = ZHA_DENSE_ROWS;  // K/V rows in flight per lane (dense)
 constexpr int kIds = 1024;  // chunk ids staged in LDS per round (sparse)
 constexpr int kWaves = kThreads / kWave;
-constexpr int kBalMinTokens = 64;  // smallest token range of a workgroup
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
@@ -386,16 +385,6 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(
                                    (int)blockIdx.y);
 }
 
-// |I(q)| of one query head: its chunks' tokens, the tail after the last full
-// chunk and the sink when chunk 0 is not selected (and exists: with no full
-// chunk the tail starts at token 0); 0 for a failed route.
-__device__ __forceinline__ int head_tokens(int c, int first_id, int64_t Th, const AttnArgs& a) {
-  if (c < 0 || c > a.cap || Th < 0) return 0;
-  const int64_t n1 = Th / a.C;
-  const int sink = (n1 > 0 && (c == 0 || first_id != 0)) ? 1 : 0;
-  return c * a.C + (int)(Th - n1 * a.C) + sink;
-}
-
 // Balanced split-KV over all heads of the call: workgroup w owns tokens
 // [w W, (w + 1) W) of the concatenated per-head token lists.  POW2: C is a
 // power of two (chunk index by shift).
@@ -407,22 +396,24 @@ template <typename T, int D, bool POW2, bool BUF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_ATTN_WAVES, ZHA_ATTN_WAVES))) void attn_balanced_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
-    float* __restrict__ part, int32_t* __restrict__ plan, AttnArgs a) {
+    float* __restrict__ part, int64_t* __restrict__ plan, AttnArgs a) {
   constexpr int VEC = Vec<T>::N;
   constexpr int LPR = D / VEC;
   constexpr int RPB = kThreads / LPR;
   constexpr int kE = kBalMaxHeads / kThreads;
-  __shared__ int32_t s_pre[kBalMaxHeads + 1];
+  __shared__ int64_t s_pre[kBalMaxHeads + 1];
   __shared__ int32_t s_ids[kIds];
   __shared__ float s_m[RPB], s_l[RPB];
   __shared__ float s_acc[RPB * D];
-  __shared__ uint32_t s_wtot[kWaves];
+  __shared__ uint64_t s_wtot[kWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int sub = tid % LPR, grp = tid / LPR;
   const int nh = (int)a.n_heads;
   const int E = (nh + kThreads - 1) / kThreads;
 
-  // 1. Prefix of per-head token counts (thread tid owns heads [tid E, tid E + E)).
+  // 1. Prefix of per-head token counts (thread tid owns heads [tid E, tid E + E)),
+  // 64-bit: a head attends up to T < 2^31 tokens, so the call's total can
+  // pass 2^31 (the plan arithmetic lives in zha_plan.hpp).
   int cv[kE], fv[kE];
   int64_t lv[kE];
 #pragma unroll
@@ -437,62 +428,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
       lv[e] = visible_len(a, h);
     }
   }
-  uint32_t tv[kE];
-  uint32_t run = 0;
+  int64_t tv[kE];
+  uint64_t run = 0;
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
-    tv[e] = (e < E && tid * E + e < nh) ? (uint32_t)head_tokens(cv[e], fv[e], lv[e], a) : 0u;
-    run += tv[e];
+    tv[e] = (e < E && tid * E + e < nh) ? bal_head_tokens(cv[e], fv[e], lv[e], a.C, a.cap) : 0;
+    run += (uint64_t)tv[e];
   }
-  const uint32_t incl = wave_incl_scan_u32(run);
+  const uint64_t incl = wave_incl_scan_u64(run);
   if (lane == kWave - 1) s_wtot[wave] = incl;
   __syncthreads();
-  uint32_t excl = incl - run;
-  uint32_t total = 0;
+  uint64_t excl = incl - run;
+  uint64_t total_u = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     if (w < wave) excl += s_wtot[w];
-    total += s_wtot[w];
+    total_u += s_wtot[w];
   }
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
     const int h = tid * E + e;
     if (e < E && h < nh) {
-      s_pre[h] = (int32_t)excl;
-      excl += tv[e];
+      s_pre[h] = (int64_t)excl;
+      excl += (uint64_t)tv[e];
     }
   }
-  if (tid == 0) s_pre[nh] = (int32_t)total;
+  const int64_t total = (int64_t)total_u;
+  if (tid == 0) s_pre[nh] = total;
   __syncthreads();
-  int64_t Wtok = ((int64_t)total + gridDim.x - 1) / gridDim.x;
-  if (Wtok < kBalMinTokens) Wtok = kBalMinTokens;
+  const int64_t Wtok = bal_width(total, gridDim.x);
   if (blockIdx.x == 0) {
     for (int h = tid; h <= nh; h += kThreads) plan[h] = s_pre[h];
-    if (tid == 0) plan[nh + 1] = (int32_t)Wtok;
+    if (tid == 0) plan[nh + 1] = Wtok;
   }
   // Range index, XCD-major: consecutive ranges (the heads of one KV group,
   // which share many chunks) run on one XCD and meet in its L2 (256K call
   // 49.1 -> 48.7 us).  The merge finds a head's partials by range index.
   const int64_t rng = xcd_major_index(blockIdx.x, gridDim.x);
   const int64_t lo = rng * Wtok;
-  const int64_t hi = min(lo + Wtok, (int64_t)total);
+  const int64_t hi = min(lo + Wtok, total);
   if (lo >= hi) return;
 
-  // 2. First head of the range: the last h with s_pre[h] <= lo.
-  int h0 = 0, h1 = nh;  // invariant: s_pre[h0] <= lo < s_pre[h1] (s_pre[nh] = total > lo)
-  while (h1 - h0 > 1) {
-    const int mid = (h0 + h1) >> 1;
-    if (s_pre[mid] <= lo) h0 = mid; else h1 = mid;
-  }
+  // 2. First head of the range.
+  const int h0 = bal_first_head(s_pre, nh, lo);
   const float inv = 1.0f / sqrtf((float)D);
 
   // 3. One segment per head overlapping the range.  Token positions and ids
   // fit in 31 bits (T < 2^31), so the index math is 32-bit; only the final
   // row address is 64-bit.
   for (int h = h0; h < nh && s_pre[h] < hi; ++h) {
-    const int P0 = s_pre[h], P1 = s_pre[h + 1];
-    if (P1 <= lo) continue;
-    const int x0 = (int)max(lo, (int64_t)P0) - P0, x1 = (int)min(hi, (int64_t)P1) - P0;
+    const int64_t P0 = s_pre[h], P1 = s_pre[h + 1];
+    if (P1 <= lo || P1 == P0) continue;  // before the range, or a failed route (no tokens)
+    const BalSegment seg = bal_segment(P0, P1, lo, hi);
+    const int x0 = seg.x0, x1 = seg.x1;
     const int c = cnt[h];
     const int32_t* ids = sel + (int64_t)h * a.cap;
     const int64_t Th = visible_len(a, h);  // valid: the head has tokens
@@ -588,8 +576,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
       }
       xr = xe;
     }
-    const bool whole = x0 == 0 && x1 == P1 - P0;
-    float* prow = whole ? nullptr : part + (rng + h) * (D + 2);
+    const bool whole = x0 == 0 && (int64_t)x1 == P1 - P0;
+    float* prow = whole ? nullptr : part + bal_slot(rng, h) * (D + 2);
     combine_groups<T, D, RPB>(m, l, acc, grp, sub, s_m, s_l, s_acc, O + (int64_t)h * D, prow);
     __syncthreads();
   }
@@ -599,7 +587,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
 // [P_h / W, (P_{h+1} - 1) / W]; their partials sit at slots (workgroup + h).
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(
-    const float* __restrict__ part, const int32_t* __restrict__ plan,
+    const float* __restrict__ part, const int64_t* __restrict__ plan,
     const int32_t* __restrict__ cnt, AttnArgs a, T* __restrict__ O) {
   const int h = blockIdx.x;
   const int cap = a.cap, nh = (int)a.n_heads;
@@ -612,9 +600,10 @@ __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(
       store_elem(O + (int64_t)h * D, t, __int_as_float(0x7fc00000));
     return;
   }
-  const int64_t fb = P0 / W, lb = (P1 - 1) / W;
-  if (fb == lb) return;  // written whole by its workgroup
-  merge_partials<T, D>(part + (fb + h) * (D + 2), (int)(lb - fb + 1), O + (int64_t)h * D);
+  const BalSpan sp = bal_head_span(P0, P1, W);
+  if (sp.first == sp.last) return;  // written whole by its workgroup
+  merge_partials<T, D>(part + bal_slot(sp.first, h) * (D + 2), (int)(sp.last - sp.first + 1),
+                       O + (int64_t)h * D);
 }
 
 // Dense decode: one workgroup per (b, t, kvh, head tile of GT) and split; GT
@@ -1539,9 +1528,9 @@ template <typename T, int D>
 int launch_attn(const AttnArgs& a, const void* Q, const void* K, const void* V,
                 const int32_t* sel, const int32_t* cnt, void* O, void* scratch, hipStream_t s) {
   if (a.n_heads <= kBalMaxHeads) {
-    int32_t* plan = reinterpret_cast<int32_t*>(scratch);
+    int64_t* plan = reinterpret_cast<int64_t*>(scratch);
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) +
-                                           align256((a.n_heads + 2) * 4));
+                                           align256((a.n_heads + 2) * 8));
     const bool buf =
         kv_block_elems(a.Tc, a.C, D, a.chunked) * (int64_t)sizeof(T) < ((int64_t)1 << 31);
 #define ZHA_BAL(P2, BF)                                                                    \

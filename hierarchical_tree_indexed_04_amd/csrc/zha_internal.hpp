@@ -3,12 +3,19 @@
 #pragma once
 
 #include "zha_common.hpp"
+#include "zha_plan.hpp"
 
 namespace zha {
 
 constexpr int kRouteFrontierMax = 4096;  // candidates per level held in LDS by the router
 constexpr int64_t kTputMinHeads = 4096;  // query heads per call for the router's throughput shape
 constexpr int kRouteSpillBlocks = 8;     // device-memory frontier slots for heads that outgrow the LDS
+// A head waiting for a device-memory frontier slot retries all slots this many
+// rounds (a ~1 us sleep each) before it gives up with cnt = ZHA_ROUTE_SLOT_BUSY.
+constexpr int32_t kRouteSpillWaitRounds = 1 << 20;
+// Fractional bits of the fixed-point candidate masses of the top-p cut: the
+// top candidate's mass is exactly 2^kMassBits.
+constexpr int kMassBits = 40;
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
@@ -37,7 +44,6 @@ inline RouteScratch route_scratch_layout(int64_t n_heads, int64_t n1c) {
   s.bytes = off;
   return s;
 }
-constexpr int kBalMaxHeads = 2048;       // balanced split-KV: per-head prefix held in LDS
 
 #ifndef ZHA_ATTN_BLOCKS
 #define ZHA_ATTN_BLOCKS 512
@@ -103,14 +109,14 @@ inline BlkLayout blk_layout(int64_t n_heads, int64_t n_trees, int64_t T, int C, 
   return L;
 }
 
-// zha_attn scratch: with n_heads <= kBalMaxHeads, a plan (n_heads + 2 int32)
+// zha_attn scratch: with n_heads <= kBalMaxHeads, a plan (n_heads + 2 int64)
 // and (workgroups + n_heads) partials of d + 2 floats; with more heads, the
 // block path's layout when it applies, else none.
 inline int64_t attn_scratch_layout_bytes(int64_t n_heads, int64_t n_trees, int64_t T, int C, int d,
                                          int dtype) {
   if (n_heads > kBalMaxHeads)
     return blk_eligible(n_heads, C, d, dtype) ? blk_layout(n_heads, n_trees, T, C, d).total : 0;
-  return ((n_heads + 2) * 4 + 255) / 256 * 256 + (ZHA_ATTN_BLOCKS + n_heads) * (int64_t)(d + 2) * 4;
+  return align256((n_heads + 2) * 8) + (ZHA_ATTN_BLOCKS + n_heads) * (int64_t)(d + 2) * 4;
 }
 
 struct BuildArgs {
@@ -149,6 +155,7 @@ struct RouteArgs {
   int32_t cap;
   float p;
   uint32_t cdiv;  // ceil(2^32 / C): floor(x / C) = umulhi(x, cdiv) for 0 <= x < 2^16
+  int32_t spill_wait;  // rounds of waiting for a frontier slot (negative: none)
 };
 
 // Tokens visible to query head h (of B * n_pos * H_q): its position's entry
