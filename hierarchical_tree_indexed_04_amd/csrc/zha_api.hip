@@ -2,6 +2,7 @@
 // on the host before any launch; nothing here allocates or synchronises.
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "zha_internal.hpp"
@@ -192,12 +193,32 @@ int zha_tree_update(const zha_geom* g, int64_t T_old, const void* K, const float
 
 int32_t zha_route_frontier_capacity(void) { return kRouteFrontierMax; }
 
+namespace {
+// A level's cut sums one fixed-point mass of up to 2^kMassBits per candidate
+// in 64 bits, so a frontier must stay below 2^(64 - kMassBits) candidates;
+// the largest frontier is every level-1 node at capacity.
+bool route_frontier_fits(const zha_geom* g) {
+  return capacity(g) / g->C < ((int64_t)1 << (64 - kMassBits));
+}
+
+// Rounds of waiting for a device-memory frontier slot before a head gives up
+// (cnt = ZHA_ROUTE_SLOT_BUSY).  ZHA_ROUTE_SPILL_WAIT overrides the default for
+// diagnostics; a negative value gives up at once, as if every slot were held.
+int32_t spill_wait_rounds() {
+  const char* e = getenv("ZHA_ROUTE_SPILL_WAIT");
+  if (e == nullptr || *e == 0) return kRouteSpillWaitRounds;
+  const long v = strtol(e, nullptr, 10);
+  return v < 0 ? -1 : (v > INT32_MAX ? INT32_MAX : (int32_t)v);
+}
+}  // namespace
+
 int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes) {
   const int rc = check_geom(g);
   if (rc) return rc;
   if (bytes == nullptr) return ZHA_ERR_NULL;
   if (n_pos < 1) return ZHA_ERR_NPOS;
   if (cap < 1) return ZHA_ERR_CAP;
+  if (!route_frontier_fits(g)) return ZHA_ERR_GEOM;
   *bytes = (size_t)route_scratch_layout((int64_t)g->B * n_pos * g->H_q, capacity(g) / g->C).bytes;
   return ZHA_OK;
 }
@@ -212,6 +233,7 @@ int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
   if (n_pos < 1) return ZHA_ERR_NPOS;
   if (cap < 1) return ZHA_ERR_CAP;
   if (!(p > 0.0f && p <= 1.0f)) return ZHA_ERR_P;
+  if (!route_frontier_fits(g)) return ZHA_ERR_GEOM;
   if (!aligned16(tree) || !aligned16(Q)) return ZHA_ERR_ALIGN;
   RouteArgs a{};
   a.lay = make_layout(g);
@@ -227,6 +249,7 @@ int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
   a.cap = cap;
   a.p = p;
   a.cdiv = (uint32_t)(((1ull << 32) + (uint64_t)g->C - 1) / (uint64_t)g->C);
+  a.spill_wait = spill_wait_rounds();
   if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
   const RouteScratch rs = route_scratch_layout(a.n_heads, a.lay.ncap[1]);
   if (rs.bytes > 0 && scratch == nullptr) return ZHA_ERR_NULL;

@@ -93,6 +93,12 @@ enum {
   ZHA_ERR_ROPE = -11    /* rope->dims odd, negative or > d, or theta NULL */
 };
 
+/* Values of a failed route's cnt entry (written by the device, see zha_route). */
+enum {
+  ZHA_ROUTE_BAD_CTX = -1,   /* the position's ctx_len entry is outside [1, T] */
+  ZHA_ROUTE_SLOT_BUSY = -2  /* no device-memory frontier slot came free in time */
+};
+
 typedef struct {
   int32_t B;     /* sequences */
   int32_t H_q;   /* query heads */
@@ -194,7 +200,11 @@ int zha_tree_update(const zha_geom* g, int64_t T_old, const void* K, const float
  * nodes whose parent is incomplete (paper App. E-E).
  * ------------------------------------------------------------------------- */
 
-/* Scratch bytes zha_route needs (0: any pointer, NULL included, may be passed):
+/* Scratch bytes zha_route needs (0: any pointer, NULL included, may be passed).
+ * zha_route and this call return ZHA_ERR_GEOM when level 1 could hold 2^24 or
+ * more nodes (floor(T_cap / C), T_cap or T): a level's cut sums a 40-bit
+ * fixed-point mass per candidate in 64 bits, so a frontier must stay below 2^24
+ * candidates.  Scratch holds:
  *   - calls of 4096 or more query heads (B * n_pos * H_q) route most heads
  *     with a smaller-frontier launch and list there the heads whose frontier
  *     outgrew it: (heads + 1) int32;
@@ -216,14 +226,25 @@ int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_
  *               prefill passes T_t = t + 1 for the token at cache position t
  *               (paper §V, Q(T) = T: every query sees the nodes completed
  *               before it and its own partial chunk).  A value outside [1, T]
- *               fails that position: cnt = -1, level_stats and gap unwritten.
+ *               fails that position: cnt = ZHA_ROUTE_BAD_CTX (-1),
+ *               level_stats and gap unwritten.
  *   p           top-p threshold in (0, 1]
  *   sel         device [B, n_pos, H_q, cap] int32, written: the level-1 chunk
  *               ids of S_1 in ascending order; entries past min(cnt, cap) are
  *               left untouched
  *   cnt         device [B, n_pos, H_q] int32, written: |S_1|, the true count
  *               even when it exceeds cap (then sel holds the cap lowest ids);
- *               -1 for a position whose ctx_len entry is invalid
+ *               ZHA_ROUTE_BAD_CTX (-1) for a position whose ctx_len entry
+ *               is invalid; ZHA_ROUTE_SLOT_BUSY (-2) for a head whose
+ *               frontier outgrew the on-chip capacity and found no free
+ *               device-memory frontier slot within the wait bound (about a
+ *               second; a holder frees its slot as soon as its head is
+ *               routed, so this means a stuck or killed holder): sel is then
+ *               unwritten and level_stats / gap hold only the levels above
+ *               the overflow; calling zha_route again routes such heads.
+ *               The environment variable ZHA_ROUTE_SPILL_WAIT, read at each
+ *               call, sets the bound in rounds of ~1 us (negative: give up
+ *               without waiting), for diagnostics.
  *   level_stats device [B, n_pos, H_q, L, 2] int32 or NULL: for level l at
  *               index l-1, (frontier size K_l, kept count |S_l|)
  *   gap         device [B, n_pos, H_q, L] fp32 or NULL: s_(m) - s_(m+1) at

@@ -210,3 +210,30 @@ def test_child_index_by_multiply_high_is_exact():
         magic = np.uint64(((1 << 32) + C - 1) // C)
         assert magic < (1 << 32)
         assert np.array_equal((x * magic) >> np.uint64(32), x // np.uint64(C)), C
+
+
+def test_route_rejects_frontiers_of_2_pow_24_candidates():
+    # A level's cut sums one 40-bit fixed-point mass per candidate in 64 bits:
+    # zha_route (and its scratch query) refuse geometries whose level 1 could
+    # hold 2^24 nodes, before any launch; build and attention do not route.
+    lib = Z.load()
+    buf = ctypes.c_void_p(16)
+    n = ctypes.c_size_t()
+    for C, T, ok in ((16, (1 << 24) * 16 - 1, True), (16, (1 << 24) * 16, False),
+                     (2, (1 << 25) - 1, True), (2, 1 << 25, False), (1024, (1 << 31) - 1, True)):
+        gm = g(C=C, L=1, T=T, H_q=2, H_kv=1)
+        rc = lib.zha_route_scratch_bytes(ctypes.byref(gm), 1, 4, ctypes.byref(n))
+        assert (rc == 0) == ok, (C, T, rc)
+        # p = 0 fails p validation first; a valid p reaches the frontier check
+        rc = lib.zha_route(ctypes.byref(gm), buf, buf, 1, None, 0.9, buf, buf, 4, None, None, None,
+                           None)
+        assert rc == (-2 if not ok else rc), (C, T, rc)
+        assert lib.zha_tree_bytes(ctypes.byref(gm), ctypes.byref(n), ctypes.byref(n)) == 0
+    # with a capacity: the capacity, not the length, bounds the frontier
+    gm = g(C=16, L=1, T=4096, T_cap=(1 << 24) * 16, H_q=2, H_kv=1)
+    assert lib.zha_route_scratch_bytes(ctypes.byref(gm), 1, 4, ctypes.byref(n)) == -2
+
+
+def test_failed_route_codes_are_declared():
+    text = open(HEADER).read()
+    assert "ZHA_ROUTE_BAD_CTX = -1" in text and "ZHA_ROUTE_SLOT_BUSY = -2" in text

@@ -188,3 +188,46 @@ def test_device_memory_frontier_causal_prefill(Z):
     assert not par.mismatched, par.mismatched[:5]
     assert not par.out_bad, par.out_bad[:5]
     assert par.exact >= 0.8 * par.heads
+
+
+def test_frontier_slot_wait_gives_up_with_its_own_code(Z, monkeypatch):
+    # The wait for a device-memory frontier slot is bounded.  Forced from the
+    # host (ZHA_ROUTE_SPILL_WAIT < 0: give up at once, as if every slot were
+    # held), each head that needs a slot ends with cnt = ZHA_ROUTE_SLOT_BUSY
+    # (-2) and its attention row is NaN, while every other head routes as
+    # before; with the default bound the same call routes every head.
+    import torch
+    g = W.custom("wide-busy", 183, dtype=W.BF16, B=1, H_q=4, H_kv=1, C=16, L=2,
+                 T=16 * 16 * 300 + 37, R=1, p=0.99)
+    K, V = W.make_kv(g)
+    gm, Kd, Vd, tree, qref = build(Z, g, K, V, False)
+    n_pos = 4
+    Qn = W.make_query_block(g, K, range(n_pos))
+    weaken(g, Qn, [1, 3], 183)
+    Qd = to_device(Qn, g.dtype)
+    cap = g.n_level(1)
+    say("frontier slot wait: default bound, then none")
+    ref = Z.route(gm, tree, Qd, n_pos, g.p, cap)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("ZHA_ROUTE_SPILL_WAIT", "-1")
+    sel, cnt, stats, gap = Z.route(gm, tree, Qd, n_pos, g.p, cap)
+    Od = Z.attn(gm, Qd, n_pos, Kd, Vd, sel, cnt, cap)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("ZHA_ROUTE_SPILL_WAIT")
+    again = Z.route(gm, tree, Qd, n_pos, g.p, cap)
+    torch.cuda.synchronize()
+    rc, rst = ref[1].cpu().numpy(), ref[2].cpu().numpy()
+    c, Og = cnt.cpu().numpy(), from_device(Od, g.dtype)
+    spilled = rst[..., 0].max(axis=-1) > Z.frontier_capacity()  # [B, n_pos, H_q]
+    say(f"  heads needing a slot: {int(spilled.sum())} of {spilled.size}")
+    assert spilled.any() and not spilled.all()
+    assert (rc >= 0).all()
+    assert (c[spilled] == -2).all()
+    assert np.isnan(Og[spilled]).all()
+    assert np.array_equal(c[~spilled], rc[~spilled])
+    s, rs = sel.cpu().numpy(), ref[0].cpu().numpy()
+    for b, t, h in zip(*np.nonzero(~spilled)):
+        n = int(rc[b, t, h])
+        assert np.array_equal(s[b, t, h, :n], rs[b, t, h, :n])
+        assert np.isfinite(Og[b, t, h]).all()
+    assert np.array_equal(again[1].cpu().numpy(), rc)
