@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "zha_internal.hpp"
 
 using namespace zha;
@@ -123,6 +125,8 @@ const char* zha_strerror(int code) {
     case ZHA_ERR_NPOS: return "n_pos must be >= 1";
     case ZHA_ERR_LAYOUT: return "unknown kv_layout, or V given with the chunked layout";
     case ZHA_ERR_ROPE: return "rope: dims must be even and in [0, d], with theta given";
+    case ZHA_ERR_SCRATCH:
+      return "the call needs more scratch than zha_attn_noalloc's fixed device buffer holds";
     default: return "unknown error";
   }
 }
@@ -270,15 +274,19 @@ int zha_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t
   return ZHA_OK;
 }
 
-int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx_len,
-             const void* K, const void* V,
-             const int32_t* sel, const int32_t* cnt, int32_t cap, void* O, void* scratch,
-             void* stream) {
+}  // extern "C"
+
+namespace {
+// Validation and arguments shared by zha_attn and zha_attn_noalloc; *need is
+// the scratch the call's launches use.
+int prepare_attn(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx_len,
+                 const void* K, const void* V, const int32_t* sel, const int32_t* cnt,
+                 int32_t cap, void* O, AttnArgs& a, int64_t* need) {
   const int rc = check_geom(g);
   if (rc) return rc;
   if (n_pos < 1) return ZHA_ERR_NPOS;
   if (cap < 1) return ZHA_ERR_CAP;
-  AttnArgs a{};
+  a = AttnArgs{};
   a.T = g->T;
   a.Tc = capacity(g);
   a.ctx = ctx_len;
@@ -294,17 +302,75 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx
   a.S = ZHA_ATTN_BLOCKS;
   a.chunked = g->kv_layout == ZHA_KV_CHUNKED;
   a.dtype = g->dtype;
-  const bool need_scratch =
-      attn_scratch_layout_bytes(a.n_heads, (int64_t)g->B * g->H_kv, g->T, g->C, g->d, g->dtype) > 0;
+  *need = attn_scratch_layout_bytes(a.n_heads, (int64_t)g->B * g->H_kv, g->T, g->C, g->d,
+                                    g->dtype);
   const int kv = check_kv(g, K, V);
   if (kv) return kv;
-  if (Q == nullptr || sel == nullptr || cnt == nullptr || O == nullptr ||
-      (need_scratch && scratch == nullptr))
-    return ZHA_ERR_NULL;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(O) || (need_scratch && !aligned16(scratch)))
-    return ZHA_ERR_ALIGN;
+  if (Q == nullptr || sel == nullptr || cnt == nullptr || O == nullptr) return ZHA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(O)) return ZHA_ERR_ALIGN;
   if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
+  return ZHA_OK;
+}
+}  // namespace
+
+// The fixed scratch of zha_attn_noalloc.  In host code `scratch` names a host
+// stand-in, not the device array: its device address (one per device, each
+// device holding its own copy) comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is ever passed on.
+static __device__ __align__(256) char scratch[ZHA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call there, then kept).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ZHA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return ZHA_ERR_LAUNCH;
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return ZHA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx_len,
+             const void* K, const void* V,
+             const int32_t* sel, const int32_t* cnt, int32_t cap, void* O, void* scratch,
+             void* stream) {
+  AttnArgs a;
+  int64_t need = 0;
+  const int rc = prepare_attn(g, Q, n_pos, ctx_len, K, V, sel, cnt, cap, O, a, &need);
+  if (rc) return rc;
+  if (need > 0 && scratch == nullptr) return ZHA_ERR_NULL;
+  if (need > 0 && !aligned16(scratch)) return ZHA_ERR_ALIGN;
   return attn_dispatch(a, g->dtype, g->d, Q, K, V, sel, cnt, O, scratch,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int zha_attn_noalloc(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx_len,
+                     const void* K, const void* V, const int32_t* sel, const int32_t* cnt,
+                     int32_t cap, void* O, void* stream) {
+  AttnArgs a;
+  int64_t need = 0;
+  const int rc = prepare_attn(g, Q, n_pos, ctx_len, K, V, sel, cnt, cap, O, a, &need);
+  if (rc) return rc;
+  if (need > (int64_t)ZHA_NOALLOC_SCRATCH_BYTES) return ZHA_ERR_SCRATCH;
+  void* buf = nullptr;
+  if (need > 0) {
+    const int sr = noalloc_scratch(&buf);
+    if (sr) return sr;
+  }
+  return attn_dispatch(a, g->dtype, g->d, Q, K, V, sel, cnt, O, buf,
                        reinterpret_cast<hipStream_t>(stream));
 }
 

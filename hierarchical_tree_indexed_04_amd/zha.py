@@ -20,8 +20,9 @@ ZHA_KV_CHUNKED = 1
 ERRORS = {
     -1: "ZHA_ERR_NULL", -2: "ZHA_ERR_GEOM", -3: "ZHA_ERR_DTYPE", -4: "ZHA_ERR_DIM",
     -5: "ZHA_ERR_P", -6: "ZHA_ERR_ALIGN", -7: "ZHA_ERR_CAP", -8: "ZHA_ERR_LAUNCH",
-    -9: "ZHA_ERR_NPOS", -10: "ZHA_ERR_LAYOUT", -11: "ZHA_ERR_ROPE",
+    -9: "ZHA_ERR_NPOS", -10: "ZHA_ERR_LAYOUT", -11: "ZHA_ERR_ROPE", -12: "ZHA_ERR_SCRATCH",
 }
+ZHA_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 # Every function the header declares, with its ctypes signature.
 _c_size_p = ctypes.POINTER(ctypes.c_size_t)
@@ -56,6 +57,8 @@ SIGNATURES = {
     "zha_route_frontier_capacity": (ctypes.c_int32, []),
     "zha_attn_scratch_bytes": (ctypes.c_int, [_GP, _I32, _I32, _c_size_p]),
     "zha_attn": (ctypes.c_int, [_GP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "zha_attn_noalloc": (ctypes.c_int, [_GP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP,
+                                        _VP]),
     "zha_dense_decode_scratch_bytes": (ctypes.c_int, [_GP, _I32, _c_size_p]),
     "zha_dense_decode": (ctypes.c_int, [_GP, _VP, _I32, _VP, _VP, _VP, _VP, _VP]),
 }
@@ -329,6 +332,27 @@ def attn(g: Geom, Q, n_pos: int, K, V, sel, cnt, cap: int, O=None, scratch=None,
     _check(load().zha_attn(ctypes.byref(g), _ptr(Q), n_pos, _ptr(ctx_len), _ptr(K), _ptr(V),
                            _ptr(sel),
                            _ptr(cnt), cap, _ptr(O), _ptr(scratch), _stream(stream)), "zha_attn")
+    return O
+
+
+def attn_noalloc(g: Geom, Q, n_pos: int, K, V, sel, cnt, cap: int, O=None, stream=None,
+                 ctx_len=None):
+    """zha_attn_noalloc: zha_attn with the library's fixed device buffer as scratch
+    (O may be given, so that the call allocates nothing at all)."""
+    torch = _torch()
+    dt = _store_dtype(g)
+    _need(Q, (g.B, n_pos, g.H_q, g.d), dt, "Q")
+    _need_ctx(g, ctx_len, n_pos)
+    _need_kv(g, K, V)
+    _need(sel, (g.B, n_pos, g.H_q, cap), torch.int32, "sel")
+    _need(cnt, (g.B, n_pos, g.H_q), torch.int32, "cnt")
+    if O is None:
+        O = torch.empty((g.B, n_pos, g.H_q, g.d), dtype=dt, device=Q.device)
+    else:
+        _need(O, (g.B, n_pos, g.H_q, g.d), dt, "O")
+    _check(load().zha_attn_noalloc(ctypes.byref(g), _ptr(Q), n_pos, _ptr(ctx_len), _ptr(K),
+                                   _ptr(V), _ptr(sel), _ptr(cnt), cap, _ptr(O), _stream(stream)),
+           "zha_attn_noalloc")
     return O
 
 

@@ -90,7 +90,8 @@ enum {
   ZHA_ERR_LAUNCH = -8, /* a kernel launch failed */
   ZHA_ERR_NPOS = -9,   /* n_pos < 1 */
   ZHA_ERR_LAYOUT = -10, /* unknown kv_layout, or V given with ZHA_KV_CHUNKED */
-  ZHA_ERR_ROPE = -11    /* rope->dims odd, negative or > d, or theta NULL */
+  ZHA_ERR_ROPE = -11,   /* rope->dims odd, negative or > d, or theta NULL */
+  ZHA_ERR_SCRATCH = -12 /* zha_attn_noalloc: the call needs more than its fixed buffer */
 };
 
 /* Values of a failed route's cnt entry (written by the device, see zha_route). */
@@ -293,6 +294,28 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx
              const void* K, const void* V,
              const int32_t* sel, const int32_t* cnt, int32_t cap, void* O, void* scratch,
              void* stream);
+
+/* Size of the device buffer zha_attn_noalloc uses in place of a scratch
+ * argument (the library holds one on each device it runs on). */
+#define ZHA_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+/* zha_attn for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no scratch argument: the split-KV plan and partials go to a fixed
+ * buffer of ZHA_NOALLOC_SCRATCH_BYTES inside the library, one per device,
+ * held from the first call on that device until the process ends; the call
+ * itself allocates nothing.  Arguments, results and errors as zha_attn, plus
+ * ZHA_ERR_SCRATCH (before any launch) for a call whose
+ * zha_attn_scratch_bytes() exceeds ZHA_NOALLOC_SCRATCH_BYTES: up to 2048
+ * query heads per call always fit at d <= 256 (about 2.7 MB at d = 256); more
+ * heads fit only where they need no scratch (fp32, d = 256 or C outside
+ * {8, 16, 32, 64}).  Every call on one device shares that device's buffer,
+ * which keeps the last call's contents (nothing in it needs to start at zero:
+ * a call writes everything it reads), so calls that overlap in time on one
+ * device race, whatever their streams. */
+int zha_attn_noalloc(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx_len,
+                     const void* K, const void* V, const int32_t* sel, const int32_t* cnt,
+                     int32_t cap, void* O, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Dense decode baseline: O = softmax(q K^T / sqrt(d)) V over all T keys.

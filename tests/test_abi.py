@@ -31,7 +31,7 @@ def g(**kw):
 def test_library_exports_every_declared_function():
     lib = Z.load()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Z.SIGNATURES)
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 def test_strerror_names_every_code():
     lib = Z.load()
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12]:
         assert lib.zha_strerror(code) not in (None, b"", b"unknown error")
     assert lib.zha_strerror(-1000) == b"unknown error"
 
@@ -237,3 +237,23 @@ def test_route_rejects_frontiers_of_2_pow_24_candidates():
 def test_failed_route_codes_are_declared():
     text = open(HEADER).read()
     assert "ZHA_ROUTE_BAD_CTX = -1" in text and "ZHA_ROUTE_SLOT_BUSY = -2" in text
+
+
+def test_attn_noalloc_rejects_calls_past_its_fixed_buffer():
+    # zha_attn_noalloc checks, before touching the device, that the call's
+    # scratch fits ZHA_NOALLOC_SCRATCH_BYTES; a balanced call of 2048 heads at
+    # d = 256 fits, the block path at the 1M block does not.
+    lib = Z.load()
+    buf = ctypes.c_void_p(256)  # never dereferenced: these calls fail validation
+    big = g(B=1, H_q=16, H_kv=2, T=1 << 20, C=32, L=4)
+    need = Z.attn_scratch_bytes(big, 2048, 32768)
+    assert need > Z.ZHA_NOALLOC_SCRATCH_BYTES
+    assert lib.zha_attn_noalloc(ctypes.byref(big), buf, 2048, None, buf, buf, buf, buf, 32768,
+                                buf, None) == -12
+    assert Z.attn_scratch_bytes(g(B=1, H_q=16, H_kv=2, d=256, T=1 << 20), 128, 64) <= \
+        Z.ZHA_NOALLOC_SCRATCH_BYTES
+    # the same argument checks as zha_attn, before the size check
+    assert lib.zha_attn_noalloc(ctypes.byref(big), None, 2048, None, buf, buf, buf, buf, 32768,
+                                buf, None) == -1
+    assert lib.zha_attn_noalloc(ctypes.byref(big), buf, 0, None, buf, buf, buf, buf, 32768,
+                                buf, None) == -9
