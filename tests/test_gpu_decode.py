@@ -15,8 +15,8 @@ import pytest
 
 import oracle as O
 from hierarchical_tree_indexed_04_amd import workload as W
-from zha_testutil import (TOL, Parity, compare_head, from_device, oracle_trees, to_device,
-                          tree_mismatch)
+from zha_testutil import (TOL, Parity, attend_on, compare_head, from_device, oracle_trees,
+                          to_device, tree_mismatch)
 
 pytestmark = pytest.mark.gpu
 
@@ -79,11 +79,12 @@ def check_length(Z, g, gm, cache, tree, qref, T, n_pos, p, steps_seed):
     Qn = W.make_query_block(gT, cache.K[:, :, :T], range(steps_seed, steps_seed + n_pos))
     Qd = to_device(Qn, g.dtype)
     cap = max(gT.n_level(1), 1)
-    sel, cnt, stats, _ = Z.route(gm, tree, Qd, n_pos, p, cap)
+    sel, cnt, stats, gap = Z.route(gm, tree, Qd, n_pos, p, cap)
     Od = Z.attn(gm, Qd, n_pos, cache.Kd, cache.Vd, sel, cnt, cap)
     Dd = Z.dense_decode(gm, Qd, n_pos, cache.Kd, cache.Vd)
     torch.cuda.synchronize()
-    sel, cnt, stats = sel.cpu().numpy(), cnt.cpu().numpy(), stats.cpu().numpy()
+    sel, cnt, stats, gap = (sel.cpu().numpy(), cnt.cpu().numpy(), stats.cpu().numpy(),
+                            gap.cpu().numpy())
     Og, Dg = from_device(Od, g.dtype), from_device(Dd, g.dtype)
     par = Parity()
     dense_err = 0.0
@@ -95,11 +96,10 @@ def check_length(Z, g, gm, cache, tree, qref, T, n_pos, p, steps_seed):
                 q = W.to_float(Qn[b, t, h], g.dtype)
                 r, o = O.zha_head(trees[(b, kvh)], q, Kf, Vf, p)
                 compare_head(par, r, sel[b, t, h], int(cnt[b, t, h]), stats[b, t, h],
-                             Og[b, t, h], o, TOL[g.dtype], (T, b, t, h))
+                             Og[b, t, h], o, TOL[g.dtype], (T, b, t, h), gap_row=gap[b, t, h],
+                             attend_set=attend_on(q, Kf, Vf, g.C, T))
                 dense_err = max(dense_err, float(np.abs(Dg[b, t, h] - O.dense(q, Kf, Vf)).max()))
-    assert not par.mismatched, par.mismatched[:5]
-    assert not par.out_bad, par.out_bad[:5]
-    assert par.exact >= 0.8 * par.heads
+    par.check()
     assert dense_err <= TOL[g.dtype], (T, dense_err)
     return par, total
 

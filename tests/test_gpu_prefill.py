@@ -16,7 +16,7 @@ import pytest
 
 import oracle as O
 from hierarchical_tree_indexed_04_amd import workload as W
-from zha_testutil import TOL, Parity, compare_head, from_device, to_device
+from zha_testutil import TOL, Parity, attend_on, compare_head, from_device, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -52,10 +52,11 @@ def run_prefill(Z, g, ctx, Qn, p, chunked=False, cap=None, qref=None):
     Qd = to_device(Qn, g.dtype)
     cd = torch.from_numpy(np.ascontiguousarray(ctx, dtype=np.int32)).cuda()
     cap = max(g.n_level(1), 1) if cap is None else cap
-    sel, cnt, stats, _ = Z.route(gm, tree, Qd, n_pos, p, cap, ctx_len=cd)
+    sel, cnt, stats, gap = Z.route(gm, tree, Qd, n_pos, p, cap, ctx_len=cd)
     Od = Z.attn(gm, Qd, n_pos, Kd, Vd, sel, cnt, cap, ctx_len=cd)
     torch.cuda.synchronize()
-    sel, cnt, stats = sel.cpu().numpy(), cnt.cpu().numpy(), stats.cpu().numpy()
+    sel, cnt, stats, gap = (sel.cpu().numpy(), cnt.cpu().numpy(), stats.cpu().numpy(),
+                            gap.cpu().numpy())
     Og = from_device(Od, g.dtype)
     par = Parity()
     bad = []
@@ -74,12 +75,12 @@ def run_prefill(Z, g, ctx, Qn, p, chunked=False, cap=None, qref=None):
                     q = W.to_float(Qn[b, t, h], g.dtype)
                     r, o = O.zha_head(trees[n], q, Kf[:n], Vf[:n], p)
                     compare_head(par, r, sel[b, t, h], int(cnt[b, t, h]), stats[b, t, h],
-                                 Og[b, t, h], o, TOL[g.dtype], (b, t, h, n))
+                                 Og[b, t, h], o, TOL[g.dtype], (b, t, h, n),
+                                 gap_row=gap[b, t, h],
+                                 attend_set=attend_on(q, Kf[:n], Vf[:n], g.C, n))
     say("  " + par.summary())
     assert not bad, bad[:5]
-    assert not par.mismatched, par.mismatched[:5]
-    assert not par.out_bad, par.out_bad[:5]
-    assert par.exact >= 0.8 * par.heads
+    par.check()
     return par
 
 

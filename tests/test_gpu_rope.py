@@ -14,8 +14,8 @@ import pytest
 
 import oracle as O
 from hierarchical_tree_indexed_04_amd import workload as W
-from zha_testutil import (TOL, Parity, compare_head, from_device, oracle_trees, to_device,
-                          tree_mismatch)
+from zha_testutil import (TOL, Parity, attend_on, compare_head, from_device, oracle_trees,
+                          to_device, tree_mismatch)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def test_rope_tree_routes_and_outputs_match_oracle(Z, name, dtype, R, dims, base
     Qn = W.make_query_block(g, K, range(n_pos))
     Qd = to_device(Qn, dtype)
     cap = g.n_level(1)
-    sel, cnt, stats, _ = Z.route(gm, tree, Qd, n_pos, g.p, cap)
+    sel, cnt, stats, gap = Z.route(gm, tree, Qd, n_pos, g.p, cap)
     Od = Z.attn(gm, Qd, n_pos, Kd, Vd, sel, cnt, cap)
     torch.cuda.synchronize()
     pairs = [(0, h) for h in range(g.H_kv)]
@@ -80,20 +80,21 @@ def test_rope_tree_routes_and_outputs_match_oracle(Z, name, dtype, R, dims, base
     # the rotation matters: the plain tree differs
     plain = oracle_trees(g, K, qref, pairs[:1])[(0, 0)]
     assert not np.array_equal(plain.levels[1].k_store, trees[(0, 0)].levels[1].k_store)
-    sel, cnt, stats = sel.cpu().numpy(), cnt.cpu().numpy(), stats.cpu().numpy()
+    sel, cnt, stats, gap = (sel.cpu().numpy(), cnt.cpu().numpy(), stats.cpu().numpy(),
+                            gap.cpu().numpy())
     Og = from_device(Od, dtype)
     par = Parity()
     for (b, kvh) in pairs:
         Kf, Vf = W.to_float(K[b, kvh], dtype), W.to_float(V[b, kvh], dtype)
         for t in range(n_pos):
             for h in range(kvh * g.G, (kvh + 1) * g.G):
-                r, o = O.zha_head(trees[(b, kvh)], W.to_float(Qn[b, t, h], dtype), Kf, Vf, g.p)
+                q = W.to_float(Qn[b, t, h], dtype)
+                r, o = O.zha_head(trees[(b, kvh)], q, Kf, Vf, g.p)
                 compare_head(par, r, sel[b, t, h], int(cnt[b, t, h]), stats[b, t, h],
-                             Og[b, t, h], o, TOL[dtype], (b, t, h))
+                             Og[b, t, h], o, TOL[dtype], (b, t, h), gap_row=gap[b, t, h],
+                             attend_set=attend_on(q, Kf, Vf, g.C, g.T))
     say("  " + par.summary())
-    assert not par.mismatched, par.mismatched[:5]
-    assert not par.out_bad, par.out_bad[:5]
-    assert par.exact >= 0.8 * par.heads
+    par.check()
 
 
 def test_rope_decode_updates_equal_the_build(Z):
