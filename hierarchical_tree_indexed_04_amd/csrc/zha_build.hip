@@ -11,8 +11,26 @@
 // rounded mean of its span; with other references the fp64 result is within
 // a few ulps of the exact summary before the single rounding to storage.
 //
-// One wave per node; lane l owns dims [l*DPL, l*DPL + DPL).  References are
-// processed one at a time (the chunk's keys are re-read from cache).
+// Layout of the work: a node is summarised by one lane group of LPR lanes,
+// lane `sub` owning the VEC dims of one 16-byte slice of every row (LPR = d /
+// VEC, VEC = 8 bf16 or 4 fp32 values), so each key or child row is read with
+// one 16-byte load per lane.  Sums over a node's rows run row by row in order,
+// per dim; the dot products of a row are summed over the group by a fixed
+// butterfly.  References are processed one at a time.
+//
+// A zero reference (the plain mean of the span; tested per node) takes a
+// shorter path with the same result bits: every score is +0, every weight
+// exp(0) = 1, Z = C, F = log C and b_hat = F, so the leaf skips the score
+// pass, the dot products and the exponentials and only sums the keys.
+//
+// A full build summarises each complete level-2 subtree in one workgroup
+// (fused_kernel): the leaves' fp64 summaries stay in LDS for the level-2
+// merge, so only nodes a later merge reads get an fp64 copy in the scratch
+// (level-2 nodes, and leaves and nodes past the last complete parent, which
+// decode-time maintenance merges later).  The other leaves and parents, and
+// every node of a decode-time update, are done by leaf_kernel and
+// merge_kernel, one lane group per node, with the same per-node arithmetic,
+// so an updated tree equals a fresh build bit for bit.
 //
 // With RoPE (§III-B, reference queries) every node is summarised at its
 // references rotated to the last position of its span, and a merge first
@@ -30,24 +48,37 @@
 #include "zha_internal.hpp"
 
 namespace zha {
+namespace {
+
+constexpr int kBuildThreads = 256;
+constexpr int kRowBatch = 4;              // key rows loaded before the first is used
+constexpr int kChildBatch = 4;            // fp64 child rows loaded before the first is used
+#ifndef ZHA_ZERO_BATCH
+#define ZHA_ZERO_BATCH 4
+#endif
+constexpr int kZeroBatch = ZHA_ZERO_BATCH;  // key rows per batch of a zero-reference stream (two in flight)
+constexpr int64_t kFusedLds = 64 * 1024;  // LDS of a fused workgroup's leaf summaries
+constexpr int64_t kFusedGrid = 1024;      // persistent workgroups of fused_kernel
+constexpr int kStreamMaxC = 16;           // zero references: one lane group per level-2 node up to this C
 
 template <typename T, int D>
-__device__ __forceinline__ void load_row_f64(const T* row, int lane, double* out) {
-  constexpr int DPL = D / kWave;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) out[e] = (double)load_elem(row, lane * DPL + e);
-}
+struct LG {
+  static constexpr int VEC = Vec<T>::N;             // dims per lane
+  static constexpr int LPR = D / VEC;               // lanes per node
+  static constexpr int NG = kBuildThreads / LPR;    // lane groups per workgroup
+};
 
 // This lane's dims of reference row qr for a node whose span ends at position
 // pos: rotated by pos * theta_j in the pairs (j, j + dims/2), or as given.
-template <int D, bool ROPE>
-__device__ __forceinline__ void node_reference(const float* __restrict__ qr, int lane,
-                                               const BuildArgs& a, double pos, double* q) {
-  constexpr int DPL = D / kWave;
+template <typename T, int D, bool ROPE>
+__device__ __forceinline__ void node_reference(const float* __restrict__ qr, int sub,
+                                               const BuildArgs& a, double pos,
+                                               double (&q)[LG<T, D>::VEC]) {
+  constexpr int VEC = LG<T, D>::VEC;
   const int dims = a.rope_dims, h = dims >> 1;
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    const int k = lane * DPL + e;
+  for (int e = 0; e < VEC; ++e) {
+    const int k = sub * VEC + e;
     double x = (double)qr[k];
     if (ROPE && k < dims) {
       const int j = k < h ? k : k - h;
@@ -60,237 +91,792 @@ __device__ __forceinline__ void node_reference(const float* __restrict__ qr, int
   }
 }
 
-template <typename T, int D, bool ROPE>
-__global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ K,
-                                                   const float* __restrict__ qref,
-                                                   char* __restrict__ tree,
-                                                   double* __restrict__ sF,
-                                                   double* __restrict__ sK, BuildArgs a) {
-  constexpr int DPL = D / kWave;
+// True when the reference slice of some lane of this lane group is nonzero
+// (uniform over the group).
+template <int LPR, int VEC>
+__device__ __forceinline__ bool group_nonzero(const double (&q)[VEC]) {
+  bool nz = false;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) nz |= q[e] != 0.0;
+  const uint64_t bal = __ballot(nz);
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t node = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t lo = a.lo[1];
-  const int64_t nn = a.lay.n[1] - lo;  // nodes to summarise per tree
+  const uint64_t gm = (LPR == kWave) ? ~0ull : (((1ull << LPR) - 1) << (lane & ~(LPR - 1)));
+  return (bal & gm) != 0;
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void widen_f64(const uint4& raw, double (&k)[VEC]) {
+  float f[VEC];
+  Vec<T>::widen(raw, f);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) k[e] = (double)f[e];
+}
+
+// Summary of one leaf chunk (C key rows from `keys`, consecutive rows of d
+// elements) at one reference q (this lane's slice).  Returns F (or the fp64
+// b_hat with ROPE, what a merge reads), writes this lane's slice of the fp64
+// k_hat to acc and b_hat to b.
+template <typename T, int D>
+__device__ __forceinline__ double leaf_node(const T* __restrict__ keys, int C, int sub,
+                                            const double (&q)[LG<T, D>::VEC], bool qnz,
+                                            double (&acc)[LG<T, D>::VEC], double& b) {
+  constexpr int VEC = LG<T, D>::VEC, LPR = LG<T, D>::LPR;
+  const double inv_sqrt_d = 1.0 / sqrt((double)D);
+  const T* base = keys + sub * VEC;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+  if (!qnz) {
+    // Zero reference: weights are exactly 1; only the key sums remain.
+    for (int j0 = 0; j0 < C; j0 += kRowBatch) {
+      uint4 raw[kRowBatch];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u)
+        raw[u] = ld16(base + (int64_t)min(j0 + u, C - 1) * D);
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        if (j0 + u >= C) break;
+        double k[VEC];
+        widen_f64<T, VEC>(raw[u], k);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += k[e];
+      }
+    }
+    const double Z = (double)C;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = acc[e] / Z;
+    const double F = 0.0 + log(Z);
+    b = F;
+    return F;
+  }
+  // First key read: the maximum score of the chunk.
+  double m = -INFINITY;
+  for (int j0 = 0; j0 < C; j0 += kRowBatch) {
+    uint4 raw[kRowBatch];
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) raw[u] = ld16c(base + (int64_t)min(j0 + u, C - 1) * D);
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) {
+      if (j0 + u >= C) break;
+      double k[VEC];
+      widen_f64<T, VEC>(raw[u], k);
+      double part = 0.0;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part = fma(q[e], k[e], part);
+      m = fmax(m, group_sum64<LPR>(part) * inv_sqrt_d);
+    }
+  }
+  // Second key read: weights exp(s - m), their sum and the weighted key sum.
+  double Z = 0.0;
+  for (int j0 = 0; j0 < C; j0 += kRowBatch) {
+    uint4 raw[kRowBatch];
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) raw[u] = ld16(base + (int64_t)min(j0 + u, C - 1) * D);
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) {
+      if (j0 + u >= C) break;
+      double k[VEC];
+      widen_f64<T, VEC>(raw[u], k);
+      double part = 0.0;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part = fma(q[e], k[e], part);
+      const double w = exp(group_sum64<LPR>(part) * inv_sqrt_d - m);
+      Z += w;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = fma(w, k[e], acc[e]);
+    }
+  }
+  const double F = m + log(Z);
+  double part = 0.0;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    acc[e] = acc[e] / Z;
+    part = fma(q[e], acc[e], part);
+  }
+  b = F - group_sum64<LPR>(part) * inv_sqrt_d;
+  return F;
+}
+
+// Parent summary from C children at the parent's reference qp (this lane's
+// slice).  childF(c) is child c's F (its fp64 b_hat with ROPE), childK(c, k)
+// loads this lane's slice of its fp64 k_hat.  Returns F (b_hat with ROPE) and
+// writes acc and b as leaf_node.  Children are taken in order.
+template <typename T, int D, bool ROPE, typename ChildF, typename ChildK>
+__device__ __forceinline__ double merge_node(int C, const double (&qp)[LG<T, D>::VEC],
+                                             ChildF childF, ChildK childK,
+                                             double (&acc)[LG<T, D>::VEC], double& b) {
+  constexpr int VEC = LG<T, D>::VEC, LPR = LG<T, D>::LPR;
+  const double inv_sqrt_d = 1.0 / sqrt((double)D);
+  // A child's log-mass at the parent's reference.
+  auto f_of = [&](int c, const double (&kc)[VEC]) {
+    double f = childF(c);
+    if constexpr (ROPE) {
+      double part = 0.0;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part = fma(qp[e], kc[e], part);
+      f += group_sum64<LPR>(part) * inv_sqrt_d;
+    }
+    return f;
+  };
+  double m = -INFINITY;
+  for (int c = 0; c < C; ++c) {
+    double kc[VEC];
+    if constexpr (ROPE) childK(c, kc);
+    m = fmax(m, f_of(c, kc));
+  }
+  double Z = 0.0;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+  for (int c0 = 0; c0 < C; c0 += kChildBatch) {
+    double kc[kChildBatch][VEC];
+#pragma unroll
+    for (int u = 0; u < kChildBatch; ++u) childK(min(c0 + u, C - 1), kc[u]);
+#pragma unroll
+    for (int u = 0; u < kChildBatch; ++u) {
+      if (c0 + u >= C) break;
+      const double w = exp(f_of(c0 + u, kc[u]) - m);
+      Z += w;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = fma(w, kc[u][e], acc[e]);
+    }
+  }
+  const double F = m + log(Z);
+  double part = 0.0;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    acc[e] = acc[e] / Z;
+    part = fma(qp[e], acc[e], part);
+  }
+  b = F - group_sum64<LPR>(part) * inv_sqrt_d;
+  return ROPE ? b : F;
+}
+
+// Stored copy of this lane's slice: k_hat rounded once to the storage dtype.
+template <typename T, int VEC>
+__device__ __forceinline__ void store_khat(T* row, int sub, const double (&acc)[VEC]) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[VEC / 2];
+#pragma unroll
+    for (int e = 0; e < VEC / 2; ++e)
+      w[e] = (uint32_t)f64_to_bf16(acc[2 * e]) | ((uint32_t)f64_to_bf16(acc[2 * e + 1]) << 16);
+    *reinterpret_cast<uint4*>(row + sub * VEC) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    *reinterpret_cast<float4*>(row + sub * VEC) =
+        make_float4((float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]);
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_f64_slice(const double* p, double (&k)[VEC]) {
+#pragma unroll
+  for (int e = 0; e < VEC; e += 2) {
+    const double2 v = *reinterpret_cast<const double2*>(p + e);
+    k[e] = v.x;
+    k[e + 1] = v.y;
+  }
+}
+template <int VEC>
+__device__ __forceinline__ void store_f64_slice(double* p, const double (&k)[VEC]) {
+#pragma unroll
+  for (int e = 0; e < VEC; e += 2) *reinterpret_cast<double2*>(p + e) = make_double2(k[e], k[e + 1]);
+}
+
+// The first key row of leaf chunk i of tree tr (chunks are C consecutive rows
+// in both layouts; chunked pages hold C key rows, then C value rows).
+template <typename T, int D>
+__device__ __forceinline__ const T* chunk_keys(const T* K, const BuildArgs& a, int64_t tr,
+                                               int64_t i) {
+  return K + tr * kv_block_elems(a.Tc, a.lay.C, D, a.chunked) +
+         i * (int64_t)a.lay.C * (a.chunked ? 2 : 1) * D;
+}
+
+// Leaves [lo, hi) of every tree, one lane group per leaf.  sF/sK: fp64 copies
+// for later merges (NULL when the tree has one level).
+template <typename T, int D, bool ROPE>
+__global__ __launch_bounds__(kBuildThreads) void leaf_kernel(const T* __restrict__ K,
+                                                             const float* __restrict__ qref,
+                                                             char* __restrict__ tree,
+                                                             double* __restrict__ sF,
+                                                             double* __restrict__ sK, BuildArgs a,
+                                                             int64_t lo, int64_t hi) {
+  using G = LG<T, D>;
+  const int sub = threadIdx.x % G::LPR;
+  const int64_t node = (int64_t)blockIdx.x * G::NG + threadIdx.x / G::LPR;
+  const int64_t nn = hi - lo;
+  // Lane groups past the end still take part in the group reductions' lanes
+  // of their own group only, so they can simply leave.
   if (node >= (int64_t)a.n_trees * nn) return;
   const int64_t tr = node / nn;
   const int64_t i = lo + (node - tr * nn);
   const int kvh = (int)(tr % a.H_kv);
-  const int C = a.lay.C;
-  const int R = a.lay.R;
-  const double inv_sqrt_d = 1.0 / sqrt((double)D);
-  // Chunk i's C keys are consecutive rows in both layouts; only the chunk's
-  // first row differs (chunked: each page holds C key rows, then C value rows).
-  const T* keys = K + tr * kv_block_elems(a.Tc, C, D, a.chunked) +
-                  i * (int64_t)C * (a.chunked ? 2 : 1) * D;
+  const int C = a.lay.C, R = a.lay.R;
+  const T* keys = chunk_keys<T, D>(K, a, tr, i);
   T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
   float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
-
   const double pos = (double)((i + 1) * C - 1);  // the chunk's last position
   for (int r = 0; r < R; ++r) {
-    double q[DPL];
-    node_reference<D, ROPE>(qref + ((int64_t)kvh * R + r) * D, lane, a, pos, q);
-    // Rows are read kB at a time, every load of a batch issued before the
-    // first is used (one memory latency per batch, not per row); the
-    // arithmetic runs row by row in order.
-    constexpr int kB = 8;
-    // First key read: the maximum score of the chunk.
-    double m = -INFINITY;
-    for (int j0 = 0; j0 < C; j0 += kB) {
-      double k[kB][DPL];
-#pragma unroll
-      for (int u = 0; u < kB; ++u) load_row_f64<T, D>(keys + (int64_t)min(j0 + u, C - 1) * D, lane, k[u]);
-#pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        if (j0 + u >= C) break;
-        double part = 0.0;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) part = fma(q[e], k[u][e], part);
-        m = fmax(m, group_sum64<kWave>(part) * inv_sqrt_d);
-      }
-    }
-    // Second key read: weights exp(s - m), their sum and the weighted key sum.
-    double Z = 0.0;
-    double acc[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
-    for (int j0 = 0; j0 < C; j0 += kB) {
-      double k[kB][DPL];
-#pragma unroll
-      for (int u = 0; u < kB; ++u) load_row_f64<T, D>(keys + (int64_t)min(j0 + u, C - 1) * D, lane, k[u]);
-#pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        if (j0 + u >= C) break;
-        double part = 0.0;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) part = fma(q[e], k[u][e], part);
-        const double w = exp(group_sum64<kWave>(part) * inv_sqrt_d - m);
-        Z += w;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fma(w, k[u][e], acc[e]);
-      }
-    }
-    const double F = m + log(Z);
-    double part = 0.0;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      acc[e] = acc[e] / Z;
-      part = fma(q[e], acc[e], part);
-    }
-    const double b = F - group_sum64<kWave>(part) * inv_sqrt_d;
+    double q[G::VEC], acc[G::VEC], b;
+    node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, q);
+    const bool qnz = group_nonzero<G::LPR, G::VEC>(q);
+    const double f = leaf_node<T, D>(keys, C, sub, q, qnz, acc, b);
     const int64_t row = i * R + r;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) store_elem64(khat, row * D + lane * DPL + e, acc[e]);
-    if (lane == 0) bhat[row] = (float)b;
+    store_khat<T, G::VEC>(khat + row * D, sub, acc);
+    if (sub == 0) bhat[row] = (float)b;
     if (sF != nullptr) {
       const int64_t srow = tr * a.lay.ncap[1] * R + row;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) sK[srow * D + lane * DPL + e] = acc[e];
-      if (lane == 0) sF[srow] = ROPE ? b : F;
+      store_f64_slice<G::VEC>(sK + srow * D + sub * G::VEC, acc);
+      if (sub == 0) sF[srow] = ROPE ? b : f;
     }
   }
 }
 
+// Parents [lo_level, n_level) of every tree from their children's fp64
+// copies, one lane group per parent.
 template <typename T, int D, bool ROPE>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ qref,
-                                                    char* __restrict__ tree,
-                                                    const double* __restrict__ cF,
-                                                    const double* __restrict__ cK,
-                                                    double* __restrict__ pF,
-                                                    double* __restrict__ pK, BuildArgs a,
-                                                    int level) {
-  constexpr int DPL = D / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
+__global__ __launch_bounds__(kBuildThreads) void merge_kernel(const float* __restrict__ qref,
+                                                              char* __restrict__ tree,
+                                                              const double* __restrict__ cF,
+                                                              const double* __restrict__ cK,
+                                                              double* __restrict__ pF,
+                                                              double* __restrict__ pK,
+                                                              BuildArgs a, int level) {
+  using G = LG<T, D>;
+  const int sub = threadIdx.x % G::LPR;
   const int64_t lo = a.lo[level];
   const int64_t nn = a.lay.n[level] - lo;  // nodes to merge per tree
-  const int64_t node = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t node = (int64_t)blockIdx.x * G::NG + threadIdx.x / G::LPR;
   if (node >= (int64_t)a.n_trees * nn) return;
   const int64_t tr = node / nn;
   const int64_t i = lo + (node - tr * nn);
   const int kvh = (int)(tr % a.H_kv);
-  const int C = a.lay.C;
-  const int R = a.lay.R;
-  const double inv_sqrt_d = 1.0 / sqrt((double)D);
+  const int C = a.lay.C, R = a.lay.R;
   T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[level]);
   float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[level]);
-  // First child's scratch row (per reference block).
-  const int64_t child0 = tr * a.lay.ncap[level - 1] + i * C;
-  // Children's log-masses at the parent's rotated reference (one wave's row).
-  __shared__ double s_f[ROPE ? 4 : 1][ROPE ? 1024 : 1];
-  double* fw = s_f[ROPE ? (threadIdx.x >> 6) : 0];
+  const int64_t child0 = tr * a.lay.ncap[level - 1] + i * C;  // first child's scratch row
   double span = 1.0;
   for (int l = 0; l < level; ++l) span *= C;
   const double pos = (double)(i + 1) * span - 1.0;  // the node's last position
-
   for (int r = 0; r < R; ++r) {
-    double qp[DPL];
-    node_reference<D, ROPE>(qref + ((int64_t)kvh * R + r) * D, lane, a, pos, qp);
-    // Maximum child log-mass.
-    double m = -INFINITY;
-    if constexpr (ROPE) {
-      for (int c = 0; c < C; ++c) {
-        const double* krow = cK + ((child0 + c) * R + r) * D + lane * DPL;
-        double part = 0.0;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) part = fma(qp[e], krow[e], part);
-        const double f = cF[(child0 + c) * R + r] + group_sum64<kWave>(part) * inv_sqrt_d;
-        fw[c] = f;  // every lane holds f; the row is read back by this wave only
-        m = fmax(m, f);
-      }
-    } else {
-      for (int c = lane; c < C; c += kWave) m = fmax(m, cF[(child0 + c) * R + r]);
-      m = group_max64<kWave>(m);
-    }
-    // Weight sum and rescaled sum of the children's summaries, children in order.
-    double Z = 0.0;
-    double acc[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
-    for (int c0 = 0; c0 < C; c0 += kWave) {
-      const double f_mine =
-          c0 + lane < C ? (ROPE ? fw[c0 + lane] : cF[(child0 + c0 + lane) * R + r]) : 0.0;
-      const double e_mine = (c0 + lane < C) ? exp(f_mine - m) : 0.0;
-      const int cn = min(kWave, C - c0);
-      // Children's rows kB at a time, all loads of a batch issued first; the
-      // sums run child by child in order.
-      constexpr int kB = 8;
-      for (int cb = 0; cb < cn; cb += kB) {
-        double kr[kB][DPL];
-#pragma unroll
-        for (int u = 0; u < kB; ++u) {
-          const double* krow = cK + ((child0 + c0 + min(cb + u, cn - 1)) * R + r) * D + lane * DPL;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) kr[u][e] = krow[e];
-        }
-#pragma unroll
-        for (int u = 0; u < kB; ++u) {
-          if (cb + u >= cn) break;
-          const double w = __shfl(e_mine, cb + u, kWave);
-          Z += w;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[e] = fma(w, kr[u][e], acc[e]);
-        }
-      }
-    }
-    const double F = m + log(Z);
-    double part = 0.0;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      acc[e] = acc[e] / Z;
-      part = fma(qp[e], acc[e], part);
-    }
-    const double b = F - group_sum64<kWave>(part) * inv_sqrt_d;
+    double qp[G::VEC], acc[G::VEC], b;
+    node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, qp);
+    const double f = merge_node<T, D, ROPE>(
+        C, qp, [&](int c) { return cF[(child0 + c) * R + r]; },
+        [&](int c, double (&k)[G::VEC]) {
+          load_f64_slice<G::VEC>(cK + ((child0 + c) * R + r) * D + sub * G::VEC, k);
+        },
+        acc, b);
     const int64_t row = i * R + r;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) store_elem64(khat, row * D + lane * DPL + e, acc[e]);
-    if (lane == 0) bhat[row] = (float)b;
+    store_khat<T, G::VEC>(khat + row * D, sub, acc);
+    if (sub == 0) bhat[row] = (float)b;
     if (pF != nullptr) {
       const int64_t prow = (tr * a.lay.ncap[level] + i) * R + r;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) pK[prow * D + lane * DPL + e] = acc[e];
-      if (lane == 0) pF[prow] = ROPE ? b : F;
+      store_f64_slice<G::VEC>(pK + prow * D + sub * G::VEC, acc);
+      if (sub == 0) pF[prow] = f;
     }
   }
 }
 
+__host__ __device__ inline int fused_f_slots(int n) { return (n + 1) & ~1; }
+
+// Workgroup-uniform: does any of KV head kvh's R references have a nonzero
+// entry?  (A rotation keeps a zero reference zero.)
+__device__ __forceinline__ bool kv_head_has_nonzero_reference(const float* __restrict__ qref,
+                                                              const BuildArgs& a, int kvh) {
+  const int n = a.lay.R * a.d;
+  const float* q = qref + (int64_t)kvh * n;
+  bool nz = false;
+  for (int x = threadIdx.x; x < n; x += kBuildThreads) nz |= q[x] != 0.0f;
+  return __syncthreads_or(nz) != 0;
+}
+
+// Parents [lo_level, n_level) of every tree, one workgroup each, when a
+// parent's children fit the LDS (C R fp64 F, C R d fp64 k_hat): the children's
+// rows are contiguous in the scratch and are staged into LDS with every load
+// in flight at once, then one lane group per reference merges them with
+// merge_node (children in order, the bits of merge_kernel).  One memory round
+// trip per parent instead of one per kChildBatch children: the small top
+// levels of a tree are latency chains otherwise.
+template <typename T, int D, bool ROPE>
+__global__ __launch_bounds__(kBuildThreads) void merge_staged_kernel(
+    const float* __restrict__ qref, char* __restrict__ tree, const double* __restrict__ cF,
+    const double* __restrict__ cK, double* __restrict__ pF, double* __restrict__ pK,
+    BuildArgs a, int level) {
+  using G = LG<T, D>;
+  extern __shared__ double lds[];  // [C R] F (padded to even), then [C R, D] k_hat
+  const int sub = threadIdx.x % G::LPR, grp = threadIdx.x / G::LPR;
+  const int C = a.lay.C, R = a.lay.R;
+  const int64_t lo = a.lo[level];
+  const int64_t nn = a.lay.n[level] - lo;
+  const int64_t tr = blockIdx.x / nn;
+  const int64_t i = lo + (blockIdx.x - tr * nn);
+  const int kvh = (int)(tr % a.H_kv);
+  const int64_t child0 = tr * a.lay.ncap[level - 1] + i * C;
+  const int nf = C * R;
+  double* lF = lds;
+  double* lK = lds + fused_f_slots(nf);
+  {
+    const double2* src = reinterpret_cast<const double2*>(cK + child0 * R * D);
+    double2* dst = reinterpret_cast<double2*>(lK);
+    const int n2 = nf * D / 2;
+    for (int x = threadIdx.x; x < n2; x += kBuildThreads) dst[x] = src[x];
+    for (int x = threadIdx.x; x < nf; x += kBuildThreads) lF[x] = cF[child0 * R + x];
+  }
+  __syncthreads();
+  T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[level]);
+  float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[level]);
+  double span = 1.0;
+  for (int l = 0; l < level; ++l) span *= C;
+  const double pos = (double)(i + 1) * span - 1.0;
+  for (int r = grp; r < R; r += G::NG) {
+    double qp[G::VEC], acc[G::VEC], b;
+    node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, qp);
+    const double f = merge_node<T, D, ROPE>(
+        C, qp, [&](int c) { return lF[c * R + r]; },
+        [&](int c, double (&k)[G::VEC]) {
+          load_f64_slice<G::VEC>(lK + ((int64_t)c * R + r) * D + sub * G::VEC, k);
+        },
+        acc, b);
+    const int64_t row = i * R + r;
+    store_khat<T, G::VEC>(khat + row * D, sub, acc);
+    if (sub == 0) bhat[row] = (float)b;
+    if (pF != nullptr) {
+      const int64_t prow = (tr * a.lay.ncap[level] + i) * R + r;
+      store_f64_slice<G::VEC>(pK + prow * D + sub * G::VEC, acc);
+      if (sub == 0) pF[prow] = f;
+    }
+  }
+}
+
+// Complete level-2 subtrees, PW parents per workgroup: the PW C leaves below
+// them are summarised into LDS (fp64, all R references), then each parent is
+// merged from LDS by one lane group.  Level-2 nodes get their fp64 copy in the
+// scratch (pF/pK, NULL when level 2 is the top); the leaves get none.
+template <typename T, int D, bool ROPE>
+__device__ __forceinline__ void fused_body(const T* __restrict__ K, const float* __restrict__ qref,
+                                           char* __restrict__ tree, double* __restrict__ pF,
+                                           double* __restrict__ pK, const BuildArgs& a, int PW,
+                                           double* lds, int64_t item) {
+  using G = LG<T, D>;
+  // lds: [LW * R] fp64 F (padded to an even count, so the k_hat rows stay
+  // 16-byte aligned), then [LW * R, D] fp64 k_hat; LW = PW C leaves.
+  const int sub = threadIdx.x % G::LPR, grp = threadIdx.x / G::LPR;
+  const int C = a.lay.C, R = a.lay.R;
+  const int64_t n2 = a.lay.n[2];
+  const int64_t wpt = (n2 + PW - 1) / PW;  // workgroups per tree
+  const int64_t tr = item / wpt;
+  const int64_t p0 = (item - tr * wpt) * PW;
+  const int np = (int)min((int64_t)PW, n2 - p0);  // parents of this workgroup
+  const int nl = np * C;                          // leaves of this workgroup
+  const int kvh = (int)(tr % a.H_kv);
+  double* lF = lds;
+  double* lK = lds + fused_f_slots(PW * C * R);
+  {
+    T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
+    float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
+    for (int x = grp; x < nl; x += G::NG) {
+      const int64_t i = p0 * C + x;
+      const T* keys = chunk_keys<T, D>(K, a, tr, i);
+      const double pos = (double)((i + 1) * C - 1);
+      for (int r = 0; r < R; ++r) {
+        double q[G::VEC], acc[G::VEC], b;
+        node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, q);
+        const bool qnz = group_nonzero<G::LPR, G::VEC>(q);
+        const double f = leaf_node<T, D>(keys, C, sub, q, qnz, acc, b);
+        const int64_t row = i * R + r;
+        store_khat<T, G::VEC>(khat + row * D, sub, acc);
+        if (sub == 0) {
+          bhat[row] = (float)b;
+          lF[x * R + r] = ROPE ? b : f;
+        }
+        store_f64_slice<G::VEC>(lK + ((int64_t)x * R + r) * D + sub * G::VEC, acc);
+      }
+    }
+  }
+  __syncthreads();
+  T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[2]);
+  float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[2]);
+  const double span = (double)C * (double)C;
+  for (int y = grp; y < np; y += G::NG) {
+    const int64_t i = p0 + y;
+    const double pos = (double)(i + 1) * span - 1.0;
+    for (int r = 0; r < R; ++r) {
+      double qp[G::VEC], acc[G::VEC], b;
+      node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, qp);
+      const double f = merge_node<T, D, ROPE>(
+          C, qp, [&](int c) { return lF[(y * C + c) * R + r]; },
+          [&](int c, double (&k)[G::VEC]) {
+            load_f64_slice<G::VEC>(lK + ((int64_t)(y * C + c) * R + r) * D + sub * G::VEC, k);
+          },
+          acc, b);
+      const int64_t row = i * R + r;
+      store_khat<T, G::VEC>(khat + row * D, sub, acc);
+      if (sub == 0) bhat[row] = (float)b;
+      if (pF != nullptr) {
+        const int64_t prow = (tr * a.lay.ncap[2] + i) * R + r;
+        store_f64_slice<G::VEC>(pK + prow * D + sub * G::VEC, acc);
+        if (sub == 0) pF[prow] = f;
+      }
+    }
+  }
+}
+
+// Parents per fused workgroup: at least C leaves, about 32 where C is
+// smaller, within the LDS budget; 0 when one parent's leaves do not fit.
+// Zero references, complete level-2 subtrees (the common case: R = 1, a zero
+// reference, every node the mean of its span).  As fused_body, for KV heads
+// whose R references are all zero: every leaf
+// then has F = log C and b_hat = F, and all references give the same summary,
+// which is computed once and stored for each.  Each lane group streams its
+// leaves' key rows kZeroBatch at a time with the next batch's loads issued
+// before the current batch is summed; a finished leaf's fp64 k_hat goes to
+// LDS (one row) for the level-2 merge.  The arithmetic is leaf_node's and
+// merge_node's with a zero reference, so the bits are theirs.
 template <typename T, int D>
-static int launch_build(const BuildArgs& a, const void* K, const float* qref, void* tree,
-                        void* scratch, hipStream_t s) {
+__device__ __forceinline__ void zero_fused_body(const T* __restrict__ K, char* __restrict__ tree,
+                                                double* __restrict__ pF, double* __restrict__ pK,
+                                                const BuildArgs& a, int PW, double* lds,
+                                                int64_t item) {
+  using G = LG<T, D>;
+  constexpr int VEC = G::VEC, NG = G::NG;
+  // lds: [PW C, D] fp64 k_hat of the leaves
+  const int sub = threadIdx.x % G::LPR, grp = threadIdx.x / G::LPR;
+  const int C = a.lay.C, R = a.lay.R;
+  const int64_t n2 = a.lay.n[2];
+  const int64_t wpt = (n2 + PW - 1) / PW;
+  const int64_t tr = item / wpt;
+  const int64_t p0 = (item - tr * wpt) * PW;
+  const int np = (int)min((int64_t)PW, n2 - p0);
+  const int nl = np * C;
+  const double Fleaf = 0.0 + log((double)C);  // leaf_node's F with a zero reference
+  {
+    T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
+    float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
+    const int mine = grp < nl ? (nl - grp + NG - 1) / NG : 0;  // leaves grp, grp + NG, ...
+    int lt = 0, lj = 0;  // load cursor: leaf (of this group) and row
+    int ct = 0, cj = 0;  // sum cursor
+    double acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+    // Row lj of this group's leaf lt: kbase + (grp + NG lt) cstride + lj D.
+    const T* kbase = chunk_keys<T, D>(K, a, tr, p0 * C) + sub * VEC;
+    const int64_t cstride = (int64_t)C * (a.chunked ? 2 : 1) * D;
+    auto load_batch = [&](uint4 (&buf)[kZeroBatch]) {
+#pragma unroll
+      for (int u = 0; u < kZeroBatch; ++u) {
+        if (lt < mine)
+          buf[u] = ld16(kbase + (grp + (int64_t)NG * lt) * cstride + (int64_t)lj * D);
+        if (++lj == C) {
+          lj = 0;
+          ++lt;
+        }
+      }
+    };
+    auto sum_batch = [&](const uint4 (&buf)[kZeroBatch]) {
+#pragma unroll
+      for (int u = 0; u < kZeroBatch; ++u) {
+        if (ct < mine) {
+          double k[VEC];
+          widen_f64<T, VEC>(buf[u], k);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[e] += k[e];
+          if (++cj == C) {  // leaf done
+            const int x = grp + NG * ct;
+            const int64_t i = p0 * C + x;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = acc[e] / (double)C;
+            for (int r = 0; r < R; ++r) {
+              store_khat<T, VEC>(khat + (i * R + r) * D, sub, acc);
+              if (sub == 0) bhat[i * R + r] = (float)Fleaf;
+            }
+            store_f64_slice<VEC>(lds + (int64_t)x * D + sub * VEC, acc);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+            cj = 0;
+            ++ct;
+          }
+        }
+      }
+    };
+    uint4 bufA[kZeroBatch], bufB[kZeroBatch];
+    load_batch(bufA);
+    while (ct < mine) {
+      load_batch(bufB);
+      sum_batch(bufA);
+      if (ct >= mine) break;
+      load_batch(bufA);
+      sum_batch(bufB);
+    }
+  }
+  __syncthreads();
+  T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[2]);
+  float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[2]);
+  double qz[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) qz[e] = 0.0;
+  for (int y = grp; y < np; y += NG) {
+    const int64_t i = p0 + y;
+    double acc[VEC], b;
+    const double f = merge_node<T, D, false>(
+        C, qz, [&](int) { return Fleaf; },
+        [&](int c, double (&k)[VEC]) {
+          load_f64_slice<VEC>(lds + (int64_t)(y * C + c) * D + sub * VEC, k);
+        },
+        acc, b);
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = i * R + r;
+      store_khat<T, VEC>(khat + row * D, sub, acc);
+      if (sub == 0) bhat[row] = (float)b;
+      if (pF != nullptr) {
+        const int64_t prow = (tr * a.lay.ncap[2] + i) * R + r;
+        store_f64_slice<VEC>(pK + prow * D + sub * VEC, acc);
+        if (sub == 0) pF[prow] = f;
+      }
+    }
+  }
+}
+
+// Complete level-2 subtrees with zero references, PW parents per workgroup
+// (one workgroup per item); a workgroup whose KV head has a nonzero reference
+// leaves it to fused_kernel.
+template <typename T, int D>
+__global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void zero_fused_kernel(const T* __restrict__ K,
+                                                                   const float* __restrict__ qref,
+                                                                   char* __restrict__ tree,
+                                                                   double* __restrict__ pF,
+                                                                   double* __restrict__ pK,
+                                                                   BuildArgs a, int PW) {
+  extern __shared__ double lds[];
+  const int64_t wpt = (a.lay.n[2] + PW - 1) / PW;
+  const int kvh = (int)((blockIdx.x / wpt) % a.H_kv);
+  if (kv_head_has_nonzero_reference(qref, a, kvh)) return;
+  zero_fused_body<T, D>(K, tree, pF, pK, a, PW, lds, blockIdx.x);
+}
+
+// Zero references and small chunks (C <= kStreamMaxC): one lane group per
+// complete level-2 node streams the C C key rows below it (kZeroBatch rows at
+// a time, the next batch in flight while one is summed), writes each leaf when
+// its C rows are in, and adds the leaf's fp64 k_hat into the parent's sum in
+// child order, which is merge_node's sum with every weight 1: no LDS, no
+// barrier, every lane group busy.  A lane group whose KV head has a nonzero
+// reference leaves it to fused_kernel.
+template <typename T, int D>
+#ifndef ZHA_STREAM_WAVES
+#define ZHA_STREAM_WAVES 1
+#endif
+__global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(ZHA_STREAM_WAVES)))
+void zero_stream_kernel(const T* __restrict__ K, const float* __restrict__ qref,
+                        char* __restrict__ tree, double* __restrict__ pF,
+                        double* __restrict__ pK, BuildArgs a) {
+  using G = LG<T, D>;
+  constexpr int VEC = G::VEC;
+  const int sub = threadIdx.x % G::LPR;
+  const int C = a.lay.C, R = a.lay.R;
+  const int64_t n2 = a.lay.n[2];
+  const int64_t node = (int64_t)blockIdx.x * G::NG + threadIdx.x / G::LPR;
+  if (node >= (int64_t)a.n_trees * n2) return;
+  const int64_t tr = node / n2;
+  const int64_t p = node - tr * n2;
+  const int kvh = (int)(tr % a.H_kv);
+  {
+    // This group's references (all R), any nonzero: not ours.
+    bool nz = false;
+    const float* q = qref + (int64_t)kvh * R * D;
+    for (int x = sub; x < R * D; x += G::LPR) nz |= q[x] != 0.0f;
+    const uint64_t bal = __ballot(nz);
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t gm = (G::LPR == kWave) ? ~0ull
+                                          : (((1ull << G::LPR) - 1) << (lane & ~(G::LPR - 1)));
+    if (bal & gm) return;
+  }
+  const double Fleaf = 0.0 + log((double)C);
+  T* khat1 = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
+  float* bhat1 = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
+  const T* kbase = chunk_keys<T, D>(K, a, tr, p * C) + sub * VEC;
+  const int64_t cstride = (int64_t)C * (a.chunked ? 2 : 1) * D;
+  // Load cursor: leaf lc, row lj (pointer lp); sum cursor: leaf cc, row cj.
+  int lc = 0, lj = 0, cc = 0, cj = 0;
+  const T* lp = kbase;
+  double acc[VEC], pacc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = pacc[e] = 0.0;
+  auto load_batch = [&](uint4 (&buf)[kZeroBatch]) {
+#pragma unroll
+    for (int u = 0; u < kZeroBatch; ++u) {
+      if (lc < C) buf[u] = ld16(lp);
+      lp += D;
+      if (++lj == C) {
+        lj = 0;
+        ++lc;
+        lp = kbase + lc * cstride;
+      }
+    }
+  };
+  auto sum_batch = [&](const uint4 (&buf)[kZeroBatch]) {
+#pragma unroll
+    for (int u = 0; u < kZeroBatch; ++u) {
+      if (cc < C) {
+        double k[VEC];
+        widen_f64<T, VEC>(buf[u], k);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += k[e];
+        if (++cj == C) {  // leaf cc done
+          cj = 0;
+          const int64_t i = p * C + cc;
+          ++cc;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            acc[e] = acc[e] / (double)C;
+            pacc[e] = fma(1.0, acc[e], pacc[e]);
+          }
+          for (int r = 0; r < R; ++r) {
+            store_khat<T, VEC>(khat1 + (i * R + r) * D, sub, acc);
+            if (sub == 0) bhat1[i * R + r] = (float)Fleaf;
+          }
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+        }
+      }
+    }
+  };
+  uint4 bufA[kZeroBatch], bufB[kZeroBatch];
+  load_batch(bufA);
+  while (cc < C) {
+    load_batch(bufB);
+    sum_batch(bufA);
+    if (cc >= C) break;
+    load_batch(bufA);
+    sum_batch(bufB);
+  }
+  // The parent: merge_node with C children of equal F: m = Fleaf, every
+  // weight exp(0) = 1, Z = C.
+  double Z = 0.0;
+  for (int c = 0; c < C; ++c) Z += exp(Fleaf - Fleaf);
+  const double F = Fleaf + log(Z);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) pacc[e] = pacc[e] / Z;
+  T* khat2 = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[2]);
+  float* bhat2 = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[2]);
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = p * R + r;
+    store_khat<T, VEC>(khat2 + row * D, sub, pacc);
+    if (sub == 0) bhat2[row] = (float)F;
+    if (pF != nullptr) {
+      const int64_t prow = (tr * a.lay.ncap[2] + p) * R + r;
+      store_f64_slice<VEC>(pK + prow * D + sub * VEC, pacc);
+      if (sub == 0) pF[prow] = F;
+    }
+  }
+}
+
+// The same items for KV heads with a nonzero reference, on a persistent grid:
+// each workgroup first marks which KV heads have one (a 64-bit mask when H_kv
+// <= 64, else a check per item), then takes items blockIdx.x, + gridDim.x, ...
+// and skips the others, so a build with zero references costs one short launch.
+template <typename T, int D, bool ROPE>
+__global__ __launch_bounds__(kBuildThreads) void fused_kernel(const T* __restrict__ K,
+                                                              const float* __restrict__ qref,
+                                                              char* __restrict__ tree,
+                                                              double* __restrict__ pF,
+                                                              double* __restrict__ pK,
+                                                              BuildArgs a, int PW) {
+  extern __shared__ double lds[];
+  const int64_t wpt = (a.lay.n[2] + PW - 1) / PW;
+  const int64_t items = (int64_t)a.n_trees * wpt;
+  uint64_t mask = 0;
+  const bool small = a.H_kv <= 64;
+  if (small)
+    for (int h = 0; h < a.H_kv; ++h)
+      if (kv_head_has_nonzero_reference(qref, a, h)) mask |= 1ull << h;
+  if (small && mask == 0) return;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int kvh = (int)((it / wpt) % a.H_kv);
+    const bool nz = small ? ((mask >> kvh) & 1ull) != 0 : kv_head_has_nonzero_reference(qref, a, kvh);
+    if (!nz) continue;
+    fused_body<T, D, ROPE>(K, qref, tree, pF, pK, a, PW, lds, it);
+    __syncthreads();  // lds is reused by the next item
+  }
+}
+
+inline int64_t fused_lds_bytes(int pw, int C, int R, int D) {
+  return ((int64_t)fused_f_slots(pw * C * R) + (int64_t)pw * C * R * D) * 8;
+}
+template <int D>
+int fused_parents(int C, int R) {
+  int pw = C >= 32 ? 1 : 32 / C;
+  while (pw > 1 && fused_lds_bytes(pw, C, R, D) > kFusedLds) pw >>= 1;
+  return fused_lds_bytes(pw, C, R, D) <= kFusedLds ? pw : 0;
+}
+
+template <typename T, int D, bool ROPE>
+int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void* tree,
+                      void* scratch, hipStream_t s) {
+  using G = LG<T, D>;
   const BuildScratch sc = build_scratch_layout(a);
   char* base = reinterpret_cast<char*>(scratch);
   auto F = [&](int l) { return reinterpret_cast<double*>(base + sc.F[l]); };
   auto Kp = [&](int l) { return reinterpret_cast<double*>(base + sc.K[l]); };
-  const int L = a.lay.L;
-  if (a.lay.n[1] > a.lo[1]) {
-    const int64_t nodes = (int64_t)a.n_trees * (a.lay.n[1] - a.lo[1]);
-    const unsigned blocks = (unsigned)((nodes + 3) / 4);
-    if (a.rope_dims)
-      leaf_kernel<T, D, true><<<blocks, 256, 0, s>>>(
-          reinterpret_cast<const T*>(K), qref, reinterpret_cast<char*>(tree),
-          L > 1 ? F(1) : nullptr, L > 1 ? Kp(1) : nullptr, a);
-    else
-      leaf_kernel<T, D, false><<<blocks, 256, 0, s>>>(
-          reinterpret_cast<const T*>(K), qref, reinterpret_cast<char*>(tree),
-          L > 1 ? F(1) : nullptr, L > 1 ? Kp(1) : nullptr, a);
-    if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
+  const int L = a.lay.L, C = a.lay.C, R = a.lay.R;
+  const T* kp = reinterpret_cast<const T*>(K);
+  char* tp = reinterpret_cast<char*>(tree);
+  auto leaves = [&](int64_t lo, int64_t hi) {
+    if (hi <= lo) return;
+    const int64_t nodes = (int64_t)a.n_trees * (hi - lo);
+    const unsigned blocks = (unsigned)((nodes + G::NG - 1) / G::NG);
+    leaf_kernel<T, D, ROPE><<<blocks, kBuildThreads, 0, s>>>(
+        kp, qref, tp, L > 1 ? F(1) : nullptr, L > 1 ? Kp(1) : nullptr, a, lo, hi);
+  };
+  // A full build takes every complete level-2 subtree in the fused kernel; the
+  // leaves past them (no complete parent yet) go through leaf_kernel with
+  // their fp64 copies kept for the merge that will complete them.
+  const int PW = (L >= 2 && a.lo[1] == 0 && a.lo[2] == 0 && a.lay.n[2] > 0)
+                     ? fused_parents<D>(C, R) : 0;
+  int first_merge = 2;
+  if (PW > 0) {
+    const int64_t wpt = (a.lay.n[2] + PW - 1) / PW;
+    const size_t lds = (size_t)fused_lds_bytes(PW, C, R, D);
+    const int64_t items = a.n_trees * wpt;
+    if (C <= kStreamMaxC) {
+      const int64_t groups = a.n_trees * a.lay.n[2];
+      zero_stream_kernel<T, D><<<(unsigned)((groups + G::NG - 1) / G::NG), kBuildThreads, 0, s>>>(
+          kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a);
+    } else {
+      zero_fused_kernel<T, D><<<(unsigned)items, kBuildThreads,
+                                (size_t)PW * C * D * sizeof(double), s>>>(
+          kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a, PW);
+    }
+    fused_kernel<T, D, ROPE><<<(unsigned)min(items, (int64_t)kFusedGrid), kBuildThreads, lds, s>>>(
+        kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a, PW);
+    leaves(a.lay.n[2] * C, a.lay.n[1]);
+    first_merge = 3;
+  } else {
+    leaves(a.lo[1], a.lay.n[1]);
   }
-  for (int l = 2; l <= L; ++l) {
+  if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
+  const int64_t staged_lds = ((int64_t)fused_f_slots(C * R) + (int64_t)C * R * D) * 8;
+  for (int l = first_merge; l <= L; ++l) {
     if (a.lay.n[l] == a.lo[l]) continue;  // no span of this level completed
     const int64_t nodes = (int64_t)a.n_trees * (a.lay.n[l] - a.lo[l]);
-    const unsigned blocks = (unsigned)((nodes + 3) / 4);
-    if (a.rope_dims)
-      merge_kernel<T, D, true><<<blocks, 256, 0, s>>>(qref, reinterpret_cast<char*>(tree),
-                                                      F(l - 1), Kp(l - 1),
-                                                      l < L ? F(l) : nullptr,
-                                                      l < L ? Kp(l) : nullptr, a, l);
-    else
-      merge_kernel<T, D, false><<<blocks, 256, 0, s>>>(qref, reinterpret_cast<char*>(tree),
-                                                       F(l - 1), Kp(l - 1),
-                                                       l < L ? F(l) : nullptr,
-                                                       l < L ? Kp(l) : nullptr, a, l);
+    if (staged_lds <= kFusedLds) {
+      merge_staged_kernel<T, D, ROPE><<<(unsigned)nodes, kBuildThreads, (size_t)staged_lds, s>>>(
+          qref, tp, F(l - 1), Kp(l - 1), l < L ? F(l) : nullptr, l < L ? Kp(l) : nullptr, a, l);
+    } else {
+      const unsigned blocks = (unsigned)((nodes + G::NG - 1) / G::NG);
+      merge_kernel<T, D, ROPE><<<blocks, kBuildThreads, 0, s>>>(
+          qref, tp, F(l - 1), Kp(l - 1), l < L ? F(l) : nullptr, l < L ? Kp(l) : nullptr, a, l);
+    }
     if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
   }
   return ZHA_OK;
 }
+
+template <typename T, int D>
+int launch_build(const BuildArgs& a, const void* K, const float* qref, void* tree,
+                 void* scratch, hipStream_t s) {
+  if (a.rope_dims) return launch_build_impl<T, D, true>(a, K, qref, tree, scratch, s);
+  return launch_build_impl<T, D, false>(a, K, qref, tree, scratch, s);
+}
+
+}  // namespace
 
 int build_dispatch(const BuildArgs& a, int dtype, int d, const void* K, const float* qref,
                    void* tree, void* scratch, hipStream_t s) {
