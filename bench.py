@@ -247,6 +247,8 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
                            device="cuda")
     ascratch = torch.zeros(max(Z.attn_scratch_bytes(gm, 1, cap), 1), dtype=torch.uint8,
                            device="cuda")
+    fscratch = torch.zeros(max(Z.route_attn_scratch_bytes(gm, 1, cap), 1), dtype=torch.uint8,
+                           device="cuda")
 
     # Timed loop: direct C-ABI calls with pointers marshalled once, so host
     # overhead stays far below the GPU time of a step.
@@ -264,7 +266,12 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     args_a = [(gref, vp(Qd[i].data_ptr()), 1, None, lp[i % n_layers][1], lp[i % n_layers][2],
                vp(sel[i].data_ptr()), vp(cnt[i].data_ptr()), cap, vp(O[i].data_ptr()), as_p,
                stream) for i in range(n)]
-    zr, za = lib.zha_route, lib.zha_attn
+    fs_p = vp(fscratch.data_ptr())
+    args_f = [(gref, lp[i % n_layers][0], vp(Qd[i].data_ptr()), 1, None, ctypes.c_float(g.p),
+               lp[i % n_layers][1], lp[i % n_layers][2], vp(sel[i].data_ptr()),
+               vp(cnt[i].data_ptr()), cap, vp(stats[i].data_ptr()), None, vp(O[i].data_ptr()),
+               fs_p, stream) for i in range(n)]
+    zr, za, zf = lib.zha_route, lib.zha_attn, lib.zha_route_attn
 
     def step(i):
         if zr(*args_r[i]) != 0 or za(*args_a[i]) != 0:
@@ -284,16 +291,22 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
 
     for i in range(warmup):
         step(i)
+        if zf(*args_f[i]) != 0:
+            raise RuntimeError("launch failed")
     torch.cuda.synchronize()
-    # The timed steps: route + attention per step, no event between them (an
-    # event recorded between two launches costs the stream ~3.5 us).
+    # The timed steps: zha_route followed by zha_attn per step, no event
+    # between them (an event recorded between two launches costs the stream
+    # ~3.5 us).  Then the same steps as one zha_route_attn call each (routing
+    # and attention in one launch).
     timed_ids = range(warmup, warmup + steps)
     total_ms = timed([c for i in timed_ids for c in ((zr, args_r[i]), (za, args_a[i]))])
+    fused_ms = timed([(zf, args_f[i]) for i in timed_ids])
     # The split, each call kind timed back to back over the same steps (the
     # attention calls reuse the routes computed above).
     route_ms = np.full(steps, timed([(zr, args_r[i]) for i in timed_ids]) / steps)
     attn_ms = np.full(steps, timed([(za, args_a[i]) for i in timed_ids]) / steps)
-    log(f"[bench] {steps} steps: {total_ms:.3f} ms total ({total_ms / steps * 1e3:.1f} us per step); "
+    log(f"[bench] {steps} steps: {total_ms:.3f} ms total ({total_ms / steps * 1e3:.1f} us per step "
+        f"as zha_route + zha_attn, {fused_ms / steps * 1e3:.1f} us in zha_route_attn); "
         f"route alone {route_ms.mean() * 1e3:.1f} us, attn alone {attn_ms.mean() * 1e3:.1f} us per call")
 
     # The same calls fully cache-cold: 1 GiB written before each call (outside
@@ -301,11 +314,11 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     # events of its own.
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     n_cold = min(steps, 10)
-    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_cold)]
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_cold)]
     for j in range(n_cold):
         i = warmup + j
-        for k, (fn, a) in enumerate(((zr, args_r[i]), (za, args_a[i]))):
-            flush.fill_((2 * j + k) & 255)
+        for k, (fn, a) in enumerate(((zr, args_r[i]), (za, args_a[i]), (zf, args_f[i]))):
+            flush.fill_((3 * j + k) & 255)
             evc[j][2 * k].record()
             if fn(*a) != 0:
                 raise RuntimeError("launch failed")
@@ -313,8 +326,10 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     torch.cuda.synchronize()
     cold_route = np.array([e[0].elapsed_time(e[1]) for e in evc])
     cold_attn = np.array([e[2].elapsed_time(e[3]) for e in evc])
+    cold_fused = np.array([e[4].elapsed_time(e[5]) for e in evc])
     log(f"[bench] {n_cold} cold steps: route {cold_route.mean() * 1e3:.1f} us, "
-        f"attn {cold_attn.mean() * 1e3:.1f} us per step")
+        f"attn {cold_attn.mean() * 1e3:.1f} us, zha_route_attn {cold_fused.mean() * 1e3:.1f} us "
+        f"per step")
     # Streaming-copy bandwidth of this device (read + write bytes of a 1 GiB copy).
     dst = torch.empty_like(flush)
     dst.copy_(flush)
@@ -360,7 +375,8 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
         dense_ms = d0.elapsed_time(d1) / dense_steps
         log(f"[bench] dense decode {dense_ms * 1e3:.1f} us per step")
     maint = decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch)
-    return {"total_ms": total_ms, "route_ms": route_ms, "attn_ms": attn_ms, "bytes": acc,
+    return {"total_ms": total_ms, "fused_ms": fused_ms, "cold_fused_ms": cold_fused,
+            "route_ms": route_ms, "attn_ms": attn_ms, "bytes": acc,
             "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap, "cold_route_ms": cold_route,
             "cold_attn_ms": cold_attn, "copy_gbs": copy_gbs, "maintenance": maint,
             "n_layers": n_layers}
@@ -796,6 +812,7 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
+        "route_attn_us_per_step": r["fused_ms"] / args.steps * 1e3,
         "route_us": route_us,
         "attn_us": attn_us,
         "step_bytes_union": step_union,
@@ -807,7 +824,8 @@ def main():
         "query_heads_per_s": value * g.H_q,
         "stream_copy_GBs": r["copy_gbs"],
         "attn_frac_of_copy": achieved / r["copy_gbs"],
-        "cold": {"route_us": float(r["cold_route_ms"].mean() * 1e3),
+        "cold": {"route_attn_us": float(r["cold_fused_ms"].mean() * 1e3),
+                 "route_us": float(r["cold_route_ms"].mean() * 1e3),
                  "attn_us": float(r["cold_attn_ms"].mean() * 1e3),
                  "us_per_step": float((r["cold_route_ms"] + r["cold_attn_ms"]).mean() * 1e3),
                  "queries_per_s": g.B / float((r["cold_route_ms"] + r["cold_attn_ms"]).mean()

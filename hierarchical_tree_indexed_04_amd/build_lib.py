@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzha.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["zha_api.hip", "zha_build.hip", "zha_route.hip", "zha_attn.hip"]
+SOURCES = ["zha_api.hip", "zha_build.hip", "zha_route.hip", "zha_attn.hip", "zha_fused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("ZHA_OFFLOAD_ARCH", "gfx950")

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "zha_internal.hpp"
@@ -227,10 +228,13 @@ int zha_route_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_
   return ZHA_OK;
 }
 
-int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
-              const int32_t* ctx_len, float p,
-              int32_t* sel, int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap,
-              void* scratch, void* stream) {
+}  // extern "C"
+
+namespace {
+// Validation and arguments of a route call.
+int prepare_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
+                  const int32_t* ctx_len, float p, int32_t* sel, int32_t* cnt, int32_t cap,
+                  RouteArgs& a) {
   const int rc = check_geom(g);
   if (rc) return rc;
   if (tree == nullptr || Q == nullptr || sel == nullptr || cnt == nullptr) return ZHA_ERR_NULL;
@@ -239,7 +243,7 @@ int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
   if (!(p > 0.0f && p <= 1.0f)) return ZHA_ERR_P;
   if (!route_frontier_fits(g)) return ZHA_ERR_GEOM;
   if (!aligned16(tree) || !aligned16(Q)) return ZHA_ERR_ALIGN;
-  RouteArgs a{};
+  a = RouteArgs{};
   a.lay = make_layout(g);
   a.T = g->T;
   a.ctx = ctx_len;
@@ -255,6 +259,19 @@ int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
   a.cdiv = (uint32_t)(((1ull << 32) + (uint64_t)g->C - 1) / (uint64_t)g->C);
   a.spill_wait = spill_wait_rounds();
   if (a.n_heads > INT32_MAX) return ZHA_ERR_GEOM;
+  return ZHA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int zha_route(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
+              const int32_t* ctx_len, float p,
+              int32_t* sel, int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap,
+              void* scratch, void* stream) {
+  RouteArgs a;
+  const int rc = prepare_route(g, tree, Q, n_pos, ctx_len, p, sel, cnt, cap, a);
+  if (rc) return rc;
   const RouteScratch rs = route_scratch_layout(a.n_heads, a.lay.ncap[1]);
   if (rs.bytes > 0 && scratch == nullptr) return ZHA_ERR_NULL;
   if (rs.bytes > 0 && !aligned16(scratch)) return ZHA_ERR_ALIGN;
@@ -372,6 +389,74 @@ int zha_attn_noalloc(const zha_geom* g, const void* Q, int32_t n_pos, const int3
   }
   return attn_dispatch(a, g->dtype, g->d, Q, K, V, sel, cnt, O, buf,
                        reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+// zha_route_attn scratch: zha_route's, then either the fused launch's partials
+// or zha_attn's scratch (whichever is larger).
+struct RouteAttnScratch {
+  int64_t route, attn, total;
+};
+RouteAttnScratch route_attn_layout(const zha_geom* g, int64_t n_heads) {
+  RouteAttnScratch l{};
+  l.route = align256(route_scratch_layout(n_heads, capacity(g) / g->C).bytes);
+  const int64_t fused = n_heads <= kFzMaxHeads ? n_heads * kFzMaxPieces * (int64_t)(g->d + 2) * 4 : 0;
+  const int64_t attn = attn_scratch_layout_bytes(n_heads, (int64_t)g->B * g->H_kv, g->T, g->C, g->d,
+                                                 g->dtype);
+  l.attn = align256(fused > attn ? fused : attn);
+  l.total = l.route + l.attn;
+  return l;
+}
+}  // namespace
+
+extern "C" {
+
+int zha_route_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes) {
+  const int rc = check_geom(g);
+  if (rc) return rc;
+  if (bytes == nullptr) return ZHA_ERR_NULL;
+  if (n_pos < 1) return ZHA_ERR_NPOS;
+  if (cap < 1) return ZHA_ERR_CAP;
+  if (!route_frontier_fits(g)) return ZHA_ERR_GEOM;
+  *bytes = (size_t)route_attn_layout(g, (int64_t)g->B * n_pos * g->H_q).total;
+  return ZHA_OK;
+}
+
+int zha_route_attn(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
+                   const int32_t* ctx_len, float p, const void* K, const void* V, int32_t* sel,
+                   int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap, void* O,
+                   void* scratch, void* stream) {
+  RouteArgs ra;
+  int rc = prepare_route(g, tree, Q, n_pos, ctx_len, p, sel, cnt, cap, ra);
+  if (rc) return rc;
+  AttnArgs aa;
+  int64_t need_attn = 0;
+  rc = prepare_attn(g, Q, n_pos, ctx_len, K, V, sel, cnt, cap, O, aa, &need_attn);
+  if (rc) return rc;
+  const RouteAttnScratch l = route_attn_layout(g, ra.n_heads);
+  if (l.total > 0 && scratch == nullptr) return ZHA_ERR_NULL;
+  if (l.total > 0 && !aligned16(scratch)) return ZHA_ERR_ALIGN;
+  char* scr = reinterpret_cast<char*>(scratch);
+  char* ascr = l.attn > 0 ? scr + l.route : nullptr;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t kv_bytes = kv_block_elems(aa.Tc, g->C, g->d, aa.chunked) *
+                           (g->dtype == ZHA_BF16 ? 2 : 4);
+  if (fused_eligible(ra.n_heads, g->R, g->C, p, kv_bytes)) {
+    const RouteScratch rs = route_scratch_layout(ra.n_heads, ra.lay.ncap[1]);
+    char* ws = rs.ws < 0 ? nullptr : scr + rs.ws;
+    // A nonzero tag, different for consecutive calls (the launch's queue items
+    // and piece counters carry it).
+    static std::atomic<uint32_t> g_tag{0};
+    uint32_t tag = ++g_tag;
+    if (tag == 0) tag = ++g_tag;
+    return fused_dispatch(ra, aa, g->dtype, g->d, tree, Q, K, V, sel, cnt, level_stats, gap, O, ws,
+                          rs.ws_stride, reinterpret_cast<float*>(ascr), kFzGrid, tag, s);
+  }
+  rc = route_dispatch(ra, g->dtype, g->d, tree, Q, sel, cnt, level_stats, gap, scratch, s);
+  if (rc) return rc;
+  return attn_dispatch(aa, g->dtype, g->d, Q, K, V, sel, cnt, O, ascr, s);
 }
 
 int zha_dense_decode_scratch_bytes(const zha_geom* g, int32_t n_pos, size_t* bytes) {

@@ -23,244 +23,10 @@
 // keys; a workgroup serves the G query heads of one KV head so each K/V row
 // is read once per group.
 
-#include "zha_internal.hpp"
-#include "zha_wave.hpp"
+#include "zha_attn_impl.hpp"
 
 namespace zha {
 namespace {
-
-constexpr int kThreads = 256;
-#ifndef ZHA_ATTN_ROWS
-#define ZHA_ATTN_ROWS 4
-#endif
-#ifndef ZHA_DENSE_ROWS
-#define ZHA_DENSE_ROWS 4
-#endif
-#ifndef ZHA_ATTN_WAVES
-#define ZHA_ATTN_WAVES 2
-#endif
-constexpr int kUA = ZHA_ATTN_ROWS;   // K/V rows in flight per lane (sparse)
-constexpr int kUD = ZHA_DENSE_ROWS;  // K/V rows in flight per lane (dense)
-constexpr int kIds = 1024;  // chunk ids staged in LDS per round (sparse)
-constexpr int kWaves = kThreads / kWave;
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
-
-// q . k over one 16-byte slice of a row.  bf16: packed bf16 dot products
-// (exact products, fp32 sums); fp32: fused multiply-adds.
-template <typename T>
-__device__ __forceinline__ float slice_dot(const uint4& k, const uint4& q) {
-  if constexpr (sizeof(T) == 2) {
-    float d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.x), as_bf16x2(q.x), 0.0f, false);
-    d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.y), as_bf16x2(q.y), d, false);
-    d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.z), as_bf16x2(q.z), d, false);
-    return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.w), as_bf16x2(q.w), d, false);
-  } else {
-    float d = __uint_as_float(k.x) * __uint_as_float(q.x);
-    d = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), d);
-    d = fmaf(__uint_as_float(k.z), __uint_as_float(q.z), d);
-    return fmaf(__uint_as_float(k.w), __uint_as_float(q.w), d);
-  }
-}
-
-// Inclusive prefix sum over the 64 lanes of a 32-bit value.
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
-  v += dpp_u32<kDppRowShr1>(0u, v);
-  v += dpp_u32<kDppRowShr2>(0u, v);
-  v += dpp_u32<kDppRowShr4>(0u, v);
-  v += dpp_u32<kDppRowShr8>(0u, v);
-  v += dpp_u32<kDppRowBcast15, 0xA>(0u, v);
-  v += dpp_u32<kDppRowBcast31, 0xC>(0u, v);
-  return v;
-}
-
-
-
-// The K/V rows of one (b, kvh) pair in either cache layout.  Rows are
-// addressed by key row: token j of chunk c is key row c * CS + j, with CS = C
-// (split: K and V are [T, d] arrays, the value row has the same index in V)
-// or 2 C (chunked: pages of C key rows then C value rows, the value row is C
-// rows further in the same buffer).  Each lane reads its 16-byte slice `sub`.
-// BUF: buffer loads (block < 2^31 bytes), a slot without a row reads nothing.
-template <typename T, int D, bool BUF>
-struct KvBlock {
-  static constexpr uint32_t kRow = D * sizeof(T);
-  const char* k;
-  const char* v;
-  buf_t rk, rv;
-  int cs;
-  __device__ __forceinline__ KvBlock(const T* K, const T* V, int64_t tr, int64_t T_, int C,
-                                     int chunked, int sub) {
-    const int64_t n = kv_block_elems(T_, C, D, chunked);
-    const T* kb = K + tr * n;
-    const T* vb = chunked ? kb + (int64_t)C * D : V + tr * n;
-    k = reinterpret_cast<const char*>(kb) + sub * 16;
-    v = reinterpret_cast<const char*>(vb) + sub * 16;
-    const int64_t bytes = BUF ? n * (int64_t)sizeof(T) : 0;
-    rk = make_buf(kb, bytes);
-    rv = chunked ? rk : make_buf(vb, bytes);
-    cs = chunked ? 2 * C : C;
-    vdelta = chunked ? (uint32_t)C * kRow : 0u;
-    sub16 = (uint32_t)sub * 16u;
-  }
-  uint32_t vdelta, sub16;
-  __device__ __forceinline__ int key_row(int chunk, int j) const { return chunk * cs + j; }
-  // K or V row alone (the same rules as load).
-  __device__ __forceinline__ uint4 load_k(int row, bool live) const {
-    if (BUF) return bld16(rk, live ? (uint32_t)row * kRow + sub16 : kBufNone);
-    return live ? ld16(k + (size_t)(uint32_t)row * kRow) : make_uint4(0u, 0u, 0u, 0u);
-  }
-  __device__ __forceinline__ uint4 load_v(int row, bool live) const {
-    if (BUF) return bld16(rv, live ? (uint32_t)row * kRow + sub16 + vdelta : kBufNone);
-    return live ? ld16(v + (size_t)(uint32_t)row * kRow) : make_uint4(0u, 0u, 0u, 0u);
-  }
-  __device__ __forceinline__ void load(int row, bool live, uint4& kv, uint4& vv) const {
-    if (BUF) {
-      // Straight-line: a slot without a row reads nothing and gets zeros.
-      const uint32_t off = live ? (uint32_t)row * kRow + sub16 : kBufNone;
-      kv = bld16(rk, off);
-      vv = bld16(rv, live ? off + vdelta : kBufNone);
-    } else if (live) {
-      const size_t off = (size_t)(uint32_t)row * kRow;
-      kv = ld16(k + off);
-      vv = ld16(v + off);
-    } else {
-      kv = make_uint4(0u, 0u, 0u, 0u);
-      vv = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-};
-
-// Combines the online-softmax states of the RPB row groups of a workgroup and
-// writes either the final output row(s) or a split partial.
-template <typename T, int D, int RPB>
-__device__ __forceinline__ void combine_groups(float m, float l, const float* acc, int grp, int sub,
-                                               float* s_m, float* s_l, float* s_acc,
-                                               T* out_row, float* part_row) {
-  constexpr int VEC = Vec<T>::N;
-  if (sub == 0) {
-    s_m[grp] = m;
-    s_l[grp] = l;
-  }
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) s_acc[grp * D + sub * VEC + e] = acc[e];
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int g = 0; g < RPB; ++g) M = fmaxf(M, s_m[g]);
-  for (int t = threadIdx.x; t < D; t += kThreads) {
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int g = 0; g < RPB; ++g) {
-      const float w = (s_m[g] == -INFINITY) ? 0.f : __expf(s_m[g] - M);
-      num = fmaf(w, s_acc[g * D + t], num);
-      den = fmaf(w, s_l[g], den);
-    }
-    if (part_row != nullptr) {
-      part_row[t] = num;
-      if (t == 0) {
-        part_row[D] = M;
-        part_row[D + 1] = den;
-      }
-    } else {
-      store_elem(out_row, t, num / den);
-    }
-  }
-}
-
-// Online-softmax update of one row group with U scores and value slices.
-template <typename T, int U>
-__device__ __forceinline__ void online_update(float& m, float& l, float* acc, const float* s,
-                                              const uint4* vv) {
-  constexpr int VEC = Vec<T>::N;
-  float mloc = m;
-#pragma unroll
-  for (int u = 0; u < U; ++u) mloc = fmaxf(mloc, s[u]);
-  // Branch-free (a branch here lets the compiler sink the V loads into it,
-  // after the waits for K): with no finite score yet, the reference point is
-  // 0 and every weight below is exp(-inf) = 0, leaving the state unchanged.
-  const float mref = (mloc == -INFINITY) ? 0.f : mloc;
-  const float scale = __expf(m - mref);  // m = -inf gives 0
-  l *= scale;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] *= scale;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const float p = __expf(s[u] - mref);  // -inf scores give 0
-    l += p;
-    float v[VEC];
-    Vec<T>::widen(vv[u], v);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = fmaf(p, v[e], acc[e]);
-  }
-  m = mloc;
-}
-
-// Merge of S split partials (o unnormalised, m, l) of one head by the whole
-// workgroup: thread (column pair c, group g) folds partials g, g + NG, ... with
-// a running maximum (loads issued kSB at a time), then group 0 combines the NG
-// group results from LDS, in group order.  Block-uniform call (one barrier).
-template <typename T, int D>
-__device__ __forceinline__ void merge_partials(const float* part_head, int S, T* out_row) {
-  constexpr int NC = D / 2;           // column pairs (rows of D + 2 floats are 8-byte aligned)
-  constexpr int NG = kThreads / NC;   // partial groups
-  constexpr int kSB = 8;
-  __shared__ float s_M[NG], s_den[NG];
-  __shared__ float2 s_num[NG][NC];
-  const int c = threadIdx.x % NC, g = threadIdx.x / NC;
-  float M = -INFINITY, den = 0.f;
-  float2 num = make_float2(0.f, 0.f);
-  for (int s0 = g; s0 < S; s0 += NG * kSB) {
-    float2 ml[kSB], av[kSB];
-#pragma unroll
-    for (int j = 0; j < kSB; ++j) {
-      const int s = s0 + j * NG;
-      const float* r = part_head + (int64_t)min(s, S - 1) * (D + 2);
-      ml[j] = *reinterpret_cast<const float2*>(r + D);
-      av[j] = *reinterpret_cast<const float2*>(r + 2 * c);
-      if (s >= S) ml[j].x = -INFINITY;
-    }
-    float Mn = M;
-#pragma unroll
-    for (int j = 0; j < kSB; ++j) Mn = fmaxf(Mn, ml[j].x);
-    if (Mn == -INFINITY) continue;
-    const float rs = M == -INFINITY ? 0.f : __expf(M - Mn);
-    num.x *= rs;
-    num.y *= rs;
-    den *= rs;
-#pragma unroll
-    for (int j = 0; j < kSB; ++j) {
-      const float w = ml[j].x == -INFINITY ? 0.f : __expf(ml[j].x - Mn);
-      num.x = fmaf(w, av[j].x, num.x);
-      num.y = fmaf(w, av[j].y, num.y);
-      den = fmaf(w, ml[j].y, den);
-    }
-    M = Mn;
-  }
-  if (c == 0) {
-    s_M[g] = M;
-    s_den[g] = den;
-  }
-  s_num[g][c] = num;
-  __syncthreads();
-  if (g == 0) {
-    float Mt = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < NG; ++k) Mt = fmaxf(Mt, s_M[k]);
-    float nx = 0.f, ny = 0.f, dt = 0.f;
-#pragma unroll
-    for (int k = 0; k < NG; ++k) {
-      const float w = s_M[k] == -INFINITY ? 0.f : __expf(s_M[k] - Mt);
-      nx = fmaf(w, s_num[k][c].x, nx);
-      ny = fmaf(w, s_num[k][c].y, ny);
-      dt = fmaf(w, s_den[k], dt);
-    }
-    store_elem(out_row, 2 * c, nx / dt);
-    store_elem(out_row, 2 * c + 1, ny / dt);
-  }
-}
-
 // Split-KV merge as its own launch: one workgroup per query head (or per
 // dense head tile); the kernel boundary makes the partials visible without
 // device-wide fences.
@@ -397,17 +163,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, T* __restrict__ O,
     float* __restrict__ part, int64_t* __restrict__ plan, AttnArgs a) {
-  constexpr int VEC = Vec<T>::N;
-  constexpr int LPR = D / VEC;
-  constexpr int RPB = kThreads / LPR;
   constexpr int kE = kBalMaxHeads / kThreads;
   __shared__ int64_t s_pre[kBalMaxHeads + 1];
-  __shared__ int32_t s_ids[kIds];
-  __shared__ float s_m[RPB], s_l[RPB];
-  __shared__ float s_acc[RPB * D];
+  __shared__ SegSmem<T, D> sm;
   __shared__ uint64_t s_wtot[kWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int sub = tid % LPR, grp = tid / LPR;
   const int nh = (int)a.n_heads;
   const int E = (nh + kThreads - 1) / kThreads;
 
@@ -471,7 +231,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
 
   // 2. First head of the range.
   const int h0 = bal_first_head(s_pre, nh, lo);
-  const float inv = 1.0f / sqrtf((float)D);
 
   // 3. One segment per head overlapping the range.  Token positions and ids
   // fit in 31 bits (T < 2^31), so the index math is 32-bit; only the final
@@ -480,106 +239,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZHA_AT
     const int64_t P0 = s_pre[h], P1 = s_pre[h + 1];
     if (P1 <= lo || P1 == P0) continue;  // before the range, or a failed route (no tokens)
     const BalSegment seg = bal_segment(P0, P1, lo, hi);
-    const int x0 = seg.x0, x1 = seg.x1;
-    const int c = cnt[h];
-    const int32_t* ids = sel + (int64_t)h * a.cap;
-    const int64_t Th = visible_len(a, h);  // valid: the head has tokens
-    const int n1 = (int)(Th / a.C);
-    const bool sink = n1 > 0 && ((c == 0) || (ids[0] != 0));
-    const int hq = (int)(h % a.H_q);
-    const int64_t b = h / ((int64_t)a.n_pos * a.H_q);
-    const int64_t tr = b * a.H_kv + hq / a.G;
-    const KvBlock<T, D, BUF> kvb(K, V, tr, a.Tc, a.C, a.chunked, sub);
-    const uint4 qv = ld16c(Q + (int64_t)h * D + sub * VEC);
-    const int Cc = a.C, log2C = a.log2C;
-    const int ct = c * Cc;  // chunk tokens come first, then the extras
-    float m = -INFINITY, l = 0.f, acc[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-
-    for (int xr = x0; xr < x1;) {
-      // Stage the chunk ids this round needs (positions [xr, xe) of the list).
-      const int fc = xr < ct ? (log2C >= 0 ? (xr >> log2C) : xr / Cc) : 0;
-      const int xe = xr < ct ? (int)min((int64_t)x1, (int64_t)(fc + kIds) * Cc) : x1;
-      if (xr < ct) {
-        const int lc = (min(xe, ct) - 1) / Cc;  // last chunk touched
-        __syncthreads();
-        for (int i = tid; i <= lc - fc; i += kThreads) s_ids[i] = ids[fc + i];
-        __syncthreads();
-      }
-      // Each tensor's rows of the next batch are loaded as soon as its rows of
-      // the current batch have been read: K(i + 1) right after the scores of
-      // batch i, V(i + 1) right after its softmax update.  Past the round's
-      // end a batch loads nothing (slots without a row use out-of-range buffer
-      // offsets), so the loads stay unconditional and each wait counts exactly
-      // the loads issued after it.  The next batch's key rows (which need
-      // branches) are computed first, so the loads and the arithmetic form one
-      // straight-line block; the empty asm statements keep them in order.
-      auto rows_of = [&](int base, int (&row)[kUA]) {
-        // Chunk ids from LDS for every slot first (clamped in bounds, one wait).
-#pragma unroll
-        for (int u = 0; u < kUA; ++u) {
-          const int x = base + u * RPB + grp;
-          const int ci = POW2 ? (x >> log2C) : x / Cc;
-          row[u] = s_ids[min(max(ci - fc, 0), kIds - 1)];
-        }
-#pragma unroll
-        for (int u = 0; u < kUA; ++u) {
-          // Position x is token j of chunk `row` (a selected chunk), or an
-          // extra: the sink (chunk 0, token 0) or token e - sink of the
-          // partial chunk n1.
-          const int x = base + u * RPB + grp;
-          const int ci = POW2 ? (x >> log2C) : x / Cc;
-          const int e = x - ct;
-          const bool is_sink = sink && e == 0;
-          const int chunk = x < ct ? row[u] : (is_sink ? 0 : n1);
-          const int j = x < ct ? x - ci * Cc : (is_sink ? 0 : e - (sink ? 1 : 0));
-          row[u] = kvb.key_row(chunk, j);
-        }
-      };
-      constexpr int kStep = RPB * kUA;
-      int row[kUA];
-      uint4 kv[kUA], vv[kUA];
-      rows_of(xr, row);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kUA; ++u) kv[u] = kvb.load_k(row[u], xr + u * RPB + grp < xe);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kUA; ++u) vv[u] = kvb.load_v(row[u], xr + u * RPB + grp < xe);
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("" ::: "memory");
-      for (int base = xr; base < xe; base += kStep) {
-        const int nb = base + kStep;
-        rows_of(nb, row);
-        asm volatile("" ::: "memory");
-        float sc[kUA];
-#pragma unroll
-        for (int u = 0; u < kUA; ++u) {
-          const float dot = group_allreduce<LPR>(slice_dot<T>(kv[u], qv), OpAdd()) * inv;
-          sc[u] = (base + u * RPB + grp < xe) ? dot : -INFINITY;
-        }
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < kUA; ++u) kv[u] = kvb.load_k(row[u], nb + u * RPB + grp < xe);
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::: "memory");
-        online_update<T, kUA>(m, l, acc, sc, vv);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < kUA; ++u) vv[u] = kvb.load_v(row[u], nb + u * RPB + grp < xe);
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::: "memory");
-      }
-      xr = xe;
-    }
-    const bool whole = x0 == 0 && (int64_t)x1 == P1 - P0;
-    float* prow = whole ? nullptr : part + bal_slot(rng, h) * (D + 2);
-    combine_groups<T, D, RPB>(m, l, acc, grp, sub, s_m, s_l, s_acc, O + (int64_t)h * D, prow);
-    __syncthreads();
+    const bool whole = seg.x0 == 0 && (int64_t)seg.x1 == P1 - P0;
+    attend_segment<T, D, POW2, BUF>(Q, K, V, sel + (int64_t)h * a.cap, cnt[h], visible_len(a, h),
+                                    a, h, seg.x0, seg.x1, O + (int64_t)h * D,
+                                    whole ? nullptr : part + bal_slot(rng, h) * (D + 2), sm);
   }
 }
 

@@ -230,6 +230,21 @@ inline BuildScratch build_scratch_layout(const BuildArgs& a) {
   return s;
 }
 
+// Fused route + attention (zha_route_attn): calls of up to kFzMaxHeads query
+// heads with R = 1, a power-of-two C, p < 1 and K/V blocks under 2^31 bytes
+// run as one persistent launch of kFzGrid workgroups; a head's attended
+// tokens are cut into at most kFzMaxPieces pieces of at least kFzPieceTokens.
+// Scratch: zha_route's (device-memory frontier slots), then fp32 partials
+// (d + 2 each) for kFzMaxPieces pieces per head.
+constexpr int kFzMaxHeads = kBalMaxHeads;
+constexpr int kFzMaxPieces = 64;
+constexpr int kFzPieceTokens = 512;
+constexpr unsigned kFzGrid = 512;
+inline bool fused_eligible(int64_t n_heads, int R, int C, float p, int64_t kv_block_bytes) {
+  return n_heads <= kFzMaxHeads && R == 1 && (C & (C - 1)) == 0 && p < 1.0f &&
+         kv_block_bytes < ((int64_t)1 << 31);
+}
+
 // Launch entry points (defined in the .hip files).
 int build_dispatch(const BuildArgs& a, int dtype, int d, const void* K, const float* qref,
                    void* tree, void* scratch, hipStream_t s);
@@ -241,6 +256,10 @@ int attn_dispatch(const AttnArgs& a, int dtype, int d, const void* Q, const void
                   hipStream_t s);
 int dense_dispatch(const DenseArgs& a, int dtype, int d, const void* Q, const void* K,
                    const void* V, void* O, void* scratch, hipStream_t s);
+int fused_dispatch(const RouteArgs& ra, const AttnArgs& aa, int dtype, int d, const void* tree,
+                   const void* Q, const void* K, const void* V, int32_t* sel, int32_t* cnt,
+                   int32_t* stats, float* gap, void* O, char* ws, int64_t ws_stride, float* part,
+                   unsigned grid, uint32_t tag, hipStream_t s);
 
 // Dense decode on the matrix cores (bf16, d in {64, 128}): S waves per (KV
 // cache, 16 query rows), each taking whole 32-token steps; S makes about

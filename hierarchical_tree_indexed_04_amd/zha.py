@@ -59,6 +59,9 @@ SIGNATURES = {
     "zha_attn": (ctypes.c_int, [_GP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
     "zha_attn_noalloc": (ctypes.c_int, [_GP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP,
                                         _VP]),
+    "zha_route_attn_scratch_bytes": (ctypes.c_int, [_GP, _I32, _I32, _c_size_p]),
+    "zha_route_attn": (ctypes.c_int, [_GP, _VP, _VP, _I32, _VP, ctypes.c_float, _VP, _VP, _VP,
+                                      _VP, _I32, _VP, _VP, _VP, _VP, _VP]),
     "zha_dense_decode_scratch_bytes": (ctypes.c_int, [_GP, _I32, _c_size_p]),
     "zha_dense_decode": (ctypes.c_int, [_GP, _VP, _I32, _VP, _VP, _VP, _VP, _VP]),
 }
@@ -354,6 +357,41 @@ def attn_noalloc(g: Geom, Q, n_pos: int, K, V, sel, cnt, cap: int, O=None, strea
                                    _ptr(V), _ptr(sel), _ptr(cnt), cap, _ptr(O), _stream(stream)),
            "zha_attn_noalloc")
     return O
+
+
+def route_attn_scratch_bytes(g: Geom, n_pos: int, cap: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().zha_route_attn_scratch_bytes(ctypes.byref(g), n_pos, cap, ctypes.byref(n)),
+           "zha_route_attn_scratch_bytes")
+    return n.value
+
+
+def route_attn(g: Geom, tree, Q, n_pos: int, p: float, K, V, cap: int, want_stats=True,
+               want_gap=True, out=None, O=None, scratch=None, stream=None, ctx_len=None):
+    """zha_route_attn: returns (sel, cnt, level_stats or None, gap or None, O)."""
+    torch = _torch()
+    dt = _store_dtype(g)
+    _need(Q, (g.B, n_pos, g.H_q, g.d), dt, "Q")
+    _need_ctx(g, ctx_len, n_pos)
+    _need_kv(g, K, V)
+    dev = Q.device
+    if out is None:
+        sel = torch.empty((g.B, n_pos, g.H_q, cap), dtype=torch.int32, device=dev)
+        cnt = torch.empty((g.B, n_pos, g.H_q), dtype=torch.int32, device=dev)
+        stats = (torch.empty((g.B, n_pos, g.H_q, g.L, 2), dtype=torch.int32, device=dev)
+                 if want_stats else None)
+        gap = torch.empty((g.B, n_pos, g.H_q, g.L), dtype=torch.float32, device=dev) if want_gap else None
+    else:
+        sel, cnt, stats, gap = out
+    if O is None:
+        O = torch.empty((g.B, n_pos, g.H_q, g.d), dtype=dt, device=dev)
+    if scratch is None:
+        scratch = _bytes(route_attn_scratch_bytes(g, n_pos, cap), dev)
+    _check(load().zha_route_attn(ctypes.byref(g), _ptr(tree), _ptr(Q), n_pos, _ptr(ctx_len),
+                                 ctypes.c_float(p), _ptr(K), _ptr(V), _ptr(sel), _ptr(cnt), cap,
+                                 _ptr(stats), _ptr(gap), _ptr(O), _ptr(scratch), _stream(stream)),
+           "zha_route_attn")
+    return sel, cnt, stats, gap, O
 
 
 def dense_decode(g: Geom, Q, n_pos: int, K, V, O=None, scratch=None, stream=None):

@@ -295,6 +295,35 @@ int zha_attn(const zha_geom* g, const void* Q, int32_t n_pos, const int32_t* ctx
              const int32_t* sel, const int32_t* cnt, int32_t cap, void* O, void* scratch,
              void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Routing and attention in one call (the paper's App. D kernel inventory
+ * lists a "fusion" kernel beside routing and attention)
+ *
+ * zha_route followed by zha_attn, with the same arguments and results: sel,
+ * cnt, level_stats and gap as zha_route writes them (bit for bit), O as
+ * zha_attn computes it (the same tokens and arithmetic; split points differ,
+ * so fp32 summation order and hence the last bits may).  Calls of up to 2048
+ * query heads with R = 1, a power-of-two C, p < 1 and a KV cache of less than
+ * 2^31 bytes per (b, kvh) run as one launch in which a head's attention
+ * starts as soon as its route ends, while other heads are still routed;
+ * other calls run zha_route then zha_attn.  The single launch keeps its work
+ * queue and counters in device memory of the library (each call leaves them
+ * cleared), so calls of zha_route_attn that overlap in time on one device
+ * race, whatever their streams and scratch buffers.
+ * ------------------------------------------------------------------------- */
+
+/* Scratch of zha_route_attn: zha_route's, then room for the attention
+ * (partials of up to 64 pieces per query head, or zha_attn's scratch). */
+int zha_route_attn_scratch_bytes(const zha_geom* g, int32_t n_pos, int32_t cap, size_t* bytes);
+
+/*   tree, Q, ctx_len, p, sel, cnt, cap, level_stats, gap  as for zha_route
+ *   K, V, O                                               as for zha_attn
+ *   scratch  device, zha_route_attn_scratch_bytes() bytes */
+int zha_route_attn(const zha_geom* g, const void* tree, const void* Q, int32_t n_pos,
+                   const int32_t* ctx_len, float p, const void* K, const void* V, int32_t* sel,
+                   int32_t* cnt, int32_t cap, int32_t* level_stats, float* gap, void* O,
+                   void* scratch, void* stream);
+
 /* Size of the device buffer zha_attn_noalloc uses in place of a scratch
  * argument (the library holds one on each device it runs on). */
 #define ZHA_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)

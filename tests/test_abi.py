@@ -31,7 +31,7 @@ def g(**kw):
 def test_library_exports_every_declared_function():
     lib = Z.load()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(Z.SIGNATURES)
