@@ -399,7 +399,7 @@ template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(kBuildThreads) void merge_staged_kernel(
     const float* __restrict__ qref, char* __restrict__ tree, const double* __restrict__ cF,
     const double* __restrict__ cK, double* __restrict__ pF, double* __restrict__ pK,
-    BuildArgs a, int level) {
+    BuildArgs a, int level, bool skip_zero) {
   using G = LG<T, D>;
   extern __shared__ double lds[];  // [C R] F (padded to even), then [C R, D] k_hat
   const int sub = threadIdx.x % G::LPR, grp = threadIdx.x / G::LPR;
@@ -409,6 +409,8 @@ __global__ __launch_bounds__(kBuildThreads) void merge_staged_kernel(
   const int64_t tr = blockIdx.x / nn;
   const int64_t i = lo + (blockIdx.x - tr * nn);
   const int kvh = (int)(tr % a.H_kv);
+  // skip_zero: zero_stream3_kernel has written this level for zero references.
+  if (skip_zero && !kv_head_has_nonzero_reference(qref, a, kvh)) return;
   const int64_t child0 = tr * a.lay.ncap[level - 1] + i * C;
   const int nf = C * R;
   double* lF = lds;
@@ -652,42 +654,34 @@ void zero_fused_kernel(const T* __restrict__ K,
   zero_fused_body<T, D>(K, tree, pF, pK, a, PW, lds, blockIdx.x);
 }
 
-// Zero references and small chunks (C <= kStreamMaxC): one lane group per
-// complete level-2 node streams the C C key rows below it (kZeroBatch rows at
-// a time, the next batch in flight while one is summed), writes each leaf when
-// its C rows are in, and adds the leaf's fp64 k_hat into the parent's sum in
-// child order, which is merge_node's sum with every weight 1: no LDS, no
-// barrier, every lane group busy.  A lane group whose KV head has a nonzero
-// reference leaves it to fused_kernel.
+// True when some lane of this lane group sees a nonzero value among the R
+// references of KV head kvh (uniform over the group; no barrier).
 template <typename T, int D>
-#ifndef ZHA_STREAM_WAVES
-#define ZHA_STREAM_WAVES 1
-#endif
-__global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(ZHA_STREAM_WAVES)))
-void zero_stream_kernel(const T* __restrict__ K, const float* __restrict__ qref,
-                        char* __restrict__ tree, double* __restrict__ pF,
-                        double* __restrict__ pK, BuildArgs a) {
+__device__ __forceinline__ bool group_has_nonzero_reference(const float* __restrict__ qref,
+                                                            int R, int kvh, int sub) {
   using G = LG<T, D>;
-  constexpr int VEC = G::VEC;
-  const int sub = threadIdx.x % G::LPR;
+  bool nz = false;
+  const float* q = qref + (int64_t)kvh * R * D;
+  for (int x = sub; x < R * D; x += G::LPR) nz |= q[x] != 0.0f;
+  const uint64_t bal = __ballot(nz);
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t gm = (G::LPR == kWave) ? ~0ull
+                                        : (((1ull << G::LPR) - 1) << (lane & ~(G::LPR - 1)));
+  return (bal & gm) != 0;
+}
+
+// Zero references and small chunks (C <= kStreamMaxC): one lane group streams
+// the C C key rows below level-2 node p of tree tr (kZeroBatch rows at a time,
+// the next batch in flight while one is summed), writes each leaf when its C
+// rows are in, and adds the leaf's fp64 k_hat into the parent's sum in child
+// order, which is merge_node's sum with every weight 1; then writes the
+// level-2 node.  Returns its F, its fp64 k_hat slice in pacc.
+template <typename T, int D>
+__device__ __forceinline__ double zero_stream_node(const T* __restrict__ K, char* __restrict__ tree,
+                                                   const BuildArgs& a, int64_t tr, int64_t p,
+                                                   int sub, double (&pacc)[LG<T, D>::VEC]) {
+  constexpr int VEC = LG<T, D>::VEC;
   const int C = a.lay.C, R = a.lay.R;
-  const int64_t n2 = a.lay.n[2];
-  const int64_t node = (int64_t)blockIdx.x * G::NG + threadIdx.x / G::LPR;
-  if (node >= (int64_t)a.n_trees * n2) return;
-  const int64_t tr = node / n2;
-  const int64_t p = node - tr * n2;
-  const int kvh = (int)(tr % a.H_kv);
-  {
-    // This group's references (all R), any nonzero: not ours.
-    bool nz = false;
-    const float* q = qref + (int64_t)kvh * R * D;
-    for (int x = sub; x < R * D; x += G::LPR) nz |= q[x] != 0.0f;
-    const uint64_t bal = __ballot(nz);
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t gm = (G::LPR == kWave) ? ~0ull
-                                          : (((1ull << G::LPR) - 1) << (lane & ~(G::LPR - 1)));
-    if (bal & gm) return;
-  }
   const double Fleaf = 0.0 + log((double)C);
   T* khat1 = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
   float* bhat1 = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
@@ -696,7 +690,7 @@ void zero_stream_kernel(const T* __restrict__ K, const float* __restrict__ qref,
   // Load cursor: leaf lc, row lj (pointer lp); sum cursor: leaf cc, row cj.
   int lc = 0, lj = 0, cc = 0, cj = 0;
   const T* lp = kbase;
-  double acc[VEC], pacc[VEC];
+  double acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = pacc[e] = 0.0;
   auto load_batch = [&](uint4 (&buf)[kZeroBatch]) {
@@ -760,10 +754,104 @@ void zero_stream_kernel(const T* __restrict__ K, const float* __restrict__ qref,
     const int64_t row = p * R + r;
     store_khat<T, VEC>(khat2 + row * D, sub, pacc);
     if (sub == 0) bhat2[row] = (float)F;
-    if (pF != nullptr) {
+  }
+  return F;
+}
+
+// Level-2 nodes [p_lo, n_2) of every tree with zero references, one lane group
+// each (zero_stream_node), each with its fp64 copy for a later merge: no LDS,
+// no barrier, every lane group busy.  A lane group whose KV head has a nonzero
+// reference leaves it to fused_kernel.
+#ifndef ZHA_STREAM_WAVES
+#define ZHA_STREAM_WAVES 1
+#endif
+template <typename T, int D>
+__global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(ZHA_STREAM_WAVES)))
+void zero_stream_kernel(const T* __restrict__ K, const float* __restrict__ qref,
+                        char* __restrict__ tree, double* __restrict__ pF,
+                        double* __restrict__ pK, BuildArgs a, int64_t p_lo) {
+  using G = LG<T, D>;
+  constexpr int VEC = G::VEC;
+  const int sub = threadIdx.x % G::LPR;
+  const int R = a.lay.R;
+  const int64_t np = a.lay.n[2] - p_lo;
+  const int64_t node = (int64_t)blockIdx.x * G::NG + threadIdx.x / G::LPR;
+  if (node >= (int64_t)a.n_trees * np) return;
+  const int64_t tr = node / np;
+  const int64_t p = p_lo + (node - tr * np);
+  const int kvh = (int)(tr % a.H_kv);
+  if (group_has_nonzero_reference<T, D>(qref, R, kvh, sub)) return;
+  double pacc[VEC];
+  const double F = zero_stream_node<T, D>(K, tree, a, tr, p, sub, pacc);
+  if (pF != nullptr) {
+    for (int r = 0; r < R; ++r) {
       const int64_t prow = (tr * a.lay.ncap[2] + p) * R + r;
       store_f64_slice<VEC>(pK + prow * D + sub * VEC, pacc);
       if (sub == 0) pF[prow] = F;
+    }
+  }
+}
+
+// Complete level-3 subtrees with zero references, NG / C per workgroup: lane
+// group g streams child g % C of subtree g / C (zero_stream_node); the C
+// level-2 k_hat meet in LDS and the subtree's first lane group merges them,
+// children in order, with every weight exp(0) = 1 (merge_node's arithmetic,
+// so the bits of merge_staged_kernel), writing the level-3 node and its fp64
+// copy (pF3/pK3, NULL when level 3 is the top).  Level-2 nodes get no fp64
+// copy: no later merge reads them.  Lane groups of a KV head with a nonzero
+// reference only take part in the barrier.
+template <typename T, int D>
+__global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(ZHA_STREAM_WAVES)))
+void zero_stream3_kernel(const T* __restrict__ K, const float* __restrict__ qref,
+                         char* __restrict__ tree, double* __restrict__ pF3,
+                         double* __restrict__ pK3, BuildArgs a) {
+  using G = LG<T, D>;
+  constexpr int VEC = G::VEC;
+  __shared__ __align__(16) double s_k2[G::NG][D];
+  const int sub = threadIdx.x % G::LPR, grp = threadIdx.x / G::LPR;
+  const int C = a.lay.C, R = a.lay.R;
+  const int P3 = G::NG / C;  // subtrees per workgroup (the host keeps C <= NG)
+  const int64_t n3 = a.lay.n[3];
+  const int64_t s3 = (int64_t)blockIdx.x * P3 + grp / C;
+  bool mine = grp < P3 * C && s3 < (int64_t)a.n_trees * n3;
+  const int64_t tr = mine ? s3 / n3 : 0;
+  const int64_t i3 = s3 - tr * n3;
+  if (mine) mine = !group_has_nonzero_reference<T, D>(qref, R, (int)(tr % a.H_kv), sub);
+  double F2 = 0.0;
+  if (mine) {
+    double pacc[VEC];
+    F2 = zero_stream_node<T, D>(K, tree, a, tr, i3 * C + grp % C, sub, pacc);
+    store_f64_slice<VEC>(&s_k2[grp][sub * VEC], pacc);
+  }
+  __syncthreads();
+  if (!mine || grp % C != 0) return;
+  // merge_node at a zero reference: children of equal F2, m = F2, w = 1.
+  double m = -INFINITY;
+  for (int c = 0; c < C; ++c) m = fmax(m, F2);
+  double Z = 0.0, acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+  for (int c = 0; c < C; ++c) {
+    double kc[VEC];
+    load_f64_slice<VEC>(&s_k2[grp + c][sub * VEC], kc);
+    const double w = exp(F2 - m);
+    Z += w;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = fma(w, kc[e], acc[e]);
+  }
+  const double F = m + log(Z);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = acc[e] / Z;
+  T* khat3 = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[3]);
+  float* bhat3 = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[3]);
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = i3 * R + r;
+    store_khat<T, VEC>(khat3 + row * D, sub, acc);
+    if (sub == 0) bhat3[row] = (float)F;
+    if (pF3 != nullptr) {
+      const int64_t prow = (tr * a.lay.ncap[3] + i3) * R + r;
+      store_f64_slice<VEC>(pK3 + prow * D + sub * VEC, acc);
+      if (sub == 0) pF3[prow] = F;
     }
   }
 }
@@ -831,14 +919,28 @@ int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void
   const int PW = (L >= 2 && a.lo[1] == 0 && a.lo[2] == 0 && a.lay.n[2] > 0)
                      ? fused_parents<D>(C, R) : 0;
   int first_merge = 2;
+  const int64_t staged_lds = ((int64_t)fused_f_slots(C * R) + (int64_t)C * R * D) * 8;
+  // Zero references with small C: complete level-3 subtrees in one pass when
+  // the level-3 merge of the other KV heads can stage (it skips these heads).
+  const bool fold3 = PW > 0 && C <= kStreamMaxC && C <= G::NG && L >= 3 && a.lo[3] == 0 &&
+                     a.lay.n[3] > 0 && staged_lds <= kFusedLds;
   if (PW > 0) {
     const int64_t wpt = (a.lay.n[2] + PW - 1) / PW;
     const size_t lds = (size_t)fused_lds_bytes(PW, C, R, D);
     const int64_t items = a.n_trees * wpt;
     if (C <= kStreamMaxC) {
-      const int64_t groups = a.n_trees * a.lay.n[2];
-      zero_stream_kernel<T, D><<<(unsigned)((groups + G::NG - 1) / G::NG), kBuildThreads, 0, s>>>(
-          kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a);
+      int64_t p_lo = 0;
+      if (fold3) {
+        const int P3 = G::NG / C;
+        const int64_t subtrees = a.n_trees * a.lay.n[3];
+        zero_stream3_kernel<T, D><<<(unsigned)((subtrees + P3 - 1) / P3), kBuildThreads, 0, s>>>(
+            kp, qref, tp, L > 3 ? F(3) : nullptr, L > 3 ? Kp(3) : nullptr, a);
+        p_lo = a.lay.n[3] * C;  // level-2 nodes below no complete level-3 node
+      }
+      const int64_t groups = a.n_trees * (a.lay.n[2] - p_lo);
+      if (groups > 0)
+        zero_stream_kernel<T, D><<<(unsigned)((groups + G::NG - 1) / G::NG), kBuildThreads, 0, s>>>(
+            kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a, p_lo);
     } else {
       zero_fused_kernel<T, D><<<(unsigned)items, kBuildThreads,
                                 (size_t)PW * C * D * sizeof(double), s>>>(
@@ -852,13 +954,13 @@ int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void
     leaves(a.lo[1], a.lay.n[1]);
   }
   if (hipGetLastError() != hipSuccess) return ZHA_ERR_LAUNCH;
-  const int64_t staged_lds = ((int64_t)fused_f_slots(C * R) + (int64_t)C * R * D) * 8;
   for (int l = first_merge; l <= L; ++l) {
     if (a.lay.n[l] == a.lo[l]) continue;  // no span of this level completed
     const int64_t nodes = (int64_t)a.n_trees * (a.lay.n[l] - a.lo[l]);
     if (staged_lds <= kFusedLds) {
       merge_staged_kernel<T, D, ROPE><<<(unsigned)nodes, kBuildThreads, (size_t)staged_lds, s>>>(
-          qref, tp, F(l - 1), Kp(l - 1), l < L ? F(l) : nullptr, l < L ? Kp(l) : nullptr, a, l);
+          qref, tp, F(l - 1), Kp(l - 1), l < L ? F(l) : nullptr, l < L ? Kp(l) : nullptr, a, l,
+          fold3 && l == 3);
     } else {
       const unsigned blocks = (unsigned)((nodes + G::NG - 1) / G::NG);
       merge_kernel<T, D, ROPE><<<blocks, kBuildThreads, 0, s>>>(
