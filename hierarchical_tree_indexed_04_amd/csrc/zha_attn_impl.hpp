@@ -154,7 +154,7 @@ __device__ __forceinline__ int32_t ld_i32(const int32_t* p) {
 
 // Combines the online-softmax states of the RPB row groups of a workgroup and
 // writes either the final output row(s) or a split partial.
-template <typename T, int D, int RPB, bool COH = false>
+template <typename T, int D, int RPB, bool COH = false, int NT = kThreads>
 __device__ __forceinline__ void combine_groups(float m, float l, const float* acc, int grp, int sub,
                                                float* s_m, float* s_l, float* s_acc,
                                                T* out_row, float* part_row) {
@@ -169,7 +169,7 @@ __device__ __forceinline__ void combine_groups(float m, float l, const float* ac
   float M = -INFINITY;
 #pragma unroll
   for (int g = 0; g < RPB; ++g) M = fmaxf(M, s_m[g]);
-  for (int t = threadIdx.x; t < D; t += kThreads) {
+  for (int t = threadIdx.x; t < D; t += NT) {
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int g = 0; g < RPB; ++g) {
@@ -221,10 +221,10 @@ __device__ __forceinline__ void online_update(float& m, float& l, float* acc, co
 // workgroup: thread (column pair c, group g) folds partials g, g + NG, ... with
 // a running maximum (loads issued kSB at a time), then group 0 combines the NG
 // group results from LDS, in group order.  Block-uniform call (one barrier).
-template <typename T, int D, bool COH = false>
+template <typename T, int D, bool COH = false, int NT = kThreads>
 __device__ __forceinline__ void merge_partials(const float* part_head, int S, T* out_row) {
   constexpr int NC = D / 2;           // column pairs (rows of D + 2 floats are 8-byte aligned)
-  constexpr int NG = kThreads / NC;   // partial groups
+  constexpr int NG = NT / NC;         // partial groups
   constexpr int kSB = 8;
   __shared__ float s_M[NG], s_den[NG];
   __shared__ float2 s_num[NG][NC];
@@ -281,10 +281,10 @@ __device__ __forceinline__ void merge_partials(const float* part_head, int S, T*
   }
 }
 
-// LDS of attend_segment.
-template <typename T, int D>
+// LDS of attend_segment (NT threads per workgroup).
+template <typename T, int D, int NT = kThreads>
 struct SegSmem {
-  static constexpr int RPB = kThreads / (D / Vec<T>::N);
+  static constexpr int RPB = NT / (D / Vec<T>::N);
   int32_t ids[kIds];
   float m[RPB], l[RPB];
   float acc[RPB * D];
@@ -298,16 +298,16 @@ struct SegSmem {
 // per lane, LPR lanes per row, kUA rows in flight per lane, q . k with packed
 // bf16 dot products), keeps an online softmax per row group and combines the
 // row groups in LDS in a fixed order.
-template <typename T, int D, bool POW2, bool BUF, bool COH = false>
+template <typename T, int D, bool POW2, bool BUF, bool COH = false, int NT = kThreads>
 __device__ __forceinline__ void attend_segment(const T* __restrict__ Q, const T* __restrict__ K,
                                                const T* __restrict__ V,
                                                const int32_t* __restrict__ ids, int c, int64_t Th,
                                                const AttnArgs& a, int64_t h, int x0, int x1,
                                                T* __restrict__ out_row, float* prow,
-                                               SegSmem<T, D>& sm) {
+                                               SegSmem<T, D, NT>& sm) {
   constexpr int VEC = Vec<T>::N;
   constexpr int LPR = D / VEC;
-  constexpr int RPB = kThreads / LPR;
+  constexpr int RPB = NT / LPR;
   const int tid = threadIdx.x;
   const int sub = tid % LPR, grp = tid / LPR;
   const int n1 = (int)(Th / a.C);
@@ -331,7 +331,7 @@ __device__ __forceinline__ void attend_segment(const T* __restrict__ Q, const T*
     if (xr < ct) {
       const int lc = (min(xe, ct) - 1) / Cc;  // last chunk touched
       __syncthreads();
-      for (int i = tid; i <= lc - fc; i += kThreads) sm.ids[i] = ld_i32<COH>(ids + fc + i);
+      for (int i = tid; i <= lc - fc; i += NT) sm.ids[i] = ld_i32<COH>(ids + fc + i);
       __syncthreads();
     }
     // Each tensor's rows of the next batch are loaded as soon as its rows of
@@ -403,7 +403,7 @@ __device__ __forceinline__ void attend_segment(const T* __restrict__ Q, const T*
     }
     xr = xe;
   }
-  combine_groups<T, D, RPB, COH>(m, l, acc, grp, sub, sm.m, sm.l, sm.acc, out_row, prow);
+  combine_groups<T, D, RPB, COH, NT>(m, l, acc, grp, sub, sm.m, sm.l, sm.acc, out_row, prow);
   __syncthreads();
 }
 

@@ -7,7 +7,7 @@
 // are merged by a launch of their own.  Here one persistent launch does all:
 //
 //   1. Routing.  Workgroups claim query heads one at a time (a device counter)
-//      and route each with the router of zha_route (its 4-wave shape, the
+//      and route each with the router of zha_route (its 8-wave shape, the
 //      4096-candidate frontier in LDS, device-memory frontier past it).
 //   2. Publishing.  A routed head's attended tokens (the sink, its chunks'
 //      tokens, the partial chunk) are cut into np pieces of about
@@ -50,17 +50,18 @@ constexpr int kMaxChildren = 1024;  // C <= 1024
 // Device-memory frontier slots of this file's router (in use: 1).
 __device__ int32_t g_route_spill_lock[kRouteSpillBlocks];
 
-// The router in the 4-wave shape of zha_route's re-routing launch.
+// The router in the 8-wave shape of zha_route's latency launch; the
+// attention of a piece uses the same 512 threads.
+constexpr int kFzThreads = 512;
 namespace fz {
-constexpr int kThreads = 256;
+constexpr int kThreads = kFzThreads;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kU = 16;
+constexpr int kU = 8;
 constexpr int kFMax = kRouteFrontierMax;
 constexpr int kMinWavesEU = 1;
 constexpr bool kSpillInPlace = true;
 #include "zha_route_impl.inc"
 }  // namespace fz
-static_assert(fz::kThreads == kThreads, "router and attention share the workgroup size");
 
 // Control state of the fused launch.
 struct FzCtl {
@@ -102,11 +103,11 @@ __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F7
 template <typename T, int D>
 union FzSmem {
   fz::RouteSmem<fz::kFMax> route;
-  SegSmem<T, D> seg;
+  SegSmem<T, D, kFzThreads> seg;
 };
 
 template <typename T, int D, bool POW2>
-__global__ __launch_bounds__(kThreads) void route_attn_kernel(
+__global__ __launch_bounds__(kFzThreads) void route_attn_kernel(
     const char* __restrict__ tree, const T* __restrict__ Q, const T* __restrict__ K,
     const T* __restrict__ V, RouteArgs ra, AttnArgs aa, int32_t* __restrict__ sel,
     int32_t* __restrict__ cnt, int32_t* __restrict__ stats, float* __restrict__ gap,
@@ -145,10 +146,10 @@ __global__ __launch_bounds__(kThreads) void route_attn_kernel(
       // The chunk list, written by the router with plain stores, again with
       // device-coherent ones for the workgroups that attend the pieces.
       int32_t* ids = sel + (int64_t)h * cap;
-      for (int j = tid; j < c; j += kThreads) st_coh(ids + j, ids[j]);
+      for (int j = tid; j < c; j += kFzThreads) st_coh(ids + j, ids[j]);
     } else {
       // A failed or overflowed route attends nothing: its row is NaN.
-      for (int t = tid; t < D; t += kThreads)
+      for (int t = tid; t < D; t += kFzThreads)
         store_elem(O + (int64_t)h * D, t, __int_as_float(0x7fc00000));
     }
     if (tid == 0) {
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void route_attn_kernel(
     wait_stores();
     __syncthreads();
     const int base = (int)s_word;
-    for (int k = tid; k < np; k += kThreads)
+    for (int k = tid; k < np; k += kFzThreads)
       st_coh(&g_fz_item[base + k], ((uint64_t)tag << 32) | ((uint64_t)h << 16) | (uint32_t)k);
     wait_stores();
     __syncthreads();
@@ -215,8 +216,9 @@ __global__ __launch_bounds__(kThreads) void route_attn_kernel(
     const int P = (ntok + np - 1) / np;
     const int x0 = k * P, x1 = min(ntok, x0 + P);
     float* prow = np > 1 ? part + (int64_t)(base + k) * (D + 2) : nullptr;
-    attend_segment<T, D, POW2, true, true>(Q, K, V, sel + (int64_t)h * cap, c, Th, aa, h, x0, x1,
-                                           O + (int64_t)h * D, prow, sm.seg);
+    attend_segment<T, D, POW2, true, true, kFzThreads>(Q, K, V, sel + (int64_t)h * cap, c, Th, aa,
+                                                       h, x0, x1, O + (int64_t)h * D, prow,
+                                                       sm.seg);
     if (np > 1) {
       wait_stores();
       __syncthreads();
@@ -236,7 +238,8 @@ __global__ __launch_bounds__(kThreads) void route_attn_kernel(
       __syncthreads();  // s_word is reused
       if (last) {  // every other piece's partial is complete: merge in piece order
         if (tid == 0) st_coh(&g_fz_done[h], (uint64_t)0);
-        merge_partials<T, D, true>(part + (int64_t)base * (D + 2), np, O + (int64_t)h * D);
+        merge_partials<T, D, true, kFzThreads>(part + (int64_t)base * (D + 2), np,
+                                               O + (int64_t)h * D);
         __syncthreads();
       }
     }
@@ -265,10 +268,10 @@ int launch_fused(const RouteArgs& ra, const AttnArgs& aa, const void* tree, cons
   const T* v = reinterpret_cast<const T*>(V);
   T* o = reinterpret_cast<T*>(O);
   if (aa.log2C >= 0)
-    route_attn_kernel<T, D, true><<<grid, kThreads, 0, s>>>(tr, q, k, v, ra, aa, sel, cnt, stats,
+    route_attn_kernel<T, D, true><<<grid, kFzThreads, 0, s>>>(tr, q, k, v, ra, aa, sel, cnt, stats,
                                                             gap, o, ws, ws_stride, part, tag);
   else
-    route_attn_kernel<T, D, false><<<grid, kThreads, 0, s>>>(tr, q, k, v, ra, aa, sel, cnt, stats,
+    route_attn_kernel<T, D, false><<<grid, kFzThreads, 0, s>>>(tr, q, k, v, ra, aa, sel, cnt, stats,
                                                              gap, o, ws, ws_stride, part, tag);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_ERR_LAUNCH;
 }

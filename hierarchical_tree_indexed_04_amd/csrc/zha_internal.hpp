@@ -238,8 +238,8 @@ inline BuildScratch build_scratch_layout(const BuildArgs& a) {
 // (d + 2 each) for kFzMaxPieces pieces per head.
 constexpr int kFzMaxHeads = kBalMaxHeads;
 constexpr int kFzMaxPieces = 64;
-constexpr int kFzPieceTokens = 512;
-constexpr unsigned kFzGrid = 512;
+constexpr int kFzPieceTokens = 1024;
+constexpr unsigned kFzGrid = 256;
 inline bool fused_eligible(int64_t n_heads, int R, int C, float p, int64_t kv_block_bytes) {
   return n_heads <= kFzMaxHeads && R == 1 && (C & (C - 1)) == 0 && p < 1.0f &&
          kv_block_bytes < ((int64_t)1 << 31);
