@@ -289,7 +289,9 @@ __device__ __forceinline__ const T* chunk_keys(const T* K, const BuildArgs& a, i
          i * (int64_t)a.lay.C * (a.chunked ? 2 : 1) * D;
 }
 
-// Leaves [lo, hi) of every tree, one lane group per leaf.  sF/sK: fp64 copies
+// Leaves [lo, hi) of every tree, one lane group per (leaf, reference): the R
+// references of a leaf are independent summaries, so they run side by side in
+// adjacent lane groups (sharing the leaf's keys in cache).  sF/sK: fp64 copies
 // for later merges (NULL when the tree has one level).
 template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(kBuildThreads) void leaf_kernel(const T* __restrict__ K,
@@ -300,20 +302,22 @@ __global__ __launch_bounds__(kBuildThreads) void leaf_kernel(const T* __restrict
                                                              int64_t lo, int64_t hi) {
   using G = LG<T, D>;
   const int sub = threadIdx.x % G::LPR;
-  const int64_t node = (int64_t)blockIdx.x * G::NG + threadIdx.x / G::LPR;
+  const int C = a.lay.C, R = a.lay.R;
+  const int64_t item = (int64_t)blockIdx.x * G::NG + threadIdx.x / G::LPR;
   const int64_t nn = hi - lo;
   // Lane groups past the end still take part in the group reductions' lanes
   // of their own group only, so they can simply leave.
-  if (node >= (int64_t)a.n_trees * nn) return;
+  if (item >= (int64_t)a.n_trees * nn * R) return;
+  const int64_t node = item / R;
+  const int r = (int)(item - node * R);
   const int64_t tr = node / nn;
   const int64_t i = lo + (node - tr * nn);
   const int kvh = (int)(tr % a.H_kv);
-  const int C = a.lay.C, R = a.lay.R;
   const T* keys = chunk_keys<T, D>(K, a, tr, i);
   T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
   float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
   const double pos = (double)((i + 1) * C - 1);  // the chunk's last position
-  for (int r = 0; r < R; ++r) {
+  {
     double q[G::VEC], acc[G::VEC], b;
     node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, q);
     const bool qnz = group_nonzero<G::LPR, G::VEC>(q);
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(kBuildThreads) void leaf_kernel(const T* __restrict
 }
 
 // Parents [lo_level, n_level) of every tree from their children's fp64
-// copies, one lane group per parent.
+// copies, one lane group per (parent, reference), as leaf_kernel.
 template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(kBuildThreads) void merge_kernel(const float* __restrict__ qref,
                                                               char* __restrict__ tree,
@@ -341,21 +345,23 @@ __global__ __launch_bounds__(kBuildThreads) void merge_kernel(const float* __res
                                                               BuildArgs a, int level) {
   using G = LG<T, D>;
   const int sub = threadIdx.x % G::LPR;
+  const int C = a.lay.C, R = a.lay.R;
   const int64_t lo = a.lo[level];
   const int64_t nn = a.lay.n[level] - lo;  // nodes to merge per tree
-  const int64_t node = (int64_t)blockIdx.x * G::NG + threadIdx.x / G::LPR;
-  if (node >= (int64_t)a.n_trees * nn) return;
+  const int64_t item = (int64_t)blockIdx.x * G::NG + threadIdx.x / G::LPR;
+  if (item >= (int64_t)a.n_trees * nn * R) return;
+  const int64_t node = item / R;
+  const int r = (int)(item - node * R);
   const int64_t tr = node / nn;
   const int64_t i = lo + (node - tr * nn);
   const int kvh = (int)(tr % a.H_kv);
-  const int C = a.lay.C, R = a.lay.R;
   T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[level]);
   float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[level]);
   const int64_t child0 = tr * a.lay.ncap[level - 1] + i * C;  // first child's scratch row
   double span = 1.0;
   for (int l = 0; l < level; ++l) span *= C;
   const double pos = (double)(i + 1) * span - 1.0;  // the node's last position
-  for (int r = 0; r < R; ++r) {
+  {
     double qp[G::VEC], acc[G::VEC], b;
     node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, qp);
     const double f = merge_node<T, D, ROPE>(
@@ -908,8 +914,8 @@ int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void
   char* tp = reinterpret_cast<char*>(tree);
   auto leaves = [&](int64_t lo, int64_t hi) {
     if (hi <= lo) return;
-    const int64_t nodes = (int64_t)a.n_trees * (hi - lo);
-    const unsigned blocks = (unsigned)((nodes + G::NG - 1) / G::NG);
+    const int64_t items = (int64_t)a.n_trees * (hi - lo) * R;  // (leaf, reference) pairs
+    const unsigned blocks = (unsigned)((items + G::NG - 1) / G::NG);
     leaf_kernel<T, D, ROPE><<<blocks, kBuildThreads, 0, s>>>(
         kp, qref, tp, L > 1 ? F(1) : nullptr, L > 1 ? Kp(1) : nullptr, a, lo, hi);
   };
@@ -962,7 +968,7 @@ int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void
           qref, tp, F(l - 1), Kp(l - 1), l < L ? F(l) : nullptr, l < L ? Kp(l) : nullptr, a, l,
           fold3 && l == 3);
     } else {
-      const unsigned blocks = (unsigned)((nodes + G::NG - 1) / G::NG);
+      const unsigned blocks = (unsigned)((nodes * R + G::NG - 1) / G::NG);  // (parent, reference)
       merge_kernel<T, D, ROPE><<<blocks, kBuildThreads, 0, s>>>(
           qref, tp, F(l - 1), Kp(l - 1), l < L ? F(l) : nullptr, l < L ? Kp(l) : nullptr, a, l);
     }
