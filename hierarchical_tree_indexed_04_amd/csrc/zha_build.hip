@@ -462,10 +462,13 @@ template <typename T, int D, bool ROPE>
 __device__ __forceinline__ void fused_body(const T* __restrict__ K, const float* __restrict__ qref,
                                            char* __restrict__ tree, double* __restrict__ pF,
                                            double* __restrict__ pK, const BuildArgs& a, int PW,
-                                           double* lds, int64_t item) {
+                                           int RB, double* lds, int64_t item) {
   using G = LG<T, D>;
-  // lds: [LW * R] fp64 F (padded to an even count, so the k_hat rows stay
-  // 16-byte aligned), then [LW * R, D] fp64 k_hat; LW = PW C leaves.
+  // lds: [LW * RB] fp64 F (padded to an even count, so the k_hat rows stay
+  // 16-byte aligned), then [LW * RB, D] fp64 k_hat; LW = PW C leaves.  The R
+  // references go through in blocks of RB (all of them when they fit); within
+  // a block the lane groups take (leaf, reference) pairs, then (parent,
+  // reference) pairs: independent summaries, the same per-node arithmetic.
   const int sub = threadIdx.x % G::LPR, grp = threadIdx.x / G::LPR;
   const int C = a.lay.C, R = a.lay.R;
   const int64_t n2 = a.lay.n[2];
@@ -476,54 +479,54 @@ __device__ __forceinline__ void fused_body(const T* __restrict__ K, const float*
   const int nl = np * C;                          // leaves of this workgroup
   const int kvh = (int)(tr % a.H_kv);
   double* lF = lds;
-  double* lK = lds + fused_f_slots(PW * C * R);
-  {
-    T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
-    float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
-    for (int x = grp; x < nl; x += G::NG) {
+  double* lK = lds + fused_f_slots(PW * C * RB);
+  T* khat1 = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[1]);
+  float* bhat1 = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[1]);
+  T* khat2 = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[2]);
+  float* bhat2 = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[2]);
+  const double span = (double)C * (double)C;
+  for (int r0 = 0; r0 < R; r0 += RB) {
+    const int nr = min(RB, R - r0);
+    for (int w = grp; w < nl * nr; w += G::NG) {
+      const int x = w / nr, rr = w - x * nr, r = r0 + rr;
       const int64_t i = p0 * C + x;
       const T* keys = chunk_keys<T, D>(K, a, tr, i);
       const double pos = (double)((i + 1) * C - 1);
-      for (int r = 0; r < R; ++r) {
-        double q[G::VEC], acc[G::VEC], b;
-        node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, q);
-        const bool qnz = group_nonzero<G::LPR, G::VEC>(q);
-        const double f = leaf_node<T, D>(keys, C, sub, q, qnz, acc, b);
-        const int64_t row = i * R + r;
-        store_khat<T, G::VEC>(khat + row * D, sub, acc);
-        if (sub == 0) {
-          bhat[row] = (float)b;
-          lF[x * R + r] = ROPE ? b : f;
-        }
-        store_f64_slice<G::VEC>(lK + ((int64_t)x * R + r) * D + sub * G::VEC, acc);
+      double q[G::VEC], acc[G::VEC], b;
+      node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, q);
+      const bool qnz = group_nonzero<G::LPR, G::VEC>(q);
+      const double f = leaf_node<T, D>(keys, C, sub, q, qnz, acc, b);
+      const int64_t row = i * R + r;
+      store_khat<T, G::VEC>(khat1 + row * D, sub, acc);
+      if (sub == 0) {
+        bhat1[row] = (float)b;
+        lF[x * RB + rr] = ROPE ? b : f;
       }
+      store_f64_slice<G::VEC>(lK + ((int64_t)x * RB + rr) * D + sub * G::VEC, acc);
     }
-  }
-  __syncthreads();
-  T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[2]);
-  float* bhat = reinterpret_cast<float*>(tree + tr * a.lay.stride + a.lay.bhat[2]);
-  const double span = (double)C * (double)C;
-  for (int y = grp; y < np; y += G::NG) {
-    const int64_t i = p0 + y;
-    const double pos = (double)(i + 1) * span - 1.0;
-    for (int r = 0; r < R; ++r) {
+    __syncthreads();
+    for (int w = grp; w < np * nr; w += G::NG) {
+      const int y = w / nr, rr = w - y * nr, r = r0 + rr;
+      const int64_t i = p0 + y;
+      const double pos = (double)(i + 1) * span - 1.0;
       double qp[G::VEC], acc[G::VEC], b;
       node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, qp);
       const double f = merge_node<T, D, ROPE>(
-          C, qp, [&](int c) { return lF[(y * C + c) * R + r]; },
+          C, qp, [&](int c) { return lF[(y * C + c) * RB + rr]; },
           [&](int c, double (&k)[G::VEC]) {
-            load_f64_slice<G::VEC>(lK + ((int64_t)(y * C + c) * R + r) * D + sub * G::VEC, k);
+            load_f64_slice<G::VEC>(lK + ((int64_t)(y * C + c) * RB + rr) * D + sub * G::VEC, k);
           },
           acc, b);
       const int64_t row = i * R + r;
-      store_khat<T, G::VEC>(khat + row * D, sub, acc);
-      if (sub == 0) bhat[row] = (float)b;
+      store_khat<T, G::VEC>(khat2 + row * D, sub, acc);
+      if (sub == 0) bhat2[row] = (float)b;
       if (pF != nullptr) {
         const int64_t prow = (tr * a.lay.ncap[2] + i) * R + r;
         store_f64_slice<G::VEC>(pK + prow * D + sub * G::VEC, acc);
         if (sub == 0) pF[prow] = f;
       }
     }
+    if (r0 + RB < R) __syncthreads();  // lds is reused by the next block of references
   }
 }
 
@@ -872,7 +875,7 @@ __global__ __launch_bounds__(kBuildThreads) void fused_kernel(const T* __restric
                                                               char* __restrict__ tree,
                                                               double* __restrict__ pF,
                                                               double* __restrict__ pK,
-                                                              BuildArgs a, int PW) {
+                                                              BuildArgs a, int PW, int RB) {
   extern __shared__ double lds[];
   const int64_t wpt = (a.lay.n[2] + PW - 1) / PW;
   const int64_t items = (int64_t)a.n_trees * wpt;
@@ -886,7 +889,7 @@ __global__ __launch_bounds__(kBuildThreads) void fused_kernel(const T* __restric
     const int kvh = (int)((it / wpt) % a.H_kv);
     const bool nz = small ? ((mask >> kvh) & 1ull) != 0 : kv_head_has_nonzero_reference(qref, a, kvh);
     if (!nz) continue;
-    fused_body<T, D, ROPE>(K, qref, tree, pF, pK, a, PW, lds, it);
+    fused_body<T, D, ROPE>(K, qref, tree, pF, pK, a, PW, RB, lds, it);
     __syncthreads();  // lds is reused by the next item
   }
 }
@@ -900,6 +903,7 @@ int fused_parents(int C, int R) {
   while (pw > 1 && fused_lds_bytes(pw, C, R, D) > kFusedLds) pw >>= 1;
   return fused_lds_bytes(pw, C, R, D) <= kFusedLds ? pw : 0;
 }
+
 
 template <typename T, int D, bool ROPE>
 int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void* tree,
@@ -922,8 +926,13 @@ int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void
   // A full build takes every complete level-2 subtree in the fused kernel; the
   // leaves past them (no complete parent yet) go through leaf_kernel with
   // their fp64 copies kept for the merge that will complete them.
-  const int PW = (L >= 2 && a.lo[1] == 0 && a.lo[2] == 0 && a.lay.n[2] > 0)
-                     ? fused_parents<D>(C, R) : 0;
+  // Parents per workgroup of the complete level-2 subtree launches; 0 when
+  // one parent's leaves at all R references do not fit the LDS.  (Taking the
+  // references in blocks instead measured slower at R = 16, 21.4 -> 28.4 ms
+  // at 256K, than leaf_kernel and merge_kernel over (node, reference) pairs.)
+  const bool full = L >= 2 && a.lo[1] == 0 && a.lo[2] == 0 && a.lay.n[2] > 0;
+  const int PW = full ? fused_parents<D>(C, R) : 0;
+  const int RB = R;
   int first_merge = 2;
   const int64_t staged_lds = ((int64_t)fused_f_slots(C * R) + (int64_t)C * R * D) * 8;
   // Zero references with small C: complete level-3 subtrees in one pass when
@@ -932,7 +941,7 @@ int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void
                      a.lay.n[3] > 0 && staged_lds <= kFusedLds;
   if (PW > 0) {
     const int64_t wpt = (a.lay.n[2] + PW - 1) / PW;
-    const size_t lds = (size_t)fused_lds_bytes(PW, C, R, D);
+    const size_t lds = (size_t)fused_lds_bytes(PW, C, RB, D);
     const int64_t items = a.n_trees * wpt;
     if (C <= kStreamMaxC) {
       int64_t p_lo = 0;
@@ -953,7 +962,7 @@ int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void
           kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a, PW);
     }
     fused_kernel<T, D, ROPE><<<(unsigned)min(items, (int64_t)kFusedGrid), kBuildThreads, lds, s>>>(
-        kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a, PW);
+        kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a, PW, RB);
     leaves(a.lay.n[2] * C, a.lay.n[1]);
     first_merge = 3;
   } else {
