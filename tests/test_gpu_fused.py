@@ -193,3 +193,50 @@ def test_fused_entry_falls_back_to_separate_calls(Z, name, kw):
     say(f"zha_route_attn where the single launch does not apply ({name}): route, then attention")
     g = W.custom(f"f-fb-{name}", 174, **kw)
     run_fused(Z, g, range(3))
+
+
+@pytest.mark.parametrize("n_pos", [64, 65])
+def test_fused_at_the_head_limit(Z, n_pos):
+    """2048 query heads (64 positions x 32 heads: the most one launch takes, its
+    queue nearly full of pieces) and 2080 (past the limit: route, then
+    attention): routes bit for bit equal to zha_route's, outputs to zha_attn's
+    within the parity tolerance, and sampled positions against the oracle."""
+    import torch
+    g = W.custom("f-limit", 175, dtype=W.BF16, B=1, H_q=32, H_kv=4, T=8 ** 5 + 21, C=8, L=5,
+                 p=0.95)
+    say(f"zha_route_attn with {n_pos * g.H_q} query heads ({n_pos} positions x {g.H_q} heads)")
+    K, V = W.make_kv(g)
+    Qn = W.make_query_block(g, K, range(n_pos))
+    gm = Z.geom(g)
+    Kd, Vd, Qd = to_device(K, g.dtype), to_device(V, g.dtype), to_device(Qn, g.dtype)
+    tree = Z.build(gm, Kd, torch.zeros((g.H_kv, 1, g.d), device="cuda"))
+    cap = g.n_level(1)
+    s_sel, s_cnt, s_st, s_gap = Z.route(gm, tree, Qd, n_pos, g.p, cap)
+    s_O = Z.attn(gm, Qd, n_pos, Kd, Vd, s_sel, s_cnt, cap)
+    for rep in range(2):
+        sel, cnt, st, gap, Od = Z.route_attn(gm, tree, Qd, n_pos, g.p, Kd, Vd, cap)
+        torch.cuda.synchronize()
+        assert torch.equal(cnt.cpu(), s_cnt.cpu()) and torch.equal(st.cpu(), s_st.cpu())
+        assert torch.equal(gap.cpu(), s_gap.cpu())
+        ch, sh = cnt.cpu().numpy(), sel.cpu().numpy()
+        ssh = s_sel.cpu().numpy()
+        for idx in np.ndindex(ch.shape):
+            assert np.array_equal(sh[idx][:ch[idx]], ssh[idx][:ch[idx]]), idx
+        a, b = from_device(Od, g.dtype), from_device(s_O, g.dtype)
+        diff = float(np.abs(a - b).max())
+        say(f"  call {rep}: routes identical, max |O diff| vs separate calls {diff:.3g}")
+        assert diff <= TOL[g.dtype]
+    trees = oracle_trees(g, K, np.zeros((g.H_kv, 1, g.d)), [(0, kvh) for kvh in range(g.H_kv)])
+    sel, cnt, st, gap = sel.cpu().numpy(), cnt.cpu().numpy(), st.cpu().numpy(), gap.cpu().numpy()
+    par = Parity()
+    for kvh in range(g.H_kv):
+        Kf, Vf = W.to_float(K[0, kvh], g.dtype), W.to_float(V[0, kvh], g.dtype)
+        for t in (0, n_pos // 2, n_pos - 1):
+            for h in range(kvh * g.G, (kvh + 1) * g.G):
+                q = W.to_float(Qn[0, t, h], g.dtype)
+                r, o = O.zha_head(trees[(0, kvh)], q, Kf, Vf, g.p)
+                compare_head(par, r, sel[0, t, h], int(cnt[0, t, h]), st[0, t, h], a[0, t, h], o,
+                             TOL[g.dtype], (t, h), gap_row=gap[0, t, h],
+                             attend_set=attend_on(q, Kf, Vf, g.C, g.T))
+    say("  " + par.summary())
+    par.check()
