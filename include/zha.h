@@ -164,8 +164,11 @@ int zha_tree_level_offset(const zha_geom* g, int32_t level, size_t* khat_offset,
  *           summarised at its rotated references and children are re-anchored
  *           to the parent's (zha_rope above).  ZHA_ERR_ROPE if invalid.
  *   tree    device, zha_tree_bytes() bytes, written (the n_l valid rows)
- *   scratch device, build_scratch_bytes: receives the fp64 summaries of
- *           levels 1..L-1, which zha_tree_update reads (keep it with the tree)
+ *   scratch device, build_scratch_bytes: receives the fp64 summaries that a
+ *           later merge reads (the nodes of a level a separate merge launch
+ *           combines, and every node whose parent is not complete yet, which
+ *           zha_tree_update merges when it completes; a full build keeps the
+ *           fp64 of complete subtrees on chip), so keep it with the tree
  * Leaves: F = LSE_j(q_r . k_j / sqrt(d)), k_hat = softmax-weighted key mean,
  * b_hat = F - q_r . k_hat / sqrt(d).  Parents, per reference: F_P = LSE_c F_c,
  * k_hat_P = sum_c exp(F_c - F_P) k_hat_c.  Accumulation is fp64, so the stored
