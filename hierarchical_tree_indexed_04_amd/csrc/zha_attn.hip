@@ -364,6 +364,7 @@ constexpr int kBlkGroup = 32;  // tokens per MFMA step
 constexpr int kBlkGrid = ZHA_BLK_GRID;  // persistent workgroups of the attention launch (3 per CU)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct BlkPtrs {
@@ -767,7 +768,7 @@ __global__ __launch_bounds__(kLaneThreads) void blk_fill_kernel(const int32_t* _
 
 // Work items: (tile, block of up to kBlkQ of its entries), persistent loop.
 // Per 32-token step of the tile (skipped when no head of the block selected
-// any of its chunks): the K rows and the transposed V rows go to LDS; each
+// any of its chunks): the K and V rows go to LDS as they are; each
 // wave (16 heads) computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (so a
 // lane holds one head's scores for 8 tokens), masks the cells its heads did
 // not select, updates the online softmax and accumulates P V with the same
@@ -787,13 +788,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
   constexpr int NTD = D / 16;  // 16-column tiles of O
   constexpr int SEG = D / 8;   // 16-byte segments per row
   constexpr int KROW = D + 8;  // padded LDS row of K (bf16 elements)
-  constexpr int VTW = kBlkGroup / 2 + 1;  // LDS row of V^T in 32-bit words (token pairs), padded
+  // LDS row of V (bf16 elements), padded so that the 16 rows one transposed
+  // read touches start 8 banks apart.
+  constexpr int VROW = D + 16;
   BlkPtrs P(scr, L);
   __shared__ int32_t s_head[kBlkQ], s_slot[kBlkQ];
   __shared__ unsigned long long s_mask[kBlkQ];
   __shared__ unsigned long long s_union;
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kBlkGroup * KROW];
-  __shared__ uint32_t s_vt[D * VTW];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kBlkGroup * VROW];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const float inv = 1.0f / sqrtf((float)D);
@@ -882,18 +885,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
         kvb.load(kvb.key_row(tok >> lc, tok & (C - 1)), stager && tok < tok_end, pk[p], pv[p]);
       }
     };
-    // Stage: K rows as they are, V rows transposed (dimension-major).
+    // Stage: K and V rows as they are (token-major); the P V product reads V
+    // with LDS transposed loads.
     auto stage = [&](const uint4 (&pk)[2], const uint4 (&pv)[2]) {
       if (stager) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) *reinterpret_cast<uint4*>(&s_k[(2 * rp + p) * KROW + sg * 8]) = pk[p];
-        const uint32_t v0[4] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w};
-        const uint32_t v1[4] = {pv[1].x, pv[1].y, pv[1].z, pv[1].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int dim = sg * 8 + 2 * e;
-          s_vt[dim * VTW + rp] = (v0[e] & 0xffffu) | (v1[e] << 16);
-          s_vt[(dim + 1) * VTW + rp] = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
+        for (int p = 0; p < 2; ++p) {
+          *reinterpret_cast<uint4*>(&s_k[(2 * rp + p) * KROW + sg * 8]) = pk[p];
+          *reinterpret_cast<uint4*>(&s_v[(2 * rp + p) * VROW + sg * 8]) = pv[p];
         }
       }
     };
@@ -955,12 +954,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
         l_i += pj;
         pa[j] = (__bf16)pj;
       }
+      // B = V in the same token order: lane (li, lg) needs tokens 4 lg + (0..3)
+      // and 16 + 4 lg + (0..3) of column n * 16 + li.  ds_read_b64_tr_b16
+      // (gfx950, checked): in each group of 16 lanes, lane i receives element
+      // i % 4 of the 4 that lanes 4 k + i / 4 address, k = 0..3.  So lane
+      // (s, lg) addresses row 4 lg + s / 4 (+ 16 for the second half),
+      // columns n * 16 + 4 (s % 4) .. + 3.
+      const uint16_t* vsrc = &s_v[(4 * lg + (li >> 2)) * VROW + 4 * (li & 3)];
 #pragma unroll
       for (int n = 0; n < NTD; ++n) {
-        // B = V in the same token order: tokens 4 lg' + (0..3) and 16 + 4 lg' + (0..3)
-        // of column n * 16 + li.
-        const uint32_t* vr = &s_vt[(n * 16 + li) * VTW];
-        const uint4 w = make_uint4(vr[2 * lg], vr[2 * lg + 1], vr[8 + 2 * lg], vr[9 + 2 * lg]);
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vsrc + n * 16));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vsrc + 16 * VROW + n * 16));
+        const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+        const uint4 w = make_uint4(a.x, a.y, b.x, b.y);
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, w), o[n],
                                                        0, 0, 0);
       }
