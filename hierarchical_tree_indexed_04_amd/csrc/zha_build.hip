@@ -53,6 +53,7 @@ namespace {
 constexpr int kBuildThreads = 256;
 constexpr int kRowBatch = 4;              // key rows loaded before the first is used
 constexpr int kChildBatch = 4;            // fp64 child rows loaded before the first is used
+constexpr int kStageBatch = 8;            // 16-byte loads in flight per thread while staging children
 #ifndef ZHA_ZERO_BATCH
 #define ZHA_ZERO_BATCH 4
 #endif
@@ -422,11 +423,24 @@ __global__ __launch_bounds__(kBuildThreads) void merge_staged_kernel(
   double* lF = lds;
   double* lK = lds + fused_f_slots(nf);
   {
+    // Loads first, then the LDS writes: a loop that stored each load before
+    // the next would wait one memory round trip per iteration.
     const double2* src = reinterpret_cast<const double2*>(cK + child0 * R * D);
     double2* dst = reinterpret_cast<double2*>(lK);
     const int n2 = nf * D / 2;
-    for (int x = threadIdx.x; x < n2; x += kBuildThreads) dst[x] = src[x];
-    for (int x = threadIdx.x; x < nf; x += kBuildThreads) lF[x] = cF[child0 * R + x];
+    const int tid = threadIdx.x;
+    const double f0 = cF[child0 * R + min(tid, nf - 1)];
+    for (int x0 = tid; x0 < n2; x0 += kStageBatch * kBuildThreads) {
+      double2 v[kStageBatch];
+      // No branch: indexes past the end are clamped to the last element (its
+      // own value rewritten), so no load is moved down into a conditional store.
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) v[u] = src[min(x0 + u * kBuildThreads, n2 - 1)];
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) dst[min(x0 + u * kBuildThreads, n2 - 1)] = v[u];
+    }
+    if (tid < nf) lF[tid] = f0;
+    for (int x = tid + kBuildThreads; x < nf; x += kBuildThreads) lF[x] = cF[child0 * R + x];
   }
   __syncthreads();
   T* khat = reinterpret_cast<T*>(tree + tr * a.lay.stride + a.lay.khat[level]);
