@@ -776,6 +776,19 @@ __global__ __launch_bounds__(kLaneThreads) void blk_fill_kernel(const int32_t* _
 // scores already sit in registers.  Operand layouts (gfx950, checked):
 // A[i][k] in lane i + 16 (k / 8), element k % 8; B[k][j] in lane j + 16 (k / 8),
 // element k % 8; D[i][j] in lane j + 16 (i / 4), element i % 4.
+// First work item of workgroup b: blocks of kBlkXcdQ consecutive items (the
+// items of one tile are consecutive) go to one XCD, so a tile staged by
+// several items is read from HBM once and then from that XCD's L2; the blocks
+// are dealt round-robin over the XCDs, which keeps the load spread.
+#ifndef ZHA_BLK_XCD_Q
+#define ZHA_BLK_XCD_Q 8  // 1M block attention call: 1 -> 337, 2 -> 334, 4..32 -> 328-331 us
+#endif
+constexpr int kBlkXcdQ = ZHA_BLK_XCD_Q;
+__device__ __forceinline__ int blk_blocked_index(int b, int n) {
+  if (kBlkXcdQ <= 1 || n % (kXcds * kBlkXcdQ) != 0) return b;
+  const int x = b % kXcds, j = b / kXcds;
+  return ((j / kBlkXcdQ) * kXcds + x) * kBlkXcdQ + j % kBlkXcdQ;
+}
 #ifndef ZHA_BLK_WAVES_EU
 #define ZHA_BLK_WAVES_EU 3  // waves per SIMD the register budget is held to
 #endif
@@ -807,7 +820,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
   // workgroup indices are placed on one XCD so those re-reads meet in its L2
   // (prefill attention 21.9 -> 21.1 ms); with about one item per tile (the 1M
   // block) the default round-robin spreads the load better (350 against 370 us).
-  const int vb = total > 2 * L.NTT ? (int)xcd_major_index(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int vb = total > 2 * L.NTT ? (int)xcd_major_index(blockIdx.x, gridDim.x)
+                                    : blk_blocked_index((int)blockIdx.x, (int)gridDim.x);
   for (int w = vb; w < total; w += gridDim.x) {
     // Tile of work item w: the last tile u with wpre[u] <= w.
     int64_t lo = 0, hi = L.NTT;
