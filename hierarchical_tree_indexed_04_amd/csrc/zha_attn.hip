@@ -784,11 +784,6 @@ __global__ __launch_bounds__(kLaneThreads) void blk_fill_kernel(const int32_t* _
 #define ZHA_BLK_XCD_Q 8  // 1M block attention call: 1 -> 337, 2 -> 334, 4..32 -> 328-331 us
 #endif
 constexpr int kBlkXcdQ = ZHA_BLK_XCD_Q;
-__device__ __forceinline__ int blk_blocked_index(int b, int n) {
-  if (kBlkXcdQ <= 1 || n % (kXcds * kBlkXcdQ) != 0) return b;
-  const int x = b % kXcds, j = b / kXcds;
-  return ((j / kBlkXcdQ) * kXcds + x) * kBlkXcdQ + j % kBlkXcdQ;
-}
 #ifndef ZHA_BLK_WAVES_EU
 #define ZHA_BLK_WAVES_EU 3  // waves per SIMD the register budget is held to
 #endif
@@ -821,7 +816,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
   // (prefill attention 21.9 -> 21.1 ms); with about one item per tile (the 1M
   // block) the default round-robin spreads the load better (350 against 370 us).
   const int vb = total > 2 * L.NTT ? (int)xcd_major_index(blockIdx.x, gridDim.x)
-                                    : blk_blocked_index((int)blockIdx.x, (int)gridDim.x);
+                                    : xcd_blocked_index((int)blockIdx.x, (int)gridDim.x, kBlkXcdQ);
   for (int w = vb; w < total; w += gridDim.x) {
     // Tile of work item w: the last tile u with wpre[u] <= w.
     int64_t lo = 0, hi = L.NTT;

@@ -193,14 +193,6 @@ __device__ __forceinline__ double group_max64(double v) {
   return v;
 }
 
-// Workgroup i of a 1-D launch runs on XCD i % 8.  Returns the work index that
-// gives XCD x the contiguous range [x * n / 8, (x + 1) * n / 8) (exactly, for
-// n divisible by 8; otherwise the identity).
-constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_major_index(int64_t i, int64_t n) {
-  if (n % kXcds != 0) return i;
-  return (i % kXcds) * (n / kXcds) + i / kXcds;
-}
 
 // Order-preserving map float -> uint32 (ascending floats give ascending keys).
 __device__ __forceinline__ uint32_t ord_f32(float f) {

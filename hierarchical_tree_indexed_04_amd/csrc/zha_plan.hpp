@@ -16,6 +16,26 @@
 
 namespace zha {
 
+// Placement of work on the XCDs: workgroup b of a 1-D launch runs on XCD
+// b mod kXcds, and each XCD has an L2 of its own.
+constexpr int kXcds = 8;
+
+// The work index that gives XCD x the contiguous range [x n / 8, (x + 1) n / 8)
+// (exactly, for n divisible by 8; otherwise the identity).
+__host__ __device__ inline int64_t xcd_major_index(int64_t i, int64_t n) {
+  if (n % kXcds != 0) return i;
+  return (i % kXcds) * (n / kXcds) + i / kXcds;
+}
+
+// The work index of workgroup b when blocks of q consecutive indexes go to one
+// XCD and the blocks are dealt round-robin over the XCDs (a permutation of
+// [0, n) for n divisible by 8 q; otherwise the identity).
+__host__ __device__ inline int xcd_blocked_index(int b, int n, int q) {
+  if (q <= 1 || n % (kXcds * q) != 0) return b;
+  const int x = b % kXcds, j = b / kXcds;
+  return ((j / q) * kXcds + x) * q + j % q;
+}
+
 constexpr int kBalMaxHeads = 2048;  // balanced split-KV: per-head prefix held in LDS
 constexpr int kBalMinTokens = 64;   // smallest token range of a workgroup
 

@@ -4,8 +4,8 @@
 // on the CPU.  For each case: every position of every head lies in exactly
 // one range, a head's segments are consecutive and cover its list, the
 // ranges a head meets are exactly those of bal_head_span, and partial slots
-// are unique and inside the buffer.  Prints one line per case; exit status
-// 0 when all hold.
+// are unique and inside the buffer.  Also the placement of work indexes on
+// the XCDs.  Prints one line per case; exit status 0 when all hold.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -83,7 +83,52 @@ static void run_case(const char* name, const std::vector<Head>& heads, int C, in
               (long long)W, slots.size());
 }
 
+// Work placement (zha_plan.hpp): both maps are permutations of [0, n); where
+// they apply, xcd_major_index gives XCD x (workgroups b with b mod 8 = x) the
+// contiguous range [x n / 8, (x + 1) n / 8), and xcd_blocked_index puts each
+// block of q consecutive indexes on one XCD with every XCD holding n / 8.
+static void check_placement() {
+  const int ns[] = {7, 100, 256, 512, 768, 1024, 2048, 4096};
+  const int qs[] = {1, 2, 3, 4, 8, 16, 32};
+  for (int n : ns) {
+    std::vector<int> seen(n, 0);
+    for (int b = 0; b < n; ++b) {
+      const int64_t w = xcd_major_index(b, n);
+      CHECK(w >= 0 && w < n);
+      if (w >= 0 && w < n) ++seen[w];
+      if (n % kXcds == 0) CHECK(w / (n / kXcds) == b % kXcds);
+    }
+    for (int w = 0; w < n; ++w) CHECK(seen[w] == 1);
+    for (int q : qs) {
+      std::vector<int> owner(n, -1);
+      for (int b = 0; b < n; ++b) {
+        const int w = xcd_blocked_index(b, n, q);
+        CHECK(w >= 0 && w < n);
+        if (w >= 0 && w < n) {
+          CHECK(owner[w] == -1);
+          owner[w] = b;
+        }
+      }
+      const bool applies = q > 1 && n % (kXcds * q) == 0;
+      std::vector<int> per_xcd(kXcds, 0);
+      for (int w = 0; w < n; ++w) {
+        CHECK(owner[w] >= 0);
+        if (owner[w] < 0) continue;
+        ++per_xcd[owner[w] % kXcds];
+        if (!applies) CHECK(owner[w] == w);
+        if (applies && w + 1 < n && (w + 1) % q != 0)
+          CHECK(owner[w] % kXcds == owner[w + 1] % kXcds);
+      }
+      if (n % kXcds == 0)
+        for (int x = 0; x < kXcds; ++x) CHECK(per_xcd[x] == n / kXcds);
+    }
+  }
+  std::printf("work placement: xcd_major_index and xcd_blocked_index are permutations%s\n",
+              fails ? " (FAILED)" : "");
+}
+
 int main() {
+  check_placement();
   const int64_t T = ((int64_t)1 << 31) - 3;  // the largest geometry: T < 2^31
   // 2048 heads that keep every chunk (p = 1): ~2^42 positions in all.
   {
