@@ -229,14 +229,15 @@ def test_attention_on_random_chunk_sets(Z, chunked):
     assert worst <= TOL[g.dtype]
 
 
-@pytest.mark.parametrize("C,chunked", [(32, False), (16, True)])
-def test_block_attention_many_heads(Z, C, chunked):
+@pytest.mark.parametrize("C,chunked,d", [(32, False, 128), (16, True, 128), (32, False, 64)])
+def test_block_attention_many_heads(Z, C, chunked, d):
     import torch
-    say(f"block attention (4096 query heads, C = {C}, {'chunked' if chunked else 'split'} KV): "
-        "clustered and scattered chunk sets, sink, partial chunk, failed rows, heads past the "
-        "pair budget")
+    say(f"block attention (4096 query heads, C = {C}, d = {d}, "
+        f"{'chunked' if chunked else 'split'} KV): clustered and scattered chunk sets, sink, "
+        "partial chunk, failed rows, heads past the pair budget")
     T = C ** 3 + C * 5 + 7 if C == 32 else C ** 3 * 4 + C * 5 + 7
-    g = W.custom(f"blk{C}", 130 + C, dtype=W.BF16, B=1, H_q=8, H_kv=1, T=T, C=C, L=2, p=0.95)
+    g = W.custom(f"blk{C}-{d}", 130 + C + (d if d != 128 else 0), dtype=W.BF16, B=1, H_q=8,
+                 H_kv=1, d=d, T=T, C=C, L=2, p=0.95)
     K, V = W.make_kv(g)
     n_pos, n_heads = 512, 4096
     Qn = W.make_query_block(g, K, range(n_pos))
