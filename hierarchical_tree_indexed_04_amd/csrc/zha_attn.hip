@@ -778,8 +778,8 @@ __global__ __launch_bounds__(kLaneThreads) void blk_fill_kernel(const int32_t* _
 // element k % 8; D[i][j] in lane j + 16 (i / 4), element i % 4.
 // First work item of workgroup b: blocks of kBlkXcdQ consecutive items (the
 // items of one tile are consecutive) go to one XCD, so a tile staged by
-// several items is read from HBM once and then from that XCD's L2; the blocks
-// are dealt round-robin over the XCDs, which keeps the load spread.
+// several items can be found in that XCD's L2 after its first read; the
+// blocks are dealt round-robin over the XCDs, which keeps the load spread.
 #ifndef ZHA_BLK_XCD_Q
 #define ZHA_BLK_XCD_Q 8  // 1M block attention call: 1 -> 337, 2 -> 334, 4..32 -> 328-331 us
 #endif
@@ -965,8 +965,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
       }
       // B = V in the same token order: lane (li, lg) needs tokens 4 lg + (0..3)
       // and 16 + 4 lg + (0..3) of column n * 16 + li.  ds_read_b64_tr_b16
-      // (gfx950, checked): in each group of 16 lanes, lane i receives element
-      // i % 4 of the 4 that lanes 4 k + i / 4 address, k = 0..3.  So lane
+      // (gfx950, checked): each lane addresses 4 consecutive bf16 values, and
+      // lane i of each 16-lane group receives as its element k (k = 0..3) value
+      // i % 4 of those that lane 4 k + i / 4 of the group addresses.  So lane
       // (s, lg) addresses row 4 lg + s / 4 (+ 16 for the second half),
       // columns n * 16 + 4 (s % 4) .. + 3.
       const uint16_t* vsrc = &s_v[(4 * lg + (li >> 2)) * VROW + 4 * (li & 3)];
