@@ -46,9 +46,34 @@
 // cache grows.
 
 #include "zha_internal.hpp"
+#include "zha_wave.hpp"
 
 namespace zha {
 namespace {
+
+// Sum over aligned groups of W lanes (W = 8 .. 64), every lane of a group
+// receiving the same bits: the xor butterfly, steps W/2, ..., 2, 1.  Steps
+// inside a 16-lane DPP row are lane moves instead of LDS permutes: after the
+// steps above a step of o lanes, lane i's value depends only on i mod 2o, so
+// rotating the row by o (o = 8, 4) or the quad permutes (o = 2, 1) bring lane i
+// the value of lane i ^ o, and every addition has the butterfly's operands.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  return __longlong_as_double((long long)dpp_u64<CTRL>(u, u));
+}
+template <int W>
+__device__ __forceinline__ double group_sum_f64(double v) {
+#pragma unroll
+  for (int o = W / 2; o >= (W < 16 ? 1 : 16); o >>= 1) v += __shfl_xor(v, o, kWave);
+  if constexpr (W >= 16) {
+    v += dpp_f64<kDppRowRor8>(v);
+    v += dpp_f64<kDppRowRor4>(v);
+    v += dpp_f64<kDppQpXor2>(v);
+    v += dpp_f64<kDppQpXor1>(v);
+  }
+  return v;
+}
 
 constexpr int kBuildThreads = 256;
 constexpr int kRowBatch = 4;              // key rows loaded before the first is used
@@ -163,7 +188,7 @@ __device__ __forceinline__ double leaf_node(const T* __restrict__ keys, int C, i
       double part = 0.0;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) part = fma(q[e], k[e], part);
-      m = fmax(m, group_sum64<LPR>(part) * inv_sqrt_d);
+      m = fmax(m, group_sum_f64<LPR>(part) * inv_sqrt_d);
     }
   }
   // Second key read: weights exp(s - m), their sum and the weighted key sum.
@@ -180,7 +205,7 @@ __device__ __forceinline__ double leaf_node(const T* __restrict__ keys, int C, i
       double part = 0.0;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) part = fma(q[e], k[e], part);
-      const double w = exp(group_sum64<LPR>(part) * inv_sqrt_d - m);
+      const double w = exp(group_sum_f64<LPR>(part) * inv_sqrt_d - m);
       Z += w;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[e] = fma(w, k[e], acc[e]);
@@ -193,7 +218,7 @@ __device__ __forceinline__ double leaf_node(const T* __restrict__ keys, int C, i
     acc[e] = acc[e] / Z;
     part = fma(q[e], acc[e], part);
   }
-  b = F - group_sum64<LPR>(part) * inv_sqrt_d;
+  b = F - group_sum_f64<LPR>(part) * inv_sqrt_d;
   return F;
 }
 
@@ -214,7 +239,7 @@ __device__ __forceinline__ double merge_node(int C, const double (&qp)[LG<T, D>:
       double part = 0.0;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) part = fma(qp[e], kc[e], part);
-      f += group_sum64<LPR>(part) * inv_sqrt_d;
+      f += group_sum_f64<LPR>(part) * inv_sqrt_d;
     }
     return f;
   };
@@ -247,7 +272,7 @@ __device__ __forceinline__ double merge_node(int C, const double (&qp)[LG<T, D>:
     acc[e] = acc[e] / Z;
     part = fma(qp[e], acc[e], part);
   }
-  b = F - group_sum64<LPR>(part) * inv_sqrt_d;
+  b = F - group_sum_f64<LPR>(part) * inv_sqrt_d;
   return ROPE ? b : F;
 }
 
