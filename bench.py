@@ -202,7 +202,9 @@ def reference_queries(g, K):
     return W.make_qref(g, K)
 
 
-def run_gpu(g, K, V, steps, warmup, dense_steps):
+def run_gpu(g, K, V, steps, warmup, dense_steps, lean=False):
+    """The decode-step measurements of workload g.  lean: only the timed steps, the build and
+    dense decode (no cache-cold repeats, copy rate or tree-maintenance timings)."""
     import torch
 
     from hierarchical_tree_indexed_04_amd import zha as Z
@@ -324,7 +326,7 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     # its timing) evicts L2 and the memory-side cache; each call between two
     # events of its own.
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    n_cold = min(steps, 10)
+    n_cold = 0 if lean else min(steps, 10)
     evc = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_cold)]
     for j in range(n_cold):
         i = warmup + j
@@ -338,20 +340,23 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
     cold_route = np.array([e[0].elapsed_time(e[1]) for e in evc])
     cold_attn = np.array([e[2].elapsed_time(e[3]) for e in evc])
     cold_fused = np.array([e[4].elapsed_time(e[5]) for e in evc])
-    log(f"[bench] {n_cold} cold steps: route {cold_route.mean() * 1e3:.1f} us, "
-        f"attn {cold_attn.mean() * 1e3:.1f} us, zha_route_attn {cold_fused.mean() * 1e3:.1f} us "
-        f"per step")
-    # Streaming-copy bandwidth of this device (read + write bytes of a 1 GiB copy).
-    dst = torch.empty_like(flush)
-    dst.copy_(flush)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(5):
+    copy_gbs = None
+    if not lean:
+        log(f"[bench] {n_cold} cold steps: route {cold_route.mean() * 1e3:.1f} us, "
+            f"attn {cold_attn.mean() * 1e3:.1f} us, zha_route_attn "
+            f"{cold_fused.mean() * 1e3:.1f} us per step")
+        # Streaming-copy bandwidth of this device (read + write bytes of a 1 GiB copy).
+        dst = torch.empty_like(flush)
         dst.copy_(flush)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * 5 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del flush, dst, layers
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            dst.copy_(flush)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * 5 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del dst
+    del flush, layers
     torch.cuda.empty_cache()
 
     cnt_h = cnt.cpu().numpy()
@@ -386,12 +391,43 @@ def run_gpu(g, K, V, steps, warmup, dense_steps):
         torch.cuda.synchronize()
         dense_ms = d0.elapsed_time(d1) / dense_steps
         log(f"[bench] dense decode {dense_ms * 1e3:.1f} us per step")
-    maint = decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch)
+    maint = None if lean else decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch)
     return {"total_ms": total_ms, "fused_ms": fused_ms, "cold_fused_ms": cold_fused,
             "route_ms": route_ms, "attn_ms": attn_ms, "bytes": acc,
             "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap, "cold_route_ms": cold_route,
             "cold_attn_ms": cold_attn, "copy_gbs": copy_gbs, "maintenance": maint,
             "n_layers": n_layers}
+
+
+def run_decode_leg(cfg: int, warmup: int = 3, dense_steps: int = 2):
+    """One of the other decode workloads at its own size: every one of its decode steps timed
+    back to back (route + attention per step, the same calls as the headline), its tree build,
+    zha_route_attn over the same steps and dense decode of the same cache."""
+    g = W.CONFIGS[cfg]
+    t0 = time.perf_counter()
+    K, V = W.make_kv(g)
+    log(f"[bench] {g.name}: generated K, V ({2 * K.nbytes / 1e9:.2f} GB) in "
+        f"{time.perf_counter() - t0:.1f} s")
+    r = run_gpu(g, K, V, g.n_steps, warmup, dense_steps, lean=True)
+    del K, V
+    us = r["total_ms"] / g.n_steps * 1e3
+    by = r["bytes"]
+    union = by["attn_union"] + by["route"]
+    return {"workload": f"{g.name}: B={g.B}, H_q={g.H_q}/H_kv={g.H_kv}, d={g.d}, T={g.T}, "
+                        f"C={g.C}, L={g.L}, p={g.p}, {g.dtype}, {g.n_steps} decode steps",
+            "steps": g.n_steps,
+            "queries_per_s": g.B / (us * 1e-6),
+            "us_per_step": us,
+            "route_us": float(r["route_ms"].mean() * 1e3),
+            "attn_us": float(r["attn_ms"].mean() * 1e3),
+            "route_attn_us_per_step": r["fused_ms"] / g.n_steps * 1e3,
+            "build_ms": r["build_ms"],
+            "step_bytes_union": union,
+            "step_hbm_frac": union / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "tokens_per_head": by["tokens_per_head"],
+            "dense_us_per_step": r["dense_ms"] * 1e3 if r["dense_ms"] else None,
+            "speedup_vs_dense": (r["dense_ms"] * 1e3 / us) if r["dense_ms"] else None,
+            "n_layers": r["n_layers"]}
 
 
 def decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch, reps: int = 200):
@@ -749,6 +785,9 @@ def main():
                          "reference; R > 1 draws them like queries)")
     ap.add_argument("--with-1m", type=int, default=1,
                     help="also time the 1M-context block workload (2048 positions routed at once)")
+    ap.add_argument("--with-configs", type=int, default=1,
+                    help="also time the other decode workloads (4K fp32, 128K GQA, 16.7M) at "
+                         "their own sizes and step counts")
     ap.add_argument("--crossover", action="store_true",
                     help="only run the context-length sweep of ZHA against dense decode")
     ap.add_argument("--prefill", type=int, default=0, metavar="BLOCK",
@@ -872,6 +911,8 @@ def main():
         "dense_ms_per_step": r["dense_ms"],
         "speedup_vs_dense": (r["dense_ms"] / ms_per_step) if r["dense_ms"] else None,
         "at_1m": run_block_1m() if args.with_1m else None,
+        "other_decode": ({W.CONFIGS[c].name: run_decode_leg(c) for c in (1, 2, 5)}
+                         if args.with_configs and args.config == 3 and args.refs == 0 else None),
     }
     print(json.dumps(out), flush=True)
 
