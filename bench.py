@@ -4,8 +4,12 @@
 A step is one decode step of the whole hot path over one batch: zha_route
 (top-down top-p routing of every query head through its tree) followed by
 zha_attn (exact attention over the routed tokens), on seeded synthetic inputs
-already resident in HBM.  The tree is built once before timing (its time is
-reported separately).  Default workload: deep-tree decode at 256K context,
+already resident in HBM.  The batch's sequences are independent, so the timed
+steps run it as two micro-batches (B/2 sequences each) on two streams, each a
+chain of zha_route then zha_attn per step: one half's latency-bound routing
+overlaps the other half's bandwidth-bound attention.  The same steps on one
+stream are reported beside it.  The tree is built once before timing (its time
+is reported separately).  Default workload: deep-tree decode at 256K context,
 B = 8 sequences, 32 query heads over 4 KV heads, d = 128, C = 8, L = 6,
 p = 0.95, bf16.
 
@@ -314,6 +318,65 @@ def run_gpu(g, K, V, steps, warmup, dense_steps, lean=False):
     timed_ids = range(warmup, warmup + steps)
     total_ms = timed([c for i in timed_ids for c in ((zr, args_r[i]), (za, args_a[i]))])
     fused_ms = timed([(zf, args_f[i]) for i in timed_ids])
+    # The same steps as two micro-batches, sequences [0, B/2) and [B/2, B), each
+    # a chain of zha_route then zha_attn per step on a stream of its own (both at
+    # the default priority): one half's routing, bound by its dependent levels,
+    # runs beside the other half's attention, bound by HBM.  The sequences are
+    # independent, so a decode loop can run them this way layer after layer; the
+    # routes are those of the full-batch calls, the outputs equal theirs up to
+    # fp32 summation order (the balanced split differs).
+    pipe_ms = None
+    if g.B >= 2 and g.B % 2 == 0:
+        hb = g.B // 2
+        gmh = Z.geom(W.replace(g, B=hb))
+        tbh, _ = Z.tree_bytes(gmh)
+        if 2 * tbh != tb:
+            raise RuntimeError("half-batch tree layout does not split the full one")
+        seq_kv = Kd[0].numel() * Kd.element_size()
+        s_half = [torch.cuda.current_stream(), torch.cuda.Stream()]
+        scr = [(torch.empty(max(Z.route_scratch_bytes(gmh, 1, cap), 1), dtype=torch.uint8,
+                            device="cuda"),
+                torch.zeros(max(Z.attn_scratch_bytes(gmh, 1, cap), 1), dtype=torch.uint8,
+                            device="cuda")) for _ in range(2)]
+        gref_h = ctypes.byref(gmh)
+        half_calls = []
+        for i in range(n):
+            k, v, t = layers[i % n_layers]
+            for h in range(2):
+                o = h * hb
+                st = vp(s_half[h].cuda_stream)
+                half_calls.append((
+                    (zr, (gref_h, vp(t.data_ptr() + h * tbh), vp(Qd[i, o].data_ptr()), 1, None,
+                          ctypes.c_float(g.p), vp(sel[i, o].data_ptr()), vp(cnt[i, o].data_ptr()),
+                          cap, vp(stats[i, o].data_ptr()), None, vp(scr[h][0].data_ptr()), st)),
+                    (za, (gref_h, vp(Qd[i, o].data_ptr()), 1, None,
+                          vp(k.data_ptr() + o * seq_kv), vp(v.data_ptr() + o * seq_kv),
+                          vp(sel[i, o].data_ptr()), vp(cnt[i, o].data_ptr()), cap,
+                          vp(O[i, o].data_ptr()), vp(scr[h][1].data_ptr()), st))))
+
+        def run_half(ids):
+            for i in ids:
+                for h in range(2):
+                    for fn, a in half_calls[2 * i + h]:
+                        if fn(*a) != 0:
+                            raise RuntimeError("launch failed")
+
+        run_half(range(warmup))
+        torch.cuda.synchronize()
+        p0 = torch.cuda.Event(enable_timing=True)
+        p_end = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        device_wait(torch)
+        p0.record(s_half[0])
+        s_half[1].wait_event(p0)
+        run_half(timed_ids)
+        for h in range(2):
+            p_end[h].record(s_half[h])
+        torch.cuda.synchronize()
+        pipe_ms = max(p0.elapsed_time(e) for e in p_end)
+        log(f"[bench] {steps} steps as two micro-batches on two streams: "
+            f"{pipe_ms / steps * 1e3:.1f} us per step")
+        del scr
+
     # The split, each call kind timed back to back over the same steps (the
     # attention calls reuse the routes computed above).
     route_ms = np.full(steps, timed([(zr, args_r[i]) for i in timed_ids]) / steps)
@@ -392,7 +455,8 @@ def run_gpu(g, K, V, steps, warmup, dense_steps, lean=False):
         dense_ms = d0.elapsed_time(d1) / dense_steps
         log(f"[bench] dense decode {dense_ms * 1e3:.1f} us per step")
     maint = None if lean else decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch)
-    return {"total_ms": total_ms, "fused_ms": fused_ms, "cold_fused_ms": cold_fused,
+    return {"total_ms": total_ms, "fused_ms": fused_ms, "pipe_ms": pipe_ms,
+            "cold_fused_ms": cold_fused,
             "route_ms": route_ms, "attn_ms": attn_ms, "bytes": acc,
             "build_ms": build_ms, "dense_ms": dense_ms, "cap": cap, "cold_route_ms": cold_route,
             "cold_attn_ms": cold_attn, "copy_gbs": copy_gbs, "maintenance": maint,
@@ -525,6 +589,64 @@ def run_block_1m(reps: int = 3):
         tb_ms.append(e0.elapsed_time(e1))
         tr_ms.append(e1.elapsed_time(e2))
         ta_ms.append(e2.elapsed_time(e3))
+    # The same block as one call pair per KV head (8 query heads over 1 KV head
+    # each), the two pairs on two streams: the KV groups share nothing, so one
+    # group's routing (VALU-bound) and bookkeeping run beside the other group's
+    # attention (HBM-bound).  The queries are laid out per KV head beforehand
+    # (outside the timing); routes and outputs are those of the single call.
+    g1 = W.replace(g, H_q=g.G, H_kv=1)
+    gm1 = Z.geom(g1)
+    tb1, _ = Z.tree_bytes(gm1)
+    if tb1 * g.H_kv != tb:
+        raise RuntimeError("per-KV-head tree layout does not split the full one")
+    kv_head = Kd[0, 0].numel() * Kd.element_size()
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(g.H_kv - 1)]
+    per = []
+    for k in range(g.H_kv):
+        qk = Qd[:, :, k * g.G:(k + 1) * g.G].contiguous()
+        sk = torch.empty((g.B, n_pos, g.G, cap), dtype=torch.int32, device="cuda")
+        ck = torch.empty((g.B, n_pos, g.G), dtype=torch.int32, device="cuda")
+        ok = torch.empty((g.B, n_pos, g.G, g.d), dtype=Kd.dtype, device="cuda")
+        rk = torch.empty(max(Z.route_scratch_bytes(gm1, n_pos, cap), 1), dtype=torch.uint8,
+                         device="cuda")
+        ak = torch.empty(max(Z.attn_scratch_bytes(gm1, n_pos, cap), 1), dtype=torch.uint8,
+                         device="cuda")
+        per.append((qk, sk, ck, ok, rk, ak))
+    tree_k = [tree[k * tb1:(k + 1) * tb1] for k in range(g.H_kv)]
+    K_k = [Kd[:, k:k + 1] for k in range(g.H_kv)]
+    V_k = [Vd[:, k:k + 1] for k in range(g.H_kv)]
+
+    def split_once():
+        for k in range(g.H_kv):
+            qk, sk, ck, ok, rk, ak = per[k]
+            Z.route(gm1, tree_k[k], qk, n_pos, g.p, cap, out=(sk, ck, None, None), scratch=rk,
+                    stream=streams[k])
+            Z.attn(gm1, qk, n_pos, K_k[k], V_k[k], sk, ck, cap, O=ok, scratch=ak,
+                   stream=streams[k])
+
+    split_once()
+    torch.cuda.synchronize()
+    ts_ms = []
+    for _ in range(reps):
+        s0 = torch.cuda.Event(enable_timing=True)
+        s_end = [torch.cuda.Event(enable_timing=True) for _ in range(g.H_kv)]
+        device_wait(torch, 1000.0)  # covers the host's submission of the four calls
+        s0.record(streams[0])
+        for st in streams[1:]:
+            st.wait_event(s0)
+        split_once()
+        for k in range(g.H_kv):
+            s_end[k].record(streams[k])
+        torch.cuda.synchronize()
+        ts_ms.append(max(s0.elapsed_time(e) for e in s_end))
+    split_ms = float(np.median(ts_ms))
+    c_split = torch.cat([per[k][2] for k in range(g.H_kv)], dim=2)
+    o_split = torch.cat([per[k][3] for k in range(g.H_kv)], dim=2)
+    if not torch.equal(c_split, cnt) or float((o_split.float() - O.float()).abs().max()) > 2e-2:
+        raise RuntimeError("1M block: the per-KV-head calls disagree with the single call")
+    log(f"[bench] 1M block as one call pair per KV head on {g.H_kv} streams: "
+        f"{split_ms:.3f} ms (route + attn)")
+
     c = cnt.cpu().numpy()
     if (c < 0).any() or (c > cap).any():
         raise RuntimeError("1M block: a route overflowed")
@@ -546,13 +668,20 @@ def run_block_1m(reps: int = 3):
     log(f"[bench] 1M block: build {b_ms:.3f} ms, route {r_ms:.3f} ms, attn {a_ms:.3f} ms")
     return {"workload": f"{g.name}: B={g.B}, H_q={g.H_q}/H_kv={g.H_kv}, d={g.d}, T={g.T}, C={g.C}, "
                         f"L={g.L}, p={g.p}, {n_pos} positions per call",
-            "queries_per_s": n_pos / ((r_ms + a_ms) * 1e-3),
-            "queries_per_s_with_build": n_pos / ((b_ms + r_ms + a_ms) * 1e-3),
+            "schedule": f"one zha_route + zha_attn pair per KV head ({g.G} query heads each), "
+                        f"the {g.H_kv} pairs on {g.H_kv} streams",
+            "queries_per_s": n_pos / (split_ms * 1e-3),
+            "route_attn_ms": split_ms,
+            "queries_per_s_with_build": n_pos / ((b_ms + split_ms) * 1e-3),
+            "single_call": {"queries_per_s": n_pos / ((r_ms + a_ms) * 1e-3),
+                            "route_ms": r_ms, "attn_ms": a_ms,
+                            "hbm_frac_union": (union + route_union) / ((r_ms + a_ms) * 1e-3)
+                            / (HBM_PEAK_GBS * 1e9)},
             "build_ms": b_ms, "route_ms": r_ms, "attn_ms": a_ms,
             "bytes_union": union + route_union, "bytes_kv_union": union,
             "bytes_route_rows_per_head_sum": route_rows, "bytes_tree": tb,
             "bytes_per_head_sum": per_head + route_rows,
-            "hbm_frac_union": (union + route_union) / ((r_ms + a_ms) * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "hbm_frac_union": (union + route_union) / (split_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "how_union": "K/V rows of the chunks selected by any head of a KV group, plus the "
                          "summary rows touched (at most the tree's bytes)"}
 
@@ -834,9 +963,12 @@ def main():
             f"{one['value']:.2f} on one ({time.perf_counter() - t0:.1f} s)")
 
     r = run_gpu(g, K, V, args.steps, args.warmup, args.dense_steps)
-    ms_per_step = r["total_ms"] / args.steps
+    # The step: the batch as two micro-batches on two streams where it splits
+    # (run_gpu), else the full-batch calls on one stream.
+    step_ms = r["pipe_ms"] if r["pipe_ms"] is not None else r["total_ms"]
+    ms_per_step = step_ms / args.steps
     queries_per_step = g.B  # one query = one token position x all H_q heads
-    value = queries_per_step * args.steps / (r["total_ms"] / 1e3)
+    value = queries_per_step * args.steps / (step_ms / 1e3)
     by = r["bytes"]
     attn_us = float(r["attn_ms"].mean() * 1e3)
     route_us = float(r["route_ms"].mean() * 1e3)
@@ -863,9 +995,15 @@ def main():
                    "global_batch": g.B, "seq_len": g.T, "parallelism": "single GPU"},
         # The step as a whole: the bytes routing and attention must move (step_bytes)
         # over the timed step (zha_route then zha_attn, back to back, HIP events).
+        "step_schedule": ("two micro-batches of B/2 sequences on two streams, each zha_route "
+                          "then zha_attn per step" if r["pipe_ms"] is not None else
+                          "zha_route then zha_attn per step, one stream"),
+        "ms_per_step_one_stream": r["total_ms"] / args.steps,
+        "value_one_stream": g.B * args.steps / (r["total_ms"] / 1e3),
         "roofline": {"bound": "hbm",
-                     "kernel": "decode step: zha_route (lat::route_kernel) + zha_attn "
-                               "(attn_balanced_kernel + merge_balanced_kernel)",
+                     "kernel": "decode step (the step_schedule above): zha_route "
+                               "(lat::route_kernel) + zha_attn (attn_balanced_kernel + "
+                               "merge_balanced_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": tr["step_bytes"] if tr else None,
