@@ -146,6 +146,16 @@ const char* zha_strerror(int code);
  * summary of node i for reference r, rounded to nearest-even from the exact
  * value; b_hat is the matching bias rounded to fp32 (paper §III-A: t_r(q) =
  * q . k_hat_r / sqrt(d) + b_hat_r).
+ *
+ * tree_stride depends on Tc, C, L, R, d and the dtype only, never on B or
+ * H_kv, so the trees of consecutive sequences, or the tree of one KV head of
+ * one sequence, form the tree blob of a geometry with fewer sequences (or with
+ * H_kv = 1 and H_q = G), as the matching rows of the KV cache form its cache.
+ * Independent parts of a batch can therefore be routed and attended by calls
+ * of their own over pointers into the same tree, cache and Q (the Q rows of
+ * the part must be contiguous: consecutive sequences, or a KV head's G query
+ * heads laid out on their own), each with its own scratch, for example on
+ * separate streams; each call gives the routes of the full call exactly.
  * ------------------------------------------------------------------------- */
 
 /* Bytes of the tree blob and of the zha_build scratch buffer. */
