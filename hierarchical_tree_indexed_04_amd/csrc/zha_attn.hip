@@ -356,12 +356,24 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(
 // Each pair leaves a softmax partial; a merge launch combines the partials of
 // each head in tile order, so results do not depend on scheduling.
 // ===========================================================================
-constexpr int kBlkQ = 64;      // query heads per work item: 4 waves x 16 MFMA rows
+// Query heads per work item: 4 waves x NB blocks of 16 MFMA rows.  Each item
+// stages the selected chunks of its tile once, so a tile whose entries span
+// several items is staged several times; two blocks per wave halve the items
+// of a tile that holds more than 64 entries, and the K and V^T operands a wave
+// reads from LDS serve both of its blocks, but the registers of the second
+// block cost a wave per SIMD (3 -> 2).  Measured: causal prefill of 128K in
+// calls of 4096 positions (~256 heads per tile) attention 19.05 -> 17.83 ms
+// with two blocks; the 1M block (~16 heads per tile, 1,727 of 2,048 tiles in
+// one item of 64) 0.331 -> 0.343 ms.  A call takes two blocks when its heads
+// are at least kBlkNB2Heads per tile.
 constexpr int kBlkGroup = 32;  // tokens per MFMA step
-#ifndef ZHA_BLK_GRID
-#define ZHA_BLK_GRID 768
-#endif
-constexpr int kBlkGrid = ZHA_BLK_GRID;  // persistent workgroups of the attention launch (3 per CU)
+constexpr int kBlkNB2Heads = 64;
+template <int NB>
+struct BlkShape {
+  static constexpr int kQ = 64 * NB;                // query heads per work item
+  static constexpr int kWavesEU = NB > 1 ? 2 : 3;   // waves per SIMD the registers are held to
+  static constexpr int kGrid = 256 * kWavesEU;      // persistent workgroups (one per wave slot)
+};
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -684,7 +696,7 @@ __global__ __launch_bounds__(kLaneThreads) void blk_tcount_kernel(
 
 // Exclusive scans over the tiles: first entry and first work item of each
 // (one workgroup), and the number of work items.
-__global__ __launch_bounds__(1024) void blk_tscan_kernel(BlkLayout L, char* scr) {
+__global__ __launch_bounds__(1024) void blk_tscan_kernel(BlkLayout L, char* scr, int q) {
   BlkPtrs P(scr, L);
   __shared__ int64_t s_v[1024], s_w[1024];
   const int tid = threadIdx.x;
@@ -693,7 +705,7 @@ __global__ __launch_bounds__(1024) void blk_tscan_kernel(BlkLayout L, char* scr)
   int64_t sc = 0, sw = 0;
   for (int64_t i = i0; i < i1; ++i) {
     sc += P.tcnt[i];
-    sw += (P.tcnt[i] + kBlkQ - 1) / kBlkQ;
+    sw += (P.tcnt[i] + q - 1) / q;
   }
   s_v[tid] = sc;
   s_w[tid] = sw;
@@ -711,7 +723,7 @@ __global__ __launch_bounds__(1024) void blk_tscan_kernel(BlkLayout L, char* scr)
     P.toff[i] = (int32_t)rc;
     P.wpre[i] = (int32_t)rw;
     rc += P.tcnt[i];
-    rw += (P.tcnt[i] + kBlkQ - 1) / kBlkQ;
+    rw += (P.tcnt[i] + q - 1) / q;
   }
   if (tid == 1023) {
     P.toff[L.NTT] = (int32_t)s_v[1023];
@@ -766,7 +778,7 @@ __global__ __launch_bounds__(kLaneThreads) void blk_fill_kernel(const int32_t* _
             });
 }
 
-// Work items: (tile, block of up to kBlkQ of its entries), persistent loop.
+// Work items: (tile, block of up to kQ of its entries), persistent loop.
 // Per 32-token step of the tile (skipped when no head of the block selected
 // any of its chunks): the K and V rows go to LDS as they are; each
 // wave (16 heads) computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (so a
@@ -784,14 +796,13 @@ __global__ __launch_bounds__(kLaneThreads) void blk_fill_kernel(const int32_t* _
 #define ZHA_BLK_XCD_Q 8  // 1M block attention call: 1 -> 337, 2 -> 334, 4..32 -> 328-331 us
 #endif
 constexpr int kBlkXcdQ = ZHA_BLK_XCD_Q;
-#ifndef ZHA_BLK_WAVES_EU
-#define ZHA_BLK_WAVES_EU 3  // waves per SIMD the register budget is held to
-#endif
-template <int D, bool BUF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAVES_EU, ZHA_BLK_WAVES_EU))) void blk_attn_kernel(const bf16_t* __restrict__ Q,
+template <int D, bool BUF, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BlkShape<NB>::kWavesEU, BlkShape<NB>::kWavesEU))) void blk_attn_kernel(const bf16_t* __restrict__ Q,
                                                        const bf16_t* __restrict__ K,
                                                        const bf16_t* __restrict__ V, AttnArgs a,
                                                        BlkLayout L, char* scr) {
+  constexpr int kBlkNB = NB;
+  constexpr int kBlkQ = BlkShape<NB>::kQ;
   constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
   constexpr int NTD = D / 16;  // 16-column tiles of O
   constexpr int SEG = D / 8;   // 16-byte segments per row
@@ -852,20 +863,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
     const int tok_end = (int)min((int64_t)(chunk0 + L.CT) * C, a.T);
     const KvBlock<bf16_t, D, BUF> kvb(K, V, tr, a.Tc, C, a.chunked, tid % SEG);
 
-    // This lane's head (row li of the wave's 16): its Q slices as the B operand.
-    const int qi = wave * 16 + li;
-    const bool qvalid = qi < ne && s_head[qi] >= 0;  // empty entries have head -1, mask 0
-    const uint64_t qmask = s_mask[qi];
-    bf16x8_t qb[KS];
+    // This lane's heads (row li of each of the wave's kBlkNB blocks of 16):
+    // their Q slices as the B operands.
+    int qi[kBlkNB];
+    bool qvalid[kBlkNB];
+    uint64_t qmask[kBlkNB];
+    bf16x8_t qb[kBlkNB][KS];
+    f32x4_t o[kBlkNB][NTD];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (qvalid) v = ld16c(Q + (int64_t)s_head[qi] * D + ks * 32 + lg * 8);
-      qb[ks] = __builtin_bit_cast(bf16x8_t, v);
+    for (int nb = 0; nb < kBlkNB; ++nb) {
+      qi[nb] = (wave * kBlkNB + nb) * 16 + li;
+      qvalid[nb] = qi[nb] < ne && s_head[qi[nb]] >= 0;  // empty entries have head -1, mask 0
+      qmask[nb] = s_mask[qi[nb]];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (qvalid[nb]) v = ld16c(Q + (int64_t)s_head[qi[nb]] * D + ks * 32 + lg * 8);
+        qb[nb][ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) o[nb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    f32x4_t o[NTD];
-#pragma unroll
-    for (int n = 0; n < NTD; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // 32-token steps that some head of the block selected.
     // Staging thread (row pair rp, 16-byte segment sg) holds rows 2 rp, 2 rp + 1,
@@ -906,62 +924,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
       }
     };
     const float c2 = 1.4426950408889634f * inv;  // log2(e) / sqrt(d)
-    float m_i = -INFINITY, l_i = 0.f;  // m in raw score units; l summed per lane
+    float m_i[kBlkNB], l_i[kBlkNB];  // m in raw score units; l summed per lane
+#pragma unroll
+    for (int nb = 0; nb < kBlkNB; ++nb) {
+      m_i[nb] = -INFINITY;
+      l_i[nb] = 0.f;
+    }
     auto compute = [&](int g0) {
-      // S^T = K Q^T for the two 16-token halves of the step.
-      f32x4_t st[2];
+      // S^T = K Q^T for the two 16-token halves of the step; each K operand
+      // read from LDS serves every block of the wave.
+      f32x4_t st[kBlkNB][2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        st[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < kBlkNB; ++nb) st[nb][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[(nt * 16 + li) * KROW + ks * 32 + lg * 8]);
-          st[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qb[ks],
-                                                          st[nt], 0, 0, 0);
+#pragma unroll
+          for (int nb = 0; nb < kBlkNB; ++nb)
+            st[nb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv),
+                                                                qb[nb][ks], st[nb][nt], 0, 0, 0);
         }
       }
-      // Lane (li, lg) holds head li's scores for tokens nt * 16 + 4 lg + e.  A
-      // step starts on a chunk boundary (g0 is a multiple of 32 and C <= 64 is
-      // a power of two >= 8), so the lane's 4 tokens of each half share a
-      // chunk: two mask bits per lane, from one shift of the head's mask.
-      float x[8];
-      float mloc = -INFINITY;
+      // Lane (li, lg) holds head li's scores (of each block) for tokens
+      // nt * 16 + 4 lg + e.  A step starts on a chunk boundary (g0 is a
+      // multiple of 32 and C <= 64 is a power of two >= 8), so the lane's 4
+      // tokens of each half share a chunk: two mask bits per lane, from one
+      // shift of the head's mask.
       const int nvalid = tok_end - g0;
-      const uint32_t smask = qvalid ? (uint32_t)(qmask >> ((g0 >> lc) - chunk0)) : 0u;
+      bf16x8_t pa[kBlkNB];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const bool on = ((smask >> ((nt * 16 + 4 * lg) >> lc)) & 1u) != 0u;
+      for (int nb = 0; nb < kBlkNB; ++nb) {
+        float x[8];
+        float mloc = -INFINITY;
+        const uint32_t smask = qvalid[nb] ? (uint32_t)(qmask[nb] >> ((g0 >> lc) - chunk0)) : 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = nt * 16 + 4 * lg + e;
-          const float v = (on & (t < nvalid)) ? st[nt][e] : -INFINITY;
-          x[nt * 4 + e] = v;
-          mloc = fmaxf(mloc, v);
+        for (int nt = 0; nt < 2; ++nt) {
+          const bool on = ((smask >> ((nt * 16 + 4 * lg) >> lc)) & 1u) != 0u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = nt * 16 + 4 * lg + e;
+            const float v = (on & (t < nvalid)) ? st[nb][nt][e] : -INFINITY;
+            x[nt * 4 + e] = v;
+            mloc = fmaxf(mloc, v);
+          }
         }
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-      const float m_new = fmaxf(m_i, mloc);
-      if (__ballot(m_new != m_i) != 0ull) {  // some head's maximum moved: rescale
-        const float sc = m_i == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_i - m_new) * c2);
-        l_i *= sc;
-        // O rows 4 lg + e belong to heads 4 lg + e: rescale by their factors.
-        float sr[4];
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+        const float m_new = fmaxf(m_i[nb], mloc);
+        if (__ballot(m_new != m_i[nb]) != 0ull) {  // some head's maximum moved: rescale
+          const float sc = m_i[nb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_i[nb] - m_new) * c2);
+          l_i[nb] *= sc;
+          // O rows 4 lg + e belong to heads 4 lg + e: rescale by their factors.
+          float sr[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sr[e] = __shfl(sc, 4 * lg + e, kWave);
+          for (int e = 0; e < 4; ++e) sr[e] = __shfl(sc, 4 * lg + e, kWave);
 #pragma unroll
-        for (int n = 0; n < NTD; ++n)
+          for (int n = 0; n < NTD; ++n)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[n][e] *= sr[e];
-        m_i = m_new;
-      }
-      const float mc = m_i == -INFINITY ? 0.f : m_i * c2;
-      bf16x8_t pa;
+            for (int e = 0; e < 4; ++e) o[nb][n][e] *= sr[e];
+          m_i[nb] = m_new;
+        }
+        const float mc = m_i[nb] == -INFINITY ? 0.f : m_i[nb] * c2;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pj = __builtin_amdgcn_exp2f(fmaf(x[j], c2, -mc));
-        l_i += pj;
-        pa[j] = (__bf16)pj;
+        for (int j = 0; j < 8; ++j) {
+          const float pj = __builtin_amdgcn_exp2f(fmaf(x[j], c2, -mc));
+          l_i[nb] += pj;
+          pa[nb][j] = (__bf16)pj;
+        }
       }
       // B = V in the same token order: lane (li, lg) needs tokens 4 lg + (0..3)
       // and 16 + 4 lg + (0..3) of column n * 16 + li.  ds_read_b64_tr_b16
@@ -969,7 +1000,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
       // lane i of each 16-lane group receives as its element k (k = 0..3) value
       // i % 4 of those that lane 4 k + i / 4 of the group addresses.  So lane
       // (s, lg) addresses row 4 lg + s / 4 (+ 16 for the second half),
-      // columns n * 16 + 4 (s % 4) .. + 3.
+      // columns n * 16 + 4 (s % 4) .. + 3.  Each V^T operand serves every
+      // block of the wave.
       const uint16_t* vsrc = &s_v[(4 * lg + (li >> 2)) * VROW + 4 * (li & 3)];
 #pragma unroll
       for (int n = 0; n < NTD; ++n) {
@@ -979,11 +1011,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
             (__attribute__((address_space(3))) v4i16_t*)(vsrc + 16 * VROW + n * 16));
         const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
         const uint4 w = make_uint4(a.x, a.y, b.x, b.y);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, w), o[n],
-                                                       0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < kBlkNB; ++nb)
+          o[nb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[nb], __builtin_bit_cast(bf16x8_t, w),
+                                                             o[nb][n], 0, 0, 0);
       }
     };
-    const bool wave_live = wave * 16 < ne;
+    const bool wave_live = wave * kBlkNB * 16 < ne;
     int g0 = next_step(tok0);
     int g1 = next_step(g0 + kBlkGroup);
     fetch(ka, va, g0);
@@ -1007,23 +1041,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ZHA_BLK_WAV
       g0 = g1;
       g1 = g2;
     }
-    l_i += __shfl_xor(l_i, 16, kWave);
-    l_i += __shfl_xor(l_i, 32, kWave);
-    // Partials: O rows 4 lg + e (heads of the wave), columns n * 16 + li; m and l
-    // from the lanes of row group 0.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = wave * 16 + 4 * lg + e;
-      if (r < ne && s_slot[r] >= 0) {
-        float* pr = P.part + (int64_t)s_slot[r] * (D + 2);
+    for (int nb = 0; nb < kBlkNB; ++nb) {
+      float l = l_i[nb];
+      l += __shfl_xor(l, 16, kWave);
+      l += __shfl_xor(l, 32, kWave);
+      // Partials: O rows 4 lg + e (heads of the block), columns n * 16 + li;
+      // m and l from the lanes of row group 0.
 #pragma unroll
-        for (int n = 0; n < NTD; ++n) pr[n * 16 + li] = o[n][e];
+      for (int e = 0; e < 4; ++e) {
+        const int r = (wave * kBlkNB + nb) * 16 + 4 * lg + e;
+        if (r < ne && s_slot[r] >= 0) {
+          float* pr = P.part + (int64_t)s_slot[r] * (D + 2);
+#pragma unroll
+          for (int n = 0; n < NTD; ++n) pr[n * 16 + li] = o[nb][n][e];
+        }
       }
-    }
-    if (lg == 0 && qvalid) {
-      float* pr = P.part + (int64_t)s_slot[qi] * (D + 2);
-      pr[D] = m_i * inv;
-      pr[D + 1] = l_i;
+      if (lg == 0 && qvalid[nb]) {
+        float* pr = P.part + (int64_t)s_slot[qi[nb]] * (D + 2);
+        pr[D] = m_i[nb] * inv;
+        pr[D + 1] = l;
+      }
     }
   }
 }
@@ -1191,11 +1229,17 @@ int launch_blk(const AttnArgs& a, const void* Q, const void* K, const void* V, c
   blk_scan_kernel<<<(unsigned)((a.n_heads + kScanChunk - 1) / kScanChunk), 1024, 0, s>>>(
       a.n_heads, L, scr);
   blk_tcount_kernel<<<tree_blocks, kLaneThreads, 0, s>>>(sel, cnt, a, L, scr);
-  blk_tscan_kernel<<<1, 1024, 0, s>>>(L, scr);
+  const bool nb2 = a.n_heads >= (int64_t)kBlkNB2Heads * L.NTT;  // many heads per tile
+  blk_tscan_kernel<<<1, 1024, 0, s>>>(L, scr, nb2 ? BlkShape<2>::kQ : BlkShape<1>::kQ);
   blk_fill_kernel<<<tree_blocks, kLaneThreads, 0, s>>>(sel, cnt, a, L, scr);
-  blk_attn_kernel<D, BUF><<<kBlkGrid, 256, 0, s>>>(
-      reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K),
-      reinterpret_cast<const bf16_t*>(V), a, L, scr);
+  if (nb2)
+    blk_attn_kernel<D, BUF, 2><<<BlkShape<2>::kGrid, 256, 0, s>>>(
+        reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K),
+        reinterpret_cast<const bf16_t*>(V), a, L, scr);
+  else
+    blk_attn_kernel<D, BUF, 1><<<BlkShape<1>::kGrid, 256, 0, s>>>(
+        reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K),
+        reinterpret_cast<const bf16_t*>(V), a, L, scr);
   blk_merge_kernel<T, D, POW2, BUF><<<group_blocks, kThreads, 0, s>>>(
       reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K),
       reinterpret_cast<const T*>(V), sel, cnt, reinterpret_cast<T*>(O), a, L, scr);
