@@ -975,7 +975,8 @@ def main():
     step_union = by["attn_union"] + by["route"]
     achieved = step_union / (ms_per_step * 1e-3) / 1e9
     achieved_attn = by["attn_union"] / (attn_us * 1e-6) / 1e9
-    tr = measured_traffic()
+    # The committed counter record covers the default workload (256K, R = 1) only.
+    tr = measured_traffic() if args.config == 3 and args.refs == 0 else None
     out = {
         "metric": METRIC,
         "value": value,
