@@ -159,10 +159,12 @@ def step_bytes(g, sel, cnt, stats):
                 c = int(cnt[b, 0, h])
                 ch = sel[b, 0, h, :c]
                 ids.append(ch)
-                toks = c * g.C + tail + (0 if (c > 0 and ch[0] == 0) else 1)
+                # The sink is a token of its own unless chunk 0 is selected or,
+                # with no complete chunk, the partial chunk already holds it.
+                toks = c * g.C + tail + (0 if (n1 == 0 or (c > 0 and ch[0] == 0)) else 1)
                 attn_sum += toks * row_kv
             u = np.unique(np.concatenate(ids)) if ids else np.zeros(0, np.int32)
-            toks_u = u.size * g.C + tail + (0 if (u.size and u[0] == 0) else 1)
+            toks_u = u.size * g.C + tail + (0 if (n1 == 0 or (u.size and u[0] == 0)) else 1)
             attn_union += toks_u * row_kv
     per_head_io = heads * (2 * g.d * s) + int(cnt.sum()) * 4
     attn_union += per_head_io
