@@ -660,7 +660,10 @@ def run_block_1m(reps: int = 3):
         for h in range(kvh * g.G, (kvh + 1) * g.G):
             for t in range(n_pos):
                 mark[s_h[0, t, h, :c[0, t, h]]] = True
-        union += int(mark.sum()) * g.C * 2 * g.d * g.elem_bytes
+        # Tokens of the group's selected chunks, the partial chunk, and the sink
+        # where no head selected chunk 0.
+        toks = int(mark.sum()) * g.C + (g.T - n1 * g.C) + (0 if mark[0] else 1)
+        union += toks * 2 * g.d * g.elem_bytes
     per_head = int(c.sum()) * g.C * 2 * g.d * g.elem_bytes
     route_rows = int(stats.cpu().numpy()[..., 0].sum()) * (g.d * g.elem_bytes + 4)
     # Summary rows touched by some head: at most the whole tree (the heads'
@@ -684,8 +687,9 @@ def run_block_1m(reps: int = 3):
             "bytes_route_rows_per_head_sum": route_rows, "bytes_tree": tb,
             "bytes_per_head_sum": per_head + route_rows,
             "hbm_frac_union": (union + route_union) / (split_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-            "how_union": "K/V rows of the chunks selected by any head of a KV group, plus the "
-                         "summary rows touched (at most the tree's bytes)"}
+            "how_union": "K/V rows of the tokens any head of a KV group attends (its selected "
+                         "chunks, the partial chunk and the sink), plus the summary rows touched "
+                         "(at most the tree's bytes)"}
 
 
 CROSSOVER_T = [4096, 8192, 16384, 32768, 65536, 131072, 262144]
