@@ -546,9 +546,10 @@ def decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch, reps: int = 200):
 
 
 def run_block_1m(reps: int = 3):
-    """Secondary figure: the 1M-token cache with a block of 2048 new positions routed and attended
-    in one call each (16 query heads over 2 KV heads, C=32, L=4, p=0.95); the tree is built from
-    scratch on the cache.  Queries/s counts the 2048 positions."""
+    """Secondary figure: the 1M-token cache with a block of 2048 new positions (16 query heads
+    over 2 KV heads, C=32, L=4, p=0.95) routed and attended as one call pair per KV head on two
+    streams, and as one call pair for all heads; the tree is built from scratch on the cache.
+    Queries/s counts the 2048 positions."""
     import torch
 
     from hierarchical_tree_indexed_04_amd import zha as Z
