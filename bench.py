@@ -390,7 +390,7 @@ def run_gpu(g, K, V, steps, warmup, dense_steps, lean=False):
     # The same calls fully cache-cold: 1 GiB written before each call (outside
     # its timing) evicts L2 and the memory-side cache; each call between two
     # events of its own.
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = None if lean else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     n_cold = 0 if lean else min(steps, 10)
     evc = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_cold)]
     for j in range(n_cold):
