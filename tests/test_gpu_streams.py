@@ -10,7 +10,8 @@ per KV head).  Both schedules must give the full call's routes exactly and its
 outputs up to fp32 summation order (the attention's split-KV plan differs with
 the number of heads in a call).  The two halves run concurrently on two
 streams, so the test also checks that concurrent calls with separate scratch
-do not interfere.
+do not interfere, also when both route heads through device-memory frontier
+slots (their locks are shared by every call on the device).
 """
 import sys
 
@@ -134,3 +135,44 @@ def test_block_split_by_kv_head_on_two_streams_equals_the_single_call(Z):
     err = float((torch.cat([o[2] for o in outs], dim=2).float() - O.float()).abs().max())
     say(f"routes equal, max |O_split - O_single| = {err:.2e}")
     assert err <= 2e-2
+
+
+def test_concurrent_calls_with_device_memory_frontiers(Z):
+    # Weak queries at p = 0.99 keep nearly every candidate, so their level-1
+    # frontiers (n_1 = 4,802) outgrow the on-chip capacity and are routed again
+    # in device-memory frontier slots.  The slots' locks are one array per
+    # device, shared by every call; each call's slots are in its own scratch.
+    # Two calls of one sequence each, on two streams at once, must give the
+    # routes of the single two-sequence call.
+    import torch
+    g = W.custom("streams-spill", 312, dtype=W.BF16, B=2, H_q=4, H_kv=1, C=16, L=2,
+                 T=16 * 16 * 300 + 37, R=1, p=0.99)
+    n_pos = 3
+    say(f"concurrent spilling calls: n_1={g.n_level(1)}, {g.B} x {n_pos} x {g.H_q} query heads")
+    K, _ = W.make_kv(g, want_v=False)
+    Qn = W.make_query_block(g, K, range(n_pos))
+    rng = np.random.default_rng(312)
+    weak = rng.standard_normal((g.B, 2, g.H_q, g.d)).astype(np.float32) * np.float32(0.05)
+    Qn[:, [0, 2]] = W.f32_to_bf16_bits(weak)
+    gm = Z.geom(g)
+    Kd, Qd = to_device(K, g.dtype), to_device(Qn, g.dtype)
+    tree = Z.build(gm, Kd, torch.zeros((g.H_kv, 1, g.d), device="cuda"))
+    cap = g.n_level(1)
+    sel, cnt, stats, _ = Z.route(gm, tree, Qd, n_pos, g.p, cap, want_gap=False)
+    torch.cuda.synchronize()
+    assert int(stats[..., 0].max()) > Z.frontier_capacity(), "the case must spill"
+
+    g1 = Z.geom(W.replace(g, B=1))
+    tb1, _ = Z.tree_bytes(g1)
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    scr = [torch.empty(max(Z.route_scratch_bytes(g1, n_pos, cap), 1), dtype=torch.uint8,
+                       device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    outs = []
+    for b in range(2):
+        outs.append(Z.route(g1, tree[b * tb1:(b + 1) * tb1], Qd[b:b + 1], n_pos, g.p, cap,
+                            want_gap=False, scratch=scr[b], stream=streams[b]))
+    torch.cuda.synchronize()
+    _same_routes(sel, cnt, torch.cat([o[0] for o in outs]), torch.cat([o[1] for o in outs]))
+    assert torch.equal(stats, torch.cat([o[2] for o in outs]))
+    say("  routes of the concurrent one-sequence calls equal the two-sequence call")
