@@ -164,9 +164,9 @@ int zha_build(const zha_geom* g, const void* K, const float* qref, const zha_rop
   const int rr = set_rope(g, rope, a);
   if (rr) return rr;
   const bool need_scratch = build_scratch_layout(a).total > 0;
-  if (K == nullptr || qref == nullptr || tree == nullptr || (need_scratch && scratch == nullptr))
+  if (K == nullptr || tree == nullptr || (need_scratch && scratch == nullptr))
     return ZHA_ERR_NULL;
-  if (!aligned16(K) || !aligned16(qref) || !aligned16(tree) ||
+  if (!aligned16(K) || (qref != nullptr && !aligned16(qref)) || !aligned16(tree) ||
       (need_scratch && !aligned16(scratch)))
     return ZHA_ERR_ALIGN;
   return build_dispatch(a, g->dtype, g->d, K, qref, tree, scratch,
@@ -187,9 +187,9 @@ int zha_tree_update(const zha_geom* g, int64_t T_old, const void* K, const float
     a.lo[l] = T_old / span;  // nodes already summarised at the old length
   }
   const bool need_scratch = build_scratch_layout(a).total > 0;
-  if (K == nullptr || qref == nullptr || tree == nullptr || (need_scratch && scratch == nullptr))
+  if (K == nullptr || tree == nullptr || (need_scratch && scratch == nullptr))
     return ZHA_ERR_NULL;
-  if (!aligned16(K) || !aligned16(qref) || !aligned16(tree) ||
+  if (!aligned16(K) || (qref != nullptr && !aligned16(qref)) || !aligned16(tree) ||
       (need_scratch && !aligned16(scratch)))
     return ZHA_ERR_ALIGN;
   return build_dispatch(a, g->dtype, g->d, K, qref, tree, scratch,

@@ -96,6 +96,13 @@ struct LG {
 
 // This lane's dims of reference row qr for a node whose span ends at position
 // pos: rotated by pos * theta_j in the pairs (j, j + dims/2), or as given.
+// Reference r of KV head kvh ([H_kv, R, d] rows), or null when the caller
+// passed no references: every reference is then zero.
+__device__ __forceinline__ const float* ref_row(const float* __restrict__ qref, int kvh, int R,
+                                                int r, int D) {
+  return qref != nullptr ? qref + ((int64_t)kvh * R + r) * D : nullptr;
+}
+
 template <typename T, int D, bool ROPE>
 __device__ __forceinline__ void node_reference(const float* __restrict__ qr, int sub,
                                                const BuildArgs& a, double pos,
@@ -105,10 +112,10 @@ __device__ __forceinline__ void node_reference(const float* __restrict__ qr, int
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     const int k = sub * VEC + e;
-    double x = (double)qr[k];
+    double x = qr != nullptr ? (double)qr[k] : 0.0;
     if (ROPE && k < dims) {
       const int j = k < h ? k : k - h;
-      const double y = (double)qr[k < h ? k + h : k - h];
+      const double y = qr != nullptr ? (double)qr[k < h ? k + h : k - h] : 0.0;
       double sn, cs;
       sincos(pos * a.theta[j], &sn, &cs);
       x = k < h ? x * cs - y * sn : y * sn + x * cs;
@@ -345,7 +352,7 @@ __global__ __launch_bounds__(kBuildThreads) void leaf_kernel(const T* __restrict
   const double pos = (double)((i + 1) * C - 1);  // the chunk's last position
   {
     double q[G::VEC], acc[G::VEC], b;
-    node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, q);
+    node_reference<T, D, ROPE>(ref_row(qref, kvh, R, r, D), sub, a, pos, q);
     const bool qnz = group_nonzero<G::LPR, G::VEC>(q);
     const double f = leaf_node<T, D>(keys, C, sub, q, qnz, acc, b);
     const int64_t row = i * R + r;
@@ -389,7 +396,7 @@ __global__ __launch_bounds__(kBuildThreads) void merge_kernel(const float* __res
   const double pos = (double)(i + 1) * span - 1.0;  // the node's last position
   {
     double qp[G::VEC], acc[G::VEC], b;
-    node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, qp);
+    node_reference<T, D, ROPE>(ref_row(qref, kvh, R, r, D), sub, a, pos, qp);
     const double f = merge_node<T, D, ROPE>(
         C, qp, [&](int c) { return cF[(child0 + c) * R + r]; },
         [&](int c, double (&k)[G::VEC]) {
@@ -413,6 +420,7 @@ __host__ __device__ inline int fused_f_slots(int n) { return (n + 1) & ~1; }
 // entry?  (A rotation keeps a zero reference zero.)
 __device__ __forceinline__ bool kv_head_has_nonzero_reference(const float* __restrict__ qref,
                                                               const BuildArgs& a, int kvh) {
+  if (qref == nullptr) return false;  // no references given: all zero (uniform)
   const int n = a.lay.R * a.d;
   const float* q = qref + (int64_t)kvh * n;
   bool nz = false;
@@ -475,7 +483,7 @@ __global__ __launch_bounds__(kBuildThreads) void merge_staged_kernel(
   const double pos = (double)(i + 1) * span - 1.0;
   for (int r = grp; r < R; r += G::NG) {
     double qp[G::VEC], acc[G::VEC], b;
-    node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, qp);
+    node_reference<T, D, ROPE>(ref_row(qref, kvh, R, r, D), sub, a, pos, qp);
     const double f = merge_node<T, D, ROPE>(
         C, qp, [&](int c) { return lF[c * R + r]; },
         [&](int c, double (&k)[G::VEC]) {
@@ -532,7 +540,7 @@ __device__ __forceinline__ void fused_body(const T* __restrict__ K, const float*
       const T* keys = chunk_keys<T, D>(K, a, tr, i);
       const double pos = (double)((i + 1) * C - 1);
       double q[G::VEC], acc[G::VEC], b;
-      node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, q);
+      node_reference<T, D, ROPE>(ref_row(qref, kvh, R, r, D), sub, a, pos, q);
       const bool qnz = group_nonzero<G::LPR, G::VEC>(q);
       const double f = leaf_node<T, D>(keys, C, sub, q, qnz, acc, b);
       const int64_t row = i * R + r;
@@ -549,7 +557,7 @@ __device__ __forceinline__ void fused_body(const T* __restrict__ K, const float*
       const int64_t i = p0 + y;
       const double pos = (double)(i + 1) * span - 1.0;
       double qp[G::VEC], acc[G::VEC], b;
-      node_reference<T, D, ROPE>(qref + ((int64_t)kvh * R + r) * D, sub, a, pos, qp);
+      node_reference<T, D, ROPE>(ref_row(qref, kvh, R, r, D), sub, a, pos, qp);
       const double f = merge_node<T, D, ROPE>(
           C, qp, [&](int c) { return lF[(y * C + c) * RB + rr]; },
           [&](int c, double (&k)[G::VEC]) {
@@ -708,6 +716,7 @@ template <typename T, int D>
 __device__ __forceinline__ bool group_has_nonzero_reference(const float* __restrict__ qref,
                                                             int R, int kvh, int sub) {
   using G = LG<T, D>;
+  if (qref == nullptr) return false;  // no references given: all zero
   bool nz = false;
   const float* q = qref + (int64_t)kvh * R * D;
   for (int x = sub; x < R * D; x += G::LPR) nz |= q[x] != 0.0f;
@@ -1000,8 +1009,9 @@ int launch_build_impl(const BuildArgs& a, const void* K, const float* qref, void
                                 (size_t)PW * C * D * sizeof(double), s>>>(
           kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a, PW);
     }
-    fused_kernel<T, D, ROPE><<<(unsigned)min(items, (int64_t)kFusedGrid), kBuildThreads, lds, s>>>(
-        kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a, PW, RB);
+    if (qref != nullptr)  // without references every KV head took the zero-reference kernels
+      fused_kernel<T, D, ROPE><<<(unsigned)min(items, (int64_t)kFusedGrid), kBuildThreads, lds, s>>>(
+          kp, qref, tp, L > 2 ? F(2) : nullptr, L > 2 ? Kp(2) : nullptr, a, PW, RB);
     leaves(a.lay.n[2] * C, a.lay.n[1]);
     first_merge = 3;
   } else {

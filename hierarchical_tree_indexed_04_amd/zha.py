@@ -247,10 +247,12 @@ def _rope_ref(r):
 
 
 def build(g: Geom, K, qref, tree=None, scratch=None, stream=None, rope=None):
-    """zha_build; returns the tree blob (uint8 tensor).  rope: zha.rope(dims, theta) or None."""
+    """zha_build; returns the tree blob (uint8 tensor).  rope: zha.rope(dims, theta) or None.
+    qref None: every reference query is zero."""
     torch = _torch()
     _need(K, kv_shape(g), _store_dtype(g), "K")
-    _need(qref, (g.H_kv, g.R, g.d), torch.float32, "qref")
+    if qref is not None:
+        _need(qref, (g.H_kv, g.R, g.d), torch.float32, "qref")
     tb, sb = tree_bytes(g)
     if tree is None:
         tree = _bytes(tb, K.device)
@@ -263,10 +265,12 @@ def build(g: Geom, K, qref, tree=None, scratch=None, stream=None, rope=None):
 
 def tree_update(g: Geom, T_old: int, K, qref, tree, scratch, stream=None, rope=None):
     """zha_tree_update: extend a tree built for T_old tokens to g.T tokens in place.
-    ``tree`` and ``scratch`` are the buffers of the earlier build or update."""
+    ``tree`` and ``scratch`` are the buffers of the earlier build or update; qref None: every
+    reference query is zero."""
     torch = _torch()
     _need(K, kv_shape(g), _store_dtype(g), "K")
-    _need(qref, (g.H_kv, g.R, g.d), torch.float32, "qref")
+    if qref is not None:
+        _need(qref, (g.H_kv, g.R, g.d), torch.float32, "qref")
     tb, sb = tree_bytes(g)
     if tree.numel() * tree.element_size() < tb or (sb and scratch.numel() * scratch.element_size() < sb):
         raise ValueError("tree_update: tree or scratch smaller than the layout needs")

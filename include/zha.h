@@ -169,7 +169,9 @@ int zha_tree_level_offset(const zha_geom* g, int32_t level, size_t* khat_offset,
  *   K       device, the keys in g->kv_layout (split: [B, H_kv, T, d]; chunked:
  *           the KV buffer, of which only the key rows are read)
  *   qref    device [H_kv, R, d] fp32 reference queries (all zero gives the
- *           plain mean of each span's keys, with b_hat = ln(span))
+ *           plain mean of each span's keys, with b_hat = ln(span)), or NULL:
+ *           every reference is zero (the same trees, bit for bit, and the
+ *           build skips the kernels that serve nonzero references)
  *   rope    host, NULL (or dims 0) for shared references; else every node is
  *           summarised at its rotated references and children are re-anchored
  *           to the parent's (zha_rope above).  ZHA_ERR_ROPE if invalid.
