@@ -224,7 +224,8 @@ def run_gpu(g, K, V, steps, warmup, dense_steps, lean=False):
     t0 = time.perf_counter()
     Kd, Vd = to_dev(torch, K, g.dtype), to_dev(torch, V, g.dtype)
     Qd = to_dev(torch, Qs, g.dtype)
-    qref = torch.from_numpy(reference_queries(g, K)).cuda()
+    # R = 1 builds take no reference queries (the zero reference); R > 1 draws them.
+    qref = None if g.R == 1 else torch.from_numpy(reference_queries(g, K)).cuda()
     torch.cuda.synchronize()
     log(f"[bench] upload {Kd.numel() * 2 * Kd.element_size() / 1e9:.2f} GB: "
         f"{time.perf_counter() - t0:.1f} s")
@@ -519,7 +520,8 @@ def decode_maintenance(Z, g, gm, Kd, qref, tree, bscratch, reps: int = 200):
         Z.tree_update(gt, t_new - 1, Kd, qref, tree, bscratch)  # checked once through the binding
         torch.cuda.synchronize()
         args = (ctypes.byref(gt), ctypes.c_int64(t_new - 1), vp(Kd.data_ptr()),
-                vp(qref.data_ptr()), None, vp(tree.data_ptr()), vp(bscratch.data_ptr()), stream)
+                None if qref is None else vp(qref.data_ptr()), None, vp(tree.data_ptr()),
+                vp(bscratch.data_ptr()), stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         # A short device-side wait first, so that every call is queued before the first
         # runs: the events then time the device work, not the host's submission rate.
@@ -565,7 +567,7 @@ def run_block_1m(reps: int = 3):
     tb, sb = Z.tree_bytes(gm)
     tree = torch.empty(tb, dtype=torch.uint8, device="cuda")
     bsc = torch.empty(max(sb, 1), dtype=torch.uint8, device="cuda")
-    qref = torch.zeros((g.H_kv, g.R, g.d), dtype=torch.float32, device="cuda")
+    qref = None  # the zero reference (R = 1)
     sel = torch.empty((g.B, n_pos, g.H_q, cap), dtype=torch.int32, device="cuda")
     cnt = torch.empty((g.B, n_pos, g.H_q), dtype=torch.int32, device="cuda")
     stats = torch.empty((g.B, n_pos, g.H_q, g.L, 2), dtype=torch.int32, device="cuda")
@@ -826,7 +828,7 @@ def run_prefill(block: int, reps: int):
                                                             device="cuda")).to(Kd.dtype)[None]
     ctx = (t + 1).to(torch.int32)[None].contiguous()
     del j
-    qref = torch.zeros((g.H_kv, g.R, g.d), dtype=torch.float32, device="cuda")
+    qref = None  # the zero reference (R = 1)
     tb, sb = Z.tree_bytes(gm)
     tree = torch.empty(tb, dtype=torch.uint8, device="cuda")
     bsc = torch.empty(max(sb, 1), dtype=torch.uint8, device="cuda")
