@@ -544,10 +544,10 @@ def test_config2_full_size_all_steps(Z):
 
 def test_config3_full_size_bench_launch(Z):
     g = W.CONFIGS[3]
-    say("config 3 at full size (B=8, one position per call): 4 steps, every head of sequences "
-        "0 and 7")
+    say("config 3 at full size (B=8, one position per call): 4 steps, every head of all 8 "
+        "sequences (1024 heads, 32 oracle trees)")
     run_full_size(Z, g, n_pos=1, steps=4,
-                  picks=lambda s: [(b, 0, h) for b in (0, 7) for h in range(g.H_q)],
+                  picks=lambda s: [(b, 0, h) for b in range(g.B) for h in range(g.H_q)],
                   label="config 3")
 
 
